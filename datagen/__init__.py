@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs shared by the GPU path, the oracle, the tests and the bench.
+
+This module only draws and rounds random numbers; it contains none of the attention
+arithmetic (no feature map, no state, no normalisation), so that the oracle and the HIP
+path share nothing beyond their inputs.
+
+Recipe (the same for every workload):
+  * draws are IID standard normal in float64 from NumPy's ``Generator(PCG64(seed))``,
+    taken in the order q, k, v, each as one full C-order tensor;
+  * each tensor is multiplied by ``scale`` (1/sqrt(d) for the workloads whose inputs are
+    N(0, 1/d), 1.0 otherwise);
+  * the result is rounded once, to nearest-even, to the input dtype (bfloat16 or float32).
+    That rounded tensor is the one canonical input: the GPU receives it as is and the
+    oracle receives its exact float64 upcast.
+
+The pages publish no dataset and no benchmark suite; these draws stand in for the
+"IID Gaussian q, k, v" workloads the sizes below describe.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def normal(shape, seed: int, scale: float = 1.0, dtype: str = "bf16") -> torch.Tensor:
+    """One tensor of IID N(0, scale^2) values, rounded to ``dtype`` (CPU tensor)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal(size=tuple(shape), dtype=np.float64)
+    if scale != 1.0:
+        x *= scale
+    return torch.from_numpy(x).to(DTYPES[dtype])
+
+
+def qkv(B: int, H: int, N: int, d: int, dv: int, seed: int, scale: float = 1.0,
+        dtype: str = "bf16"):
+    """q, k: [B,H,N,d]; v: [B,H,N,dv]; drawn from one stream in the order q, k, v."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for shape in ((B, H, N, d), (B, H, N, d), (B, H, N, dv)):
+        x = g.standard_normal(size=shape, dtype=np.float64)
+        if scale != 1.0:
+            x *= scale
+        out.append(torch.from_numpy(x).to(DTYPES[dtype]))
+    return tuple(out)
+
+
+def qkv_cuda(B: int, H: int, N: int, d: int, dv: int, seed: int, scale: float = 1.0,
+             dtype: str = "bf16", device: str = "cuda"):
+    """Large inputs drawn directly on the device with torch's seeded Philox generator.
+
+    Used where a host draw would take minutes (the decode workload's per-step tokens and
+    its 4096-token prior). Same distribution as :func:`qkv`, different stream; a test that
+    needs the oracle on such data copies the device tensors back to the host.
+    """
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = []
+    for shape in ((B, H, N, d), (B, H, N, d), (B, H, N, dv)):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)
+        out.append(x.to(DTYPES[dtype]))
+    return tuple(out)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a bf16/fp32 tensor (both embed exactly in float64)."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    form: str          # "causal" | "global" | "decode"
+    B: int
+    H: int
+    N: int
+    d: int
+    dv: int
+    dtype: str
+    scale: float
+    seed: int
+    chunk: int = 0
+    steps: int = 1     # decode only
+    prior: int = 0     # decode only: tokens summed into the starting state
+
+    @property
+    def token_heads(self) -> int:
+        return self.B * self.H * self.N
+
+
+# The five workloads: sizes, dtypes and value distributions of the linear-attention
+# workloads this library is measured on (seed = 1000 + workload number).
+WORKLOADS = {
+    1: Workload("causal_b1h1n64_d16_f32", "causal", 1, 1, 64, 16, 16, "f32", 1.0, 1001),
+    2: Workload("causal_b4h8n2048_d64_bf16", "causal", 4, 8, 2048, 64, 64, "bf16",
+                1.0 / math.sqrt(64), 1002, chunk=64),
+    3: Workload("causal_b2h16n8192_d128_bf16", "causal", 2, 16, 8192, 128, 128, "bf16",
+                1.0 / math.sqrt(128), 1003),
+    4: Workload("global_b1h8n100000_d128_bf16", "global", 1, 8, 100000, 128, 128, "bf16",
+                1.0 / math.sqrt(128), 1004),
+    5: Workload("decode_b256h32_d128_bf16_state4096", "decode", 256, 32, 1, 128, 128, "bf16",
+                1.0 / math.sqrt(128), 1005, steps=1000, prior=4096),
+}

@@ -1,0 +1,126 @@
+"""float64 CPU oracle for normalized kernelized linear attention -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may use
+this package. It shares no code with the HIP library (``causal_linear_attention_la_amd``) and
+neither imports the other; the product path never falls back to it.
+
+Two independent formulations live here:
+  * ``oracle.c`` (wrapped below): the token-serial recurrence of the pages, in float64;
+  * ``brute.py``: the plain pairwise definition o_i = sum_j w_ij v_j / sum_j w_ij with
+    w_ij = phi(q_i) . phi(k_j), computed with NumPy over all pairs (tiny sizes only).
+``compare.py`` holds the error metric the parity tests use.
+
+Inputs are float64 NumPy arrays holding exactly the values the GPU saw (bf16/fp32 upcast
+exactly); shapes q, k [B,H,N,d], v [B,H,N,dv], S [B,H,d,dv], z [B,H,d].
+``mode`` = "elu1" applies phi(x) = ELU(x) + 1; "identity" takes q and k as already mapped
+(the convention of the pages' worked examples).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_DIR = Path(__file__).resolve().parent
+_SRC = _DIR / "oracle.c"
+_LIB = _DIR / "liboracle.so"
+_lib = None
+
+_MODES = {"elu1": 0, "identity": 1}
+
+
+def build(force: bool = False) -> Path:
+    """Compile oracle.c with gcc (float64, no FMA contraction, OpenMP over heads)."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(f".so.tmp{os.getpid()}")
+        subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+                        "-fPIC", "-shared", str(_SRC), "-o", str(tmp), "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(path):
+    lib = ctypes.CDLL(str(path))
+    P = ctypes.POINTER(ctypes.c_double)
+    L = ctypes.c_long
+    lib.oracle_causal.argtypes = [P, P, P, P, P, P, P, P, L, L, L, L, ctypes.c_int]
+    lib.oracle_global.argtypes = [P, P, P, P, P, P, P, P, L, L, L, L, ctypes.c_int]
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, L, L, L, ctypes.c_int]
+    lib.oracle_causal.restype = None
+    lib.oracle_global.restype = None
+    lib.oracle_decode.restype = None
+    lib.oracle_threads.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _bind(_LIB)
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def threads(lib=None) -> int:
+    """OpenMP threads the C oracle runs on."""
+    return int((lib or _load()).oracle_threads())
+
+
+def causal(q, k, v, S0=None, z0=None, mode: str = "elu1", lib=None):
+    """Causal recurrence. Returns (o, S_N, z_N, num, den).
+
+    S0, z0 (optional) are the state before the first token (zeros if omitted)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, H, N, d) and v.shape == (B, H, N, dv)
+    S = np.zeros((B, H, d, dv)) if S0 is None else _f64(S0).copy()
+    z = np.zeros((B, H, d)) if z0 is None else _f64(z0).copy()
+    o = np.empty((B, H, N, dv))
+    num = np.empty((B, H, N, dv))
+    den = np.empty((B, H, N))
+    (lib or _load()).oracle_causal(_p(q), _p(k), _p(v), _p(o), _p(num), _p(den), _p(S), _p(z),
+                          B * H, N, d, dv, _MODES[mode])
+    return o, S, z, num, den
+
+
+def global_(q, k, v, mode: str = "elu1", lib=None):
+    """Global (non-causal) form. Returns (o, S, z, num, den)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, N, d = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, H, N, d) and v.shape == (B, H, N, dv)
+    S = np.empty((B, H, d, dv))
+    z = np.empty((B, H, d))
+    o = np.empty((B, H, N, dv))
+    num = np.empty((B, H, N, dv))
+    den = np.empty((B, H, N))
+    (lib or _load()).oracle_global(_p(q), _p(k), _p(v), _p(o), _p(num), _p(den), _p(S), _p(z),
+                          B * H, N, d, dv, _MODES[mode])
+    return o, S, z, num, den
+
+
+def decode_step(q, k, v, S, z, mode: str = "elu1", lib=None):
+    """One recurrent step for every head; q, k [B,H,d] (or [B,H,1,d]), v [B,H,dv] (or
+    [B,H,1,dv]). Returns (o [B,H,dv], S', z'); the inputs S, z are not modified."""
+    S = _f64(S).copy()
+    z = _f64(z).copy()
+    B, H, d, dv = S.shape
+    q = _f64(q).reshape(B, H, d)
+    k = _f64(k).reshape(B, H, d)
+    v = _f64(v).reshape(B, H, dv)
+    o = np.empty((B, H, dv))
+    (lib or _load()).oracle_decode(_p(q), _p(k), _p(v), _p(o), _p(S), _p(z), B * H, d, dv,
+                          _MODES[mode])
+    return o, S, z
