@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the linear-attention hot path on one MI355X.
+
+One step = one causal prefill call (la_causal_fwd: phi on the loads, chunked matrix-core
+intra-chunk product, carried float32 state, normaliser, bf16 store, final state) over the
+workload B=2 H=16 N=8192 d=d_v=128 bf16, inputs IID N(0, 1/128), state out. K steps are timed
+between device synchronisations; input sets rotate over three copies (806 MB > the 256 MB
+last-level cache) so a step does not find its inputs cached by the previous one.
+
+Printed: one JSON line with the headline (token-heads per second), the HBM roofline of the
+prefill call measured with HIP events on its stream, the float64 oracle timed on the host, and
+the decode (B=256 H=32 d=128, 4096-token state) and global (B=1 H=8 N=100000) forms.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5e15         # flop/s, dense bf16 MFMA
+METRIC = "causal prefill tokens/s (B·H·N/s) at d=128 + %MFMA peak; decode step GB/s"
+
+
+def algo_prefill(B, H, N, d, dv, es=2):
+    """Algorithmic bytes and flops of one causal call: read q, k, v, write out, write the
+    final float32 state; 4*d*dv + 3*d + dv flops per token-head."""
+    th = B * H * N
+    byts = th * ((2 * d + dv) * es + dv * es) + B * H * (d * dv + d) * 4
+    flops = th * (4 * d * dv + 3 * d + dv)
+    return byts, flops
+
+
+def mfma_issued_prefill(B, H, N, P, d=128):
+    """Matrix-core flops the chunked kernels issue (16x16x32 bf16 = 16384 flops each) for
+    d = d_v = 128, chunk 64: per chunk 40 score + 48 intra + 128 state-read + 128 state-write
+    instructions in the output kernel, and 128 in the segment-sum kernel for segments 0..P-2."""
+    chunks = B * H * math.ceil(N / 64)
+    per_chunk = 40 + 48 + 128 + 128 + 128 * (P - 1) / P
+    return chunks * per_chunk * 16384
+
+
+def time_calls(fn, steps, warmup):
+    """Average ms per call measured with HIP events on the current (launch) stream."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(st)
+    for i in range(steps):
+        fn(i)
+    ev1.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / steps, wall
+
+
+def bench_prefill(args):
+    import torch
+    import causal_linear_attention_la_amd as la
+    import datagen
+
+    w = datagen.WORKLOADS[3]
+    dev = torch.device("cuda:0")
+    sets = []
+    for r in range(args.rotate):
+        q, k, v = datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed + 100 * r, w.scale, "bf16")
+        out = torch.empty_like(q)
+        # S and z share one allocation so that the zero fill a fresh sequence needs is one launch
+        state = torch.zeros(w.B * w.H * (w.d * w.dv + w.d), device=dev)
+        S = state[: w.B * w.H * w.d * w.dv].view(w.B, w.H, w.d, w.dv)
+        z = state[w.B * w.H * w.d * w.dv:].view(w.B, w.H, w.d)
+        sets.append((q, k, v, out, S, z, state))
+
+    def step(i):
+        q, k, v, out, S, z, state = sets[i % len(sets)]
+        state.zero_()
+        la.la_causal_fwd(q, k, v, out, S, z, chunk=args.chunk, seg_len=args.seg_len)
+
+    ms, wall = time_calls(step, args.steps, args.warmup)
+    # same buffers every step (inputs may stay in the last-level cache)
+    ms_hot, _ = time_calls(lambda i: step(0), args.steps, 2)
+    byts, flops = algo_prefill(w.B, w.H, w.N, w.d, w.dv)
+    P = math.ceil(w.N / (args.seg_len or _auto_seg(w.B * w.H, w.N)))
+    return w, ms, ms_hot, wall, byts, flops, P
+
+
+def _auto_seg(BH, N, chunk=64, target=512):
+    nchunks = math.ceil(N / chunk)
+    want = min(max(1, math.ceil(target / BH)), nchunks)
+    return math.ceil(nchunks / want) * chunk
+
+
+def bench_decode(args):
+    import torch
+    import causal_linear_attention_la_amd as la
+    import datagen
+
+    w = datagen.WORKLOADS[5]
+    dev = torch.device("cuda:0")
+    S = torch.empty(w.B, w.H, w.d, w.dv, device=dev)
+    z = torch.empty(w.B, w.H, w.d, device=dev)
+    # starting state: sums of phi(k) v^T over a 4096-token seeded prior, built with the
+    # library's global form (state only) in blocks of batch rows
+    blk = 16
+    for b0 in range(0, w.B, blk):
+        _, kp, vp = datagen.qkv_cuda(blk, w.H, w.prior, w.d, w.dv, w.seed * 1000 + b0, w.scale, "bf16")
+        la.la_global_fwd(None, kp, vp, None, S[b0:b0 + blk], z[b0:b0 + blk])
+        del kp, vp
+    steps = args.decode_steps
+    # fresh q, k, v for every step, drawn up front: [steps, B*H, 1, d] viewed as [steps, B, H, d]
+    toks = datagen.qkv_cuda(steps, w.B * w.H, 1, w.d, w.dv, w.seed + 1, w.scale, "bf16")
+    toks = [x.view(steps, w.B, w.H, -1) for x in toks]
+    out = torch.empty(w.B, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        la.la_decode_step(toks[0][i % steps], toks[1][i % steps], toks[2][i % steps], out, S, z)
+
+    ms, _ = time_calls(step, steps, 0)
+    heads = w.B * w.H
+    byts = heads * (2 * (w.d * w.dv + w.d) * 4 + (2 * w.d + w.dv) * 2 + w.dv * 2)
+    return w, ms, byts
+
+
+def bench_global(args):
+    import torch
+    import causal_linear_attention_la_amd as la
+    import datagen
+
+    w = datagen.WORKLOADS[4]
+    dev = torch.device("cuda:0")
+    q, k, v = datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale, "bf16")
+    out = torch.empty_like(q)
+    S = torch.empty(w.B, w.H, w.d, w.dv, device=dev)
+    z = torch.empty(w.B, w.H, w.d, device=dev)
+    ms, _ = time_calls(lambda i: la.la_global_fwd(q, k, v, out, S, z), max(5, args.steps // 2), 2)
+    th = w.B * w.H * w.N
+    byts = th * (4 * w.d * 2) + w.B * w.H * (w.d * w.dv + w.d) * 4
+    return w, ms, byts
+
+
+def cpu_baseline():
+    """The float64 oracle, as it stands, on the prefill workload's 32 heads (full size; about
+    10 s of CPU work on 8 host threads)."""
+    import datagen
+    import oracle
+
+    w = datagen.WORKLOADS[3]
+    heads = 32
+    q, k, v = datagen.qkv(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale, "bf16")
+    qd, kd, vd = (datagen.to_f64(x) for x in (q, k, v))
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.causal(qd, kd, vd)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": w.B * w.H * w.N / t, "unit": "tokens/s (B*H*N/s)", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"causal B={w.B} H={w.H} N={w.N} d=128 ({heads} heads, the whole workload), "
+                      f"float64 token-serial recurrence, median of 3 runs of {t:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--seg-len", dest="seg_len", type=int, default=0)
+    ap.add_argument("--rotate", type=int, default=3, help="input sets cycled over the steps")
+    ap.add_argument("--decode-steps", dest="decode_steps", type=int, default=1000)
+    ap.add_argument("--only", choices=["prefill", "decode", "global"], default=None,
+                    help="run one form only (for profiling); no JSON line")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the heads of this "
+              "workload shard across GPUs without communication, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.init()
+
+    if args.only:
+        fn = {"prefill": bench_prefill, "decode": bench_decode, "global": bench_global}[args.only]
+        r = fn(args)
+        print(f"{args.only}: {r[1]:.4f} ms/step", flush=True)
+        return
+
+    w, ms, ms_hot, wall, byts, flops, P = bench_prefill(args)
+    print(f"prefill: {ms * 1e3:.1f} us/step (hot {ms_hot * 1e3:.1f} us)", file=sys.stderr, flush=True)
+    th = w.B * w.H * w.N
+    value = th / (ms * 1e-3)
+    achieved = byts / (ms * 1e-3)
+    issued = mfma_issued_prefill(w.B, w.H, w.N, P)
+    wd, ms_d, byts_d = bench_decode(args)
+    print(f"decode: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    wg, ms_g, byts_g = bench_global(args)
+    print(f"global: {ms_g * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s (B*H*N/s)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "form": "causal", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "d_v": w.dv, "chunk": args.chunk or 64, "segments_per_head": P,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
+                   "input_sets_rotated": args.rotate},
+        "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
+                     "kernel": "la_causal_fwd call (segment sums + segment scan + causal output)",
+                     "algorithmic_bytes_per_call": byts},
+        "mfma": {"algorithmic_frac": flops / (ms * 1e-3) / BF16_PEAK,
+                 "issued_frac": issued / (ms * 1e-3) / BF16_PEAK,
+                 "peak_tflops": BF16_PEAK / 1e12},
+        "hot_cache_ms_per_step": ms_hot,
+        "decode": {"workload": wd.name, "us_per_step": ms_d * 1e3,
+                   "GB_per_s": byts_d / (ms_d * 1e-3) / 1e9,
+                   "hbm_frac": byts_d / (ms_d * 1e-3) / HBM_PEAK, "steps": args.decode_steps},
+        "global": {"workload": wg.name, "us_per_call": ms_g * 1e3,
+                   "token_heads_per_s": wg.B * wg.H * wg.N / (ms_g * 1e-3),
+                   "hbm_frac": byts_g / (ms_g * 1e-3) / HBM_PEAK},
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+"""Python binding of liblinattn: normalized kernelized linear attention on AMD MI355X.
+
+A thin ctypes layer over the C ABI in ``include/la.h``: it only reads tensor shapes, data
+pointers and the current HIP stream and passes them on. Every step of the computation runs in
+the library's HIP kernels. PyTorch supplies device memory and streams; nothing else.
+
+The entry points keep the C names:
+    la_causal_fwd(q, k, v, out, S=None, z=None, chunk=0, seg_len=0)
+    la_global_fwd(q, k, v, out, S, z, chunk=0)         # q, out may be None: state only
+    la_decode_step(q, k, v, out, S, z)
+with q, k [B,H,N,d], v, out [B,H,N,d_v] (bf16 or float32, contiguous, on the GPU),
+S [B,H,d,d_v] and z [B,H,d] float32. A non-zero status raises ``LAError``.
+
+If the shared library is missing or fails to load, importing this package raises: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = Path(os.environ.get("LINATTN_LIB", _PKG / "liblinattn.so"))
+
+LA_F32, LA_BF16 = 0, 1
+LA_OK, LA_EINVAL, LA_ENOTSUP, LA_EHIP = 0, 1, 2, 3
+
+# Every symbol include/la.h declares.
+EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_global_fwd", "la_decode_step",
+           "la_workspace_bytes", "la_strerror", "la_version")
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__(f"{fn}: status {status}: {strerror(status)}")
+
+
+def _load(path: Path):
+    if not path.exists():
+        raise ImportError(f"liblinattn not built: {path} is missing "
+                          "(run python -m causal_linear_attention_la_amd.build)")
+    lib = ctypes.CDLL(str(path))
+    vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+    core = [vp, vp, vp, vp, fp, fp, i, i, i, i, i, i]
+    lib.la_causal_fwd.argtypes = core + [i, vp]
+    lib.la_causal_fwd_seg.argtypes = core + [i, i, vp]
+    lib.la_global_fwd.argtypes = core + [i, vp]
+    lib.la_decode_step.argtypes = core + [i, vp]
+    for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_global_fwd", "la_decode_step"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.la_workspace_bytes.argtypes = [i] * 8 + [i]
+    lib.la_workspace_bytes.restype = ctypes.c_size_t
+    lib.la_strerror.argtypes = [i]
+    lib.la_strerror.restype = ctypes.c_char_p
+    lib.la_version.argtypes = []
+    lib.la_version.restype = ctypes.c_int
+    return lib
+
+
+lib = _load(LIB_PATH)
+
+
+def strerror(status: int) -> str:
+    return lib.la_strerror(int(status)).decode()
+
+
+def version() -> tuple:
+    v = lib.la_version()
+    return (v >> 16, (v >> 8) & 0xFF, v & 0xFF)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _check_tensors(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("liblinattn takes device tensors only")
+        if not t.is_contiguous():
+            raise ValueError("liblinattn takes contiguous tensors only")
+        if dev is not None and t.device != dev:
+            raise ValueError("all tensors must be on one device")
+        dev = t.device
+
+
+def _dims(q, k, v):
+    if k.dim() == 3:  # decode tensors given as [B, H, d]
+        B, H, d = k.shape
+        return B, H, 1, d, v.shape[-1]
+    B, H, N, d = k.shape
+    return B, H, N, d, v.shape[-1]
+
+
+def _check(status, fn):
+    if status != LA_OK:
+        raise LAError(status, fn)
+
+
+def la_causal_fwd(q, k, v, out, S=None, z=None, chunk: int = 0, seg_len: int = 0):
+    """Causal prefill (see include/la.h). S, z: optional float32 in/out state."""
+    _check_tensors(q, k, v, out, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    st = lib.la_causal_fwd_seg(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d,
+                               dv, chunk, seg_len, _dtype_code(k), _stream(k))
+    _check(st, "la_causal_fwd")
+    return out
+
+
+def la_global_fwd(q, k, v, out, S, z, chunk: int = 0):
+    """Global (non-causal) form; S, z are written. q and out may both be None."""
+    _check_tensors(q, k, v, out, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    st = lib.la_global_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d, dv,
+                           chunk, _dtype_code(k), _stream(k))
+    _check(st, "la_global_fwd")
+    return out
+
+
+def la_decode_step(q, k, v, out, S, z):
+    """One decode step; S, z are updated in place."""
+    _check_tensors(q, k, v, out, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    st = lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d, dv,
+                            0, _dtype_code(k), _stream(k))
+    _check(st, "la_decode_step")
+    return out
+
+
+def la_workspace_bytes(form: int, B: int, H: int, N: int, d: int, d_v: int, chunk: int = 0,
+                       seg_len: int = 0, dtype: int = LA_BF16) -> int:
+    return int(lib.la_workspace_bytes(form, B, H, N, d, d_v, chunk, seg_len, dtype))

@@ -1,0 +1,192 @@
+// k_state.hip -- state kernels of liblinattn: the joins between sequence segments and the
+// single-token decode step.
+//
+// Segment joins. The causal state is a prefix sum over tokens ("Linear Attention: From
+// Pairwise Reads to a Recurrent State", section "A recurrence need not force token-serial
+// training"), so the state before segment p is the initial state plus the sums of segments
+// 0..p-1; the global state is the sum of all segments ("Linear Attention Math", section "The
+// associativity trick, written out"). Each thread owns one float of the E = d*d_v + d
+// floats of a head's state and walks the P segment slots in order (fixed order: the result
+// does not depend on scheduling).
+//
+// Decode step ("Linear Attention Math", section "The recurrent form"): for each head,
+// S' = S + phi(k) v^T and z' = z + phi(k) are written back in place, then
+// out = phi(q)^T S' / phi(q)^T z'. One workgroup per head streams the float32 state once in
+// and once out with 16-byte accesses; the read phi(q)^T S' reuses the updated values while
+// they are in registers, so each state byte crosses HBM exactly twice.
+#include "la_device.h"
+#include "la_launch.h"
+
+namespace la {
+namespace {
+
+constexpr int NT = 256;
+
+__global__ __launch_bounds__(NT) void k_seg_scan(float *__restrict__ ws, const float *__restrict__ S0,
+                                                 const float *__restrict__ z0, int P, int d,
+                                                 int dv, int blocks_per_head)
+{
+    const int E = d * dv + d;
+    const int bh = blockIdx.x / blocks_per_head;
+    const int e = (blockIdx.x % blocks_per_head) * NT + threadIdx.x;
+    if (e >= E)
+        return;
+    float run = 0.f;
+    if (S0)
+        run = e < d * dv ? S0[(size_t)bh * d * dv + e] : z0[(size_t)bh * d + (e - d * dv)];
+    float *slot = ws + (size_t)bh * P * E + e;
+    for (int p = 0; p < P - 1; ++p) {
+        const float t = slot[(size_t)p * E];
+        slot[(size_t)p * E] = run;
+        run += t;
+    }
+    slot[(size_t)(P - 1) * E] = run;
+}
+
+__global__ __launch_bounds__(NT) void k_seg_total(const float *__restrict__ ws, float *__restrict__ S,
+                                                  float *__restrict__ z, int P, int d, int dv,
+                                                  int blocks_per_head)
+{
+    const int E = d * dv + d;
+    const int bh = blockIdx.x / blocks_per_head;
+    const int e = (blockIdx.x % blocks_per_head) * NT + threadIdx.x;
+    if (e >= E)
+        return;
+    const float *slot = ws + (size_t)bh * P * E + e;
+    float run = 0.f;
+    for (int p = 0; p < P; ++p)
+        run += slot[(size_t)p * E];
+    if (e < d * dv)
+        S[(size_t)bh * d * dv + e] = run;
+    else
+        z[(size_t)bh * d + (e - d * dv)] = run;
+}
+
+// One head per workgroup. Thread layout over the [D, DV] state: CG = DV/4 column groups of 4
+// floats, RP = 256/CG row phases; thread (rp, cg) owns rows rp, rp+RP, ... of columns
+// 4cg..4cg+3.
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T *__restrict__ k,
+                                               const T *__restrict__ v, T *__restrict__ out,
+                                               float *__restrict__ S, float *__restrict__ z)
+{
+    constexpr int CG = DV / 4, RP = NT / CG, RPT = (D + RP - 1) / RP;
+    __shared__ float skf[D], sqf[D];
+    __shared__ float red[RP][DV + 4];
+    __shared__ float sden[NT / 64];
+
+    const int tid = threadIdx.x, cg = tid % CG, rp = tid / CG;
+    const size_t bh = blockIdx.x;
+    f32x4 *Sh = reinterpret_cast<f32x4 *>(S + bh * D * DV);
+
+    // the head's state rows, all loads in flight before any use
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rp + RP * i;
+        if (r < D)
+            s[i] = Sh[r * CG + cg];
+    }
+
+    float part = 0.f;
+    if (tid < D) {
+        const float kf = phi_exact(Elem<T>::ld(k, bh * D + tid));
+        const float qf = phi_exact(Elem<T>::ld(q, bh * D + tid));
+        skf[tid] = kf;
+        sqf[tid] = qf;
+        const float zn = z[bh * D + tid] + kf;
+        z[bh * D + tid] = zn;
+        part = qf * zn;
+    }
+    part = wave_sum(part);
+    if ((tid & 63) == 0)
+        sden[tid >> 6] = part;
+    f32x4 vv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        vv[c] = Elem<T>::ld(v, bh * DV + 4 * cg + c);
+    __syncthreads();
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rp + RP * i;
+        if (r < D) {
+            const float kf = skf[r], qf = sqf[r];
+            f32x4 sn;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                sn[c] = s[i][c] + kf * vv[c];
+                acc[c] += qf * sn[c];
+            }
+            Sh[r * CG + cg] = sn;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        red[rp][4 * cg + c] = acc[c];
+    __syncthreads();
+    if (tid < DV) {
+        float num = 0.f;
+#pragma unroll
+        for (int i = 0; i < RP; ++i)
+            num += red[i][tid];
+        float den = 0.f;
+#pragma unroll
+        for (int w = 0; w < NT / 64; ++w)
+            den += sden[w];
+        Elem<T>::st(out, bh * DV + tid, num / den);
+    }
+}
+
+template <typename T>
+hipError_t decode_t(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                    int BH, int d, int dv, hipStream_t st)
+{
+    const dim3 grid((unsigned)BH), block(NT);
+    const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
+            *vv = static_cast<const T *>(v);
+    T *oo = static_cast<T *>(out);
+#define LA_DEC(DD, VV)                                                                          \
+    if (d == DD && dv == VV) {                                                                  \
+        hipLaunchKernelGGL((k_decode<T, DD, VV>), grid, block, 0, st, qq, kk, vv, oo, S, z);    \
+        return hipGetLastError();                                                               \
+    }
+#define LA_DEC_ROW(DD) LA_DEC(DD, 16) LA_DEC(DD, 32) LA_DEC(DD, 64) LA_DEC(DD, 128)
+    LA_DEC_ROW(16)
+    LA_DEC_ROW(32)
+    LA_DEC_ROW(64)
+    LA_DEC_ROW(128)
+#undef LA_DEC_ROW
+#undef LA_DEC
+    return hipErrorInvalidValue;
+}
+
+} // namespace
+
+hipError_t seg_exclusive_scan(float *ws, const float *S0, const float *z0, int BH, int P, int d,
+                              int dv, hipStream_t st)
+{
+    const int E = d * dv + d, bph = (E + NT - 1) / NT;
+    hipLaunchKernelGGL(k_seg_scan, dim3((unsigned)(BH * bph)), dim3(NT), 0, st, ws, S0, z0, P, d,
+                       dv, bph);
+    return hipGetLastError();
+}
+
+hipError_t seg_total(const float *ws, float *S, float *z, int BH, int P, int d, int dv,
+                     hipStream_t st)
+{
+    const int E = d * dv + d, bph = (E + NT - 1) / NT;
+    hipLaunchKernelGGL(k_seg_total, dim3((unsigned)(BH * bph)), dim3(NT), 0, st, ws, S, z, P, d,
+                       dv, bph);
+    return hipGetLastError();
+}
+
+hipError_t decode_step(bool bf16, const void *q, const void *k, const void *v, void *out,
+                       float *S, float *z, int BH, int d, int dv, hipStream_t st)
+{
+    return bf16 ? decode_t<bf16_t>(q, k, v, out, S, z, BH, d, dv, st)
+                : decode_t<float>(q, k, v, out, S, z, BH, d, dv, st);
+}
+
+} // namespace la

@@ -1,0 +1,254 @@
+// k_valu.hip -- vector-ALU kernels of liblinattn for the shapes the matrix-core kernels do not
+// take: float32 inputs (all arithmetic stays in float32) and any d, d_v in {16, 32, 64, 128}
+// with either input dtype. One workgroup of 256 threads per (segment, head); the float32
+// state of the head lives in LDS; chunks of CH in {16, 32} tokens.
+//
+// Per chunk, with Qf = phi(Q_c), Kf = phi(K_c) and the state S, z before the chunk:
+//   A[i][j] = Qf_i . Kf_j for j <= i (inclusive causal mask), 0 otherwise
+//   den_i   = sum_j A[i][j] + Qf_i . z,   num_i = sum_j A[i][j] v_j + Qf_i^T S
+//   out_i   = num_i / den_i;   then S += Kf^T V_c, z += colsum(Kf)
+// -- the recurrence of "Linear Attention Math", section "The recurrent form: a running KV
+// state", grouped by chunk. With causal = false the kernel is the global read
+// out_i = Qf_i^T S / Qf_i . z of section "The associativity trick, written out".
+#include "la_device.h"
+#include "la_launch.h"
+
+namespace la {
+namespace {
+
+constexpr int NT = 256;
+
+// dynamic LDS carve-up (float32): S [d*dv] | z [d] | Qf [CH*d] | Kf [CH*d] | V [CH*dv] |
+// A [CH*CH] | den [CH]
+struct Lay {
+    int oS, oz, oQ, oK, oV, oA, oden, total;
+    __host__ __device__ Lay(int d, int dv, int ch)
+    {
+        oS = 0;
+        oz = oS + d * dv;
+        oQ = oz + d;
+        oK = oQ + ch * d;
+        oV = oK + ch * d;
+        oA = oV + ch * dv;
+        oden = oA + ch * ch;
+        total = oden + ch;
+    }
+};
+
+template <typename T>
+__global__ __launch_bounds__(NT) void k_agg_valu(const T *__restrict__ k, const T *__restrict__ v,
+                                                 float *__restrict__ dstS,
+                                                 float *__restrict__ dstz, long sstride,
+                                                 long zstride, int N, int d, int dv, int ch,
+                                                 int L, int nseg, int P)
+{
+    extern __shared__ float sm[];
+    const Lay lay(d, dv, ch);
+    float *sS = sm + lay.oS, *sz = sm + lay.oz, *sK = sm + lay.oK, *sV = sm + lay.oV;
+    const int tid = threadIdx.x;
+    const int p = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+    const int tb = p * L, te = min(N, tb + L);
+    const T *kb = k + (size_t)bh * N * d;
+    const T *vb = v + (size_t)bh * N * dv;
+
+    for (int e = tid; e < d * dv; e += NT)
+        sS[e] = 0.f;
+    for (int f = tid; f < d; f += NT)
+        sz[f] = 0.f;
+    for (int t0 = tb; t0 < te; t0 += ch) {
+        const int nvalid = min(ch, te - t0);
+        __syncthreads();
+        for (int e = tid; e < ch * d; e += NT) {
+            const int j = e / d;
+            sK[e] = j < nvalid ? phi_exact(Elem<T>::ld(kb, (size_t)(t0 + j) * d + e % d)) : 0.f;
+        }
+        for (int e = tid; e < ch * dv; e += NT) {
+            const int j = e / dv;
+            sV[e] = j < nvalid ? Elem<T>::ld(vb, (size_t)(t0 + j) * dv + e % dv) : 0.f;
+        }
+        __syncthreads();
+        for (int e = tid; e < d * dv; e += NT) {
+            const int f = e / dv, c = e % dv;
+            float s = 0.f;
+            for (int j = 0; j < ch; ++j)
+                s += sK[j * d + f] * sV[j * dv + c];
+            sS[e] += s;
+        }
+        for (int f = tid; f < d; f += NT) {
+            float s = 0.f;
+            for (int j = 0; j < ch; ++j)
+                s += sK[j * d + f];
+            sz[f] += s;
+        }
+    }
+    __syncthreads();
+    float *S = dstS + ((long)bh * P + p) * sstride;
+    for (int e = tid; e < d * dv; e += NT)
+        S[e] = sS[e];
+    for (int f = tid; f < d; f += NT)
+        dstz[((long)bh * P + p) * zstride + f] = sz[f];
+}
+
+template <typename T, bool CAUSAL>
+__global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const T *__restrict__ k,
+                                                 const T *__restrict__ v, T *__restrict__ out,
+                                                 const float *__restrict__ preS,
+                                                 const float *__restrict__ prez, long pstride,
+                                                 long pzstride, int pslots,
+                                                 float *__restrict__ Sout,
+                                                 float *__restrict__ zout, int N, int d, int dv,
+                                                 int ch, int L, int P)
+{
+    extern __shared__ float sm[];
+    const Lay lay(d, dv, ch);
+    float *sS = sm + lay.oS, *sz = sm + lay.oz, *sQ = sm + lay.oQ, *sK = sm + lay.oK;
+    float *sV = sm + lay.oV, *sA = sm + lay.oA, *sden = sm + lay.oden;
+    const int tid = threadIdx.x;
+    const int p = blockIdx.x % P, bh = blockIdx.x / P;
+    const int tb = p * L, te = min(N, tb + L);
+    const T *qb = q + (size_t)bh * N * d;
+    const T *kb = CAUSAL ? k + (size_t)bh * N * d : nullptr;
+    const T *vb = CAUSAL ? v + (size_t)bh * N * dv : nullptr;
+    T *ob = out + (size_t)bh * N * dv;
+
+    const long slot = (long)bh * pslots + min(p, pslots - 1);
+    const float *S0 = preS ? preS + slot * pstride : nullptr;
+    const float *z0 = preS ? prez + slot * pzstride : nullptr;
+    for (int e = tid; e < d * dv; e += NT)
+        sS[e] = S0 ? S0[e] : 0.f;
+    for (int f = tid; f < d; f += NT)
+        sz[f] = z0 ? z0[f] : 0.f;
+
+    for (int t0 = tb; t0 < te; t0 += ch) {
+        const int nvalid = min(ch, te - t0);
+        __syncthreads();
+        for (int e = tid; e < ch * d; e += NT) {
+            const int j = e / d;
+            const size_t gi = (size_t)(t0 + j) * d + e % d;
+            sQ[e] = j < nvalid ? phi_exact(Elem<T>::ld(qb, gi)) : 0.f;
+            if (CAUSAL)
+                sK[e] = j < nvalid ? phi_exact(Elem<T>::ld(kb, gi)) : 0.f;
+        }
+        if (CAUSAL)
+            for (int e = tid; e < ch * dv; e += NT) {
+                const int j = e / dv;
+                sV[e] = j < nvalid ? Elem<T>::ld(vb, (size_t)(t0 + j) * dv + e % dv) : 0.f;
+            }
+        __syncthreads();
+        if (CAUSAL)
+            for (int e = tid; e < ch * ch; e += NT) {
+                const int i = e / ch, j = e % ch;
+                float s = 0.f;
+                if (j <= i)
+                    for (int f = 0; f < d; ++f)
+                        s += sQ[i * d + f] * sK[j * d + f];
+                sA[e] = s;
+            }
+        __syncthreads();
+        for (int i = tid; i < ch; i += NT) {
+            float s = 0.f;
+            for (int f = 0; f < d; ++f)
+                s += sQ[i * d + f] * sz[f];
+            if (CAUSAL)
+                for (int j = 0; j <= i; ++j)
+                    s += sA[i * ch + j];
+            sden[i] = s;
+        }
+        __syncthreads();
+        for (int e = tid; e < ch * dv; e += NT) {
+            const int i = e / dv, c = e % dv;
+            if (i >= nvalid)
+                continue;
+            float s = 0.f;
+            for (int f = 0; f < d; ++f)
+                s += sQ[i * d + f] * sS[f * dv + c];
+            if (CAUSAL)
+                for (int j = 0; j <= i; ++j)
+                    s += sA[i * ch + j] * sV[j * dv + c];
+            Elem<T>::st(ob, (size_t)(t0 + i) * dv + c, s / sden[i]);
+        }
+        if (CAUSAL) {
+            __syncthreads();
+            for (int e = tid; e < d * dv; e += NT) {
+                const int f = e / dv, c = e % dv;
+                float s = 0.f;
+                for (int j = 0; j < ch; ++j)
+                    s += sK[j * d + f] * sV[j * dv + c];
+                sS[e] += s;
+            }
+            for (int f = tid; f < d; f += NT) {
+                float s = 0.f;
+                for (int j = 0; j < ch; ++j)
+                    s += sK[j * d + f];
+                sz[f] += s;
+            }
+        }
+    }
+    if (CAUSAL && Sout && p == P - 1) {
+        __syncthreads();
+        for (int e = tid; e < d * dv; e += NT)
+            Sout[(size_t)bh * d * dv + e] = sS[e];
+        for (int f = tid; f < d; f += NT)
+            zout[(size_t)bh * d + f] = sz[f];
+    }
+}
+
+} // namespace
+
+hipError_t agg_valu(bool bf16, const void *k, const void *v, float *dstS, float *dstz,
+                    long sstride, long zstride, int BH, int N, int d, int dv, int chunk, int L,
+                    int nseg, int P, hipStream_t st)
+{
+    const Lay lay(d, dv, chunk);
+    const size_t lds = sizeof(float) * lay.total;
+    const dim3 grid((unsigned)(BH * nseg)), block(NT);
+    hipError_t e = bf16 ? hipFuncSetAttribute(reinterpret_cast<const void *>(k_agg_valu<bf16_t>),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+                        : hipFuncSetAttribute(reinterpret_cast<const void *>(k_agg_valu<float>),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+        return e;
+    if (bf16)
+        hipLaunchKernelGGL(k_agg_valu<bf16_t>, grid, block, lds, st, static_cast<const bf16_t *>(k),
+                           static_cast<const bf16_t *>(v), dstS, dstz, sstride, zstride, N, d, dv,
+                           chunk, L, nseg, P);
+    else
+        hipLaunchKernelGGL(k_agg_valu<float>, grid, block, lds, st, static_cast<const float *>(k),
+                           static_cast<const float *>(v), dstS, dstz, sstride, zstride, N, d, dv,
+                           chunk, L, nseg, P);
+    return hipGetLastError();
+}
+
+template <typename T, bool CAUSAL>
+hipError_t out_valu_t(const void *q, const void *k, const void *v, void *out, const float *preS,
+                      const float *prez, long pstride, long pzstride, int pslots, float *Sout,
+                      float *zout, int BH, int N, int d, int dv, int chunk, int L, int P,
+                      hipStream_t st)
+{
+    const size_t lds = sizeof(float) * Lay(d, dv, chunk).total;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_out_valu<T, CAUSAL>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((k_out_valu<T, CAUSAL>), dim3((unsigned)(BH * P)), dim3(NT), lds, st,
+                       static_cast<const T *>(q), static_cast<const T *>(k),
+                       static_cast<const T *>(v), static_cast<T *>(out), preS, prez, pstride,
+                       pzstride, pslots, Sout, zout, N, d, dv, chunk, L, P);
+    return hipGetLastError();
+}
+
+hipError_t out_valu(bool bf16, bool causal, const void *q, const void *k, const void *v,
+                    void *out, const float *preS, const float *prez, long pstride,
+                    long pzstride, int pslots, float *Sout, float *zout, int BH, int N, int d,
+                    int dv, int chunk, int L, int P, hipStream_t st)
+{
+    auto f = bf16 ? (causal ? out_valu_t<bf16_t, true> : out_valu_t<bf16_t, false>)
+                  : (causal ? out_valu_t<float, true> : out_valu_t<float, false>);
+    return f(q, k, v, out, preS, prez, pstride, pzstride, pslots, Sout, zout, BH, N, d, dv, chunk,
+             L, P, st);
+}
+
+// Largest dynamic LDS the vector-ALU kernels take (d = d_v = 128, chunk 32): 118,912 bytes.
+size_t valu_lds_bytes(int d, int dv, int chunk) { return sizeof(float) * Lay(d, dv, chunk).total; }
+
+} // namespace la

@@ -1,0 +1,329 @@
+// la_api.hip -- the C ABI of liblinattn (declared in include/la.h): argument validation,
+// kernel selection, sequence split and stream-ordered workspace.
+#include "la.h"
+#include "la_launch.h"
+
+#include <mutex>
+#include <stdint.h>
+
+namespace {
+
+constexpr int LA_VERSION = (0 << 16) | (1 << 8) | 0;
+
+enum Form { CAUSAL = 0, GLOBAL = 1, DECODE = 2 };
+
+// Target number of workgroups for one launch: two per compute unit of an MI355X (256 CUs).
+constexpr long kTargetGroups = 512;
+
+bool dim_ok(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
+
+struct Span {
+    uintptr_t lo, hi; // [lo, hi); empty when lo == hi
+};
+
+Span span(const void *p, size_t bytes)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return p ? Span{a, a + bytes} : Span{0, 0};
+}
+
+bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+    bool mfma;  // matrix-core family
+    int chunk;  // tokens per chunk
+    int L;      // tokens per segment
+    int P;      // segments per head
+    long BH;
+    size_t ws_bytes;
+};
+
+// Shape/size checks and the launch plan (no pointer checks). Returns LA_OK or a status.
+int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_len, int dtype,
+              Plan *plan)
+{
+    if (dtype != LA_F32 && dtype != LA_BF16)
+        return LA_EINVAL;
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || dv <= 0 || chunk < 0 || seg_len < 0)
+        return LA_EINVAL;
+    if (form == DECODE && N != 1)
+        return LA_EINVAL;
+    if (!dim_ok(d) || !dim_ok(dv))
+        return LA_ENOTSUP;
+    const size_t BH = (size_t)B * (size_t)H;
+    // 32-bit grid and per-head index arithmetic
+    if (BH > (size_t)INT32_MAX / 8 || (size_t)N * (size_t)(d > dv ? d : dv) > (size_t)INT32_MAX)
+        return LA_ENOTSUP;
+
+    Plan pl{};
+    pl.BH = (long)BH;
+    if (form == DECODE) {
+        *plan = pl;
+        return LA_OK;
+    }
+    const bool mfma_ok = dtype == LA_BF16 && d == dv && (d == 64 || d == 128);
+    if (chunk == 0) {
+        pl.mfma = mfma_ok;
+        pl.chunk = mfma_ok ? 64 : 32;
+    } else if (chunk == 64) {
+        if (!mfma_ok)
+            return LA_ENOTSUP;
+        pl.mfma = true;
+        pl.chunk = 64;
+    } else if (chunk == 16 || chunk == 32) {
+        pl.mfma = false;
+        pl.chunk = chunk;
+    } else {
+        return LA_ENOTSUP;
+    }
+
+    const long nchunks = (N + pl.chunk - 1) / pl.chunk;
+    if (seg_len > 0) {
+        if (seg_len % pl.chunk != 0)
+            return LA_ENOTSUP;
+        pl.L = seg_len;
+    } else {
+        long want = (kTargetGroups + (long)BH - 1) / (long)BH; // segments per head
+        if (want > nchunks)
+            want = nchunks;
+        pl.L = (int)((nchunks + want - 1) / want) * pl.chunk;
+    }
+    pl.P = (int)((N + (long)pl.L - 1) / pl.L);
+    if ((size_t)pl.P * BH > (size_t)INT32_MAX / 8)
+        return LA_ENOTSUP;
+    const size_t E = (size_t)d * dv + d;
+    pl.ws_bytes = pl.P > 1 ? BH * (size_t)pl.P * E * sizeof(float) : 0;
+    *plan = pl;
+    return LA_OK;
+}
+
+// Full validation of an entry point's arguments: pointers, then make_plan.
+int validate(Form form, const void *q, const void *k, const void *v, void *out, float *S,
+             float *z, int B, int H, int N, int d, int dv, int chunk, int seg_len, int dtype,
+             Plan *plan)
+{
+    if (!k || !v)
+        return LA_EINVAL;
+    if (form == GLOBAL) {
+        if ((q == nullptr) != (out == nullptr))
+            return LA_EINVAL;
+    } else if (!q || !out) {
+        return LA_EINVAL;
+    }
+    if (form == CAUSAL && ((S == nullptr) != (z == nullptr)))
+        return LA_EINVAL;
+    if (form != CAUSAL && (!S || !z))
+        return LA_EINVAL;
+    const void *ptrs[] = {q, k, v, out, S, z};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return LA_EINVAL;
+    const int s = make_plan(form, B, H, N, d, dv, chunk, seg_len, dtype, plan);
+    if (s != LA_OK)
+        return s;
+
+    const size_t es = dtype == LA_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * (size_t)H;
+    const Span sq = span(q, BH * N * d * es), sk = span(k, BH * N * d * es);
+    const Span sv = span(v, BH * N * dv * es), so = span(out, BH * N * dv * es);
+    const Span sS = span(S, BH * d * dv * 4), sz = span(z, BH * d * 4);
+    for (Span in : {sq, sk, sv})
+        if (overlap(so, in))
+            return LA_EINVAL;
+    for (Span st : {sS, sz})
+        for (Span o : {sq, sk, sv, so})
+            if (overlap(st, o))
+                return LA_EINVAL;
+    if (overlap(sS, sz))
+        return LA_EINVAL;
+    return LA_OK;
+}
+
+// Private stream-ordered pool per device, kept for the life of the process so that temporary
+// segment states are recycled between calls instead of returned to the driver each time.
+hipError_t pool_for_current_device(hipMemPool_t *out)
+{
+    static std::mutex mu;
+    static hipMemPool_t pools[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= 64)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        e = hipMemPoolCreate(&p, &props);
+        if (e != hipSuccess)
+            return e;
+        uint64_t keep = UINT64_MAX;
+        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess)
+            return e;
+        pools[dev] = p;
+    }
+    *out = pools[dev];
+    return hipSuccess;
+}
+
+struct Workspace {
+    float *ptr = nullptr;
+    hipStream_t st = nullptr;
+    hipError_t init(size_t bytes, hipStream_t stream)
+    {
+        st = stream;
+        if (!bytes)
+            return hipSuccess;
+        hipMemPool_t pool;
+        hipError_t e = pool_for_current_device(&pool);
+        if (e != hipSuccess)
+            return e;
+        return hipMallocFromPoolAsync(reinterpret_cast<void **>(&ptr), bytes, pool, stream);
+    }
+    ~Workspace()
+    {
+        if (ptr)
+            (void)hipFreeAsync(ptr, st);
+    }
+};
+
+int run_causal(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+               int N, int d, int dv, bool bf16, const Plan &pl, hipStream_t st)
+{
+    const int BH = (int)pl.BH, P = pl.P, L = pl.L;
+    const long E = (long)d * dv + d;
+    Workspace ws;
+    if (ws.init(pl.ws_bytes, st) != hipSuccess)
+        return LA_EHIP;
+    hipError_t e = hipSuccess;
+    const float *preS = S, *prez = z; // P == 1: the caller's state (or none) is the prefix
+    long ps = (long)d * dv, pzs = d;
+    if (P > 1) {
+        // sums of segments 0..P-2, then the exclusive prefix over segments in place
+        e = pl.mfma ? la::agg_mfma(d, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L, P - 1, P, st)
+                    : la::agg_valu(bf16, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, d, dv,
+                                   pl.chunk, L, P - 1, P, st);
+        if (e == hipSuccess)
+            e = la::seg_exclusive_scan(ws.ptr, S, z, BH, P, d, dv, st);
+        preS = ws.ptr;
+        prez = ws.ptr + (long)d * dv;
+        ps = pzs = E;
+    }
+    if (e == hipSuccess)
+        e = pl.mfma ? la::causal_mfma(d, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N, L, P, st)
+                    : la::out_valu(bf16, true, q, k, v, out, preS, prez, ps, pzs, P > 1 ? P : 1, S,
+                                   z, BH, N, d, dv, pl.chunk, L, P, st);
+    return e == hipSuccess ? LA_OK : LA_EHIP;
+}
+
+int run_global(const void *q, const void *k, const void *v, void *out, float *S, float *z, int N,
+               int d, int dv, bool bf16, const Plan &pl, hipStream_t st)
+{
+    const int BH = (int)pl.BH, P = pl.P, L = pl.L;
+    const long E = (long)d * dv + d;
+    Workspace ws;
+    if (ws.init(pl.ws_bytes, st) != hipSuccess)
+        return LA_EHIP;
+    hipError_t e;
+    if (P > 1) {
+        e = pl.mfma ? la::agg_mfma(d, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L, P, P, st)
+                    : la::agg_valu(bf16, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, d, dv,
+                                   pl.chunk, L, P, P, st);
+        if (e == hipSuccess)
+            e = la::seg_total(ws.ptr, S, z, BH, P, d, dv, st);
+    } else {
+        e = pl.mfma ? la::agg_mfma(d, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1, st)
+                    : la::agg_valu(bf16, k, v, S, z, (long)d * dv, d, BH, N, d, dv, pl.chunk, L, 1,
+                                   1, st);
+    }
+    if (e == hipSuccess && q)
+        e = pl.mfma ? la::global_read_mfma(d, q, out, S, z, BH, N, L, P, st)
+                    : la::out_valu(bf16, false, q, nullptr, nullptr, out, S, z, (long)d * dv, d, 1,
+                                   nullptr, nullptr, BH, N, d, dv, pl.chunk, L, P, st);
+    return e == hipSuccess ? LA_OK : LA_EHIP;
+}
+
+} // namespace
+
+extern "C" {
+
+int la_causal_fwd_seg(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                      int B, int H, int N, int d, int d_v, int chunk, int seg_len, la_dtype dtype,
+                      hipStream_t stream)
+{
+    Plan pl;
+    const int s = validate(CAUSAL, q, k, v, out, S, z, B, H, N, d, d_v, chunk, seg_len, dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    return run_causal(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream);
+}
+
+int la_causal_fwd(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                  int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype, hipStream_t stream)
+{
+    return la_causal_fwd_seg(q, k, v, out, S, z, B, H, N, d, d_v, chunk, 0, dtype, stream);
+}
+
+int la_global_fwd(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                  int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype, hipStream_t stream)
+{
+    Plan pl;
+    const int s = validate(GLOBAL, q, k, v, out, S, z, B, H, N, d, d_v, chunk, 0, dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    return run_global(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream);
+}
+
+int la_decode_step(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                   int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype,
+                   hipStream_t stream)
+{
+    (void)chunk;
+    Plan pl;
+    const int s = validate(DECODE, q, k, v, out, S, z, B, H, N, d, d_v, 0, 0, dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    const hipError_t e = la::decode_step(dtype == LA_BF16, q, k, v, out, S, z, (int)pl.BH, d, d_v, stream);
+    return e == hipSuccess ? LA_OK : LA_EHIP;
+}
+
+size_t la_workspace_bytes(int form, int B, int H, int N, int d, int d_v, int chunk, int seg_len,
+                          la_dtype dtype)
+{
+    if (form != 0 && form != 1)
+        return 0;
+    Plan pl;
+    if (make_plan(form == 0 ? CAUSAL : GLOBAL, B, H, N, d, d_v, chunk, seg_len, dtype, &pl) != LA_OK)
+        return 0;
+    return pl.ws_bytes;
+}
+
+const char *la_strerror(int status)
+{
+    switch (status) {
+    case LA_OK:
+        return "success";
+    case LA_EINVAL:
+        return "invalid argument (null, misaligned or overlapping buffer, non-positive size, "
+               "decode with N != 1, or unknown dtype)";
+    case LA_ENOTSUP:
+        return "unsupported shape or chunk (d and d_v must be 16, 32, 64 or 128; chunk 0, 16, "
+               "32 or 64 as the shape allows)";
+    case LA_EHIP:
+        return "HIP runtime error (allocation or kernel launch failed)";
+    default:
+        return "unknown status";
+    }
+}
+
+int la_version(void) { return LA_VERSION; }
+
+} // extern "C"

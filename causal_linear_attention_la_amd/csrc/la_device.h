@@ -1,0 +1,65 @@
+// la_device.h -- device-side helpers shared by the liblinattn kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Storage tag for bfloat16 tensors (the ABI passes raw 16-bit words).
+struct bf16_t {
+    uint16_t bits;
+};
+
+// ---- bfloat16 <-> float ------------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> two bf16 (round to nearest even) packed low/high in one dword.
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi)
+{
+    f32x2 f = {lo, hi};
+    bf16x2 b = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ uint16_t to_bf(float x)
+{
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// ---- feature map ------------------------------------------------------------------------
+// phi(x) = ELU(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise (strictly positive).
+// The fast form feeds bf16 matrix-core operands (its result is rounded to bf16 right after);
+// the accurate form is used where the arithmetic stays in float32.
+__device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ float phi_exact(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+// ---- generic element access for the vector-ALU kernels -----------------------------------
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ static float ld(const float *p, size_t i) { return p[i]; }
+    __device__ static void st(float *p, size_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<bf16_t> {
+    __device__ static float ld(const bf16_t *p, size_t i) { return __uint_as_float(uint32_t(p[i].bits) << 16); }
+    __device__ static void st(bf16_t *p, size_t i, float x) { p[i].bits = to_bf(x); }
+};
+
+// ---- wave-level reductions (64 lanes) ----------------------------------------------------
+__device__ __forceinline__ float wave_sum(float x)
+{
+    for (int off = 32; off > 0; off >>= 1)
+        x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+} // namespace la

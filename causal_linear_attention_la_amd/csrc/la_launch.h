@@ -1,0 +1,58 @@
+// la_launch.h -- internal launchers behind the C ABI (not exported).
+//
+// Sequence split shared by the causal and global forms: each (b, h) pair -- "bh", 0..B*H-1 --
+// is cut into P segments of L tokens (L a multiple of the chunk; the last segment may be
+// shorter). Per-segment partial states live in a float32 workspace of B*H*P slots, slot
+// (bh, p) at offset (bh * P + p) * E floats with E = d * d_v + d: the d x d_v state first
+// (row-major, rows = key features), then the d-vector z.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace la {
+
+// ---- matrix-core family: bf16, d == d_v in {64, 128}, chunk 64 ---------------------------
+// Segment sums dS = phi(K_seg)^T V_seg, dz = phi(K_seg)^T 1 of segments p < nseg of every
+// head, written to dstS + (bh * P + p) * sstride and dstz + (bh * P + p) * zstride.
+hipError_t agg_mfma(int D, const void *k, const void *v, float *dstS, float *dstz,
+                    long sstride, long zstride, int BH, int N, int L, int nseg, int P,
+                    hipStream_t st);
+// Causal outputs of all P segments. Segment p starts from the state at preS/prez +
+// (bh * P + p) * stride (zero state if preS is null). The last segment writes the final
+// state to Sout/zout when they are non-null.
+hipError_t causal_mfma(int D, const void *q, const void *k, const void *v, void *out,
+                       const float *preS, const float *prez, long pstride, long pzstride,
+                       float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st);
+// Global read: out = phi(Q) S / phi(Q) z for every token, S/z per head ([BH, D, D], [BH, D]).
+hipError_t global_read_mfma(int D, const void *q, void *out, const float *S, const float *z,
+                            int BH, int N, int L, int P, hipStream_t st);
+
+// ---- vector-ALU family: any d, d_v in {16, 32, 64, 128}, float32 or bf16, chunk 16/32 ----
+hipError_t agg_valu(bool bf16, const void *k, const void *v, float *dstS, float *dstz,
+                    long sstride, long zstride, int BH, int N, int d, int dv, int chunk, int L,
+                    int nseg, int P, hipStream_t st);
+// Segment p of head bh starts from the state in slot bh * pslots + min(p, pslots - 1) of
+// preS/prez (zero state if preS is null). causal = false gives the global read (pslots = 1:
+// every segment reads the head's full state; nothing is updated).
+hipError_t out_valu(bool bf16, bool causal, const void *q, const void *k, const void *v,
+                    void *out, const float *preS, const float *prez, long pstride,
+                    long pzstride, int pslots, float *Sout, float *zout, int BH, int N, int d,
+                    int dv, int chunk, int L, int P, hipStream_t st);
+
+// Dynamic LDS bytes of the vector-ALU kernels for this shape.
+size_t valu_lds_bytes(int d, int dv, int chunk);
+
+// ---- segment joins -----------------------------------------------------------------------
+// In place: slots 0..P-2 hold segment sums on entry; on return slot p (0..P-1) holds the
+// state before segment p (the sum of earlier segments plus the optional initial state).
+hipError_t seg_exclusive_scan(float *ws, const float *S0, const float *z0, int BH, int P,
+                              int d, int dv, hipStream_t st);
+// S, z = sum of the P slots (fixed order p = 0..P-1).
+hipError_t seg_total(const float *ws, float *S, float *z, int BH, int P, int d, int dv,
+                     hipStream_t st);
+
+// ---- decode ------------------------------------------------------------------------------
+hipError_t decode_step(bool bf16, const void *q, const void *k, const void *v, void *out,
+                       float *S, float *z, int BH, int d, int dv, hipStream_t st);
+
+} // namespace la

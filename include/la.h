@@ -1,0 +1,136 @@
+/*
+ * la.h -- C ABI of liblinattn, normalized kernelized linear attention on AMD MI355X (gfx950).
+ *
+ * The operation (all three entry points), with the feature map phi(x) = ELU(x) + 1 (alpha = 1)
+ * applied element-wise to q and k:
+ *
+ *     o_i = phi(q_i)^T S_i / phi(q_i)^T z_i,   S_i = sum_{j in W(i)} phi(k_j) v_j^T,
+ *                                              z_i = sum_{j in W(i)} phi(k_j)
+ *
+ *   causal  W(i) = {j <= i} (token i sees itself: the state is updated, then read)
+ *           -- "Linear Attention Math", section "The recurrent form: a running KV state";
+ *              "Linear Attention: Accumulating KV in a Fixed-Size State", section
+ *              "Summarize state updates and reads with equations".
+ *   global  W(i) = all tokens -- "Linear Attention Math", section "The associativity trick,
+ *              written out"; "线性注意力从头到尾讲清楚", section 5 (matrix form).
+ *   decode  one step of the causal recurrence on a caller-held state
+ *           -- "Linear Attention Math", section "The recurrent form" (O(1) per token);
+ *              "线性注意力从头到尾讲清楚", section 7 (only S_t and z_t are kept).
+ * No epsilon is added to the denominator ("Linear Attention: From Pairwise Reads to a
+ * Recurrent State", section "The reassociation that works": a clamp changes the operation).
+ *
+ * Layout: every tensor is contiguous, row-major, in device memory.
+ *   q, k  [B, H, N, d]       dtype given by `dtype`
+ *   v     [B, H, N, d_v]     dtype given by `dtype`
+ *   out   [B, H, N, d_v]     dtype given by `dtype` (rounded to nearest even for bf16)
+ *   S     [B, H, d, d_v]     float32; rows are key features, columns value components
+ *   z     [B, H, d]          float32
+ * Arithmetic is float32 throughout (bf16 operands of matrix-core products, float32 accumulation
+ * and state). d and d_v must each be one of 16, 32, 64, 128. Pointers must be 16-byte aligned.
+ * q, k and v must not overlap out; S and z must not overlap each other or q, k, v, out.
+ *
+ * Ownership and concurrency: all memory belongs to the caller. The library never frees or
+ * retains a pointer past the call and keeps no mutable global state. Work is enqueued on
+ * `stream` (NULL = the null stream) and the call returns without waiting; the results are
+ * ready when the stream reaches that point. Calls on different streams may run concurrently.
+ * The causal and global forms take stream-ordered temporary device memory (hipMallocAsync /
+ * hipFreeAsync on `stream`) for per-segment partial states; its size is returned by
+ * la_workspace_bytes().
+ *
+ * Errors: every call validates all arguments before enqueuing anything and returns a status.
+ *   LA_OK       enqueued
+ *   LA_EINVAL   a required pointer is NULL or misaligned, a size is <= 0, decode with N != 1,
+ *               dtype unknown, or buffers overlap as forbidden above; nothing was enqueued
+ *   LA_ENOTSUP  valid but unsupported: d or d_v not in {16, 32, 64, 128}, chunk not accepted
+ *               for this shape/dtype, or a size whose index arithmetic would overflow
+ *   LA_EHIP     the HIP runtime reported an error (allocation or launch); work enqueued before
+ *               the failure may have run
+ * Nothing aborts, exits or throws across this interface.
+ */
+#ifndef LINATTN_LA_H
+#define LINATTN_LA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+enum { LA_OK = 0, LA_EINVAL = 1, LA_ENOTSUP = 2, LA_EHIP = 3 };
+
+/*
+ * Causal prefill: out[b,h,i] = phi(q_i)^T S_i / phi(q_i)^T z_i over tokens j <= i, starting
+ * from an optional carried state.
+ *   S, z   both NULL: start from the zero state; the final state is not returned.
+ *          both non-NULL: read as the state before token 0 (zero-fill them for a fresh
+ *          sequence) and overwritten with the state after token N-1, so a long sequence can
+ *          be processed in pieces and handed to la_decode_step. One NULL and one not: LA_EINVAL.
+ *   chunk  tokens per intra-chunk tile: 0 lets the library choose; 64 selects the
+ *          matrix-core kernel (bf16, d = d_v in {64, 128}); 16 or 32 select the vector-ALU
+ *          kernel (any supported d, d_v, either dtype). Other values: LA_ENOTSUP. Results are
+ *          the same within rounding for every accepted chunk.
+ * Defined by the recurrence S_i = S_{i-1} + phi(k_i) v_i^T, z_i = z_{i-1} + phi(k_i) of
+ * "Linear Attention Math", section "The recurrent form: a running KV state"; the chunked
+ * evaluation (within-chunk part plus the state carried from earlier chunks) is the one that
+ * "Linear Attention: From Pairwise Reads to a Recurrent State", section "A recurrence need
+ * not force token-serial training", describes.
+ */
+int la_causal_fwd(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                  int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype,
+                  hipStream_t stream);
+
+/*
+ * Same as la_causal_fwd with an explicit sequence split: each (b, h) is cut into segments of
+ * `seg_len` tokens (a positive multiple of the chunk in use) that run in parallel, joined by
+ * an exclusive prefix over segment states. seg_len = 0 lets the library choose (what
+ * la_causal_fwd does). A seg_len that is not a positive multiple of the chunk: LA_ENOTSUP.
+ */
+int la_causal_fwd_seg(const void *q, const void *k, const void *v, void *out, float *S,
+                      float *z, int B, int H, int N, int d, int d_v, int chunk, int seg_len,
+                      la_dtype dtype, hipStream_t stream);
+
+/*
+ * Global (non-causal): S = phi(K)^T V and z = phi(K)^T 1 per (b, h) over all N tokens, then
+ * out[b,h,i] = phi(q_i)^T S / phi(q_i)^T z for every token.
+ *   S, z   required; written (not read) with the full-sequence state.
+ *   q, out may both be NULL: only S and z are computed (a state summary of a context).
+ *   chunk  as for la_causal_fwd (0, 16, 32, 64).
+ * "Linear Attention Math", section "The associativity trick, written out";
+ * "线性注意力从头到尾讲清楚", section 5, O = Phi(Q)(Phi(K)^T V) / Phi(Q)(Phi(K)^T 1).
+ */
+int la_global_fwd(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                  int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype,
+                  hipStream_t stream);
+
+/*
+ * One recurrent decode step for B*H heads: N must be 1; q, k [B,H,1,d], v, out [B,H,1,d_v].
+ *   S, z   required; read as the state before this token and updated in place:
+ *          S <- S + phi(k) v^T, z <- z + phi(k); then out = phi(q)^T S / phi(q)^T z.
+ *   chunk  ignored.
+ * "Linear Attention Math", section "The recurrent form" (update, then read; constant time
+ * and memory per token).
+ */
+int la_decode_step(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                   int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype,
+                   hipStream_t stream);
+
+/* Bytes of stream-ordered temporary device memory a causal (form = 0) or global (form = 1)
+ * call with these arguments takes (0 when none). seg_len as in la_causal_fwd_seg (0 = auto).
+ * Returns 0 for invalid or unsupported arguments as well. */
+size_t la_workspace_bytes(int form, int B, int H, int N, int d, int d_v, int chunk,
+                          int seg_len, la_dtype dtype);
+
+/* Static, NUL-terminated description of a status code; never NULL. */
+const char *la_strerror(int status);
+
+/* Library version as (major << 16) | (minor << 8) | patch. */
+int la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_LA_H */

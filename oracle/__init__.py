@@ -47,7 +47,7 @@ def _bind(path):
     P = ctypes.POINTER(ctypes.c_double)
     L = ctypes.c_long
     lib.oracle_causal.argtypes = [P, P, P, P, P, P, P, P, L, L, L, L, ctypes.c_int]
-    lib.oracle_global.argtypes = [P, P, P, P, P, P, P, P, L, L, L, L, ctypes.c_int]
+    lib.oracle_global.argtypes = [P, P, P, P, P, P, P, P, L, L, L, L, L, ctypes.c_int]
     lib.oracle_decode.argtypes = [P, P, P, P, P, P, L, L, L, ctypes.c_int]
     lib.oracle_causal.restype = None
     lib.oracle_global.restype = None
@@ -91,23 +91,33 @@ def causal(q, k, v, S0=None, z0=None, mode: str = "elu1", lib=None):
     num = np.empty((B, H, N, dv))
     den = np.empty((B, H, N))
     (lib or _load()).oracle_causal(_p(q), _p(k), _p(v), _p(o), _p(num), _p(den), _p(S), _p(z),
-                          B * H, N, d, dv, _MODES[mode])
+                                   B * H, N, d, dv, _MODES[mode])
     return o, S, z, num, den
 
 
 def global_(q, k, v, mode: str = "elu1", lib=None):
-    """Global (non-causal) form. Returns (o, S, z, num, den)."""
-    q, k, v = _f64(q), _f64(k), _f64(v)
-    B, H, N, d = q.shape
+    """Global (non-causal) form. Returns (o, S, z, num, den).
+
+    q may hold a different number of rows Nq than k and v (each query row is read against the
+    state of all N keys), or be None (state only: o, num, den are None)."""
+    k, v = _f64(k), _f64(v)
+    B, H, N, d = k.shape
     dv = v.shape[-1]
-    assert k.shape == (B, H, N, d) and v.shape == (B, H, N, dv)
+    assert v.shape == (B, H, N, dv)
     S = np.empty((B, H, d, dv))
     z = np.empty((B, H, d))
-    o = np.empty((B, H, N, dv))
-    num = np.empty((B, H, N, dv))
-    den = np.empty((B, H, N))
+    if q is None:
+        (lib or _load()).oracle_global(None, _p(k), _p(v), None, None, None, _p(S), _p(z),
+                                       B * H, N, 0, d, dv, _MODES[mode])
+        return None, S, z, None, None
+    q = _f64(q)
+    Nq = q.shape[2]
+    assert q.shape == (B, H, Nq, d)
+    o = np.empty((B, H, Nq, dv))
+    num = np.empty((B, H, Nq, dv))
+    den = np.empty((B, H, Nq))
     (lib or _load()).oracle_global(_p(q), _p(k), _p(v), _p(o), _p(num), _p(den), _p(S), _p(z),
-                          B * H, N, d, dv, _MODES[mode])
+                                   B * H, N, Nq, d, dv, _MODES[mode])
     return o, S, z, num, den
 
 
@@ -122,5 +132,5 @@ def decode_step(q, k, v, S, z, mode: str = "elu1", lib=None):
     v = _f64(v).reshape(B, H, dv)
     o = np.empty((B, H, dv))
     (lib or _load()).oracle_decode(_p(q), _p(k), _p(v), _p(o), _p(S), _p(z), B * H, d, dv,
-                          _MODES[mode])
+                                   _MODES[mode])
     return o, S, z

@@ -74,12 +74,12 @@ void oracle_causal(const double *q, const double *k, const double *v, double *o,
             double dn = 0.0;
             for (long i = 0; i < d; ++i)
                 dn += qf[i] * zh[i];
-            for (long j = 0; j < dv; ++j) {
-                double s = 0.0;
-                for (long i = 0; i < d; ++i)
-                    s += qf[i] * Sh[i * dv + j];
-                nm[j] = s;
-            }
+            /* nm[j] = sum_i qf[i] S[i][j], summed in increasing i (row-wise traversal) */
+            for (long j = 0; j < dv; ++j)
+                nm[j] = 0.0;
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < dv; ++j)
+                    nm[j] += qf[i] * Sh[i * dv + j];
             for (long j = 0; j < dv; ++j) {
                 o[(h * N + t) * dv + j] = nm[j] / dn;
                 if (num)
@@ -94,15 +94,19 @@ void oracle_causal(const double *q, const double *k, const double *v, double *o,
     }
 }
 
-/* Global (non-causal) form: first accumulate S and z over all N tokens (S, z are overwritten),
- * then read every query against that one state. */
+/* Global (non-causal) form: first accumulate S and z over all N key/value tokens (S, z are
+ * overwritten), then read each of the Nq queries q [BH, Nq, d] against that one state
+ * (Nq = N for the full layer; a smaller Nq reads a chosen subset of query rows). q == NULL
+ * computes the state only. */
 void oracle_global(const double *q, const double *k, const double *v, double *o, double *num,
-                   double *den, double *S, double *z, long BH, long N, long d, long dv, int mode)
+                   double *den, double *S, double *z, long BH, long N, long Nq, long d, long dv,
+                   int mode)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (long h = 0; h < BH; ++h) {
         double *kf = malloc(sizeof(double) * d);
         double *qf = malloc(sizeof(double) * d);
+        double *nm = malloc(sizeof(double) * dv);
         double *Sh = S + h * d * dv;
         double *zh = z + h * d;
         memset(Sh, 0, sizeof(double) * d * dv);
@@ -117,26 +121,29 @@ void oracle_global(const double *q, const double *k, const double *v, double *o,
                 zh[i] += kf[i];
             }
         }
-        for (long t = 0; t < N; ++t) {
-            const double *qt = q + (h * N + t) * d;
+        for (long t = 0; q && t < Nq; ++t) {
+            const double *qt = q + (h * Nq + t) * d;
             for (long i = 0; i < d; ++i)
                 qf[i] = phi(qt[i], mode);
             double dn = 0.0;
             for (long i = 0; i < d; ++i)
                 dn += qf[i] * zh[i];
+            for (long j = 0; j < dv; ++j)
+                nm[j] = 0.0;
+            for (long i = 0; i < d; ++i)
+                for (long j = 0; j < dv; ++j)
+                    nm[j] += qf[i] * Sh[i * dv + j];
             for (long j = 0; j < dv; ++j) {
-                double s = 0.0;
-                for (long i = 0; i < d; ++i)
-                    s += qf[i] * Sh[i * dv + j];
-                o[(h * N + t) * dv + j] = s / dn;
+                o[(h * Nq + t) * dv + j] = nm[j] / dn;
                 if (num)
-                    num[(h * N + t) * dv + j] = s;
+                    num[(h * Nq + t) * dv + j] = nm[j];
             }
             if (den)
-                den[h * N + t] = dn;
+                den[h * Nq + t] = dn;
         }
         free(kf);
         free(qf);
+        free(nm);
     }
 }
 
@@ -161,12 +168,15 @@ void oracle_decode(const double *q, const double *k, const double *v, double *o,
         double dn = 0.0;
         for (long i = 0; i < d; ++i)
             dn += phi(qh[i], mode) * zh[i];
-        for (long j = 0; j < dv; ++j) {
-            double s = 0.0;
-            for (long i = 0; i < d; ++i)
-                s += phi(qh[i], mode) * Sh[i * dv + j];
-            o[h * dv + j] = s / dn;
+        for (long j = 0; j < dv; ++j)
+            o[h * dv + j] = 0.0;
+        for (long i = 0; i < d; ++i) {
+            const double qfi = phi(qh[i], mode);
+            for (long j = 0; j < dv; ++j)
+                o[h * dv + j] += qfi * Sh[i * dv + j];
         }
+        for (long j = 0; j < dv; ++j)
+            o[h * dv + j] /= dn;
     }
 }
 

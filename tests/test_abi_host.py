@@ -1,0 +1,118 @@
+"""The C ABI on the host: the library loads, exports every symbol include/la.h declares, and
+rejects invalid arguments with the documented status before any HIP call (CPU only; every
+call here fails validation, so nothing is ever enqueued)."""
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import causal_linear_attention_la_amd as la
+
+ROOT = Path(__file__).resolve().parents[1]
+A = 1 << 20  # fake, 16-byte aligned "device" addresses; never dereferenced
+
+
+def declared_symbols():
+    text = (ROOT / "include" / "la.h").read_text()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*\**\s*(la_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_match_header():
+    decl = declared_symbols()
+    assert set(decl) == set(la.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", str(la.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (la_\w+)$", out, re.M))
+    for name in decl:
+        assert name in exported, name
+        assert hasattr(la.lib, name)
+
+
+def test_version_and_strerror():
+    assert la.version() >= (0, 1, 0)
+    for code in (la.LA_OK, la.LA_EINVAL, la.LA_ENOTSUP, la.LA_EHIP):
+        msg = la.strerror(code)
+        assert msg and msg != "unknown status"
+    assert la.strerror(12345) == "unknown status"
+
+
+def call(fn, q=A, k=2 * A, v=3 * A, out=4 * A, S=5 * A, z=6 * A, B=1, H=2, N=8, d=16, dv=16,
+         chunk=0, dtype=la.LA_BF16, seg=None):
+    f = getattr(la.lib, fn)
+    args = [q, k, v, out, S, z, B, H, N, d, dv, chunk]
+    if fn == "la_causal_fwd_seg":
+        args.append(0 if seg is None else seg)
+    args += [dtype, None]
+    return f(*args)
+
+
+FORMS = ["la_causal_fwd", "la_causal_fwd_seg", "la_global_fwd", "la_decode_step"]
+
+
+@pytest.mark.parametrize("fn", FORMS)
+def test_null_and_size_checks(fn):
+    N = 1 if fn == "la_decode_step" else 8
+    assert call(fn, k=None, N=N) == la.LA_EINVAL
+    assert call(fn, v=None, N=N) == la.LA_EINVAL
+    assert call(fn, B=0, N=N) == la.LA_EINVAL
+    assert call(fn, H=-1, N=N) == la.LA_EINVAL
+    assert call(fn, N=0) == la.LA_EINVAL
+    assert call(fn, d=0, N=N) == la.LA_EINVAL
+    assert call(fn, dtype=7, N=N) == la.LA_EINVAL
+    assert call(fn, k=2 * A + 8, N=N) == la.LA_EINVAL           # misaligned
+    assert call(fn, out=A + 16, N=N) == la.LA_EINVAL            # out overlaps q
+    assert call(fn, S=6 * A, z=6 * A, N=N) == la.LA_EINVAL      # S overlaps z
+    assert call(fn, S=3 * A, N=N) == la.LA_EINVAL               # S overlaps v
+    assert call(fn, d=48, N=N) == la.LA_ENOTSUP
+    assert call(fn, dv=256, N=N) == la.LA_ENOTSUP
+
+
+def test_form_specific_checks():
+    assert call("la_decode_step", N=2) == la.LA_EINVAL
+    assert call("la_decode_step", S=None) == la.LA_EINVAL
+    assert call("la_decode_step", N=1, z=None) == la.LA_EINVAL
+    assert call("la_causal_fwd", S=None) == la.LA_EINVAL        # one of S, z
+    assert call("la_causal_fwd", q=None) == la.LA_EINVAL
+    assert call("la_causal_fwd", out=None) == la.LA_EINVAL
+    assert call("la_global_fwd", q=None) == la.LA_EINVAL        # q without out
+    assert call("la_global_fwd", S=None) == la.LA_EINVAL
+    assert call("la_global_fwd", z=None) == la.LA_EINVAL
+
+
+def test_chunk_and_segment_checks():
+    assert call("la_causal_fwd", chunk=128) == la.LA_ENOTSUP
+    assert call("la_causal_fwd", chunk=-1) == la.LA_EINVAL
+    # the matrix-core chunk needs bf16 with d == d_v in {64, 128}
+    assert call("la_causal_fwd", chunk=64, d=16, dv=16) == la.LA_ENOTSUP
+    assert call("la_causal_fwd", chunk=64, d=64, dv=64, dtype=la.LA_F32) == la.LA_ENOTSUP
+    assert call("la_causal_fwd", chunk=64, d=64, dv=128) == la.LA_ENOTSUP
+    assert call("la_global_fwd", chunk=48) == la.LA_ENOTSUP
+    assert call("la_causal_fwd_seg", chunk=32, seg=48) == la.LA_ENOTSUP
+    assert call("la_causal_fwd_seg", chunk=32, seg=-32) == la.LA_EINVAL
+
+
+def test_workspace_bytes():
+    # causal B=2 H=16 N=8192 d=128 bf16: chunk 64, 16 segments of 512 tokens per head
+    E = 128 * 128 + 128
+    assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128) == 32 * 16 * E * 4
+    assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128, 64, 1024) == 32 * 8 * E * 4
+    # N=64 float32: chunk 32, split in two segments of one chunk; one segment needs no workspace
+    assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 2 * (16 * 16 + 16) * 4
+    assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 64, la.LA_F32) == 0
+    assert la.la_workspace_bytes(1, 1, 8, 100000, 128, 128) > 0
+    assert la.la_workspace_bytes(2, 1, 8, 10, 128, 128) == 0
+    assert la.la_workspace_bytes(0, 1, 1, 64, 48, 16) == 0
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        la.la_causal_fwd(q, q, q, torch.zeros(1, 1, 4, 16))
+
+
+def test_error_type_carries_status():
+    e = la.LAError(la.LA_ENOTSUP, "la_causal_fwd")
+    assert e.status == la.LA_ENOTSUP and "unsupported" in str(e)

@@ -1,0 +1,289 @@
+"""GPU parity: the HIP path, called through the C ABI, against the float64 oracle.
+
+Criterion: row-wise max-norm relative error (oracle/compare.py) within 1e-5 for float32 inputs
+and 2e-2 for bfloat16 inputs; the pages' worked examples, embedded in the supported head
+sizes, are checked to one rounding of the output dtype.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from gpu_util import causal, check, f64, global_, say, to_dev, DEV, la
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+# one rounding of the output dtype (worked examples with exact inputs)
+EXACT_TOL = {"f32": 2e-7, "bf16": 2.0 ** -8}
+RAW = {0: -1000.0, 1: 0.0, 3: 2.0}   # raw inputs whose ELU+1 features are 0, 1, 3
+
+# (dtype, d, chunk): the matrix-core kernel (bf16, d in {64,128}, chunk 64) and the
+# vector-ALU kernel (chunks 16/32, either dtype)
+PATHS = [("f32", 16, 16), ("f32", 16, 32), ("bf16", 16, 32), ("bf16", 64, 64),
+         ("bf16", 128, 64), ("f32", 128, 32), ("bf16", 128, 16)]
+
+
+def _embed_feat(rows, d):
+    """Feature rows (0/1/3 values, width <= d) -> raw [1,1,N,d] inputs, padding feature 0."""
+    rows = np.asarray(rows, dtype=np.float64)
+    out = np.full((1, 1, rows.shape[0], d), RAW[0])
+    for i in range(rows.shape[0]):
+        for j in range(rows.shape[1]):
+            out[0, 0, i, j] = RAW[int(rows[i, j])]
+    return out
+
+
+def _embed_val(rows, dv):
+    rows = np.asarray(rows, dtype=np.float64)
+    out = np.zeros((1, 1, rows.shape[0], dv))
+    out[0, 0, :, : rows.shape[1]] = rows
+    return out
+
+
+def _t(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(datagen.DTYPES[dtype])
+
+
+@pytest.mark.parametrize("dtype,d,chunk", PATHS)
+def test_worked_examples_causal(golden, dtype, d, chunk):
+    """Two-token read (10/3) and the three-token example, through ELU+1, on the GPU."""
+    g1 = golden("w1_two_token_read.json")
+    q1 = np.array(g1["q_at_position_1"], float)
+    q = _t(_embed_feat(np.stack([q1, q1]), d), dtype)
+    k = _t(_embed_feat(g1["k"], d), dtype)
+    v = _t(_embed_val(g1["v"], d), dtype)
+    say(f"W1 two-token read dtype={dtype} d={d} chunk={chunk}")
+    o, S, z = causal(q, k, v, chunk=chunk)
+    want = np.zeros((1, 1, 2, d))
+    want[0, 0, :, 0] = [g1["derived"]["output_at_position_0"], 10.0 / 3.0]
+    check("W1 out", o, want, EXACT_TOL[dtype])
+    Sw = np.zeros((1, 1, d, d))
+    Sw[0, 0, :2, 0] = np.array(g1["printed"]["S_after_token_1"], float)[:, 0]
+    check("W1 S", S, Sw, 1e-6)
+    zw = np.zeros((1, 1, d))
+    zw[0, 0, :2] = g1["printed"]["z_after_token_1"]
+    check("W1 z", z[..., None], zw[..., None], 1e-6)
+
+    g2 = golden("w2_three_token.json")
+    k = _t(_embed_feat(g2["k"], d), dtype)
+    v = _t(_embed_val(g2["v"], d), dtype)
+    say(f"W2 three-token dtype={dtype} d={d} chunk={chunk}")
+    o, S, z = causal(k, k, v, chunk=chunk)
+    want = _embed_val(g2["derived"]["causal_outputs_with_q_equal_k"], d)
+    check("W2 out", o, want, EXACT_TOL[dtype])
+    Sw = np.zeros((1, 1, d, d))
+    Sw[0, 0, :2, :2] = g2["printed"]["S3"]
+    check("W2 S", S, Sw, 1e-6)
+
+
+@pytest.mark.parametrize("dtype,d,chunk", PATHS)
+def test_worked_example_global(golden, dtype, d, chunk):
+    g = golden("w6_global_example.json")
+    q = _t(_embed_feat(g["q"], d), dtype)
+    k = _t(_embed_feat(g["k"], d), dtype)
+    v = _t(_embed_val(g["v"], d), dtype)
+    say(f"W6 global dtype={dtype} d={d} chunk={chunk}")
+    o, S, z = global_(q, k, v, chunk=chunk)
+    check("W6 out", o, _embed_val(g["derived"]["global_outputs"], d), EXACT_TOL[dtype])
+    Sw = np.zeros((1, 1, d, d))
+    Sw[0, 0, :2, :2] = g["printed_state"]["S"]
+    check("W6 S", S, Sw, 1e-6)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 16), ("bf16", 16), ("bf16", 128), ("f32", 128)])
+def test_worked_example_decode(golden, dtype, d):
+    """The decode example: two steps from the zero state; phi(q) = [3, 1] -> [0.75, 0.5]."""
+    g = golden("w3_decode_example.json")
+    S = torch.zeros((1, 1, d, d), dtype=torch.float32, device=DEV)
+    z = torch.zeros((1, 1, d), dtype=torch.float32, device=DEV)
+    qr = to_dev(_t(_embed_feat([g["phi_q"]], d)[:, :, 0], dtype))
+    for t in range(2):
+        kr = to_dev(_t(_embed_feat([g["phi_k"][t]], d)[:, :, 0], dtype))
+        vr = to_dev(_t(_embed_val([g["v"][t]], d)[:, :, 0], dtype))
+        out = torch.empty((1, 1, d), dtype=kr.dtype, device=DEV)
+        say(f"W3 decode step {t} dtype={dtype} d={d}")
+        la().la_decode_step(qr, kr, vr, out, S, z)
+    torch.cuda.synchronize()
+    want = np.zeros((1, 1, d))
+    want[0, 0, :2] = g["printed"]["output"]
+    check("W3 out", f64(out), want, EXACT_TOL[dtype])
+    Sw = np.zeros((1, 1, d, d))
+    Sw[0, 0, :2, :2] = g["printed"]["S"]
+    check("W3 S", f64(S), Sw, 1e-7)
+
+
+# ---------------------------------------------------------------- the five workloads
+def _workload(n):
+    w = datagen.WORKLOADS[n]
+    q, k, v = datagen.qkv(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale, w.dtype)
+    return w, q, k, v
+
+
+@pytest.mark.parametrize("chunk", [0, 16, 32])
+def test_workload1_causal_f32(chunk):
+    w, q, k, v = _workload(1)
+    say(f"workload 1 {w.name} chunk={chunk}")
+    o, S, z = causal(q, k, v, chunk=chunk)
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v))
+    check("out", o, oo, TOL["f32"])
+    check("S", S, So, TOL["f32"])
+    check("z", z[..., None], zo[..., None], TOL["f32"])
+
+
+@pytest.mark.parametrize("chunk,seg", [(64, 0), (64, 64), (64, 2048), (32, 0)])
+def test_workload2_causal(chunk, seg):
+    w, q, k, v = _workload(2)
+    say(f"workload 2 {w.name} chunk={chunk} seg_len={seg}")
+    o, S, z = causal(q, k, v, chunk=chunk, seg_len=seg)
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v))
+    check("out", o, oo, TOL["bf16"])
+    check("S", S, So, TOL["bf16"])
+    check("z", z[..., None], zo[..., None], TOL["bf16"])
+
+
+def test_workload3_causal_full():
+    w, q, k, v = _workload(3)
+    say(f"workload 3 {w.name} (launch configuration of the bench)")
+    o, S, z = causal(q, k, v)
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v))
+    check("out", o, oo, TOL["bf16"])
+    check("S", S, So, TOL["bf16"])
+    check("z", z[..., None], zo[..., None], TOL["bf16"])
+
+
+def test_workload4_global_sampled():
+    """Full state; outputs on 2048 sampled rows per head plus the ragged tail (N = 100000)."""
+    w, q, k, v = _workload(4)
+    say(f"workload 4 {w.name}")
+    o, S, z = global_(q, k, v)
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([rng.choice(w.N, 2048, replace=False), np.arange(w.N - 96, w.N)]))
+    qs = q[:, :, torch.from_numpy(rows)]
+    oo, So, zo, _, _ = oracle.global_(f64(qs), f64(k), f64(v))
+    check("out[sampled rows]", o[:, :, rows], oo, TOL["bf16"])
+    check("S", S, So, TOL["bf16"])
+    check("z", z[..., None], zo[..., None], TOL["bf16"])
+
+
+def _decode_run(B, H, d, prior, steps, seed):
+    """Seeded prior tokens -> oracle state (float64, rounded to float32) -> `steps` decode
+    steps on the GPU and in the oracle."""
+    kp, vp = datagen.qkv(B, H, prior, d, d, seed, 1 / math.sqrt(d), "bf16")[1:]
+    _, S0, z0, _, _ = oracle.global_(None, f64(kp), f64(vp))
+    S0 = S0.astype(np.float32)
+    z0 = z0.astype(np.float32)
+    S = torch.from_numpy(S0).to(DEV)
+    z = torch.from_numpy(z0).to(DEV)
+    So, zo = S0.astype(np.float64), z0.astype(np.float64)
+    toks = datagen.qkv(B, H, steps, d, d, seed + 1, 1 / math.sqrt(d), "bf16")
+    for t in range(steps):
+        q, k, v = (x[:, :, t].contiguous() for x in toks)
+        out = torch.empty((B, H, d), dtype=torch.bfloat16, device=DEV)
+        say(f"decode B={B} H={H} d={d} prior={prior} step {t}")
+        la().la_decode_step(to_dev(q), to_dev(k), to_dev(v), out, S, z)
+        torch.cuda.synchronize()
+        oo, So, zo = oracle.decode_step(f64(q), f64(k), f64(v), So, zo)
+        check(f"out step {t}", f64(out), oo, TOL["bf16"])
+    check("S", f64(S), So, 1e-6)
+    check("z", f64(z)[..., None], zo[..., None], 1e-6)
+
+
+def test_workload5_decode_all_heads():
+    """All 256 x 32 heads of the decode workload (prior of 32 tokens to keep the oracle short)."""
+    w = datagen.WORKLOADS[5]
+    _decode_run(w.B, w.H, w.d, prior=32, steps=3, seed=w.seed)
+
+
+def test_workload5_decode_full_prior():
+    """The decode workload's 4096-token prior state, on 64 of its heads."""
+    w = datagen.WORKLOADS[5]
+    _decode_run(2, w.H, w.d, prior=w.prior, steps=2, seed=w.seed + 10)
+
+
+# ---------------------------------------------------------------- edges and invariants
+@pytest.mark.parametrize("dtype,d,dv,N,chunk", [
+    ("bf16", 128, 128, 1, 0), ("bf16", 128, 128, 63, 0), ("bf16", 128, 128, 65, 0),
+    ("bf16", 128, 128, 1000, 0), ("bf16", 64, 64, 1, 0), ("bf16", 64, 64, 129, 0),
+    ("f32", 128, 128, 65, 16), ("f32", 64, 32, 77, 32), ("bf16", 32, 128, 50, 0),
+    ("bf16", 128, 16, 50, 0), ("f32", 16, 16, 1, 0), ("bf16", 16, 64, 300, 16)])
+def test_ragged_and_mixed_shapes(dtype, d, dv, N, chunk):
+    q, k, v = datagen.qkv(2, 3, N, d, dv, 77 + N, 1 / math.sqrt(d), dtype)
+    say(f"ragged dtype={dtype} d={d} dv={dv} N={N} chunk={chunk}")
+    o, S, z = causal(q, k, v, chunk=chunk)
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v))
+    check("out", o, oo, TOL[dtype])
+    check("S", S, So, TOL[dtype])
+    og, Sg, zg = global_(q, k, v, chunk=chunk)
+    oo, So, zo, _, _ = oracle.global_(f64(q), f64(k), f64(v))
+    check("global out", og, oo, TOL[dtype])
+    check("global S", Sg, So, TOL[dtype])
+
+
+@pytest.mark.parametrize("seg", [64, 128, 512, 1024, 4096])
+def test_segment_split_sweep(seg):
+    """Results do not depend on how the sequence is split across workgroups."""
+    q, k, v = datagen.qkv(1, 4, 4096 + 40, 128, 128, 5, 1 / math.sqrt(128), "bf16")
+    say(f"segment sweep seg_len={seg}")
+    o, S, z = causal(q, k, v, seg_len=seg)
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v))
+    check("out", o, oo, TOL["bf16"])
+    check("S", S, So, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 0), ("bf16", 64, 0), ("f32", 32, 16)])
+def test_state_carry_split(dtype, d, chunk):
+    """Causal over [0, N) equals [0, N1) then [N1, N) with the state carried through S, z,
+    and a prefill followed by one decode step equals causal over N + 1 at position N."""
+    N, n1 = 700, 333
+    q, k, v = datagen.qkv(2, 2, N + 1, d, d, 9, 1 / math.sqrt(d), dtype)
+    qa, ka, va = (x[:, :, :n1].contiguous() for x in (q, k, v))
+    qb, kb, vb = (x[:, :, n1:N].contiguous() for x in (q, k, v))
+    say(f"state carry dtype={dtype} d={d}")
+    oa, Sa, za = causal(qa, ka, va, chunk=chunk)
+    ob, Sb, zb = causal(qb, kb, vb, S0=Sa.astype(np.float32), z0=za.astype(np.float32), chunk=chunk)
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v))
+    check("two-piece out", np.concatenate([oa, ob], axis=2), oo[:, :, :N], TOL[dtype])
+    _, Sn, zn, _, _ = oracle.causal(f64(q[:, :, :N]), f64(k[:, :, :N]), f64(v[:, :, :N]))
+    check("two-piece S", Sb, Sn, TOL[dtype])
+    S = torch.from_numpy(Sb.astype(np.float32)).to(DEV)
+    z = torch.from_numpy(zb.astype(np.float32)).to(DEV)
+    out = torch.empty((2, 2, 1, d), dtype=q.dtype, device=DEV)
+    la().la_decode_step(to_dev(q[:, :, N:]), to_dev(k[:, :, N:]), to_dev(v[:, :, N:]), out, S, z)
+    torch.cuda.synchronize()
+    check("prefill+decode", f64(out), oo[:, :, N:], TOL[dtype])
+
+
+def test_bit_reproducible():
+    """Fixed reduction order: two runs give identical bytes (causal, global, decode)."""
+    q, k, v = datagen.qkv(2, 8, 3000, 128, 128, 21, 1 / math.sqrt(128), "bf16")
+    say("reproducibility")
+    a = causal(q, k, v)
+    b = causal(q, k, v)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    a = global_(q, k, v)
+    b = global_(q, k, v)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_global_state_only():
+    q, k, v = datagen.qkv(1, 4, 5000, 128, 128, 31, 1 / math.sqrt(128), "bf16")
+    say("global state only")
+    _, S, z = global_(None, k, v)
+    _, So, zo, _, _ = oracle.global_(None, f64(k), f64(v))
+    check("S", S, So, TOL["bf16"])
+    check("z", z[..., None], zo[..., None], TOL["bf16"])
+
+
+def test_causal_last_row_equals_global():
+    q, k, v = datagen.qkv(1, 2, 1500, 64, 64, 41, 1 / 8, "bf16")
+    say("causal last row vs global")
+    oc, Sc, zc = causal(q, k, v)
+    og, Sg, zg = global_(q, k, v)
+    check("last row", oc[:, :, -1:], og[:, :, -1:], TOL["bf16"])
+    check("state", Sc, Sg, 1e-5)

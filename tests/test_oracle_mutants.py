@@ -24,7 +24,8 @@ MUTANTS = [
     ("z_counts_tokens", "zh[i] += kf[i];", "zh[i] += 1.0;", 1),
     ("no_normalisation", "o[(h * N + t) * dv + j] = nm[j] / dn;",
      "o[(h * N + t) * dv + j] = nm[j];", 1),
-    ("read_transposed_state", "s += qf[i] * Sh[i * dv + j];", "s += qf[i] * Sh[j * d + i];", 1),
+    ("read_transposed_state", "nm[j] += qf[i] * Sh[i * dv + j];",
+     "nm[j] += qf[i] * Sh[j * d + i];", 1),
     ("key_off_by_one", "const double *kt = k + (h * N + t) * d;",
      "const double *kt = k + (h * N + (t ? t - 1 : t)) * d;", 1),
     ("value_of_next_token", "const double *vt = v + (h * N + t) * dv;",
