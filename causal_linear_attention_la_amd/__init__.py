@@ -13,12 +13,19 @@ S [B,H,d,d_v] and z [B,H,d] float32. A non-zero status raises ``LAError``.
 
 If the shared library is missing or fails to load, importing this package raises: there is
 no fallback implementation.
+
+PyTorch ships its own copy of the HIP runtime. The library links the system one by soname, so
+PyTorch is imported first: the loader then binds the library to the runtime already in the
+process and one runtime serves both (two copies in one process do not share devices, memory
+or streams). ``hip_runtimes()`` lists the HIP runtime copies mapped into the process.
 """
 from __future__ import annotations
 
 import ctypes
 import os
 from pathlib import Path
+
+import torch  # noqa: F401  (must precede loading liblinattn; see above)
 
 _PKG = Path(__file__).resolve().parent
 LIB_PATH = Path(os.environ.get("LINATTN_LIB", _PKG / "liblinattn.so"))
@@ -62,6 +69,17 @@ def _load(path: Path):
 lib = _load(LIB_PATH)
 
 
+def hip_runtimes() -> list:
+    """Paths of the HIP runtime libraries (libamdhip64) mapped into this process."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 6 and "libamdhip64" in parts[-1]:
+                paths.add(os.path.realpath(parts[-1]))
+    return sorted(paths)
+
+
 def strerror(status: int) -> str:
     return lib.la_strerror(int(status)).decode()
 
@@ -72,7 +90,6 @@ def version() -> tuple:
 
 
 def _dtype_code(t):
-    import torch
     if t.dtype == torch.bfloat16:
         return LA_BF16
     if t.dtype == torch.float32:
@@ -85,7 +102,6 @@ def _ptr(t):
 
 
 def _stream(t):
-    import torch
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 

@@ -30,6 +30,12 @@ def test_exports_match_header():
         assert hasattr(la.lib, name)
 
 
+def test_one_hip_runtime():
+    """The library binds to the HIP runtime PyTorch already loaded (one copy per process)."""
+    rts = la.hip_runtimes()
+    assert len(rts) == 1, rts
+
+
 def test_version_and_strerror():
     assert la.version() >= (0, 1, 0)
     for code in (la.LA_OK, la.LA_EINVAL, la.LA_ENOTSUP, la.LA_EHIP):
