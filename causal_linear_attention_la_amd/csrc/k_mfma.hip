@@ -90,17 +90,16 @@ template <int D> struct Tile {
         a = K::LA * w + (l % K::LA);
         b = l / K::LA;
     }
-    // rows [0, nvalid) of the chunk starting at `base`; rows past nvalid read as zero
+    // rows of the chunk starting at `base`, clamped to the chunk's last valid row so every
+    // access is in bounds and no load sits in a branch (a load merged with a zero in a branch
+    // makes the compiler wait for it right away); rows past nvalid are masked when staged.
     __device__ __forceinline__ void load(u32x4 (&r)[K::TM], const uint16_t *__restrict__ base,
                                          int nvalid) const
     {
 #pragma unroll
         for (int i = 0; i < K::TM; ++i) {
-            const int row = K::TM * a + i;
-            if (row < nvalid)
-                r[i] = *reinterpret_cast<const u32x4 *>(base + (size_t)row * D + 8 * b);
-            else
-                r[i] = u32x4{0u, 0u, 0u, 0u};
+            const int row = min(K::TM * a + i, nvalid - 1);
+            r[i] = *reinterpret_cast<const u32x4 *>(base + (size_t)row * D + 8 * b);
         }
     }
     __device__ __forceinline__ bool valid(int i, int nvalid) const { return K::TM * a + i < nvalid; }
@@ -232,6 +231,28 @@ __device__ __forceinline__ void store_out(const f32x4 (&acc)[Cfg<D>::NCT][4], co
     }
 }
 
+// sdi[i] = phi(Q)[i] . z for the C rows of a staged chunk (256 threads: row tid/4, a quarter of
+// the features each).
+template <int D>
+__device__ __forceinline__ void den_inter(float *sdi, const uint16_t *sQ, const float *sz, int tid)
+{
+    using K = Cfg<D>;
+    const int i = tid >> 2, qq = tid & 3;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) {
+        const int f = qq * (D / 4) + 8 * e;
+        const u32x4 qw = lds<u32x4>(sQ + i * K::QS + f);
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+            s += bf_lo(qw[h]) * sz[f + 2 * h] + bf_hi(qw[h]) * sz[f + 2 * h + 1];
+    }
+    s += __shfl_xor(s, 1, 64);
+    s += __shfl_xor(s, 2, 64);
+    if (qq == 0)
+        sdi[i] = s;
+}
+
 // ------------------------------------------------------------------------------------------
 // Segment sums: dS = phi(K_seg)^T V_seg, dz = colsum phi(K_seg).
 template <int D>
@@ -264,17 +285,22 @@ __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
     u32x4 rk[K::TM], rv[K::TM];
     tile.load(rk, kb + (size_t)tb * D, te - tb);
     tile.load(rv, vb + (size_t)tb * D, te - tb);
+    const int tlast = tb + ((te - tb - 1) / C) * C; // first token of the segment's last chunk
     for (int t0 = tb; t0 < te; t0 += C) {
         const int nvalid = min(C, te - t0);
 #pragma unroll
-        for (int i = 0; i < K::TM; ++i)
-            rk[i] = tile.valid(i, nvalid) ? phi8(rk[i]) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < K::TM; ++i) {
+            const bool ok = tile.valid(i, nvalid);
+            rk[i] = ok ? phi8(rk[i]) : u32x4{0u, 0u, 0u, 0u};
+            rv[i] = ok ? rv[i] : u32x4{0u, 0u, 0u, 0u};
+        }
         tile.store_cols(sKT, rk);
         tile.store_cols(sVT, rv);
         __syncthreads();
-        if (t0 + C < te) {
-            tile.load(rk, kb + (size_t)(t0 + C) * D, te - t0 - C);
-            tile.load(rv, vb + (size_t)(t0 + C) * D, te - t0 - C);
+        {   // prefetch the next chunk (the last chunk again at the end: always in bounds)
+            const int tn = min(t0 + C, tlast);
+            tile.load(rk, kb + (size_t)tn * D, te - tn);
+            tile.load(rv, vb + (size_t)tn * D, te - tn);
         }
         state_update<D>(sacc, sKT, sVT, cw0, li, g);
         zpart += kf_colsum_half<D>(sKT, tid);
@@ -296,85 +322,73 @@ __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
 
 // ------------------------------------------------------------------------------------------
 // Causal outputs of one segment, starting from the state before the segment.
+//
+// 512 threads in two roles that share every SIMD. Waves 0-3 ("compute") hold the float32 state
+// S in accumulators (wave w owns value columns [w*D/4, (w+1)*D/4)) and run the matrix-core
+// products of chunk c. Waves 4-7 ("stage") meanwhile prepare chunk c+1 in the other half of the
+// double-buffered LDS: they apply phi, write phi(Q), phi(K) row-major and phi(K), V
+// token-major, keep the key sum z (float32, LDS) and compute the inter-chunk part of the
+// denominators, phi(q_i) . z. Two workgroup barriers per chunk:
+//   phase 1  compute: scores A of chunk c (query rows 16w..16w+15), den = rowsum(A) + phi(q).z
+//            stage:   z += colsum(phi(K_c)); phi(Q_{c+1}) -> LDS; load Q_{c+2}
+//   --- barrier X ---
+//   phase 2  compute: num = A V_c + phi(Q_c) S; out = num / den; S += phi(K_c)^T V_c
+//            stage:   phi(K_{c+1}), V_{c+1} -> LDS; load K_{c+2}, V_{c+2}; phi(Q_{c+1}) . z
+//   --- barrier Y ---
+template <int D> struct CausalLds {
+    uint16_t sQ[2][C * Cfg<D>::QS];
+    uint16_t sK[2][C * Cfg<D>::QS];
+    uint16_t sKT[2][D * Cfg<D>::TS];
+    uint16_t sVT[2][D * Cfg<D>::TS];
+    uint16_t sA[C * Cfg<D>::TS];
+    float sz[2][D];  // z before chunk c lives in sz[c & 1]
+    float sdi[2][C]; // phi(q_i) . z for chunk c in sdi[c & 1]
+    float sden[C];
+};
+
+struct CausalArgs {
+    const uint16_t *qh, *kh, *vh; // the head's [N, D] rows
+    uint16_t *oh;
+    const float *S0, *z0;         // state before the segment (null: zero)
+    float *Sout, *zout;           // final state of the head (null: not written)
+    int tb, te, nch;              // token range of the segment, chunks in it
+};
+
+// Compute role (waves 0-3). Barrier sequence: 2 in the prologue, 2 per chunk.
 template <int D>
-__global__ __launch_bounds__(NT) void k_causal(const uint16_t *__restrict__ q,
-                                               const uint16_t *__restrict__ k,
-                                               const uint16_t *__restrict__ v,
-                                               uint16_t *__restrict__ out,
-                                               const float *__restrict__ preS,
-                                               const float *__restrict__ prez, long pstride,
-                                               long pzstride, float *__restrict__ Sout,
-                                               float *__restrict__ zout, int N, int L, int P)
+__device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArgs &a, int w,
+                                               int li, int g)
 {
     using K = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[C * K::QS];
-    __shared__ __attribute__((aligned(16))) uint16_t sK[C * K::QS];
-    __shared__ __attribute__((aligned(16))) uint16_t sKT[D * K::TS];
-    __shared__ __attribute__((aligned(16))) uint16_t sVT[D * K::TS];
-    __shared__ __attribute__((aligned(16))) uint16_t sA[C * K::TS];
-    __shared__ float sz[D];
-    __shared__ float sden[C];
-
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, g = l >> 4;
-    const int p = blockIdx.x % P, bh = blockIdx.x / P;
-    const int tb = p * L, te = min(N, tb + L);
-    const size_t hoff = (size_t)bh * N * D;
     const int cw0 = w * (D / 4);
-    const Tile<D> tile(tid);
-
-    // state before the segment
     f32x4 sacc[K::NFT][K::NCT];
-    const float *S0 = preS ? preS + ((long)bh * P + p) * pstride : nullptr;
+    bf16x8 sf[K::NCT][K::NKB];
 #pragma unroll
     for (int ft = 0; ft < K::NFT; ++ft)
 #pragma unroll
         for (int ct = 0; ct < K::NCT; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                sacc[ft][ct][r] = S0 ? S0[(16 * ft + 4 * g + r) * D + cw0 + 16 * ct + li] : 0.f;
-    if (tid < D)
-        sz[tid] = S0 ? prez[((long)bh * P + p) * pzstride + tid] : 0.f;
-    bf16x8 sf[K::NCT][K::NKB];
+                sacc[ft][ct][r] = a.S0 ? a.S0[(16 * ft + 4 * g + r) * D + cw0 + 16 * ct + li] : 0.f;
     state_frags<D>(sf, sacc);
+    __syncthreads();
+    __syncthreads();
 
-    u32x4 rq[K::TM], rk[K::TM], rv[K::TM];
-    tile.load(rq, q + hoff + (size_t)tb * D, te - tb);
-    tile.load(rk, k + hoff + (size_t)tb * D, te - tb);
-    tile.load(rv, v + hoff + (size_t)tb * D, te - tb);
-
-    for (int t0 = tb; t0 < te; t0 += C) {
-        const int nvalid = min(C, te - t0);
-        // ---- stage the chunk: phi(Q), phi(K) natural; phi(K), V transposed
-#pragma unroll
-        for (int i = 0; i < K::TM; ++i) {
-            const bool ok = tile.valid(i, nvalid);
-            rq[i] = ok ? phi8(rq[i]) : u32x4{0u, 0u, 0u, 0u};
-            rk[i] = ok ? phi8(rk[i]) : u32x4{0u, 0u, 0u, 0u};
-        }
-        tile.store_rows(sQ, rq);
-        tile.store_rows(sK, rk);
-        tile.store_cols(sKT, rk);
-        tile.store_cols(sVT, rv);
-        __syncthreads();
-        if (t0 + C < te) {
-            const int nn = te - t0 - C;
-            tile.load(rq, q + hoff + (size_t)(t0 + C) * D, nn);
-            tile.load(rk, k + hoff + (size_t)(t0 + C) * D, nn);
-            tile.load(rv, v + hoff + (size_t)(t0 + C) * D, nn);
-        }
-
-        // ---- scores of query rows 16w..16w+15 against keys j <= i; den = rowsum + Qf z
+    for (int c = 0; c < a.nch; ++c) {
+        const int b = c & 1;
+        const int t0 = a.tb + c * C, nvalid = min(C, a.te - t0);
+        // phase 1: scores of query rows 16w..16w+15 against keys j <= i; den = rowsum + phi(q).z
         {
             bf16x8 qb[K::NKB];
 #pragma unroll
             for (int kk = 0; kk < K::NKB; ++kk)
-                qb[kk] = lds<bf16x8>(sQ + (16 * w + li) * K::QS + 32 * kk + 8 * g);
+                qb[kk] = lds<bf16x8>(sm.sQ[b] + (16 * w + li) * K::QS + 32 * kk + 8 * g);
             float rs = 0.f;
             for (int jt = 0; jt <= w; ++jt) {
                 f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < K::NKB; ++kk)
-                    t = mfma(lds<bf16x8>(sK + (16 * jt + li) * K::QS + 32 * kk + 8 * g), qb[kk], t);
+                    t = mfma(lds<bf16x8>(sm.sK[b] + (16 * jt + li) * K::QS + 32 * kk + 8 * g), qb[kk], t);
                 // t[r] = A[i = 16w + li][j = 16jt + 4g + r]
                 if (jt == w) {
 #pragma unroll
@@ -383,30 +397,18 @@ __global__ __launch_bounds__(NT) void k_causal(const uint16_t *__restrict__ q,
                             t[r] = 0.f;
                 }
                 const uint32_t p0 = pack_bf2(t[0], t[1]), p1 = pack_bf2(t[2], t[3]);
-                sts<u32x2>(sA + (16 * w + li) * K::TS + 16 * jt + 4 * g, u32x2{p0, p1});
+                sts<u32x2>(sm.sA + (16 * w + li) * K::TS + 16 * jt + 4 * g, u32x2{p0, p1});
                 rs += (bf_lo(p0) + bf_hi(p0)) + (bf_lo(p1) + bf_hi(p1));
             }
             if ((w & 1) == 0) // the 32-token block read below also covers j-tile w+1: zero it
-                sts<u32x2>(sA + (16 * w + li) * K::TS + 16 * (w + 1) + 4 * g, u32x2{0u, 0u});
-            float qz = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < K::NKB; ++kk) {
-                const u32x4 qw = __builtin_bit_cast(u32x4, qb[kk]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int f = 32 * kk + 8 * g + 2 * e;
-                    qz += bf_lo(qw[e]) * sz[f] + bf_hi(qw[e]) * sz[f + 1];
-                }
-            }
-            float den = rs + qz;
-            den += __shfl_xor(den, 16, 64);
-            den += __shfl_xor(den, 32, 64);
+                sts<u32x2>(sm.sA + (16 * w + li) * K::TS + 16 * (w + 1) + 4 * g, u32x2{0u, 0u});
+            rs += __shfl_xor(rs, 16, 64);
+            rs += __shfl_xor(rs, 32, 64);
             if (g == 0)
-                sden[16 * w + li] = den;
+                sm.sden[16 * w + li] = rs + sm.sdi[b][16 * w + li];
         }
         __syncthreads();
-
-        // ---- outputs of the wave's columns: num^T = V^T A^T + S^T Qf^T
+        // phase 2: num^T = V^T A^T + S^T Qf^T for the wave's columns; out; S += Kf^T V
         {
             f32x4 acc[K::NCT][4];
 #pragma unroll
@@ -418,40 +420,157 @@ __global__ __launch_bounds__(NT) void k_causal(const uint16_t *__restrict__ q,
             for (int it = 0; it < 4; ++it)
 #pragma unroll
                 for (int m = 0; m <= it / 2; ++m) {
-                    const bf16x8 ba = lds<bf16x8>(sA + (16 * it + li) * K::TS + 32 * m + 8 * g);
+                    const bf16x8 ba = lds<bf16x8>(sm.sA + (16 * it + li) * K::TS + 32 * m + 8 * g);
 #pragma unroll
                     for (int ct = 0; ct < K::NCT; ++ct)
-                        acc[ct][it] = mfma(lds<bf16x8>(sVT + tix<D>(cw0 + 16 * ct + li, 32 * m + 8 * g)),
+                        acc[ct][it] = mfma(lds<bf16x8>(sm.sVT[b] + tix<D>(cw0 + 16 * ct + li, 32 * m + 8 * g)),
                                            ba, acc[ct][it]);
                 }
-            state_read<D>(acc, sf, sQ, li, g);
-            store_out<D>(acc, sden, out + hoff + (size_t)t0 * D, nvalid, cw0, li, g);
+            state_read<D>(acc, sf, sm.sQ[b], li, g);
+            store_out<D>(acc, sm.sden, a.oh + (size_t)t0 * D, nvalid, cw0, li, g);
+            state_update<D>(sacc, sm.sKT[b], sm.sVT[b], cw0, li, g);
+            state_frags<D>(sf, sacc);
         }
-
-        // ---- write the chunk into the state
-        state_update<D>(sacc, sKT, sVT, cw0, li, g);
-        {
-            float zs = kf_colsum_half<D>(sKT, tid);
-            zs += __shfl_xor(zs, 1, 64);
-            if (tid < 2 * D && (tid & 1) == 0)
-                sz[tid >> 1] += zs;
-        }
-        state_frags<D>(sf, sacc);
         __syncthreads();
     }
-
-    if (Sout && p == P - 1) {
-        float *Sd = Sout + (size_t)bh * D * D;
+    if (a.Sout) {
 #pragma unroll
         for (int ft = 0; ft < K::NFT; ++ft)
 #pragma unroll
             for (int ct = 0; ct < K::NCT; ++ct)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    Sd[(16 * ft + 4 * g + r) * D + cw0 + 16 * ct + li] = sacc[ft][ct][r];
-        if (tid < D)
-            zout[(size_t)bh * D + tid] = sz[tid];
+                    a.Sout[(16 * ft + 4 * g + r) * D + cw0 + 16 * ct + li] = sacc[ft][ct][r];
     }
+}
+
+// Stage role (waves 4-7, thread index ht = 0..255). Same barrier sequence as the compute role.
+template <int D>
+__device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs &a, int ht)
+{
+    using K = Cfg<D>;
+    const Tile<D> tile(ht);
+    u32x4 rq[K::TM], rk[K::TM], rv[K::TM];
+    const int tb = a.tb, te = a.te, nch = a.nch;
+
+    if (ht < D)
+        sm.sz[0][ht] = a.z0 ? a.z0[ht] : 0.f;
+    // first token of chunk c' (clamped to the last chunk, so prefetches past the end re-read
+    // it: every load is in bounds and unconditional)
+    auto chunk_t0 = [&](int cc) { return tb + min(cc, nch - 1) * C; };
+    tile.load(rq, a.qh + (size_t)tb * D, te - tb);
+    tile.load(rk, a.kh + (size_t)tb * D, te - tb);
+    tile.load(rv, a.vh + (size_t)tb * D, te - tb);
+#pragma unroll
+    for (int i = 0; i < K::TM; ++i) {
+        const bool ok = tile.valid(i, te - tb);
+        rq[i] = ok ? phi8(rq[i]) : u32x4{0u, 0u, 0u, 0u};
+        rk[i] = ok ? phi8(rk[i]) : u32x4{0u, 0u, 0u, 0u};
+        rv[i] = ok ? rv[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+    tile.store_rows(sm.sQ[0], rq);
+    tile.store_rows(sm.sK[0], rk);
+    tile.store_cols(sm.sKT[0], rk);
+    tile.store_cols(sm.sVT[0], rv);
+    {
+        const int tn = chunk_t0(1);
+        tile.load(rq, a.qh + (size_t)tn * D, te - tn);
+        tile.load(rk, a.kh + (size_t)tn * D, te - tn);
+        tile.load(rv, a.vh + (size_t)tn * D, te - tn);
+    }
+    __syncthreads();
+    den_inter<D>(sm.sdi[0], sm.sQ[0], sm.sz[0], ht);
+    __syncthreads();
+
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1, nb = b ^ 1;
+        const int t0 = tb + c * C;
+        const int n1 = min(C, te - t0 - C); // valid rows of chunk c+1 (if it exists)
+        const int tn = chunk_t0(c + 2), nn = te - tn;
+        // phase 1: z after chunk c; phi(Q_{c+1}) -> LDS; load Q_{c+2}
+        {
+            float zs = kf_colsum_half<D>(sm.sKT[b], ht);
+            zs += __shfl_xor(zs, 1, 64);
+            if (ht < 2 * D && (ht & 1) == 0)
+                sm.sz[nb][ht >> 1] = sm.sz[b][ht >> 1] + zs;
+            if (c + 1 < nch) {
+#pragma unroll
+                for (int i = 0; i < K::TM; ++i)
+                    rq[i] = tile.valid(i, n1) ? phi8(rq[i]) : u32x4{0u, 0u, 0u, 0u};
+                tile.store_rows(sm.sQ[nb], rq);
+            }
+            tile.load(rq, a.qh + (size_t)tn * D, nn);
+        }
+        __syncthreads();
+        // phase 2: phi(K_{c+1}), V_{c+1} -> LDS; load K_{c+2}, V_{c+2}; phi(Q_{c+1}) . z
+        if (c + 1 < nch) {
+#pragma unroll
+            for (int i = 0; i < K::TM; ++i) {
+                const bool ok = tile.valid(i, n1);
+                rk[i] = ok ? phi8(rk[i]) : u32x4{0u, 0u, 0u, 0u};
+                rv[i] = ok ? rv[i] : u32x4{0u, 0u, 0u, 0u};
+            }
+            tile.store_rows(sm.sK[nb], rk);
+            tile.store_cols(sm.sKT[nb], rk);
+            tile.store_cols(sm.sVT[nb], rv);
+        }
+        tile.load(rk, a.kh + (size_t)tn * D, nn);
+        tile.load(rv, a.vh + (size_t)tn * D, nn);
+        if (c + 1 < nch)
+            den_inter<D>(sm.sdi[nb], sm.sQ[nb], sm.sz[nb], ht);
+        __syncthreads();
+    }
+    if (a.zout && ht < D)
+        a.zout[ht] = sm.sz[nch & 1][ht];
+}
+
+// ------------------------------------------------------------------------------------------
+// Causal outputs of one segment, starting from the state before the segment.
+//
+// 512 threads in two roles that share every SIMD. Waves 0-3 ("compute") hold the float32 state
+// S in accumulators (wave w owns value columns [w*D/4, (w+1)*D/4)) and run the matrix-core
+// products of chunk c. Waves 4-7 ("stage") meanwhile prepare chunk c+1 in the other half of the
+// double-buffered LDS: they apply phi, write phi(Q), phi(K) row-major and phi(K), V
+// token-major, keep the key sum z (float32, LDS) and compute the inter-chunk part of the
+// denominators, phi(q_i) . z. Two workgroup barriers per chunk:
+//   phase 1  compute: scores A of chunk c (query rows 16w..16w+15), den = rowsum(A) + phi(q).z
+//            stage:   z += colsum(phi(K_c)); phi(Q_{c+1}) -> LDS; load Q_{c+2}
+//   --- barrier ---
+//   phase 2  compute: num = A V_c + phi(Q_c) S; out = num / den; S += phi(K_c)^T V_c
+//            stage:   phi(K_{c+1}), V_{c+1} -> LDS; load K_{c+2}, V_{c+2}; phi(Q_{c+1}) . z
+//   --- barrier ---
+// The roles are wave-uniform, so every wave executes the same sequence of barriers.
+template <int D>
+__global__ __launch_bounds__(2 * NT) void k_causal(const uint16_t *__restrict__ q,
+                                                   const uint16_t *__restrict__ k,
+                                                   const uint16_t *__restrict__ v,
+                                                   uint16_t *__restrict__ out,
+                                                   const float *__restrict__ preS,
+                                                   const float *__restrict__ prez, long pstride,
+                                                   long pzstride, float *__restrict__ Sout,
+                                                   float *__restrict__ zout, int N, int L, int P)
+{
+    __shared__ __attribute__((aligned(16))) CausalLds<D> sm;
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    const int p = blockIdx.x % P, bh = blockIdx.x / P;
+    const size_t hoff = (size_t)bh * N * D;
+    CausalArgs a;
+    a.qh = q + hoff;
+    a.kh = k + hoff;
+    a.vh = v + hoff;
+    a.oh = out + hoff;
+    a.S0 = preS ? preS + ((long)bh * P + p) * pstride : nullptr;
+    a.z0 = preS ? prez + ((long)bh * P + p) * pzstride : nullptr;
+    const bool last = p == P - 1;
+    a.Sout = Sout && last ? Sout + (size_t)bh * D * D : nullptr;
+    a.zout = Sout && last ? zout + (size_t)bh * D : nullptr;
+    a.tb = p * L;
+    a.te = min(N, a.tb + L);
+    a.nch = (a.te - a.tb + C - 1) / C;
+    if (wave < 4)
+        causal_compute<D>(sm, a, wave, l & 15, l >> 4);
+    else
+        causal_stage<D>(sm, a, tid - NT);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -497,6 +616,7 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
 
     u32x4 rq[K::TM];
     tile.load(rq, q + hoff + (size_t)tb * D, te - tb);
+    const int tlast = tb + ((te - tb - 1) / C) * C;
     for (int t0 = tb; t0 < te; t0 += C) {
         const int nvalid = min(C, te - t0);
 #pragma unroll
@@ -504,8 +624,10 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
             rq[i] = tile.valid(i, nvalid) ? phi8(rq[i]) : u32x4{0u, 0u, 0u, 0u};
         tile.store_rows(sQ, rq);
         __syncthreads();
-        if (t0 + C < te)
-            tile.load(rq, q + hoff + (size_t)(t0 + C) * D, te - t0 - C);
+        {
+            const int tn = min(t0 + C, tlast);
+            tile.load(rq, q + hoff + (size_t)tn * D, te - tn);
+        }
         {
             // den[i] = Qf[i] . z: 4 threads per row, D/4 features each
             const int i = tid >> 2, qq = tid & 3;
@@ -556,7 +678,7 @@ hipError_t causal_mfma(int D, const void *q, const void *k, const void *v, void 
                        const float *preS, const float *prez, long pstride, long pzstride,
                        float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st)
 {
-    const dim3 grid((unsigned)(BH * P)), block(NT);
+    const dim3 grid((unsigned)(BH * P)), block(2 * NT);
     const auto *qq = static_cast<const uint16_t *>(q);
     const auto *kk = static_cast<const uint16_t *>(k);
     const auto *vv = static_cast<const uint16_t *>(v);

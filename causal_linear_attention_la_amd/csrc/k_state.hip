@@ -22,6 +22,10 @@ namespace {
 
 constexpr int NT = 256;
 
+// Slots are read in batches of SB independent loads before any store, so the walk over P
+// segments costs P / SB memory round trips instead of P.
+constexpr int SB = 16;
+
 __global__ __launch_bounds__(NT) void k_seg_scan(float *__restrict__ ws, const float *__restrict__ S0,
                                                  const float *__restrict__ z0, int P, int d,
                                                  int dv, int blocks_per_head)
@@ -35,10 +39,18 @@ __global__ __launch_bounds__(NT) void k_seg_scan(float *__restrict__ ws, const f
     if (S0)
         run = e < d * dv ? S0[(size_t)bh * d * dv + e] : z0[(size_t)bh * d + (e - d * dv)];
     float *slot = ws + (size_t)bh * P * E + e;
-    for (int p = 0; p < P - 1; ++p) {
-        const float t = slot[(size_t)p * E];
-        slot[(size_t)p * E] = run;
-        run += t;
+    for (int p0 = 0; p0 < P - 1; p0 += SB) {
+        float t[SB];
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+            if (p0 + i < P - 1)
+                t[i] = slot[(size_t)(p0 + i) * E];
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+            if (p0 + i < P - 1) {
+                slot[(size_t)(p0 + i) * E] = run;
+                run += t[i];
+            }
     }
     slot[(size_t)(P - 1) * E] = run;
 }
@@ -54,8 +66,15 @@ __global__ __launch_bounds__(NT) void k_seg_total(const float *__restrict__ ws, 
         return;
     const float *slot = ws + (size_t)bh * P * E + e;
     float run = 0.f;
-    for (int p = 0; p < P; ++p)
-        run += slot[(size_t)p * E];
+    for (int p0 = 0; p0 < P; p0 += SB) {
+        float t[SB];
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+            t[i] = p0 + i < P ? slot[(size_t)(p0 + i) * E] : 0.f;
+#pragma unroll
+        for (int i = 0; i < SB; ++i)
+            run += t[i];
+    }
     if (e < d * dv)
         S[(size_t)bh * d * dv + e] = run;
     else
