@@ -1,6 +1,5 @@
 // k_mfma.hip -- matrix-core kernels of liblinattn: bf16 inputs, d == d_v = D in {64, 128},
-// chunks of C = 64 tokens, 256 threads (4 wave64s) per workgroup, gfx950 MFMA
-// v_mfma_f32_16x16x32_bf16 with float32 accumulation.
+// chunks of C = 64 tokens, gfx950 MFMA v_mfma_f32_16x16x32_bf16 with float32 accumulation.
 //
 // Chunked causal evaluation (the within-chunk part plus the state carried from earlier chunks,
 // as "Linear Attention: From Pairwise Reads to a Recurrent State", section "A recurrence need
@@ -9,7 +8,7 @@
 //   A       = mask_{j <= i}(Qf Kf^T)                     (C x C, inclusive: token i sees itself)
 //   num     = A V_c + Qf S,    den = rowsum(A) + Qf z    (the recurrence's read, all rows at once)
 //   out     = num / den
-//   S, z   += Kf^T V_c, colsum(Kf)                       (the recurrence's write, summed over c)
+//   S, z   += Kf^T V_c, Kf^T 1                           (the recurrence's write, summed over c)
 // which is the recurrence S_i = S_{i-1} + phi(k_i) v_i^T, z_i = z_{i-1} + phi(k_i),
 // o_i = phi(q_i)^T S_i / phi(q_i)^T z_i of "Linear Attention Math", section "The recurrent
 // form: a running KV state", regrouped by associativity.
@@ -21,9 +20,11 @@
 // state read uses the permutation {4g..4g+3, 16+4g..16+4g+3}, which is exactly how an
 // accumulator pair holds a 32-row block, so the float32 state S never goes through LDS.
 //
-// Work split inside a workgroup: wave w owns value columns [w*D/4, (w+1)*D/4) of the state S
-// (all D feature rows, in accumulators) and of the outputs; for the C x C score block wave w
-// computes query rows 16w..16w+15.
+// Chunks live in LDS row-major (token x feature), the layout in which they arrive from HBM.
+// Products that contract over features read them directly; products that contract over tokens
+// (S += Kf^T V, the key sum Kf^T 1, and A V) take their operands through the LDS transpose read
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j addresses the 8-byte piece at
+// (row j/4, columns 4(j%4)..4(j%4)+3) of a 4 x 16 block and receives column j of the block.
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -31,19 +32,33 @@ namespace la {
 namespace {
 
 constexpr int C = 64;   // tokens per chunk
-constexpr int NT = 256; // threads per workgroup
+constexpr int NT = 256; // threads of the segment-sum and global-read kernels; stage threads
 
 template <int D> struct Cfg {
-    static constexpr int TM = C * D / (8 * NT); // tokens per loader micro-tile (4 or 2)
-    static constexpr int TG = C / TM;           // token groups per chunk
-    static constexpr int LA = TG / 4;           // token groups per wave
-    static constexpr int QS = D + 8;            // row stride (elements) of sQ, sK
-    static constexpr int TS = C + 8;            // row stride of sKT, sVT, sA
-    static constexpr int NCT = D / 64;          // 16-wide column tiles owned by one wave
+    static constexpr int FG = D / 8;            // 16-byte feature groups per row
+    static constexpr int RPI = NT / FG;         // chunk rows one staging instruction covers
+    static constexpr int TM = C / RPI;          // staging rows per thread (4 or 2)
+    static constexpr int RS = D + 16;           // row stride (elements) of the chunk arrays
+    static constexpr int AS = C * RS + (C / 8 - 1) * 64; // chunk array size (elements)
+    static constexpr int TS = C + 8;            // row stride (elements) of the score block
+    static constexpr int NCT = D / 64;          // 16-wide value-column tiles per wave (4 waves)
     static constexpr int NFT = D / 16;          // 16-row feature tiles of S
     static constexpr int NKB = D / 32;          // 32-feature k blocks
-    static_assert(TM == 2 || TM == 4, "loader micro-tile");
+    static constexpr int ZFT = NFT / 4;         // feature tiles of z one wave keeps (4 waves)
+    static_assert(TM == 2 || TM == 4, "staging micro-tile");
 };
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Index of the calling wave within its workgroup, as a wave-uniform (scalar) value. Branches on
+// it then compile to scalar branches; matrix-core instructions do not honour the EXEC mask, so
+// they must never sit under a lane-masked branch.
+__device__ __forceinline__ int wave_id()
+{
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
 {
@@ -59,13 +74,43 @@ template <typename T> __device__ __forceinline__ void sts(uint16_t *p, T x)
     *reinterpret_cast<T *>(p) = x;
 }
 
-// Element index of (row f, token j) in a token-contiguous [D][TS] array. Tokens are grouped
-// in 8-byte granules of 4; the granule index is XOR-swizzled by an even value taken from the
-// row so that the transposing stores below spread over all LDS banks, while 16-byte reads of
-// 8 consecutive tokens (an even granule pair) stay contiguous.
-template <int D> __device__ __forceinline__ int tix(int f, int j)
+// LDS layout of the row-major [C][D] chunk arrays. gfx950 LDS has 64 banks of 4 bytes for
+// reads and 32 for writes; a 16-byte store is served 8 lanes at a time, an 8-byte read 32
+// lanes at a time, and a 16-byte read 16 lanes at a time, grouped as lanes 4q..4q+3 of one
+// half-wave whose quad index q has the same bit parity. Layout: rows padded to D + 16 elements,
+// a further 64 elements after every 8 rows, and the low bit of the 16-byte granule index
+// flipped in rows with bit 3 set. With it, every access below is free of bank conflicts:
+//   staging stores (8 lanes = 128 contiguous bytes of one row),
+//   16-byte operand reads (16 consecutive rows x one granule per lane group),
+//   8-byte reads of 16 consecutive rows x one granule, and the transpose reads
+//   (8 consecutive rows x 32 bytes),
+// and every per-access address is a lane base plus a constant.
+template <int D> __device__ __forceinline__ int nix(int row, int col)
 {
-    return f * Cfg<D>::TS + ((((j >> 2) ^ ((f >> 3) & 14))) << 2) + (j & 3);
+    return row * Cfg<D>::RS + 64 * (row >> 3) + ((((col >> 3) ^ ((row >> 3) & 1))) << 3) + (col & 7);
+}
+
+// Operand fragment whose k-slots run over tokens, read from a row-major chunk M (tokens x
+// columns) with two transpose reads: slot 4h + y holds M[row0 + 16h + 4g + y][col0 + li].
+// (The k-slot order is a permutation of the 32 tokens of the block; every product pairs it
+// with an operand in the same order.)
+template <int D>
+__device__ __forceinline__ bf16x8 frag_tok(const uint16_t *M, int row0, int col0, int li, int g)
+{
+    const int r = row0 + 4 * g + (li >> 2), c = col0 + 4 * (li & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(M + nix<D>(r, c)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(M + nix<D>(r + 16, c)));
+    const i16x8 x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, x);
+}
+
+// Score block: [query row][key], row stride TS. Within each 32-key block, key 16h + 4q + y is
+// stored at position 8q + 4h + y, so a 16-byte read at position 8g holds the keys in the
+// k-slot order of frag_tok (slot 4h + y = key 16h + 4g + y), and one lane's two 4-key score
+// pieces of a tile pair form one 16-byte store.
+__device__ __forceinline__ int sa_ix(int row, int kblock, int g)
+{
+    return row * (C + 8) + 32 * kblock + 8 * g;
 }
 
 // φ applied to 8 packed bf16 values, result rounded to bf16 (nearest even).
@@ -78,18 +123,15 @@ __device__ __forceinline__ u32x4 phi8(u32x4 x)
     return y;
 }
 
-// Each thread owns a micro-tile of TM consecutive tokens x 8 consecutive features of a
-// [C, D] chunk. Within a wave the TM-row groups vary fastest, so one load instruction reads
-// whole 2*D-byte rows.
+// Staging of one [C, D] chunk by NT threads: consecutive lanes own consecutive 16-byte feature
+// groups of one row (FG lanes per row), so a wave's global load reads whole rows (1 KiB
+// contiguous) and 8 lanes of a staging store cover 128 contiguous bytes of one row. Thread t
+// owns rows t / FG + RPI * i, i < TM.
 template <int D> struct Tile {
     using K = Cfg<D>;
-    int a, b; // token group, feature group
-    __device__ explicit Tile(int tid)
-    {
-        const int w = tid >> 6, l = tid & 63;
-        a = K::LA * w + (l % K::LA);
-        b = l / K::LA;
-    }
+    int a, b; // first row, feature group
+    __device__ explicit Tile(int tid) : a(tid / K::FG), b(tid % K::FG) {}
+    __device__ __forceinline__ int row(int i) const { return a + K::RPI * i; }
     // rows of the chunk starting at `base`, clamped to the chunk's last valid row so every
     // access is in bounds and no load sits in a branch (a load merged with a zero in a branch
     // makes the compiler wait for it right away); rows past nvalid are masked when staged.
@@ -98,131 +140,104 @@ template <int D> struct Tile {
     {
 #pragma unroll
         for (int i = 0; i < K::TM; ++i) {
-            const int row = min(K::TM * a + i, nvalid - 1);
-            r[i] = *reinterpret_cast<const u32x4 *>(base + (size_t)row * D + 8 * b);
+            const int rr = min(row(i), nvalid - 1);
+            r[i] = *reinterpret_cast<const u32x4 *>(base + (size_t)rr * D + 8 * b);
         }
     }
-    __device__ __forceinline__ bool valid(int i, int nvalid) const { return K::TM * a + i < nvalid; }
-    // natural [C][QS] layout
-    __device__ __forceinline__ void store_rows(uint16_t *s, const u32x4 (&r)[K::TM]) const
+    __device__ __forceinline__ bool valid(int i, int nvalid) const { return row(i) < nvalid; }
+    // rows >= nvalid become 0 (phi(K) and V rows of a ragged last chunk must not contribute)
+    __device__ __forceinline__ void store(uint16_t *s, const u32x4 (&r)[K::TM], int nvalid,
+                                          bool apply_phi) const
     {
 #pragma unroll
-        for (int i = 0; i < K::TM; ++i)
-            sts<u32x4>(s + (K::TM * a + i) * K::QS + 8 * b, r[i]);
-    }
-    // transposed [D][TS] layout: feature row 8b+e receives the TM tokens of this micro-tile
-    __device__ __forceinline__ void store_cols(uint16_t *s, const u32x4 (&r)[K::TM]) const
-    {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int sh = 16 * (e & 1);
-            uint32_t h[K::TM];
-#pragma unroll
-            for (int i = 0; i < K::TM; ++i)
-                h[i] = (r[i][e >> 1] >> sh) & 0xffffu;
-            const int f = 8 * b + e;
-            if constexpr (K::TM == 4)
-                sts<u32x2>(s + tix<D>(f, 4 * a), u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)});
-            else
-                sts<uint32_t>(s + tix<D>(f, 2 * a), h[0] | (h[1] << 16));
+        for (int i = 0; i < K::TM; ++i) {
+            const u32x4 y = apply_phi ? phi8(r[i]) : r[i];
+            sts<u32x4>(s + nix<D>(row(i), 8 * b), valid(i, nvalid) ? y : u32x4{0u, 0u, 0u, 0u});
         }
     }
 };
 
-// S += Kf^T V over one chunk for the columns this wave owns. sacc[ft][ct]: rows
-// f = 16ft + 4g + r, column cw0 + 16ct + li.
-template <int D>
-__device__ __forceinline__ void state_update(f32x4 (&sacc)[Cfg<D>::NFT][Cfg<D>::NCT],
-                                             const uint16_t *sKT, const uint16_t *sVT, int cw0,
-                                             int li, int g)
+// bf16 A-operand fragment of S^T for the state read: value-column tile ct, 32-feature block m,
+// k = feature permuted as {4g..4g+3, 16+4g..16+4g+3} -- exactly the rows an accumulator pair
+// (feature tiles 2m, 2m+1) holds in this lane.
+template <int D, int NCT>
+__device__ __forceinline__ bf16x8 state_frag(const f32x4 (&sacc)[Cfg<D>::NFT][NCT], int ct, int m)
 {
-    using K = Cfg<D>;
-#pragma unroll
-    for (int m = 0; m < C / 32; ++m) {
-        bf16x8 bv[K::NCT];
-#pragma unroll
-        for (int ct = 0; ct < K::NCT; ++ct)
-            bv[ct] = lds<bf16x8>(sVT + tix<D>(cw0 + 16 * ct + li, 32 * m + 8 * g));
-#pragma unroll
-        for (int ft = 0; ft < K::NFT; ++ft) {
-            const bf16x8 ak = lds<bf16x8>(sKT + tix<D>(16 * ft + li, 32 * m + 8 * g));
-#pragma unroll
-            for (int ct = 0; ct < K::NCT; ++ct)
-                sacc[ft][ct] = mfma(ak, bv[ct], sacc[ft][ct]);
-        }
-    }
+    const f32x4 lo = sacc[2 * m][ct], hi = sacc[2 * m + 1][ct];
+    const u32x4 w = {pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(hi[0], hi[1]),
+                     pack_bf2(hi[2], hi[3])};
+    return __builtin_bit_cast(bf16x8, w);
 }
 
-// Column sums of Kf over one chunk (threads 0..2D-1: feature tid/2, half tid%2 of the chunk).
-template <int D> __device__ __forceinline__ float kf_colsum_half(const uint16_t *sKT, int tid)
-{
-    float s = 0.f;
-    if (tid < 2 * D) {
-        const int f = tid >> 1, h = tid & 1;
-#pragma unroll
-        for (int i = 0; i < C / 16; ++i) {
-            const u32x4 w = lds<u32x4>(sKT + tix<D>(f, (C / 2) * h + 8 * i));
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                s += bf_lo(w[e]) + bf_hi(w[e]);
-        }
-    }
-    return s;
-}
-
-// bf16 A-operand fragments of S^T for the state read (k = feature, permuted as
-// {4g..4g+3, 16+4g..16+4g+3} within each 32-feature block m).
-template <int D>
-__device__ __forceinline__ void state_frags(bf16x8 (&sf)[Cfg<D>::NCT][Cfg<D>::NKB],
-                                            const f32x4 (&sacc)[Cfg<D>::NFT][Cfg<D>::NCT])
-{
-    using K = Cfg<D>;
-#pragma unroll
-    for (int ct = 0; ct < K::NCT; ++ct)
-#pragma unroll
-        for (int m = 0; m < K::NKB; ++m) {
-            const f32x4 lo = sacc[2 * m][ct], hi = sacc[2 * m + 1][ct];
-            const u32x4 w = {pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(hi[0], hi[1]),
-                             pack_bf2(hi[2], hi[3])};
-            sf[ct][m] = __builtin_bit_cast(bf16x8, w);
-        }
-}
-
-// num^T += S^T Qf^T for the wave's columns and all C query rows. acc[ct][it]: rows (value
-// columns) cw0 + 16ct + 4g + r, column (query) 16it + li.
-template <int D>
-__device__ __forceinline__ void state_read(f32x4 (&acc)[Cfg<D>::NCT][4],
-                                           const bf16x8 (&sf)[Cfg<D>::NCT][Cfg<D>::NKB],
+// num^T += S^T Qf^T for the wave's value columns and all C query rows, with S the state in
+// sacc (float32, rounded to bf16 fragments here). acc[ct][it]: rows (value columns)
+// cw0 + 16ct + 4g + r, column (query) 16it + li.
+template <int D, int NCT>
+__device__ __forceinline__ void state_read(f32x4 (&acc)[NCT][4], const f32x4 (&sacc)[Cfg<D>::NFT][NCT],
                                            const uint16_t *sQ, int li, int g)
 {
     using K = Cfg<D>;
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+    for (int m = 0; m < K::NKB; ++m) {
+        bf16x8 sf[NCT];
 #pragma unroll
-        for (int m = 0; m < K::NKB; ++m) {
-            const uint16_t *row = sQ + (16 * it + li) * K::QS + 32 * m + 4 * g;
-            const u32x2 q0 = lds<u32x2>(row), q1 = lds<u32x2>(row + 16);
+        for (int ct = 0; ct < NCT; ++ct)
+            sf[ct] = state_frag<D, NCT>(sacc, ct, m);
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int r = 16 * it + li;
+            const u32x2 q0 = lds<u32x2>(sQ + nix<D>(r, 32 * m + 4 * g));
+            const u32x2 q1 = lds<u32x2>(sQ + nix<D>(r, 32 * m + 16 + 4 * g));
             const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
 #pragma unroll
-            for (int ct = 0; ct < K::NCT; ++ct)
-                acc[ct][it] = mfma(sf[ct][m], bq, acc[ct][it]);
+            for (int ct = 0; ct < NCT; ++ct)
+                acc[ct][it] = mfma(sf[ct], bq, acc[ct][it]);
         }
+    }
+}
+
+// S += Kf^T V over one chunk for the NCT value-column tiles this wave owns (from cw0), and
+// z += Kf^T 1 for the ZT feature tiles starting at zf0 (every column of a zacc tile holds the
+// same sum). sacc[ft][ct]: rows f = 16ft + 4g + r, column cw0 + 16ct + li.
+template <int D, int NCT, int ZT>
+__device__ __forceinline__ void state_update(f32x4 (&sacc)[Cfg<D>::NFT][NCT], f32x4 (&zacc)[ZT],
+                                             const uint16_t *sK, const uint16_t *sV, int zf0,
+                                             int cw0, int li, int g)
+{
+    using K = Cfg<D>;
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+    for (int m = 0; m < C / 32; ++m) {
+        bf16x8 bv[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            bv[ct] = frag_tok<D>(sV, 32 * m, cw0 + 16 * ct, li, g);
+#pragma unroll
+        for (int ft = 0; ft < K::NFT; ++ft) {
+            const bf16x8 ak = frag_tok<D>(sK, 32 * m, 16 * ft, li, g);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                sacc[ft][ct] = mfma(ak, bv[ct], sacc[ft][ct]);
+            if (ft >= zf0 && ft < zf0 + ZT) // zf0 is wave-uniform: a scalar branch
+                zacc[ft - zf0] = mfma(ak, ones, zacc[ft - zf0]);
+        }
+    }
 }
 
 // out rows [0, nvalid) of the chunk at `ob`: out = num / den, rounded to bf16.
-template <int D>
-__device__ __forceinline__ void store_out(const f32x4 (&acc)[Cfg<D>::NCT][4], const float *sden,
-                                          uint16_t *__restrict__ ob, int nvalid, int cw0, int li,
-                                          int g)
+// The denominator of row i is sden[i] (+ sden2[i] when given).
+template <int D, int NCT>
+__device__ __forceinline__ void store_out(const f32x4 (&acc)[NCT][4], const float *sden,
+                                          const float *sden2, uint16_t *__restrict__ ob, int nvalid,
+                                          int cw0, int li, int g)
 {
-    using K = Cfg<D>;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int i = 16 * it + li;
         if (i < nvalid) {
-            const float inv = __builtin_amdgcn_rcpf(sden[i]);
+            const float inv = __builtin_amdgcn_rcpf(sden2 ? sden[i] + sden2[i] : sden[i]);
 #pragma unroll
-            for (int ct = 0; ct < K::NCT; ++ct) {
+            for (int ct = 0; ct < NCT; ++ct) {
                 const f32x4 a = acc[ct][it];
                 const u32x2 w = {pack_bf2(a[0] * inv, a[1] * inv), pack_bf2(a[2] * inv, a[3] * inv)};
                 *reinterpret_cast<u32x2 *>(ob + (size_t)i * D + cw0 + 16 * ct + 4 * g) = w;
@@ -231,30 +246,23 @@ __device__ __forceinline__ void store_out(const f32x4 (&acc)[Cfg<D>::NCT][4], co
     }
 }
 
-// sdi[i] = phi(Q)[i] . z for the C rows of a staged chunk (256 threads: row tid/4, a quarter of
-// the features each).
-template <int D>
-__device__ __forceinline__ void den_inter(float *sdi, const uint16_t *sQ, const float *sz, int tid)
+template <int D, int NCT, int ZT>
+__device__ __forceinline__ void zero_acc(f32x4 (&sacc)[Cfg<D>::NFT][NCT], f32x4 (&zacc)[ZT])
 {
-    using K = Cfg<D>;
-    const int i = tid >> 2, qq = tid & 3;
-    float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e) {
-        const int f = qq * (D / 4) + 8 * e;
-        const u32x4 qw = lds<u32x4>(sQ + i * K::QS + f);
+    for (int ft = 0; ft < Cfg<D>::NFT; ++ft)
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-            s += bf_lo(qw[h]) * sz[f + 2 * h] + bf_hi(qw[h]) * sz[f + 2 * h + 1];
-    }
-    s += __shfl_xor(s, 1, 64);
-    s += __shfl_xor(s, 2, 64);
-    if (qq == 0)
-        sdi[i] = s;
+        for (int ct = 0; ct < NCT; ++ct)
+            sacc[ft][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int zt = 0; zt < ZT; ++zt)
+        zacc[zt] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // ------------------------------------------------------------------------------------------
-// Segment sums: dS = phi(K_seg)^T V_seg, dz = colsum phi(K_seg).
+// Segment sums: dS = phi(K_seg)^T V_seg, dz = phi(K_seg)^T 1. 256 threads; every wave stages
+// the next chunk into the other half of a double-buffered LDS and then runs the matrix-core
+// update on the current one (one barrier per chunk).
 template <int D>
 __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
                                             const uint16_t *__restrict__ v,
@@ -263,47 +271,47 @@ __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
                                             int P)
 {
     using K = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t sKT[D * K::TS];
-    __shared__ __attribute__((aligned(16))) uint16_t sVT[D * K::TS];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][K::AS];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][K::AS];
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, li = l & 15, g = l >> 4;
     const int p = blockIdx.x % nseg, bh = blockIdx.x / nseg;
     const int tb = p * L, te = min(N, tb + L);
+    const int nch = (te - tb + C - 1) / C;
     const uint16_t *kb = k + (size_t)bh * N * D;
     const uint16_t *vb = v + (size_t)bh * N * D;
     const int cw0 = w * (D / 4);
     const Tile<D> tile(tid);
+    auto chunk_t0 = [&](int cc) { return tb + min(cc, nch - 1) * C; };
 
     f32x4 sacc[K::NFT][K::NCT];
-#pragma unroll
-    for (int ft = 0; ft < K::NFT; ++ft)
-#pragma unroll
-        for (int ct = 0; ct < K::NCT; ++ct)
-            sacc[ft][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float zpart = 0.f;
+    f32x4 zacc[K::ZFT];
+    zero_acc<D, K::NCT, K::ZFT>(sacc, zacc);
 
     u32x4 rk[K::TM], rv[K::TM];
     tile.load(rk, kb + (size_t)tb * D, te - tb);
     tile.load(rv, vb + (size_t)tb * D, te - tb);
-    const int tlast = tb + ((te - tb - 1) / C) * C; // first token of the segment's last chunk
-    for (int t0 = tb; t0 < te; t0 += C) {
-        const int nvalid = min(C, te - t0);
-#pragma unroll
-        for (int i = 0; i < K::TM; ++i) {
-            const bool ok = tile.valid(i, nvalid);
-            rk[i] = ok ? phi8(rk[i]) : u32x4{0u, 0u, 0u, 0u};
-            rv[i] = ok ? rv[i] : u32x4{0u, 0u, 0u, 0u};
+    tile.store(sK[0], rk, te - tb, true);
+    tile.store(sV[0], rv, te - tb, false);
+    {
+        const int tn = chunk_t0(1);
+        tile.load(rk, kb + (size_t)tn * D, te - tn);
+        tile.load(rv, vb + (size_t)tn * D, te - tn);
+    }
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1, nb = b ^ 1;
+        if (c + 1 < nch) {
+            const int n1 = min(C, te - (tb + (c + 1) * C));
+            tile.store(sK[nb], rk, n1, true);
+            tile.store(sV[nb], rv, n1, false);
         }
-        tile.store_cols(sKT, rk);
-        tile.store_cols(sVT, rv);
-        __syncthreads();
-        {   // prefetch the next chunk (the last chunk again at the end: always in bounds)
-            const int tn = min(t0 + C, tlast);
+        {
+            const int tn = chunk_t0(c + 2);
             tile.load(rk, kb + (size_t)tn * D, te - tn);
             tile.load(rv, vb + (size_t)tn * D, te - tn);
         }
-        state_update<D>(sacc, sKT, sVT, cw0, li, g);
-        zpart += kf_colsum_half<D>(sKT, tid);
+        state_update<D, K::NCT, K::ZFT>(sacc, zacc, sK[b], sV[b], w * K::ZFT, cw0, li, g);
         __syncthreads();
     }
 
@@ -315,35 +323,32 @@ __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 S[(16 * ft + 4 * g + r) * D + cw0 + 16 * ct + li] = sacc[ft][ct][r];
-    zpart += __shfl_xor(zpart, 1, 64);
-    if (tid < 2 * D && (tid & 1) == 0)
-        dstz[((long)bh * P + p) * zstride + (tid >> 1)] = zpart;
+    if (li == 0) {
+        float *z = dstz + ((long)bh * P + p) * zstride;
+#pragma unroll
+        for (int zt = 0; zt < K::ZFT; ++zt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                z[16 * (w * K::ZFT + zt) + 4 * g + r] = zacc[zt][r];
+    }
 }
 
 // ------------------------------------------------------------------------------------------
-// Causal outputs of one segment, starting from the state before the segment.
-//
-// 512 threads in two roles that share every SIMD. Waves 0-3 ("compute") hold the float32 state
-// S in accumulators (wave w owns value columns [w*D/4, (w+1)*D/4)) and run the matrix-core
-// products of chunk c. Waves 4-7 ("stage") meanwhile prepare chunk c+1 in the other half of the
-// double-buffered LDS: they apply phi, write phi(Q), phi(K) row-major and phi(K), V
-// token-major, keep the key sum z (float32, LDS) and compute the inter-chunk part of the
-// denominators, phi(q_i) . z. Two workgroup barriers per chunk:
-//   phase 1  compute: scores A of chunk c (query rows 16w..16w+15), den = rowsum(A) + phi(q).z
-//            stage:   z += colsum(phi(K_c)); phi(Q_{c+1}) -> LDS; load Q_{c+2}
-//   --- barrier X ---
-//   phase 2  compute: num = A V_c + phi(Q_c) S; out = num / den; S += phi(K_c)^T V_c
-//            stage:   phi(K_{c+1}), V_{c+1} -> LDS; load K_{c+2}, V_{c+2}; phi(Q_{c+1}) . z
-//   --- barrier Y ---
+// Causal kernel geometry: NCW = D/16 compute waves, each owning 16 value columns of S and one
+// 16-feature tile of z, plus 4 stage waves (NT threads).
+template <int D> struct CausalCfg {
+    static constexpr int NCW = D / 16;
+    static constexpr int THREADS = (NCW + 4) * 64;
+};
+
 template <int D> struct CausalLds {
-    uint16_t sQ[2][C * Cfg<D>::QS];
-    uint16_t sK[2][C * Cfg<D>::QS];
-    uint16_t sKT[2][D * Cfg<D>::TS];
-    uint16_t sVT[2][D * Cfg<D>::TS];
+    uint16_t sQ[2][Cfg<D>::AS]; // phi(Q), double-buffered (read in both phases)
+    uint16_t sK[2][Cfg<D>::AS]; // phi(K), double-buffered (read in both phases)
+    uint16_t sV[Cfg<D>::AS];    // V, read only in phase 2
     uint16_t sA[C * Cfg<D>::TS];
-    float sz[2][D];  // z before chunk c lives in sz[c & 1]
-    float sdi[2][C]; // phi(q_i) . z for chunk c in sdi[c & 1]
-    float sden[C];
+    float sz[D];           // key sum before the chunk being computed
+    float srs[C];          // rowsum(A) per query row of the chunk
+    float sqz[C];          // phi(q) . z per query row of the chunk
 };
 
 struct CausalArgs {
@@ -354,82 +359,120 @@ struct CausalArgs {
     int tb, te, nch;              // token range of the segment, chunks in it
 };
 
-// Compute role (waves 0-3). Barrier sequence: 2 in the prologue, 2 per chunk.
+// Compute role (waves 0..NCW-1). Wave w owns value columns [16w, 16w+16) of S and the key-sum
+// features [16w, 16w+16). Barrier sequence: 1 in the prologue, 2 per chunk.
 template <int D>
 __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArgs &a, int w,
                                                int li, int g)
 {
     using K = Cfg<D>;
-    const int cw0 = w * (D / 4);
-    f32x4 sacc[K::NFT][K::NCT];
-    bf16x8 sf[K::NCT][K::NKB];
+    constexpr int NCW = CausalCfg<D>::NCW;
+    const int cw0 = 16 * w;
+    f32x4 sacc[K::NFT][1];
+    f32x4 zacc[1];
+    zero_acc<D, 1, 1>(sacc, zacc);
+    if (a.S0) {
 #pragma unroll
-    for (int ft = 0; ft < K::NFT; ++ft)
-#pragma unroll
-        for (int ct = 0; ct < K::NCT; ++ct)
+        for (int ft = 0; ft < K::NFT; ++ft)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                sacc[ft][ct][r] = a.S0 ? a.S0[(16 * ft + 4 * g + r) * D + cw0 + 16 * ct + li] : 0.f;
-    state_frags<D>(sf, sacc);
-    __syncthreads();
+                sacc[ft][0][r] = a.S0[(16 * ft + 4 * g + r) * D + cw0 + li];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zacc[0][r] = a.z0[16 * w + 4 * g + r];
+    }
+    if (li == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            sm.sz[16 * w + 4 * g + r] = zacc[0][r];
+    }
     __syncthreads();
 
+    // phase-1 jobs: waves 0-3 compute the scores of query rows 16w..16w+15; the waves that
+    // compute phi(q) . z for rows 16(w%4).. are waves 4-7 (D = 128) or the same waves (D = 64)
+    const bool scores = w < 4;
+    const bool qz = NCW == 8 ? w >= 4 : true;
+    const int iw = w & 3;
     for (int c = 0; c < a.nch; ++c) {
         const int b = c & 1;
         const int t0 = a.tb + c * C, nvalid = min(C, a.te - t0);
-        // phase 1: scores of query rows 16w..16w+15 against keys j <= i; den = rowsum + phi(q).z
-        {
+        // ---- phase 1
+        if (scores) {
             bf16x8 qb[K::NKB];
 #pragma unroll
             for (int kk = 0; kk < K::NKB; ++kk)
-                qb[kk] = lds<bf16x8>(sm.sQ[b] + (16 * w + li) * K::QS + 32 * kk + 8 * g);
+                qb[kk] = lds<bf16x8>(sm.sQ[b] + nix<D>(16 * w + li, 32 * kk + 8 * g));
             float rs = 0.f;
-            for (int jt = 0; jt <= w; ++jt) {
-                f32x4 t = {0.f, 0.f, 0.f, 0.f};
+            // key tiles 2mp and 2mp + 1 (the second one is all zero past the diagonal tile)
+            for (int mp = 0; 2 * mp <= w; ++mp) {
+                uint32_t pk[4];
 #pragma unroll
-                for (int kk = 0; kk < K::NKB; ++kk)
-                    t = mfma(lds<bf16x8>(sm.sK[b] + (16 * jt + li) * K::QS + 32 * kk + 8 * g), qb[kk], t);
-                // t[r] = A[i = 16w + li][j = 16jt + 4g + r]
-                if (jt == w) {
+                for (int h = 0; h < 2; ++h) {
+                    const int jt = 2 * mp + h;
+                    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+                    if (jt <= w) { // wave-uniform
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (4 * g + r > li)
-                            t[r] = 0.f;
+                        for (int kk = 0; kk < K::NKB; ++kk)
+                            t = mfma(lds<bf16x8>(sm.sK[b] + nix<D>(16 * jt + li, 32 * kk + 8 * g)), qb[kk], t);
+                    }
+                    // t[r] = A[i = 16w + li][j = 16jt + 4g + r]
+                    if (jt == w) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (4 * g + r > li)
+                                t[r] = 0.f;
+                    }
+                    pk[2 * h] = pack_bf2(t[0], t[1]);
+                    pk[2 * h + 1] = pack_bf2(t[2], t[3]);
+                    rs += (bf_lo(pk[2 * h]) + bf_hi(pk[2 * h])) + (bf_lo(pk[2 * h + 1]) + bf_hi(pk[2 * h + 1]));
                 }
-                const uint32_t p0 = pack_bf2(t[0], t[1]), p1 = pack_bf2(t[2], t[3]);
-                sts<u32x2>(sm.sA + (16 * w + li) * K::TS + 16 * jt + 4 * g, u32x2{p0, p1});
-                rs += (bf_lo(p0) + bf_hi(p0)) + (bf_lo(p1) + bf_hi(p1));
+                sts<u32x4>(sm.sA + sa_ix(16 * w + li, mp, g), u32x4{pk[0], pk[1], pk[2], pk[3]});
             }
-            if ((w & 1) == 0) // the 32-token block read below also covers j-tile w+1: zero it
-                sts<u32x2>(sm.sA + (16 * w + li) * K::TS + 16 * (w + 1) + 4 * g, u32x2{0u, 0u});
             rs += __shfl_xor(rs, 16, 64);
             rs += __shfl_xor(rs, 32, 64);
             if (g == 0)
-                sm.sden[16 * w + li] = rs + sm.sdi[b][16 * w + li];
+                sm.srs[16 * w + li] = rs;
+        }
+        if (qz) {
+            float s = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < K::NKB; ++kk) {
+                const u32x4 qw = lds<u32x4>(sm.sQ[b] + nix<D>(16 * iw + li, 32 * kk + 8 * g));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int f = 32 * kk + 8 * g + 2 * e;
+                    s += bf_lo(qw[e]) * sm.sz[f] + bf_hi(qw[e]) * sm.sz[f + 1];
+                }
+            }
+            s += __shfl_xor(s, 16, 64);
+            s += __shfl_xor(s, 32, 64);
+            if (g == 0)
+                sm.sqz[16 * iw + li] = s;
         }
         __syncthreads();
-        // phase 2: num^T = V^T A^T + S^T Qf^T for the wave's columns; out; S += Kf^T V
+        // ---- phase 2: num^T = V^T A^T + S^T Qf^T for the wave's columns; out; S, z += Kf^T [V 1]
         {
-            f32x4 acc[K::NCT][4];
-#pragma unroll
-            for (int ct = 0; ct < K::NCT; ++ct)
-#pragma unroll
-                for (int it = 0; it < 4; ++it)
-                    acc[ct][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 acc[1][4];
 #pragma unroll
             for (int it = 0; it < 4; ++it)
+                acc[0][it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int m = 0; m <= it / 2; ++m) {
-                    const bf16x8 ba = lds<bf16x8>(sm.sA + (16 * it + li) * K::TS + 32 * m + 8 * g);
+            for (int m = 0; m < 2; ++m) {
+                const bf16x8 av = frag_tok<D>(sm.sV, 32 * m, cw0, li, g);
 #pragma unroll
-                    for (int ct = 0; ct < K::NCT; ++ct)
-                        acc[ct][it] = mfma(lds<bf16x8>(sm.sVT[b] + tix<D>(cw0 + 16 * ct + li, 32 * m + 8 * g)),
-                                           ba, acc[ct][it]);
+                for (int it = 2 * m; it < 4; ++it) {
+                    const bf16x8 ba = lds<bf16x8>(sm.sA + sa_ix(16 * it + li, m, g));
+                    acc[0][it] = mfma(av, ba, acc[0][it]);
                 }
-            state_read<D>(acc, sf, sm.sQ[b], li, g);
-            store_out<D>(acc, sm.sden, a.oh + (size_t)t0 * D, nvalid, cw0, li, g);
-            state_update<D>(sacc, sm.sKT[b], sm.sVT[b], cw0, li, g);
-            state_frags<D>(sf, sacc);
+            }
+            state_read<D, 1>(acc, sacc, sm.sQ[b], li, g);
+            store_out<D, 1>(acc, sm.srs, sm.sqz, a.oh + (size_t)t0 * D, nvalid, cw0, li, g);
+            state_update<D, 1, 1>(sacc, zacc, sm.sK[b], sm.sV, w, cw0, li, g);
+            if (li == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sm.sz[16 * w + 4 * g + r] = zacc[0][r];
+            }
         }
         __syncthreads();
     }
@@ -437,14 +480,18 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
 #pragma unroll
         for (int ft = 0; ft < K::NFT; ++ft)
 #pragma unroll
-            for (int ct = 0; ct < K::NCT; ++ct)
+            for (int r = 0; r < 4; ++r)
+                a.Sout[(16 * ft + 4 * g + r) * D + cw0 + li] = sacc[ft][0][r];
+        if (li == 0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    a.Sout[(16 * ft + 4 * g + r) * D + cw0 + 16 * ct + li] = sacc[ft][ct][r];
+            for (int r = 0; r < 4; ++r)
+                a.zout[16 * w + 4 * g + r] = zacc[0][r];
+        }
     }
 }
 
-// Stage role (waves 4-7, thread index ht = 0..255). Same barrier sequence as the compute role.
+// Stage role (4 waves after the compute waves, thread index ht = 0..255). Same barrier sequence
+// as the compute role.
 template <int D>
 __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs &a, int ht)
 {
@@ -452,106 +499,77 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
     const Tile<D> tile(ht);
     u32x4 rq[K::TM], rk[K::TM], rv[K::TM];
     const int tb = a.tb, te = a.te, nch = a.nch;
-
-    if (ht < D)
-        sm.sz[0][ht] = a.z0 ? a.z0[ht] : 0.f;
     // first token of chunk c' (clamped to the last chunk, so prefetches past the end re-read
     // it: every load is in bounds and unconditional)
     auto chunk_t0 = [&](int cc) { return tb + min(cc, nch - 1) * C; };
+
     tile.load(rq, a.qh + (size_t)tb * D, te - tb);
     tile.load(rk, a.kh + (size_t)tb * D, te - tb);
     tile.load(rv, a.vh + (size_t)tb * D, te - tb);
-#pragma unroll
-    for (int i = 0; i < K::TM; ++i) {
-        const bool ok = tile.valid(i, te - tb);
-        rq[i] = ok ? phi8(rq[i]) : u32x4{0u, 0u, 0u, 0u};
-        rk[i] = ok ? phi8(rk[i]) : u32x4{0u, 0u, 0u, 0u};
-        rv[i] = ok ? rv[i] : u32x4{0u, 0u, 0u, 0u};
-    }
-    tile.store_rows(sm.sQ[0], rq);
-    tile.store_rows(sm.sK[0], rk);
-    tile.store_cols(sm.sKT[0], rk);
-    tile.store_cols(sm.sVT[0], rv);
+    tile.store(sm.sQ[0], rq, te - tb, true);
+    tile.store(sm.sK[0], rk, te - tb, true);
     {
         const int tn = chunk_t0(1);
         tile.load(rq, a.qh + (size_t)tn * D, te - tn);
         tile.load(rk, a.kh + (size_t)tn * D, te - tn);
-        tile.load(rv, a.vh + (size_t)tn * D, te - tn);
     }
-    __syncthreads();
-    den_inter<D>(sm.sdi[0], sm.sQ[0], sm.sz[0], ht);
     __syncthreads();
 
     for (int c = 0; c < nch; ++c) {
-        const int b = c & 1, nb = b ^ 1;
+        const int nb = (c & 1) ^ 1;
         const int t0 = tb + c * C;
+        const int n0 = min(C, te - t0);     // valid rows of chunk c
         const int n1 = min(C, te - t0 - C); // valid rows of chunk c+1 (if it exists)
-        const int tn = chunk_t0(c + 2), nn = te - tn;
-        // phase 1: z after chunk c; phi(Q_{c+1}) -> LDS; load Q_{c+2}
+        // phase 1: V_c -> LDS, load V_{c+1}; phi(Q_{c+1}) -> LDS, load Q_{c+2}
+        tile.store(sm.sV, rv, n0, false);
         {
-            float zs = kf_colsum_half<D>(sm.sKT[b], ht);
-            zs += __shfl_xor(zs, 1, 64);
-            if (ht < 2 * D && (ht & 1) == 0)
-                sm.sz[nb][ht >> 1] = sm.sz[b][ht >> 1] + zs;
-            if (c + 1 < nch) {
-#pragma unroll
-                for (int i = 0; i < K::TM; ++i)
-                    rq[i] = tile.valid(i, n1) ? phi8(rq[i]) : u32x4{0u, 0u, 0u, 0u};
-                tile.store_rows(sm.sQ[nb], rq);
-            }
-            tile.load(rq, a.qh + (size_t)tn * D, nn);
+            const int tn = chunk_t0(c + 1);
+            tile.load(rv, a.vh + (size_t)tn * D, te - tn);
+        }
+        if (c + 1 < nch)
+            tile.store(sm.sQ[nb], rq, n1, true);
+        {
+            const int tn = chunk_t0(c + 2);
+            tile.load(rq, a.qh + (size_t)tn * D, te - tn);
         }
         __syncthreads();
-        // phase 2: phi(K_{c+1}), V_{c+1} -> LDS; load K_{c+2}, V_{c+2}; phi(Q_{c+1}) . z
-        if (c + 1 < nch) {
-#pragma unroll
-            for (int i = 0; i < K::TM; ++i) {
-                const bool ok = tile.valid(i, n1);
-                rk[i] = ok ? phi8(rk[i]) : u32x4{0u, 0u, 0u, 0u};
-                rv[i] = ok ? rv[i] : u32x4{0u, 0u, 0u, 0u};
-            }
-            tile.store_rows(sm.sK[nb], rk);
-            tile.store_cols(sm.sKT[nb], rk);
-            tile.store_cols(sm.sVT[nb], rv);
-        }
-        tile.load(rk, a.kh + (size_t)tn * D, nn);
-        tile.load(rv, a.vh + (size_t)tn * D, nn);
+        // phase 2: phi(K_{c+1}) -> LDS, load K_{c+2}
         if (c + 1 < nch)
-            den_inter<D>(sm.sdi[nb], sm.sQ[nb], sm.sz[nb], ht);
+            tile.store(sm.sK[nb], rk, n1, true);
+        {
+            const int tn = chunk_t0(c + 2);
+            tile.load(rk, a.kh + (size_t)tn * D, te - tn);
+        }
         __syncthreads();
     }
-    if (a.zout && ht < D)
-        a.zout[ht] = sm.sz[nch & 1][ht];
 }
 
 // ------------------------------------------------------------------------------------------
 // Causal outputs of one segment, starting from the state before the segment.
 //
-// 512 threads in two roles that share every SIMD. Waves 0-3 ("compute") hold the float32 state
-// S in accumulators (wave w owns value columns [w*D/4, (w+1)*D/4)) and run the matrix-core
-// products of chunk c. Waves 4-7 ("stage") meanwhile prepare chunk c+1 in the other half of the
-// double-buffered LDS: they apply phi, write phi(Q), phi(K) row-major and phi(K), V
-// token-major, keep the key sum z (float32, LDS) and compute the inter-chunk part of the
-// denominators, phi(q_i) . z. Two workgroup barriers per chunk:
-//   phase 1  compute: scores A of chunk c (query rows 16w..16w+15), den = rowsum(A) + phi(q).z
-//            stage:   z += colsum(phi(K_c)); phi(Q_{c+1}) -> LDS; load Q_{c+2}
+// Two roles share every SIMD. D/16 "compute" waves hold the float32 state S and key sum z in
+// accumulators (16 value columns of S and 16 features of z each) and run the matrix-core
+// products of chunk c. Four "stage" waves load the next chunks from HBM, apply phi and store
+// them row-major into LDS. Two barriers per chunk:
+//   phase 1  compute: scores A of chunk c (waves 0-3: query rows 16w..16w+15), rowsum(A) and
+//                     phi(q) . z per query row
+//            stage:   V_c -> LDS, load V_{c+1}; phi(Q_{c+1}) -> LDS, load Q_{c+2}
 //   --- barrier ---
-//   phase 2  compute: num = A V_c + phi(Q_c) S; out = num / den; S += phi(K_c)^T V_c
-//            stage:   phi(K_{c+1}), V_{c+1} -> LDS; load K_{c+2}, V_{c+2}; phi(Q_{c+1}) . z
+//   phase 2  compute: num = A V_c + phi(Q_c) S; out = num / den; S, z += phi(K_c)^T [V_c 1]
+//            stage:   phi(K_{c+1}) -> LDS, load K_{c+2}
 //   --- barrier ---
-// The roles are wave-uniform, so every wave executes the same sequence of barriers.
+// Roles are chosen by the wave-uniform wave index, so every wave executes the same sequence of
+// barriers.
 template <int D>
-__global__ __launch_bounds__(2 * NT) void k_causal(const uint16_t *__restrict__ q,
-                                                   const uint16_t *__restrict__ k,
-                                                   const uint16_t *__restrict__ v,
-                                                   uint16_t *__restrict__ out,
-                                                   const float *__restrict__ preS,
-                                                   const float *__restrict__ prez, long pstride,
-                                                   long pzstride, float *__restrict__ Sout,
-                                                   float *__restrict__ zout, int N, int L, int P)
+__global__ __launch_bounds__(CausalCfg<D>::THREADS) void k_causal(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    uint16_t *__restrict__ out, const float *__restrict__ preS, const float *__restrict__ prez,
+    long pstride, long pzstride, float *__restrict__ Sout, float *__restrict__ zout, int N, int L,
+    int P)
 {
+    constexpr int NCW = CausalCfg<D>::NCW;
     __shared__ __attribute__((aligned(16))) CausalLds<D> sm;
-    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), l = tid & 63;
     const int p = blockIdx.x % P, bh = blockIdx.x / P;
     const size_t hoff = (size_t)bh * N * D;
     CausalArgs a;
@@ -567,10 +585,10 @@ __global__ __launch_bounds__(2 * NT) void k_causal(const uint16_t *__restrict__ 
     a.tb = p * L;
     a.te = min(N, a.tb + L);
     a.nch = (a.te - a.tb + C - 1) / C;
-    if (wave < 4)
+    if (wave < NCW)
         causal_compute<D>(sm, a, wave, l & 15, l >> 4);
     else
-        causal_stage<D>(sm, a, tid - NT);
+        causal_stage<D>(sm, a, tid - NCW * 64);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -582,11 +600,11 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
                                               const float *__restrict__ z, int N, int L, int P)
 {
     using K = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[C * K::QS];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[K::AS];
     __shared__ float sz[D];
     __shared__ float sden[C];
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, g = l >> 4;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, li = l & 15, g = l >> 4;
     const int p = blockIdx.x % P, bh = blockIdx.x / P;
     const int tb = p * L, te = min(N, tb + L);
     const size_t hoff = (size_t)bh * N * D;
@@ -619,10 +637,7 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
     const int tlast = tb + ((te - tb - 1) / C) * C;
     for (int t0 = tb; t0 < te; t0 += C) {
         const int nvalid = min(C, te - t0);
-#pragma unroll
-        for (int i = 0; i < K::TM; ++i)
-            rq[i] = tile.valid(i, nvalid) ? phi8(rq[i]) : u32x4{0u, 0u, 0u, 0u};
-        tile.store_rows(sQ, rq);
+        tile.store(sQ, rq, nvalid, true);
         __syncthreads();
         {
             const int tn = min(t0 + C, tlast);
@@ -635,7 +650,7 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
 #pragma unroll
             for (int e = 0; e < D / 32; ++e) {
                 const int f = qq * (D / 4) + 8 * e;
-                const u32x4 qw = lds<u32x4>(sQ + i * K::QS + f);
+                const u32x4 qw = lds<u32x4>(sQ + nix<D>(i, f));
 #pragma unroll
                 for (int h = 0; h < 4; ++h)
                     s += bf_lo(qw[h]) * sz[f + 2 * h] + bf_hi(qw[h]) * sz[f + 2 * h + 1];
@@ -652,8 +667,19 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
 #pragma unroll
             for (int it = 0; it < 4; ++it)
                 acc[ct][it] = f32x4{0.f, 0.f, 0.f, 0.f};
-        state_read<D>(acc, sf, sQ, li, g);
-        store_out<D>(acc, sden, out + hoff + (size_t)t0 * D, nvalid, cw0, li, g);
+#pragma unroll
+        for (int m = 0; m < K::NKB; ++m)
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int r = 16 * it + li;
+                const u32x2 q0 = lds<u32x2>(sQ + nix<D>(r, 32 * m + 4 * g));
+                const u32x2 q1 = lds<u32x2>(sQ + nix<D>(r, 32 * m + 16 + 4 * g));
+                const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
+#pragma unroll
+                for (int ct = 0; ct < K::NCT; ++ct)
+                    acc[ct][it] = mfma(sf[ct][m], bq, acc[ct][it]);
+            }
+        store_out<D, K::NCT>(acc, sden, nullptr, out + hoff + (size_t)t0 * D, nvalid, cw0, li, g);
         __syncthreads();
     }
 }
@@ -678,16 +704,16 @@ hipError_t causal_mfma(int D, const void *q, const void *k, const void *v, void 
                        const float *preS, const float *prez, long pstride, long pzstride,
                        float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st)
 {
-    const dim3 grid((unsigned)(BH * P)), block(2 * NT);
+    const dim3 grid((unsigned)(BH * P));
     const auto *qq = static_cast<const uint16_t *>(q);
     const auto *kk = static_cast<const uint16_t *>(k);
     const auto *vv = static_cast<const uint16_t *>(v);
     auto *oo = static_cast<uint16_t *>(out);
     if (D == 128)
-        hipLaunchKernelGGL(k_causal<128>, grid, block, 0, st, qq, kk, vv, oo, preS, prez, pstride,
+        hipLaunchKernelGGL(k_causal<128>, grid, dim3(CausalCfg<128>::THREADS), 0, st, qq, kk, vv, oo, preS, prez, pstride,
                            pzstride, Sout, zout, N, L, P);
     else
-        hipLaunchKernelGGL(k_causal<64>, grid, block, 0, st, qq, kk, vv, oo, preS, prez, pstride,
+        hipLaunchKernelGGL(k_causal<64>, grid, dim3(CausalCfg<64>::THREADS), 0, st, qq, kk, vv, oo, preS, prez, pstride,
                            pzstride, Sout, zout, N, L, P);
     return hipGetLastError();
 }
