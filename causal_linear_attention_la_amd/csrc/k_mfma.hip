@@ -83,23 +83,31 @@ template <typename T> __device__ __forceinline__ void sts(uint16_t *p, T x)
 //   staging stores (8 lanes = 128 contiguous bytes of one row),
 //   16-byte operand reads (16 consecutive rows x one granule per lane group),
 //   8-byte reads of 16 consecutive rows x one granule, and the transpose reads
-//   (8 consecutive rows x 32 bytes),
-// and every per-access address is a lane base plus a constant.
+//   (8 consecutive rows x 32 bytes).
 template <int D> __device__ __forceinline__ int nix(int row, int col)
 {
     return row * Cfg<D>::RS + 64 * (row >> 3) + ((((col >> 3) ^ ((row >> 3) & 1))) << 3) + (col & 7);
 }
-
-// Operand fragment whose k-slots run over tokens, read from a row-major chunk M (tokens x
-// columns) with two transpose reads: slot 4h + y holds M[row0 + 16h + 4g + y][col0 + li].
-// (The k-slot order is a permutation of the 32 tokens of the block; every product pairs it
-// with an operand in the same order.)
-template <int D>
-__device__ __forceinline__ bf16x8 frag_tok(const uint16_t *M, int row0, int col0, int li, int g)
+// For row0 % 16 == 0 and col0 % 16 == 0: nix(row0 + r, col0 + c) == blk(row0, col0) + nix(r, c).
+// Every access below splits its address this way into a lane part computed once and a
+// compile-time block part that becomes the instruction's immediate offset.
+template <int D> __host__ __device__ constexpr int blk(int row0, int col0)
 {
-    const int r = row0 + 4 * g + (li >> 2), c = col0 + 4 * (li & 3);
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(M + nix<D>(r, c)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(M + nix<D>(r + 16, c)));
+    return row0 * (Cfg<D>::RS + 8) + col0;
+}
+
+// Operand fragment whose k-slots run over tokens, read with two transpose reads from a
+// row-major chunk (tokens x columns): slot 4h + y holds M[row0 + 16h + 4g + y][col0 + li].
+// `p` = chunk base + blk(row0, col0) + tr_lane(li, g). (The k-slot order is a permutation of
+// the 32 tokens of the block; every product pairs it with an operand in the same order.)
+template <int D> __device__ __forceinline__ int tr_lane(int li, int g)
+{
+    return nix<D>(4 * g + (li >> 2), 4 * (li & 3));
+}
+template <int D> __device__ __forceinline__ bf16x8 frag_tok(const uint16_t *p)
+{
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + blk<D>(16, 0)));
     const i16x8 x = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, x);
 }
@@ -113,13 +121,21 @@ __device__ __forceinline__ int sa_ix(int row, int kblock, int g)
     return row * (C + 8) + 32 * kblock + 8 * g;
 }
 
-// φ applied to 8 packed bf16 values, result rounded to bf16 (nearest even).
+// phi(x) = ELU(x) + 1 = exp(min(x, 0)) + max(x, 0) on 8 packed bf16 values, rounded to bf16
+// (nearest even). min and max are taken on the bit patterns (an integer compare orders floats
+// correctly against zero), so no compare/select pair is needed.
+__device__ __forceinline__ float phi_bits(uint32_t xb)
+{
+    const int xi = (int)xb;
+    const float neg = __int_as_float(min(xi, 0)), pos = __int_as_float(max(xi, 0));
+    return __builtin_amdgcn_exp2f(neg * 1.44269504088896341f) + pos;
+}
 __device__ __forceinline__ u32x4 phi8(u32x4 x)
 {
     u32x4 y;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        y[i] = pack_bf2(phi_fast(bf_lo(x[i])), phi_fast(bf_hi(x[i])));
+        y[i] = pack_bf2(phi_bits(x[i] << 16), phi_bits(x[i] & 0xffff0000u));
     return y;
 }
 
@@ -129,33 +145,51 @@ __device__ __forceinline__ u32x4 phi8(u32x4 x)
 // owns rows t / FG + RPI * i, i < TM.
 template <int D> struct Tile {
     using K = Cfg<D>;
-    int a, b; // first row, feature group
-    __device__ explicit Tile(int tid) : a(tid / K::FG), b(tid % K::FG) {}
-    __device__ __forceinline__ int row(int i) const { return a + K::RPI * i; }
-    // rows of the chunk starting at `base`, clamped to the chunk's last valid row so every
-    // access is in bounds and no load sits in a branch (a load merged with a zero in a branch
-    // makes the compiler wait for it right away); rows past nvalid are masked when staged.
+    int a, b;  // first row, feature group
+    int lofs;  // LDS offset (elements) of (row a, group b)
+    __device__ explicit Tile(int tid) : a(tid / K::FG), b(tid % K::FG), lofs(nix<D>(a, 8 * b)) {}
+    // rows of the chunk starting at `base` (wave-uniform), clamped to the chunk's last valid row
+    // so every access is in bounds and no load sits in a branch (a load merged with a zero in a
+    // branch makes the compiler wait for it right away); rows past nvalid are masked when staged.
+    // Offsets are 32-bit from the uniform base, so the loads use scalar-base addressing.
     __device__ __forceinline__ void load(u32x4 (&r)[K::TM], const uint16_t *__restrict__ base,
                                          int nvalid) const
     {
+        const char *bb = reinterpret_cast<const char *>(base);
 #pragma unroll
         for (int i = 0; i < K::TM; ++i) {
-            const int rr = min(row(i), nvalid - 1);
-            r[i] = *reinterpret_cast<const u32x4 *>(base + (size_t)rr * D + 8 * b);
+            const uint32_t rr = (uint32_t)min(a + K::RPI * i, nvalid - 1);
+            r[i] = *reinterpret_cast<const u32x4 *>(bb + (rr * (uint32_t)(2 * D) + 16u * (uint32_t)b));
         }
     }
-    __device__ __forceinline__ bool valid(int i, int nvalid) const { return row(i) < nvalid; }
     // rows >= nvalid become 0 (phi(K) and V rows of a ragged last chunk must not contribute)
     __device__ __forceinline__ void store(uint16_t *s, const u32x4 (&r)[K::TM], int nvalid,
                                           bool apply_phi) const
     {
+        if (nvalid >= C) { // wave-uniform: a full chunk needs no masking
 #pragma unroll
-        for (int i = 0; i < K::TM; ++i) {
-            const u32x4 y = apply_phi ? phi8(r[i]) : r[i];
-            sts<u32x4>(s + nix<D>(row(i), 8 * b), valid(i, nvalid) ? y : u32x4{0u, 0u, 0u, 0u});
+            for (int i = 0; i < K::TM; ++i)
+                sts<u32x4>(s + lofs + blk<D>(K::RPI * i, 0), apply_phi ? phi8(r[i]) : r[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < K::TM; ++i) {
+                const u32x4 y = apply_phi ? phi8(r[i]) : r[i];
+                const bool ok = a + K::RPI * i < nvalid;
+                sts<u32x4>(s + lofs + blk<D>(K::RPI * i, 0), ok ? y : u32x4{0u, 0u, 0u, 0u});
+            }
         }
     }
 };
+
+// An offset hidden from the compiler. The 8-byte state-read pieces of one lane sit 32 or 64
+// bytes apart; with their offsets visible the compiler merges them into ds_read2_b64, which
+// gfx950 serves with bank conflicts that separate 8-byte reads do not have. Reads off distinct
+// hidden bases cannot be merged (same-base reads below are >= 4 KiB apart, out of its range).
+__device__ __forceinline__ int hidden(int x)
+{
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // bf16 A-operand fragment of S^T for the state read: value-column tile ct, 32-feature block m,
 // k = feature permuted as {4g..4g+3, 16+4g..16+4g+3} -- exactly the rows an accumulator pair
@@ -171,10 +205,10 @@ __device__ __forceinline__ bf16x8 state_frag(const f32x4 (&sacc)[Cfg<D>::NFT][NC
 
 // num^T += S^T Qf^T for the wave's value columns and all C query rows, with S the state in
 // sacc (float32, rounded to bf16 fragments here). acc[ct][it]: rows (value columns)
-// cw0 + 16ct + 4g + r, column (query) 16it + li.
+// cw0 + 16ct + 4g + r, column (query) 16it + li. `q` = Qf chunk base + nix(li, 4g).
 template <int D, int NCT>
 __device__ __forceinline__ void state_read(f32x4 (&acc)[NCT][4], const f32x4 (&sacc)[Cfg<D>::NFT][NCT],
-                                           const uint16_t *sQ, int li, int g)
+                                           const uint16_t *q)
 {
     using K = Cfg<D>;
 #pragma unroll
@@ -183,11 +217,11 @@ __device__ __forceinline__ void state_read(f32x4 (&acc)[NCT][4], const f32x4 (&s
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
             sf[ct] = state_frag<D, NCT>(sacc, ct, m);
+        const uint16_t *q0b = q + hidden(32 * m), *q1b = q + hidden(32 * m + 16);
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int r = 16 * it + li;
-            const u32x2 q0 = lds<u32x2>(sQ + nix<D>(r, 32 * m + 4 * g));
-            const u32x2 q1 = lds<u32x2>(sQ + nix<D>(r, 32 * m + 16 + 4 * g));
+            const u32x2 q0 = lds<u32x2>(q0b + blk<D>(16 * it, 0));
+            const u32x2 q1 = lds<u32x2>(q1b + blk<D>(16 * it, 0));
             const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
@@ -196,32 +230,41 @@ __device__ __forceinline__ void state_read(f32x4 (&acc)[NCT][4], const f32x4 (&s
     }
 }
 
-// S += Kf^T V over one chunk for the NCT value-column tiles this wave owns (from cw0), and
-// z += Kf^T 1 for the ZT feature tiles starting at zf0 (every column of a zacc tile holds the
-// same sum). sacc[ft][ct]: rows f = 16ft + 4g + r, column cw0 + 16ct + li.
-template <int D, int NCT, int ZT>
-__device__ __forceinline__ void state_update(f32x4 (&sacc)[Cfg<D>::NFT][NCT], f32x4 (&zacc)[ZT],
-                                             const uint16_t *sK, const uint16_t *sV, int zf0,
-                                             int cw0, int li, int g)
+// S += Kf^T V over one chunk for the NCT value-column tiles of this wave. sacc[ft][ct]: rows
+// f = 16ft + 4g + r, column 16ct + li of the wave's columns. `k` = Kf chunk base + tr_lane,
+// `v` = V chunk base + (first column of the wave) + tr_lane.
+template <int D, int NCT>
+__device__ __forceinline__ void state_update(f32x4 (&sacc)[Cfg<D>::NFT][NCT], const uint16_t *k,
+                                             const uint16_t *v)
 {
     using K = Cfg<D>;
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 #pragma unroll
     for (int m = 0; m < C / 32; ++m) {
         bf16x8 bv[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
-            bv[ct] = frag_tok<D>(sV, 32 * m, cw0 + 16 * ct, li, g);
+            bv[ct] = frag_tok<D>(v + blk<D>(32 * m, 16 * ct));
 #pragma unroll
         for (int ft = 0; ft < K::NFT; ++ft) {
-            const bf16x8 ak = frag_tok<D>(sK, 32 * m, 16 * ft, li, g);
+            const bf16x8 ak = frag_tok<D>(k + blk<D>(32 * m, 16 * ft));
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
                 sacc[ft][ct] = mfma(ak, bv[ct], sacc[ft][ct]);
-            if (ft >= zf0 && ft < zf0 + ZT) // zf0 is wave-uniform: a scalar branch
-                zacc[ft - zf0] = mfma(ak, ones, zacc[ft - zf0]);
         }
     }
+}
+
+// z += Kf^T 1 for ZT feature tiles (every column of a zacc tile holds the same sum).
+// `k` = Kf chunk base + (first feature of the tiles) + tr_lane.
+template <int D, int ZT>
+__device__ __forceinline__ void key_sum(f32x4 (&zacc)[ZT], const uint16_t *k)
+{
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+#pragma unroll
+    for (int m = 0; m < C / 32; ++m)
+#pragma unroll
+        for (int zt = 0; zt < ZT; ++zt)
+            zacc[zt] = mfma(frag_tok<D>(k + blk<D>(32 * m, 16 * zt)), ones, zacc[zt]);
 }
 
 // out rows [0, nvalid) of the chunk at `ob`: out = num / den, rounded to bf16.
@@ -281,6 +324,7 @@ __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
     const uint16_t *kb = k + (size_t)bh * N * D;
     const uint16_t *vb = v + (size_t)bh * N * D;
     const int cw0 = w * (D / 4);
+    const int trl = tr_lane<D>(li, g);
     const Tile<D> tile(tid);
     auto chunk_t0 = [&](int cc) { return tb + min(cc, nch - 1) * C; };
 
@@ -311,7 +355,8 @@ __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
             tile.load(rk, kb + (size_t)tn * D, te - tn);
             tile.load(rv, vb + (size_t)tn * D, te - tn);
         }
-        state_update<D, K::NCT, K::ZFT>(sacc, zacc, sK[b], sV[b], w * K::ZFT, cw0, li, g);
+        state_update<D, K::NCT>(sacc, sK[b] + trl, sV[b] + cw0 + trl);
+        key_sum<D, K::ZFT>(zacc, sK[b] + 16 * (w * K::ZFT) + trl);
         __syncthreads();
     }
 
@@ -368,6 +413,10 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
     using K = Cfg<D>;
     constexpr int NCW = CausalCfg<D>::NCW;
     const int cw0 = 16 * w;
+    // per-lane LDS offsets of the access patterns (elements)
+    const int trl = tr_lane<D>(li, g); // transpose reads
+    const int opl = nix<D>(li, 8 * g); // 16-byte operand reads, rows 16t + li
+    const int sql = nix<D>(li, 4 * g); // 8-byte state-read pieces, rows 16t + li
     f32x4 sacc[K::NFT][1];
     f32x4 zacc[1];
     zero_acc<D, 1, 1>(sacc, zacc);
@@ -396,12 +445,13 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
     for (int c = 0; c < a.nch; ++c) {
         const int b = c & 1;
         const int t0 = a.tb + c * C, nvalid = min(C, a.te - t0);
+        const uint16_t *sQ = sm.sQ[b], *sK = sm.sK[b];
         // ---- phase 1
         if (scores) {
             bf16x8 qb[K::NKB];
 #pragma unroll
             for (int kk = 0; kk < K::NKB; ++kk)
-                qb[kk] = lds<bf16x8>(sm.sQ[b] + nix<D>(16 * w + li, 32 * kk + 8 * g));
+                qb[kk] = lds<bf16x8>(sQ + opl + blk<D>(16 * w, 32 * kk));
             float rs = 0.f;
             // key tiles 2mp and 2mp + 1 (the second one is all zero past the diagonal tile)
             for (int mp = 0; 2 * mp <= w; ++mp) {
@@ -413,7 +463,7 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
                     if (jt <= w) { // wave-uniform
 #pragma unroll
                         for (int kk = 0; kk < K::NKB; ++kk)
-                            t = mfma(lds<bf16x8>(sm.sK[b] + nix<D>(16 * jt + li, 32 * kk + 8 * g)), qb[kk], t);
+                            t = mfma(lds<bf16x8>(sK + opl + blk<D>(16 * jt, 32 * kk)), qb[kk], t);
                     }
                     // t[r] = A[i = 16w + li][j = 16jt + 4g + r]
                     if (jt == w) {
@@ -437,12 +487,11 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
             float s = 0.f;
 #pragma unroll
             for (int kk = 0; kk < K::NKB; ++kk) {
-                const u32x4 qw = lds<u32x4>(sm.sQ[b] + nix<D>(16 * iw + li, 32 * kk + 8 * g));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int f = 32 * kk + 8 * g + 2 * e;
-                    s += bf_lo(qw[e]) * sm.sz[f] + bf_hi(qw[e]) * sm.sz[f + 1];
-                }
+                const u32x4 qw = lds<u32x4>(sQ + opl + blk<D>(16 * iw, 32 * kk));
+                const f32x4 z0 = *reinterpret_cast<const f32x4 *>(sm.sz + 32 * kk + 8 * g);
+                const f32x4 z1 = *reinterpret_cast<const f32x4 *>(sm.sz + 32 * kk + 8 * g + 4);
+                s += bf_lo(qw[0]) * z0[0] + bf_hi(qw[0]) * z0[1] + bf_lo(qw[1]) * z0[2] + bf_hi(qw[1]) * z0[3];
+                s += bf_lo(qw[2]) * z1[0] + bf_hi(qw[2]) * z1[1] + bf_lo(qw[3]) * z1[2] + bf_hi(qw[3]) * z1[3];
             }
             s += __shfl_xor(s, 16, 64);
             s += __shfl_xor(s, 32, 64);
@@ -458,16 +507,17 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
                 acc[0][it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const bf16x8 av = frag_tok<D>(sm.sV, 32 * m, cw0, li, g);
+                const bf16x8 av = frag_tok<D>(sm.sV + cw0 + trl + blk<D>(32 * m, 0));
 #pragma unroll
                 for (int it = 2 * m; it < 4; ++it) {
                     const bf16x8 ba = lds<bf16x8>(sm.sA + sa_ix(16 * it + li, m, g));
                     acc[0][it] = mfma(av, ba, acc[0][it]);
                 }
             }
-            state_read<D, 1>(acc, sacc, sm.sQ[b], li, g);
+            state_read<D, 1>(acc, sacc, sQ + sql);
             store_out<D, 1>(acc, sm.srs, sm.sqz, a.oh + (size_t)t0 * D, nvalid, cw0, li, g);
-            state_update<D, 1, 1>(sacc, zacc, sm.sK[b], sm.sV, w, cw0, li, g);
+            state_update<D, 1>(sacc, sK + trl, sm.sV + cw0 + trl);
+            key_sum<D, 1>(zacc, sK + 16 * w + trl);
             if (li == 0) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -609,6 +659,7 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
     const int tb = p * L, te = min(N, tb + L);
     const size_t hoff = (size_t)bh * N * D;
     const int cw0 = w * (D / 4);
+    const int sql = nix<D>(li, 4 * g);
     const Tile<D> tile(tid);
 
     bf16x8 sf[K::NCT][K::NKB];
@@ -668,17 +719,18 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
             for (int it = 0; it < 4; ++it)
                 acc[ct][it] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < K::NKB; ++m)
+        for (int m = 0; m < K::NKB; ++m) {
+            const uint16_t *q0b = sQ + sql + hidden(32 * m), *q1b = sQ + sql + hidden(32 * m + 16);
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
-                const int r = 16 * it + li;
-                const u32x2 q0 = lds<u32x2>(sQ + nix<D>(r, 32 * m + 4 * g));
-                const u32x2 q1 = lds<u32x2>(sQ + nix<D>(r, 32 * m + 16 + 4 * g));
+                const u32x2 q0 = lds<u32x2>(q0b + blk<D>(16 * it, 0));
+                const u32x2 q1 = lds<u32x2>(q1b + blk<D>(16 * it, 0));
                 const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
 #pragma unroll
                 for (int ct = 0; ct < K::NCT; ++ct)
                     acc[ct][it] = mfma(sf[ct][m], bq, acc[ct][it]);
             }
+        }
         store_out<D, K::NCT>(acc, sden, nullptr, out + hoff + (size_t)t0 * D, nvalid, cw0, li, g);
         __syncthreads();
     }
