@@ -7,9 +7,11 @@ workload B=2 H=16 N=8192 d=d_v=128 bf16, inputs IID N(0, 1/128), state out. K st
 between device synchronisations; input sets rotate over three copies (806 MB > the 256 MB
 last-level cache) so a step does not find its inputs cached by the previous one.
 
-Printed: one JSON line with the headline (token-heads per second), the HBM roofline of the
-prefill call measured with HIP events on its stream, the float64 oracle timed on the host, and
-the decode (B=256 H=32 d=128, 4096-token state) and global (B=1 H=8 N=100000) forms.
+Printed: one JSON line with the headline (token-heads per second); the HBM roofline of the
+dominant kernel, k_causal, from HIP events the library records on the launch stream around each
+of its kernels (la_causal_fwd_profiled), with the whole call's fraction beside it; the float64
+oracle timed on the host; and the decode (B=256 H=32 d=128, 4096-token state) and global
+(B=1 H=8 N=100000) forms.
 """
 from __future__ import annotations
 
@@ -91,9 +93,19 @@ def bench_prefill(args):
     ms, wall = time_calls(step, args.steps, args.warmup)
     # same buffers every step (inputs may stay in the last-level cache)
     ms_hot, _ = time_calls(lambda i: step(0), args.steps, 2)
+
+    # per-kernel device times: HIP events recorded by the library on the launch stream around
+    # each of the call's kernels (segment sums, segment scan, causal outputs)
+    phases = []
+    for i in range(args.steps):
+        q, k, v, out, S, z, state = sets[i % len(sets)]
+        state.zero_()
+        phases.append(la.la_causal_fwd_profiled(q, k, v, out, S, z, chunk=args.chunk,
+                                                seg_len=args.seg_len))
+    kern_ms = [statistics.fmean(p[j] for p in phases) for j in range(3)]
     byts, flops = algo_prefill(w.B, w.H, w.N, w.d, w.dv)
     P = math.ceil(w.N / (args.seg_len or _auto_seg(w.B * w.H, w.N)))
-    return w, ms, ms_hot, wall, byts, flops, P
+    return w, ms, ms_hot, wall, byts, flops, P, kern_ms
 
 
 def _auto_seg(BH, N, chunk=64, target=512):
@@ -172,6 +184,35 @@ def cpu_baseline():
                       f"float64 token-serial recurrence, median of 3 runs of {t:.2f} s"}
 
 
+def copy_calibration(nbytes=256 << 20, reps=5):
+    """A plain elementwise copy kernel of known size (dst = src * 1, float32), for scaling the
+    HBM byte counters FETCH_SIZE and WRITE_SIZE: each launch reads and writes nbytes."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    return nbytes
+
+
+def recorded_traffic(kernel_src):
+    """HBM bytes per launch of the causal kernel as last measured with rocprofv3 counters
+    (profiles/k_causal_b2h16n8192_d128_traffic.json), or None when the kernel source has changed
+    since (the file stores the SHA-256 of the source it was measured with)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_causal_b2h16n8192_d128_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(kernel_src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != digest:
+        return None
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,9 +222,11 @@ def main():
     ap.add_argument("--seg-len", dest="seg_len", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled over the steps")
     ap.add_argument("--decode-steps", dest="decode_steps", type=int, default=1000)
-    ap.add_argument("--only", choices=["prefill", "decode", "global"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "global", "copycal"], default=None,
                     help="run one form only (for profiling); no JSON line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copycal", action="store_true",
+                    help="with --only: run the copy calibration kernel first (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the heads of this "
@@ -193,17 +236,27 @@ def main():
     import torch
     torch.cuda.init()
 
+    if args.only == "copycal":
+        n = copy_calibration()
+        print(f"copycal: copied {n} bytes x 5", flush=True)
+        return
     if args.only:
+        if args.copycal:
+            copy_calibration()
         fn = {"prefill": bench_prefill, "decode": bench_decode, "global": bench_global}[args.only]
         r = fn(args)
         print(f"{args.only}: {r[1]:.4f} ms/step", flush=True)
         return
 
-    w, ms, ms_hot, wall, byts, flops, P = bench_prefill(args)
-    print(f"prefill: {ms * 1e3:.1f} us/step (hot {ms_hot * 1e3:.1f} us)", file=sys.stderr, flush=True)
+    w, ms, ms_hot, wall, byts, flops, P, kern_ms = bench_prefill(args)
+    print(f"prefill: {ms * 1e3:.1f} us/step (hot {ms_hot * 1e3:.1f} us); kernels "
+          f"agg {kern_ms[0] * 1e3:.1f} scan {kern_ms[1] * 1e3:.1f} causal {kern_ms[2] * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
     th = w.B * w.H * w.N
     value = th / (ms * 1e-3)
-    achieved = byts / (ms * 1e-3)
+    achieved = byts / (kern_ms[2] * 1e-3)
+    traffic = recorded_traffic(os.path.join(ROOT, "causal_linear_attention_la_amd", "csrc",
+                                            "k_mfma.hip"))
     issued = mfma_issued_prefill(w.B, w.H, w.N, P)
     wd, ms_d, byts_d = bench_decode(args)
     print(f"decode: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)
@@ -228,9 +281,16 @@ def main():
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
                    "input_sets_rotated": args.rotate},
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK, "traffic": None,
-                     "kernel": "la_causal_fwd call (segment sums + segment scan + causal output)",
-                     "algorithmic_bytes_per_call": byts},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                     "traffic": traffic["bytes_per_launch"] if traffic else None,
+                     "kernel": "k_causal<128> (causal outputs + final state; reads q, k, v and "
+                               "the segment prefix states, writes out and S, z)",
+                     "kernel_us": kern_ms[2] * 1e3,
+                     "algorithmic_bytes_per_launch": byts,
+                     "call_us": ms * 1e3, "call_frac": byts / (ms * 1e-3) / HBM_PEAK,
+                     "call_kernels_us": {"segment_sums": kern_ms[0] * 1e3,
+                                         "segment_scan": kern_ms[1] * 1e3,
+                                         "causal": kern_ms[2] * 1e3}},
         "mfma": {"algorithmic_frac": flops / (ms * 1e-3) / BF16_PEAK,
                  "issued_frac": issued / (ms * 1e-3) / BF16_PEAK,
                  "peak_tflops": BF16_PEAK / 1e12},

@@ -34,8 +34,8 @@ LA_F32, LA_BF16 = 0, 1
 LA_OK, LA_EINVAL, LA_ENOTSUP, LA_EHIP = 0, 1, 2, 3
 
 # Every symbol include/la.h declares.
-EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_global_fwd", "la_decode_step",
-           "la_workspace_bytes", "la_strerror", "la_version")
+EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_profiled", "la_global_fwd",
+           "la_decode_step", "la_workspace_bytes", "la_strerror", "la_version")
 
 
 class LAError(RuntimeError):
@@ -47,15 +47,17 @@ class LAError(RuntimeError):
 def _load(path: Path):
     if not path.exists():
         raise ImportError(f"liblinattn not built: {path} is missing "
-                          "(run python -m causal_linear_attention_la_amd.build)")
+                          "(run python causal_linear_attention_la_amd/build.py)")
     lib = ctypes.CDLL(str(path))
     vp, fp, i = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
     core = [vp, vp, vp, vp, fp, fp, i, i, i, i, i, i]
     lib.la_causal_fwd.argtypes = core + [i, vp]
     lib.la_causal_fwd_seg.argtypes = core + [i, i, vp]
+    lib.la_causal_fwd_profiled.argtypes = core + [i, i, vp, ctypes.POINTER(ctypes.c_float)]
     lib.la_global_fwd.argtypes = core + [i, vp]
     lib.la_decode_step.argtypes = core + [i, vp]
-    for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_global_fwd", "la_decode_step"):
+    for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_profiled", "la_global_fwd",
+              "la_decode_step"):
         getattr(lib, f).restype = ctypes.c_int
     lib.la_workspace_bytes.argtypes = [i] * 8 + [i]
     lib.la_workspace_bytes.restype = ctypes.c_size_t
@@ -140,6 +142,18 @@ def la_causal_fwd(q, k, v, out, S=None, z=None, chunk: int = 0, seg_len: int = 0
                                dv, chunk, seg_len, _dtype_code(k), _stream(k))
     _check(st, "la_causal_fwd")
     return out
+
+
+def la_causal_fwd_profiled(q, k, v, out, S=None, z=None, chunk: int = 0, seg_len: int = 0):
+    """la_causal_fwd with HIP events around its kernels; waits for them and returns the device
+    milliseconds of (segment sums, segment scan, causal outputs)."""
+    _check_tensors(q, k, v, out, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    ms = (ctypes.c_float * 3)()
+    st = lib.la_causal_fwd_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H,
+                                    N, d, dv, chunk, seg_len, _dtype_code(k), _stream(k), ms)
+    _check(st, "la_causal_fwd_profiled")
+    return tuple(float(x) for x in ms)
 
 
 def la_global_fwd(q, k, v, out, S, z, chunk: int = 0):

@@ -1,6 +1,9 @@
 """Builds liblinattn.so (the HIP kernels and the C ABI) in-tree with hipcc for gfx950.
 
-Usage: python -m causal_linear_attention_la_amd.build   (or build() from Python)
+Usage: python causal_linear_attention_la_amd/build.py   (or build() from Python)
+
+The file is self-contained and is run or loaded by path: importing the package loads the
+library, which must not be needed in order to build it.
 """
 from __future__ import annotations
 

@@ -195,32 +195,66 @@ struct Workspace {
     }
 };
 
+// HIP events marking the phase boundaries of one causal call (profiling form only).
+struct Stamps {
+    hipEvent_t ev[4] = {};
+    hipError_t init()
+    {
+        for (hipEvent_t &x : ev) {
+            const hipError_t e = hipEventCreate(&x);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipSuccess;
+    }
+    ~Stamps()
+    {
+        for (hipEvent_t x : ev)
+            if (x)
+                (void)hipEventDestroy(x);
+    }
+};
+
+hipError_t mark(Stamps *ts, int i, hipStream_t st)
+{
+    return ts ? hipEventRecord(ts->ev[i], st) : hipSuccess;
+}
+
 int run_causal(const void *q, const void *k, const void *v, void *out, float *S, float *z,
-               int N, int d, int dv, bool bf16, const Plan &pl, hipStream_t st)
+               int N, int d, int dv, bool bf16, const Plan &pl, hipStream_t st,
+               Stamps *ts = nullptr)
 {
     const int BH = (int)pl.BH, P = pl.P, L = pl.L;
     const long E = (long)d * dv + d;
     Workspace ws;
     if (ws.init(pl.ws_bytes, st) != hipSuccess)
         return LA_EHIP;
-    hipError_t e = hipSuccess;
+    hipError_t e = mark(ts, 0, st);
     const float *preS = S, *prez = z; // P == 1: the caller's state (or none) is the prefix
     long ps = (long)d * dv, pzs = d;
-    if (P > 1) {
+    if (P > 1 && e == hipSuccess) {
         // sums of segments 0..P-2, then the exclusive prefix over segments in place
         e = pl.mfma ? la::agg_mfma(d, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L, P - 1, P, st)
                     : la::agg_valu(bf16, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, d, dv,
                                    pl.chunk, L, P - 1, P, st);
         if (e == hipSuccess)
+            e = mark(ts, 1, st);
+        if (e == hipSuccess)
             e = la::seg_exclusive_scan(ws.ptr, S, z, BH, P, d, dv, st);
         preS = ws.ptr;
         prez = ws.ptr + (long)d * dv;
         ps = pzs = E;
+    } else if (e == hipSuccess) {
+        e = mark(ts, 1, st);
     }
+    if (e == hipSuccess)
+        e = mark(ts, 2, st);
     if (e == hipSuccess)
         e = pl.mfma ? la::causal_mfma(d, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N, L, P, st)
                     : la::out_valu(bf16, true, q, k, v, out, preS, prez, ps, pzs, P > 1 ? P : 1, S,
                                    z, BH, N, d, dv, pl.chunk, L, P, st);
+    if (e == hipSuccess)
+        e = mark(ts, 3, st);
     return e == hipSuccess ? LA_OK : LA_EHIP;
 }
 
@@ -264,6 +298,33 @@ int la_causal_fwd_seg(const void *q, const void *k, const void *v, void *out, fl
     if (s != LA_OK)
         return s;
     return run_causal(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream);
+}
+
+int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *out, float *S,
+                           float *z, int B, int H, int N, int d, int d_v, int chunk, int seg_len,
+                           la_dtype dtype, hipStream_t stream, float *ms)
+{
+    if (!ms)
+        return LA_EINVAL;
+    Plan pl;
+    const int s = validate(CAUSAL, q, k, v, out, S, z, B, H, N, d, d_v, chunk, seg_len, dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    Stamps ts;
+    if (ts.init() != hipSuccess)
+        return LA_EHIP;
+    const int r = run_causal(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream, &ts);
+    if (r != LA_OK)
+        return r;
+    if (hipEventSynchronize(ts.ev[3]) != hipSuccess)
+        return LA_EHIP;
+    for (int i = 0; i < 3; ++i) {
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, ts.ev[i], ts.ev[i + 1]) != hipSuccess)
+            return LA_EHIP;
+        ms[i] = t;
+    }
+    return LA_OK;
 }
 
 int la_causal_fwd(const void *q, const void *k, const void *v, void *out, float *S, float *z,

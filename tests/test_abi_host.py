@@ -48,13 +48,16 @@ def call(fn, q=A, k=2 * A, v=3 * A, out=4 * A, S=5 * A, z=6 * A, B=1, H=2, N=8, 
          chunk=0, dtype=la.LA_BF16, seg=None):
     f = getattr(la.lib, fn)
     args = [q, k, v, out, S, z, B, H, N, d, dv, chunk]
-    if fn == "la_causal_fwd_seg":
+    if fn in ("la_causal_fwd_seg", "la_causal_fwd_profiled"):
         args.append(0 if seg is None else seg)
     args += [dtype, None]
+    if fn == "la_causal_fwd_profiled":
+        args.append((ctypes.c_float * 3)())
     return f(*args)
 
 
-FORMS = ["la_causal_fwd", "la_causal_fwd_seg", "la_global_fwd", "la_decode_step"]
+FORMS = ["la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_profiled", "la_global_fwd",
+         "la_decode_step"]
 
 
 @pytest.mark.parametrize("fn", FORMS)
@@ -85,6 +88,12 @@ def test_form_specific_checks():
     assert call("la_global_fwd", q=None) == la.LA_EINVAL        # q without out
     assert call("la_global_fwd", S=None) == la.LA_EINVAL
     assert call("la_global_fwd", z=None) == la.LA_EINVAL
+
+
+def test_profiled_needs_result_array():
+    f = la.lib.la_causal_fwd_profiled
+    assert f(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 1, 2, 8, 16, 16, 0, 0, la.LA_BF16, None,
+             None) == la.LA_EINVAL
 
 
 def test_chunk_and_segment_checks():
