@@ -95,23 +95,16 @@ def bench_prefill(args):
     ms_hot, _ = time_calls(lambda i: step(0), args.steps, 2)
 
     # per-kernel device times: HIP events recorded by the library on the launch stream around
-    # each of the call's kernels (segment sums, segment scan, causal outputs)
-    phases = []
-    for i in range(args.steps):
-        q, k, v, out, S, z, state = sets[i % len(sets)]
-        state.zero_()
-        phases.append(la.la_causal_fwd_profiled(q, k, v, out, S, z, chunk=args.chunk,
-                                                seg_len=args.seg_len))
-    kern_ms = [statistics.fmean(p[j] for p in phases) for j in range(3)]
+    # each kernel of `steps` back-to-back calls (segment sums, segment scan, causal outputs)
+    q, k, v, out, S, z, state = sets[0]
+    la.la_causal_fwd_profiled(q, k, v, out, S, z, chunk=args.chunk, seg_len=args.seg_len, reps=2)
+    kern_ms = list(la.la_causal_fwd_profiled(q, k, v, out, S, z, chunk=args.chunk,
+                                             seg_len=args.seg_len, reps=args.steps))
     byts, flops = algo_prefill(w.B, w.H, w.N, w.d, w.dv)
-    P = math.ceil(w.N / (args.seg_len or _auto_seg(w.B * w.H, w.N)))
+    # segments per head the library chose: its temporary memory is one state per segment
+    ws = la.la_workspace_bytes(0, w.B, w.H, w.N, w.d, w.dv, args.chunk, args.seg_len)
+    P = max(1, ws // (w.B * w.H * (w.d * w.dv + w.d) * 4))
     return w, ms, ms_hot, wall, byts, flops, P, kern_ms
-
-
-def _auto_seg(BH, N, chunk=64, target=512):
-    nchunks = math.ceil(N / chunk)
-    want = min(max(1, math.ceil(target / BH)), nchunks)
-    return math.ceil(nchunks / want) * chunk
 
 
 def bench_decode(args):
@@ -196,19 +189,31 @@ def copy_calibration(nbytes=256 << 20, reps=5):
     return nbytes
 
 
-def recorded_traffic(kernel_src):
-    """HBM bytes per launch of the causal kernel as last measured with rocprofv3 counters
-    (profiles/k_causal_b2h16n8192_d128_traffic.json), or None when the kernel source has changed
-    since (the file stores the SHA-256 of the source it was measured with)."""
+TRAFFIC_SOURCES = ("causal_linear_attention_la_amd/csrc/k_mfma.hip",
+                   "causal_linear_attention_la_amd/csrc/la_api.hip")
+
+
+def sources_digest():
+    """SHA-256 over the sources that decide the causal kernel's memory traffic (the kernel and
+    the launch plan that sizes its segments)."""
     import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the causal kernel as last measured with rocprofv3 counters
+    (profiles/k_causal_b2h16n8192_d128_traffic.json), or None when the kernel or its launch plan
+    has changed since (the file stores the digest of the sources it was measured with)."""
     path = os.path.join(ROOT, "profiles", "k_causal_b2h16n8192_d128_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(kernel_src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("source_sha256") != digest:
+    if rec.get("sources_sha256") != sources_digest():
         return None
     return rec
 
@@ -245,7 +250,10 @@ def main():
             copy_calibration()
         fn = {"prefill": bench_prefill, "decode": bench_decode, "global": bench_global}[args.only]
         r = fn(args)
-        print(f"{args.only}: {r[1]:.4f} ms/step", flush=True)
+        extra = ""
+        if args.only == "prefill":
+            extra = " (kernels: " + ", ".join(f"{t * 1e3:.1f}" for t in r[7]) + " us)"
+        print(f"{args.only}: {r[1]:.4f} ms/step{extra}", flush=True)
         return
 
     w, ms, ms_hot, wall, byts, flops, P, kern_ms = bench_prefill(args)
@@ -255,8 +263,7 @@ def main():
     th = w.B * w.H * w.N
     value = th / (ms * 1e-3)
     achieved = byts / (kern_ms[2] * 1e-3)
-    traffic = recorded_traffic(os.path.join(ROOT, "causal_linear_attention_la_amd", "csrc",
-                                            "k_mfma.hip"))
+    traffic = recorded_traffic()
     issued = mfma_issued_prefill(w.B, w.H, w.N, P)
     wd, ms_d, byts_d = bench_decode(args)
     print(f"decode: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)

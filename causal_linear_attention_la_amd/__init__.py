@@ -53,7 +53,7 @@ def _load(path: Path):
     core = [vp, vp, vp, vp, fp, fp, i, i, i, i, i, i]
     lib.la_causal_fwd.argtypes = core + [i, vp]
     lib.la_causal_fwd_seg.argtypes = core + [i, i, vp]
-    lib.la_causal_fwd_profiled.argtypes = core + [i, i, vp, ctypes.POINTER(ctypes.c_float)]
+    lib.la_causal_fwd_profiled.argtypes = core + [i, i, vp, i, ctypes.POINTER(ctypes.c_float)]
     lib.la_global_fwd.argtypes = core + [i, vp]
     lib.la_decode_step.argtypes = core + [i, vp]
     for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_profiled", "la_global_fwd",
@@ -144,14 +144,16 @@ def la_causal_fwd(q, k, v, out, S=None, z=None, chunk: int = 0, seg_len: int = 0
     return out
 
 
-def la_causal_fwd_profiled(q, k, v, out, S=None, z=None, chunk: int = 0, seg_len: int = 0):
-    """la_causal_fwd with HIP events around its kernels; waits for them and returns the device
-    milliseconds of (segment sums, segment scan, causal outputs)."""
+def la_causal_fwd_profiled(q, k, v, out, S=None, z=None, chunk: int = 0, seg_len: int = 0,
+                           reps: int = 1):
+    """la_causal_fwd enqueued `reps` times back to back with HIP events around its kernels;
+    waits for them and returns the average device milliseconds of (segment sums, segment scan,
+    causal outputs)."""
     _check_tensors(q, k, v, out, S, z)
     B, H, N, d, dv = _dims(q, k, v)
     ms = (ctypes.c_float * 3)()
     st = lib.la_causal_fwd_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H,
-                                    N, d, dv, chunk, seg_len, _dtype_code(k), _stream(k), ms)
+                                    N, d, dv, chunk, seg_len, _dtype_code(k), _stream(k), reps, ms)
     _check(st, "la_causal_fwd_profiled")
     return tuple(float(x) for x in ms)
 

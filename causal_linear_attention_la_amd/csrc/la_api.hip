@@ -5,6 +5,7 @@
 
 #include <mutex>
 #include <stdint.h>
+#include <vector>
 
 namespace {
 
@@ -12,8 +13,11 @@ constexpr int LA_VERSION = (0 << 16) | (1 << 8) | 0;
 
 enum Form { CAUSAL = 0, GLOBAL = 1, DECODE = 2 };
 
-// Target number of workgroups for one launch: two per compute unit of an MI355X (256 CUs).
-constexpr long kTargetGroups = 512;
+// Target number of workgroups per launch on an MI355X (256 CUs): as many as run at once. The
+// d = 128 matrix-core causal kernel holds a whole CU (its LDS), so its segments are sized for
+// one wave of 256 workgroups; the other kernels fit two per CU. More segments than that only
+// add segment-state traffic (66 KB read and written per extra segment at d = 128).
+constexpr long kCUs = 256;
 
 bool dim_ok(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
 
@@ -85,7 +89,8 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
             return LA_ENOTSUP;
         pl.L = seg_len;
     } else {
-        long want = (kTargetGroups + (long)BH - 1) / (long)BH; // segments per head
+        const long target = (form == CAUSAL && pl.mfma && d == 128) ? kCUs : 2 * kCUs;
+        long want = (target + (long)BH - 1) / (long)BH; // segments per head
         if (want > nchunks)
             want = nchunks;
         pl.L = (int)((nchunks + want - 1) / want) * pl.chunk;
@@ -198,6 +203,9 @@ struct Workspace {
 // HIP events marking the phase boundaries of one causal call (profiling form only).
 struct Stamps {
     hipEvent_t ev[4] = {};
+    Stamps() = default;
+    Stamps(const Stamps &) = delete;
+    Stamps &operator=(const Stamps &) = delete;
     hipError_t init()
     {
         for (hipEvent_t &x : ev) {
@@ -302,28 +310,35 @@ int la_causal_fwd_seg(const void *q, const void *k, const void *v, void *out, fl
 
 int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *out, float *S,
                            float *z, int B, int H, int N, int d, int d_v, int chunk, int seg_len,
-                           la_dtype dtype, hipStream_t stream, float *ms)
+                           la_dtype dtype, hipStream_t stream, int reps, float *ms)
 {
-    if (!ms)
+    if (!ms || reps < 1 || reps > 4096)
         return LA_EINVAL;
     Plan pl;
     const int s = validate(CAUSAL, q, k, v, out, S, z, B, H, N, d, d_v, chunk, seg_len, dtype, &pl);
     if (s != LA_OK)
         return s;
-    Stamps ts;
-    if (ts.init() != hipSuccess)
-        return LA_EHIP;
-    const int r = run_causal(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream, &ts);
-    if (r != LA_OK)
-        return r;
-    if (hipEventSynchronize(ts.ev[3]) != hipSuccess)
-        return LA_EHIP;
-    for (int i = 0; i < 3; ++i) {
-        float t = 0.f;
-        if (hipEventElapsedTime(&t, ts.ev[i], ts.ev[i + 1]) != hipSuccess)
+    std::vector<Stamps> ts(reps);
+    for (Stamps &t : ts)
+        if (t.init() != hipSuccess)
             return LA_EHIP;
-        ms[i] = t;
+    for (Stamps &t : ts) {
+        const int r = run_causal(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream, &t);
+        if (r != LA_OK)
+            return r;
     }
+    if (hipEventSynchronize(ts.back().ev[3]) != hipSuccess)
+        return LA_EHIP;
+    double sum[3] = {0.0, 0.0, 0.0};
+    for (Stamps &t : ts)
+        for (int i = 0; i < 3; ++i) {
+            float x = 0.f;
+            if (hipEventElapsedTime(&x, t.ev[i], t.ev[i + 1]) != hipSuccess)
+                return LA_EHIP;
+            sum[i] += x;
+        }
+    for (int i = 0; i < 3; ++i)
+        ms[i] = (float)(sum[i] / reps);
     return LA_OK;
 }
 

@@ -118,18 +118,20 @@ int la_decode_step(const void *q, const void *k, const void *v, void *out, float
                    hipStream_t stream);
 
 /*
- * Profiling form of la_causal_fwd_seg: the same work on `stream`, with a HIP event recorded on
- * that stream before and after each of the call's kernels. The call then waits for the last
- * event and writes the device time in milliseconds of each phase to ms[0..2]:
+ * Profiling form of la_causal_fwd_seg: the same call enqueued `reps` times back to back on
+ * `stream` (each call reads S, z as the previous one left them, so the work per call is
+ * identical), with a HIP event recorded on that stream before and after each of every call's
+ * kernels. The function then waits for the last event and writes the average device time in
+ * milliseconds of each phase to ms[0..2]:
  *   ms[0] segment sums (segments 0..P-2), ms[1] exclusive scan over segment states,
  *   ms[2] causal outputs and final state; a phase the call did not launch (P = 1) gets 0.
- *   ms     host array of 3 floats; NULL -> LA_EINVAL (nothing enqueued).
+ *   reps   1..4096; ms host array of 3 floats. reps out of range or ms NULL -> LA_EINVAL.
  * Blocks the calling thread until the work is done; for measurement, not for pipelines.
- * Errors as for la_causal_fwd_seg; a failure while waiting for the events -> LA_EHIP.
+ * Errors as for la_causal_fwd_seg; a failure while creating or reading events -> LA_EHIP.
  */
 int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *out, float *S,
                            float *z, int B, int H, int N, int d, int d_v, int chunk, int seg_len,
-                           la_dtype dtype, hipStream_t stream, float *ms);
+                           la_dtype dtype, hipStream_t stream, int reps, float *ms);
 
 /* Bytes of stream-ordered temporary device memory a causal (form = 0) or global (form = 1)
  * call with these arguments takes (0 when none). seg_len as in la_causal_fwd_seg (0 = auto).

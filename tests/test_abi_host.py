@@ -52,7 +52,7 @@ def call(fn, q=A, k=2 * A, v=3 * A, out=4 * A, S=5 * A, z=6 * A, B=1, H=2, N=8, 
         args.append(0 if seg is None else seg)
     args += [dtype, None]
     if fn == "la_causal_fwd_profiled":
-        args.append((ctypes.c_float * 3)())
+        args += [1, (ctypes.c_float * 3)()]
     return f(*args)
 
 
@@ -90,10 +90,13 @@ def test_form_specific_checks():
     assert call("la_global_fwd", z=None) == la.LA_EINVAL
 
 
-def test_profiled_needs_result_array():
+def test_profiled_argument_checks():
     f = la.lib.la_causal_fwd_profiled
-    assert f(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 1, 2, 8, 16, 16, 0, 0, la.LA_BF16, None,
-             None) == la.LA_EINVAL
+    args = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 1, 2, 8, 16, 16, 0, 0, la.LA_BF16, None]
+    ms = (ctypes.c_float * 3)()
+    assert f(*args, 1, None) == la.LA_EINVAL
+    assert f(*args, 0, ms) == la.LA_EINVAL
+    assert f(*args, 4097, ms) == la.LA_EINVAL
 
 
 def test_chunk_and_segment_checks():
@@ -109,10 +112,14 @@ def test_chunk_and_segment_checks():
 
 
 def test_workspace_bytes():
-    # causal B=2 H=16 N=8192 d=128 bf16: chunk 64, 16 segments of 512 tokens per head
+    # causal B=2 H=16 N=8192 d=128 bf16: chunk 64; the d = 128 matrix-core kernel takes one
+    # workgroup per CU, so 256 / 32 = 8 segments of 1024 tokens per head
     E = 128 * 128 + 128
-    assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128) == 32 * 16 * E * 4
-    assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128, 64, 1024) == 32 * 8 * E * 4
+    assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128) == 32 * 8 * E * 4
+    assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128, 64, 512) == 32 * 16 * E * 4
+    # d = 64: two workgroups per CU, 512 / 32 = 16 segments of 128 tokens
+    E64 = 64 * 64 + 64
+    assert la.la_workspace_bytes(0, 4, 8, 2048, 64, 64) == 32 * 16 * E64 * 4
     # N=64 float32: chunk 32, split in two segments of one chunk; one segment needs no workspace
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 2 * (16 * 16 + 16) * 4
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 64, la.LA_F32) == 0
