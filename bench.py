@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the linear-attention hot path on one MI355X.
 
-One step = one causal prefill call (la_causal_fwd: phi on the loads, chunked matrix-core
-intra-chunk product, carried float32 state, normaliser, bf16 store, final state) over the
-workload B=2 H=16 N=8192 d=d_v=128 bf16, inputs IID N(0, 1/128), state out. K steps are timed
+One step = one causal prefill call of a fresh sequence (la_causal_fwd_state from the zero
+state: phi on the loads, chunked matrix-core intra-chunk product, carried float32 state,
+normaliser, bf16 store, final state S, z written) over the workload B=2 H=16 N=8192
+d=d_v=128 bf16, inputs IID N(0, 1/128). K steps are timed
 between device synchronisations; input sets rotate over three copies (806 MB > the 256 MB
 last-level cache) so a step does not find its inputs cached by the previous one.
 
@@ -79,16 +80,15 @@ def bench_prefill(args):
     for r in range(args.rotate):
         q, k, v = datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed + 100 * r, w.scale, "bf16")
         out = torch.empty_like(q)
-        # S and z share one allocation so that the zero fill a fresh sequence needs is one launch
-        state = torch.zeros(w.B * w.H * (w.d * w.dv + w.d), device=dev)
-        S = state[: w.B * w.H * w.d * w.dv].view(w.B, w.H, w.d, w.dv)
-        z = state[w.B * w.H * w.d * w.dv:].view(w.B, w.H, w.d)
-        sets.append((q, k, v, out, S, z, state))
+        S = torch.empty(w.B, w.H, w.d, w.dv, device=dev)
+        z = torch.empty(w.B, w.H, w.d, device=dev)
+        sets.append((q, k, v, out, S, z))
 
     def step(i):
-        q, k, v, out, S, z, state = sets[i % len(sets)]
-        state.zero_()
-        la.la_causal_fwd(q, k, v, out, S, z, chunk=args.chunk, seg_len=args.seg_len)
+        # a fresh sequence: zero initial state (no buffer), final state written to S, z
+        q, k, v, out, S, z = sets[i % len(sets)]
+        la.la_causal_fwd_state(q, k, v, out, None, None, S, z, chunk=args.chunk,
+                               seg_len=args.seg_len)
 
     ms, wall = time_calls(step, args.steps, args.warmup)
     # same buffers every step (inputs may stay in the last-level cache)
@@ -96,9 +96,10 @@ def bench_prefill(args):
 
     # per-kernel device times: HIP events recorded by the library on the launch stream around
     # each kernel of `steps` back-to-back calls (segment sums, segment scan, causal outputs)
-    q, k, v, out, S, z, state = sets[0]
-    la.la_causal_fwd_profiled(q, k, v, out, S, z, chunk=args.chunk, seg_len=args.seg_len, reps=2)
-    kern_ms = list(la.la_causal_fwd_profiled(q, k, v, out, S, z, chunk=args.chunk,
+    q, k, v, out, S, z = sets[0]
+    la.la_causal_fwd_profiled(q, k, v, out, None, None, S, z, chunk=args.chunk,
+                              seg_len=args.seg_len, reps=2)
+    kern_ms = list(la.la_causal_fwd_profiled(q, k, v, out, None, None, S, z, chunk=args.chunk,
                                              seg_len=args.seg_len, reps=args.steps))
     byts, flops = algo_prefill(w.B, w.H, w.N, w.d, w.dv)
     # segments per head the library chose: its temporary memory is one state per segment

@@ -34,8 +34,8 @@ LA_F32, LA_BF16 = 0, 1
 LA_OK, LA_EINVAL, LA_ENOTSUP, LA_EHIP = 0, 1, 2, 3
 
 # Every symbol include/la.h declares.
-EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_profiled", "la_global_fwd",
-           "la_decode_step", "la_workspace_bytes", "la_strerror", "la_version")
+EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_profiled",
+           "la_global_fwd", "la_decode_step", "la_workspace_bytes", "la_strerror", "la_version")
 
 
 class LAError(RuntimeError):
@@ -53,11 +53,13 @@ def _load(path: Path):
     core = [vp, vp, vp, vp, fp, fp, i, i, i, i, i, i]
     lib.la_causal_fwd.argtypes = core + [i, vp]
     lib.la_causal_fwd_seg.argtypes = core + [i, i, vp]
-    lib.la_causal_fwd_profiled.argtypes = core + [i, i, vp, i, ctypes.POINTER(ctypes.c_float)]
+    state = [vp, vp, vp, vp, fp, fp, fp, fp, i, i, i, i, i, i, i, i, vp]
+    lib.la_causal_fwd_state.argtypes = state
+    lib.la_causal_fwd_profiled.argtypes = state + [i, ctypes.POINTER(ctypes.c_float)]
     lib.la_global_fwd.argtypes = core + [i, vp]
     lib.la_decode_step.argtypes = core + [i, vp]
-    for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_profiled", "la_global_fwd",
-              "la_decode_step"):
+    for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_profiled",
+              "la_global_fwd", "la_decode_step"):
         getattr(lib, f).restype = ctypes.c_int
     lib.la_workspace_bytes.argtypes = [i] * 8 + [i]
     lib.la_workspace_bytes.restype = ctypes.c_size_t
@@ -144,16 +146,29 @@ def la_causal_fwd(q, k, v, out, S=None, z=None, chunk: int = 0, seg_len: int = 0
     return out
 
 
-def la_causal_fwd_profiled(q, k, v, out, S=None, z=None, chunk: int = 0, seg_len: int = 0,
-                           reps: int = 1):
-    """la_causal_fwd enqueued `reps` times back to back with HIP events around its kernels;
-    waits for them and returns the average device milliseconds of (segment sums, segment scan,
-    causal outputs)."""
-    _check_tensors(q, k, v, out, S, z)
+def la_causal_fwd_state(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk: int = 0,
+                        seg_len: int = 0):
+    """Causal prefill with the initial state (S0, z0; None: zero) and the final state (S, z;
+    None: not returned) in separate float32 tensors (see include/la.h)."""
+    _check_tensors(q, k, v, out, S0, z0, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    st = lib.la_causal_fwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0), _ptr(S),
+                                 _ptr(z), B, H, N, d, dv, chunk, seg_len, _dtype_code(k), _stream(k))
+    _check(st, "la_causal_fwd_state")
+    return out
+
+
+def la_causal_fwd_profiled(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk: int = 0,
+                           seg_len: int = 0, reps: int = 1):
+    """la_causal_fwd_state enqueued `reps` times back to back with HIP events around its
+    kernels; waits for them and returns the average device milliseconds of (segment sums,
+    segment scan, causal outputs)."""
+    _check_tensors(q, k, v, out, S0, z0, S, z)
     B, H, N, d, dv = _dims(q, k, v)
     ms = (ctypes.c_float * 3)()
-    st = lib.la_causal_fwd_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H,
-                                    N, d, dv, chunk, seg_len, _dtype_code(k), _stream(k), reps, ms)
+    st = lib.la_causal_fwd_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0),
+                                    _ptr(S), _ptr(z), B, H, N, d, dv, chunk, seg_len,
+                                    _dtype_code(k), _stream(k), reps, ms)
     _check(st, "la_causal_fwd_profiled")
     return tuple(float(x) for x in ms)
 

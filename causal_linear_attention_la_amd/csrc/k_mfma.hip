@@ -35,9 +35,6 @@ constexpr int C = 64;   // tokens per chunk
 constexpr int NT = 256; // threads of the segment-sum and global-read kernels; stage threads
 
 template <int D> struct Cfg {
-    static constexpr int FG = D / 8;            // 16-byte feature groups per row
-    static constexpr int RPI = NT / FG;         // chunk rows one staging instruction covers
-    static constexpr int TM = C / RPI;          // staging rows per thread (4 or 2)
     static constexpr int RS = D + 16;           // row stride (elements) of the chunk arrays
     static constexpr int AS = C * RS + (C / 8 - 1) * 64; // chunk array size (elements)
     static constexpr int TS = C + 8;            // row stride (elements) of the score block
@@ -45,7 +42,6 @@ template <int D> struct Cfg {
     static constexpr int NFT = D / 16;          // 16-row feature tiles of S
     static constexpr int NKB = D / 32;          // 32-feature k blocks
     static constexpr int ZFT = NFT / 4;         // feature tiles of z one wave keeps (4 waves)
-    static_assert(TM == 2 || TM == 4, "staging micro-tile");
 };
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -143,39 +139,42 @@ __device__ __forceinline__ u32x4 phi8(u32x4 x)
 // groups of one row (FG lanes per row), so a wave's global load reads whole rows (1 KiB
 // contiguous) and 8 lanes of a staging store cover 128 contiguous bytes of one row. Thread t
 // owns rows t / FG + RPI * i, i < TM.
-template <int D> struct Tile {
-    using K = Cfg<D>;
+template <int D, int NTH = NT> struct Tile {
+    static constexpr int FG = D / 8;       // 16-byte feature groups per row
+    static constexpr int RPI = NTH / FG;   // chunk rows one staging instruction covers
+    static constexpr int TM = C / RPI;     // staging rows per thread
+    static_assert(TM >= 1 && TM * RPI == C, "staging tile");
     int a, b;  // first row, feature group
     int lofs;  // LDS offset (elements) of (row a, group b)
-    __device__ explicit Tile(int tid) : a(tid / K::FG), b(tid % K::FG), lofs(nix<D>(a, 8 * b)) {}
+    __device__ explicit Tile(int tid) : a(tid / FG), b(tid % FG), lofs(nix<D>(a, 8 * b)) {}
     // rows of the chunk starting at `base` (wave-uniform), clamped to the chunk's last valid row
     // so every access is in bounds and no load sits in a branch (a load merged with a zero in a
     // branch makes the compiler wait for it right away); rows past nvalid are masked when staged.
     // Offsets are 32-bit from the uniform base, so the loads use scalar-base addressing.
-    __device__ __forceinline__ void load(u32x4 (&r)[K::TM], const uint16_t *__restrict__ base,
+    __device__ __forceinline__ void load(u32x4 (&r)[TM], const uint16_t *__restrict__ base,
                                          int nvalid) const
     {
         const char *bb = reinterpret_cast<const char *>(base);
 #pragma unroll
-        for (int i = 0; i < K::TM; ++i) {
-            const uint32_t rr = (uint32_t)min(a + K::RPI * i, nvalid - 1);
+        for (int i = 0; i < TM; ++i) {
+            const uint32_t rr = (uint32_t)min(a + RPI * i, nvalid - 1);
             r[i] = *reinterpret_cast<const u32x4 *>(bb + (rr * (uint32_t)(2 * D) + 16u * (uint32_t)b));
         }
     }
     // rows >= nvalid become 0 (phi(K) and V rows of a ragged last chunk must not contribute)
-    __device__ __forceinline__ void store(uint16_t *s, const u32x4 (&r)[K::TM], int nvalid,
+    __device__ __forceinline__ void store(uint16_t *s, const u32x4 (&r)[TM], int nvalid,
                                           bool apply_phi) const
     {
         if (nvalid >= C) { // wave-uniform: a full chunk needs no masking
 #pragma unroll
-            for (int i = 0; i < K::TM; ++i)
-                sts<u32x4>(s + lofs + blk<D>(K::RPI * i, 0), apply_phi ? phi8(r[i]) : r[i]);
+            for (int i = 0; i < TM; ++i)
+                sts<u32x4>(s + lofs + blk<D>(RPI * i, 0), apply_phi ? phi8(r[i]) : r[i]);
         } else {
 #pragma unroll
-            for (int i = 0; i < K::TM; ++i) {
+            for (int i = 0; i < TM; ++i) {
                 const u32x4 y = apply_phi ? phi8(r[i]) : r[i];
-                const bool ok = a + K::RPI * i < nvalid;
-                sts<u32x4>(s + lofs + blk<D>(K::RPI * i, 0), ok ? y : u32x4{0u, 0u, 0u, 0u});
+                const bool ok = a + RPI * i < nvalid;
+                sts<u32x4>(s + lofs + blk<D>(RPI * i, 0), ok ? y : u32x4{0u, 0u, 0u, 0u});
             }
         }
     }
@@ -303,17 +302,26 @@ __device__ __forceinline__ void zero_acc(f32x4 (&sacc)[Cfg<D>::NFT][NCT], f32x4 
 }
 
 // ------------------------------------------------------------------------------------------
-// Segment sums: dS = phi(K_seg)^T V_seg, dz = phi(K_seg)^T 1. 256 threads; every wave stages
-// the next chunk into the other half of a double-buffered LDS and then runs the matrix-core
-// update on the current one (one barrier per chunk).
+// Segment sums: dS = phi(K_seg)^T V_seg, dz = phi(K_seg)^T 1. One wave per 16 value columns of
+// S (and per 16 features of z), D/16 waves; every wave also stages 1/(D/16) of the next chunk
+// into the other half of a double-buffered LDS before running the matrix-core update on the
+// current one (one barrier per chunk). The wave count is what keeps enough loads in flight
+// when each CU runs a single workgroup.
+template <int D> struct AggCfg {
+    static constexpr int NW = D / 16;
+    static constexpr int THREADS = NW * 64;
+};
+
 template <int D>
-__global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
-                                            const uint16_t *__restrict__ v,
-                                            float *__restrict__ dstS, float *__restrict__ dstz,
-                                            long sstride, long zstride, int N, int L, int nseg,
-                                            int P)
+__global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__restrict__ k,
+                                                           const uint16_t *__restrict__ v,
+                                                           float *__restrict__ dstS,
+                                                           float *__restrict__ dstz, long sstride,
+                                                           long zstride, int N, int L, int nseg,
+                                                           int P)
 {
     using K = Cfg<D>;
+    using TL = Tile<D, AggCfg<D>::THREADS>;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][K::AS];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][K::AS];
 
@@ -323,16 +331,16 @@ __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
     const int nch = (te - tb + C - 1) / C;
     const uint16_t *kb = k + (size_t)bh * N * D;
     const uint16_t *vb = v + (size_t)bh * N * D;
-    const int cw0 = w * (D / 4);
+    const int cw0 = 16 * w;
     const int trl = tr_lane<D>(li, g);
-    const Tile<D> tile(tid);
+    const TL tile(tid);
     auto chunk_t0 = [&](int cc) { return tb + min(cc, nch - 1) * C; };
 
-    f32x4 sacc[K::NFT][K::NCT];
-    f32x4 zacc[K::ZFT];
-    zero_acc<D, K::NCT, K::ZFT>(sacc, zacc);
+    f32x4 sacc[K::NFT][1];
+    f32x4 zacc[1];
+    zero_acc<D, 1, 1>(sacc, zacc);
 
-    u32x4 rk[K::TM], rv[K::TM];
+    u32x4 rk[TL::TM], rv[TL::TM];
     tile.load(rk, kb + (size_t)tb * D, te - tb);
     tile.load(rv, vb + (size_t)tb * D, te - tb);
     tile.store(sK[0], rk, te - tb, true);
@@ -355,8 +363,8 @@ __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
             tile.load(rk, kb + (size_t)tn * D, te - tn);
             tile.load(rv, vb + (size_t)tn * D, te - tn);
         }
-        state_update<D, K::NCT>(sacc, sK[b] + trl, sV[b] + cw0 + trl);
-        key_sum<D, K::ZFT>(zacc, sK[b] + 16 * (w * K::ZFT) + trl);
+        state_update<D, 1>(sacc, sK[b] + trl, sV[b] + cw0 + trl);
+        key_sum<D, 1>(zacc, sK[b] + cw0 + trl);
         __syncthreads();
     }
 
@@ -364,17 +372,13 @@ __global__ __launch_bounds__(NT) void k_agg(const uint16_t *__restrict__ k,
 #pragma unroll
     for (int ft = 0; ft < K::NFT; ++ft)
 #pragma unroll
-        for (int ct = 0; ct < K::NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[(16 * ft + 4 * g + r) * D + cw0 + 16 * ct + li] = sacc[ft][ct][r];
+        for (int r = 0; r < 4; ++r)
+            S[(16 * ft + 4 * g + r) * D + cw0 + li] = sacc[ft][0][r];
     if (li == 0) {
         float *z = dstz + ((long)bh * P + p) * zstride;
 #pragma unroll
-        for (int zt = 0; zt < K::ZFT; ++zt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                z[16 * (w * K::ZFT + zt) + 4 * g + r] = zacc[zt][r];
+        for (int r = 0; r < 4; ++r)
+            z[cw0 + 4 * g + r] = zacc[0][r];
     }
 }
 
@@ -547,7 +551,7 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
 {
     using K = Cfg<D>;
     const Tile<D> tile(ht);
-    u32x4 rq[K::TM], rk[K::TM], rv[K::TM];
+    u32x4 rq[Tile<D>::TM], rk[Tile<D>::TM], rv[Tile<D>::TM];
     const int tb = a.tb, te = a.te, nch = a.nch;
     // first token of chunk c' (clamped to the last chunk, so prefetches past the end re-read
     // it: every load is in bounds and unconditional)
@@ -683,7 +687,7 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
     if (tid < D)
         sz[tid] = z[(size_t)bh * D + tid];
 
-    u32x4 rq[K::TM];
+    u32x4 rq[Tile<D>::TM];
     tile.load(rq, q + hoff + (size_t)tb * D, te - tb);
     const int tlast = tb + ((te - tb - 1) / C) * C;
     for (int t0 = tb; t0 < te; t0 += C) {
@@ -742,13 +746,15 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
 hipError_t agg_mfma(int D, const void *k, const void *v, float *dstS, float *dstz, long sstride,
                     long zstride, int BH, int N, int L, int nseg, int P, hipStream_t st)
 {
-    const dim3 grid((unsigned)(BH * nseg)), block(NT);
+    const dim3 grid((unsigned)(BH * nseg));
     const auto *kk = static_cast<const uint16_t *>(k);
     const auto *vv = static_cast<const uint16_t *>(v);
     if (D == 128)
-        hipLaunchKernelGGL(k_agg<128>, grid, block, 0, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
+        hipLaunchKernelGGL(k_agg<128>, grid, dim3(AggCfg<128>::THREADS), 0, st, kk, vv, dstS, dstz, sstride, zstride, N,
+                           L, nseg, P);
     else
-        hipLaunchKernelGGL(k_agg<64>, grid, block, 0, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
+        hipLaunchKernelGGL(k_agg<64>, grid, dim3(AggCfg<64>::THREADS), 0, st, kk, vv, dstS, dstz, sstride, zstride, N,
+                           L, nseg, P);
     return hipGetLastError();
 }
 

@@ -104,10 +104,12 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
     return LA_OK;
 }
 
-// Full validation of an entry point's arguments: pointers, then make_plan.
-int validate(Form form, const void *q, const void *k, const void *v, void *out, float *S,
-             float *z, int B, int H, int N, int d, int dv, int chunk, int seg_len, int dtype,
-             Plan *plan)
+// Full validation of an entry point's arguments: pointers, then make_plan. S0, z0 are the
+// causal form's initial state (read only; may be the same buffers as S, z, which receive the
+// final state); the other forms pass S0 = z0 = NULL.
+int validate(Form form, const void *q, const void *k, const void *v, void *out, const float *S0,
+             const float *z0, float *S, float *z, int B, int H, int N, int d, int dv, int chunk,
+             int seg_len, int dtype, Plan *plan)
 {
     if (!k || !v)
         return LA_EINVAL;
@@ -117,11 +119,11 @@ int validate(Form form, const void *q, const void *k, const void *v, void *out, 
     } else if (!q || !out) {
         return LA_EINVAL;
     }
-    if (form == CAUSAL && ((S == nullptr) != (z == nullptr)))
+    if (form == CAUSAL && ((S == nullptr) != (z == nullptr) || (S0 == nullptr) != (z0 == nullptr)))
         return LA_EINVAL;
-    if (form != CAUSAL && (!S || !z))
+    if (form != CAUSAL && (!S || !z || S0 || z0))
         return LA_EINVAL;
-    const void *ptrs[] = {q, k, v, out, S, z};
+    const void *ptrs[] = {q, k, v, out, S0, z0, S, z};
     for (const void *p : ptrs)
         if (p && !aligned16(p))
             return LA_EINVAL;
@@ -134,14 +136,22 @@ int validate(Form form, const void *q, const void *k, const void *v, void *out, 
     const Span sq = span(q, BH * N * d * es), sk = span(k, BH * N * d * es);
     const Span sv = span(v, BH * N * dv * es), so = span(out, BH * N * dv * es);
     const Span sS = span(S, BH * d * dv * 4), sz = span(z, BH * d * 4);
+    const Span sS0 = span(S0, BH * d * dv * 4), sz0 = span(z0, BH * d * 4);
     for (Span in : {sq, sk, sv})
         if (overlap(so, in))
             return LA_EINVAL;
-    for (Span st : {sS, sz})
+    for (Span st : {sS, sz, sS0, sz0})
         for (Span o : {sq, sk, sv, so})
             if (overlap(st, o))
                 return LA_EINVAL;
-    if (overlap(sS, sz))
+    if (overlap(sS, sz) || overlap(sS0, sz0))
+        return LA_EINVAL;
+    // the initial state is either the final state's own buffers (in place) or apart from them
+    if (S0 && S0 != S && (overlap(sS0, sS) || overlap(sS0, sz)))
+        return LA_EINVAL;
+    if (z0 && z0 != z && (overlap(sz0, sS) || overlap(sz0, sz)))
+        return LA_EINVAL;
+    if (S0 && ((S0 == S) != (z0 == z)))
         return LA_EINVAL;
     return LA_OK;
 }
@@ -228,9 +238,9 @@ hipError_t mark(Stamps *ts, int i, hipStream_t st)
     return ts ? hipEventRecord(ts->ev[i], st) : hipSuccess;
 }
 
-int run_causal(const void *q, const void *k, const void *v, void *out, float *S, float *z,
-               int N, int d, int dv, bool bf16, const Plan &pl, hipStream_t st,
-               Stamps *ts = nullptr)
+int run_causal(const void *q, const void *k, const void *v, void *out, const float *S0,
+               const float *z0, float *S, float *z, int N, int d, int dv, bool bf16,
+               const Plan &pl, hipStream_t st, Stamps *ts = nullptr)
 {
     const int BH = (int)pl.BH, P = pl.P, L = pl.L;
     const long E = (long)d * dv + d;
@@ -238,7 +248,7 @@ int run_causal(const void *q, const void *k, const void *v, void *out, float *S,
     if (ws.init(pl.ws_bytes, st) != hipSuccess)
         return LA_EHIP;
     hipError_t e = mark(ts, 0, st);
-    const float *preS = S, *prez = z; // P == 1: the caller's state (or none) is the prefix
+    const float *preS = S0, *prez = z0; // P == 1: the initial state (or none) is the prefix
     long ps = (long)d * dv, pzs = d;
     if (P > 1 && e == hipSuccess) {
         // sums of segments 0..P-2, then the exclusive prefix over segments in place
@@ -248,7 +258,7 @@ int run_causal(const void *q, const void *k, const void *v, void *out, float *S,
         if (e == hipSuccess)
             e = mark(ts, 1, st);
         if (e == hipSuccess)
-            e = la::seg_exclusive_scan(ws.ptr, S, z, BH, P, d, dv, st);
+            e = la::seg_exclusive_scan(ws.ptr, S0, z0, BH, P, d, dv, st);
         preS = ws.ptr;
         prez = ws.ptr + (long)d * dv;
         ps = pzs = E;
@@ -297,25 +307,36 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
 
 extern "C" {
 
+int la_causal_fwd_state(const void *q, const void *k, const void *v, void *out, const float *S0,
+                        const float *z0, float *S, float *z, int B, int H, int N, int d, int d_v,
+                        int chunk, int seg_len, la_dtype dtype, hipStream_t stream)
+{
+    Plan pl;
+    const int s = validate(CAUSAL, q, k, v, out, S0, z0, S, z, B, H, N, d, d_v, chunk, seg_len,
+                           dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, pl, stream);
+}
+
 int la_causal_fwd_seg(const void *q, const void *k, const void *v, void *out, float *S, float *z,
                       int B, int H, int N, int d, int d_v, int chunk, int seg_len, la_dtype dtype,
                       hipStream_t stream)
 {
-    Plan pl;
-    const int s = validate(CAUSAL, q, k, v, out, S, z, B, H, N, d, d_v, chunk, seg_len, dtype, &pl);
-    if (s != LA_OK)
-        return s;
-    return run_causal(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream);
+    return la_causal_fwd_state(q, k, v, out, S, z, S, z, B, H, N, d, d_v, chunk, seg_len, dtype,
+                               stream);
 }
 
-int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *out, float *S,
-                           float *z, int B, int H, int N, int d, int d_v, int chunk, int seg_len,
-                           la_dtype dtype, hipStream_t stream, int reps, float *ms)
+int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *out,
+                           const float *S0, const float *z0, float *S, float *z, int B, int H,
+                           int N, int d, int d_v, int chunk, int seg_len, la_dtype dtype,
+                           hipStream_t stream, int reps, float *ms)
 {
     if (!ms || reps < 1 || reps > 4096)
         return LA_EINVAL;
     Plan pl;
-    const int s = validate(CAUSAL, q, k, v, out, S, z, B, H, N, d, d_v, chunk, seg_len, dtype, &pl);
+    const int s = validate(CAUSAL, q, k, v, out, S0, z0, S, z, B, H, N, d, d_v, chunk, seg_len,
+                           dtype, &pl);
     if (s != LA_OK)
         return s;
     std::vector<Stamps> ts(reps);
@@ -323,7 +344,8 @@ int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *ou
         if (t.init() != hipSuccess)
             return LA_EHIP;
     for (Stamps &t : ts) {
-        const int r = run_causal(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream, &t);
+        const int r = run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, pl,
+                                 stream, &t);
         if (r != LA_OK)
             return r;
     }
@@ -352,7 +374,8 @@ int la_global_fwd(const void *q, const void *k, const void *v, void *out, float 
                   int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype, hipStream_t stream)
 {
     Plan pl;
-    const int s = validate(GLOBAL, q, k, v, out, S, z, B, H, N, d, d_v, chunk, 0, dtype, &pl);
+    const int s = validate(GLOBAL, q, k, v, out, nullptr, nullptr, S, z, B, H, N, d, d_v, chunk, 0,
+                           dtype, &pl);
     if (s != LA_OK)
         return s;
     return run_global(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream);
@@ -364,7 +387,8 @@ int la_decode_step(const void *q, const void *k, const void *v, void *out, float
 {
     (void)chunk;
     Plan pl;
-    const int s = validate(DECODE, q, k, v, out, S, z, B, H, N, d, d_v, 0, 0, dtype, &pl);
+    const int s = validate(DECODE, q, k, v, out, nullptr, nullptr, S, z, B, H, N, d, d_v, 0, 0,
+                           dtype, &pl);
     if (s != LA_OK)
         return s;
     const hipError_t e = la::decode_step(dtype == LA_BF16, q, k, v, out, S, z, (int)pl.BH, d, d_v, stream);

@@ -93,6 +93,21 @@ int la_causal_fwd_seg(const void *q, const void *k, const void *v, void *out, fl
                       la_dtype dtype, hipStream_t stream);
 
 /*
+ * la_causal_fwd_seg with the initial and the final state in separate arguments:
+ *   S0, z0 the state before token 0, read only; both NULL: the zero state (nothing is read,
+ *          so a fresh sequence needs no zero-filled buffers).
+ *   S, z   receive the state after token N-1; both NULL: not returned.
+ * S0, z0 may be the same buffers as S, z (then this is la_causal_fwd_seg) or must not
+ * overlap them; neither may overlap q, k, v, out. One of a pair NULL and the other not,
+ * misalignment or a forbidden overlap: LA_EINVAL.
+ * Same definition and citations as la_causal_fwd ("Linear Attention Math", section "The
+ * recurrent form": S_0 = 0, z_0 = 0 for a fresh sequence).
+ */
+int la_causal_fwd_state(const void *q, const void *k, const void *v, void *out, const float *S0,
+                        const float *z0, float *S, float *z, int B, int H, int N, int d, int d_v,
+                        int chunk, int seg_len, la_dtype dtype, hipStream_t stream);
+
+/*
  * Global (non-causal): S = phi(K)^T V and z = phi(K)^T 1 per (b, h) over all N tokens, then
  * out[b,h,i] = phi(q_i)^T S / phi(q_i)^T z for every token.
  *   S, z   required; written (not read) with the full-sequence state.
@@ -118,20 +133,21 @@ int la_decode_step(const void *q, const void *k, const void *v, void *out, float
                    hipStream_t stream);
 
 /*
- * Profiling form of la_causal_fwd_seg: the same call enqueued `reps` times back to back on
- * `stream` (each call reads S, z as the previous one left them, so the work per call is
- * identical), with a HIP event recorded on that stream before and after each of every call's
- * kernels. The function then waits for the last event and writes the average device time in
- * milliseconds of each phase to ms[0..2]:
+ * Profiling form of la_causal_fwd_state: the same call enqueued `reps` times back to back on
+ * `stream` (with S0 == S each call reads the state the previous one left; the work per call
+ * is identical either way), with a HIP event recorded on that stream before and after each of
+ * every call's kernels. The function then waits for the last event and writes the average
+ * device time in milliseconds of each phase to ms[0..2]:
  *   ms[0] segment sums (segments 0..P-2), ms[1] exclusive scan over segment states,
  *   ms[2] causal outputs and final state; a phase the call did not launch (P = 1) gets 0.
  *   reps   1..4096; ms host array of 3 floats. reps out of range or ms NULL -> LA_EINVAL.
  * Blocks the calling thread until the work is done; for measurement, not for pipelines.
- * Errors as for la_causal_fwd_seg; a failure while creating or reading events -> LA_EHIP.
+ * Errors as for la_causal_fwd_state; a failure while creating or reading events -> LA_EHIP.
  */
-int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *out, float *S,
-                           float *z, int B, int H, int N, int d, int d_v, int chunk, int seg_len,
-                           la_dtype dtype, hipStream_t stream, int reps, float *ms);
+int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *out,
+                           const float *S0, const float *z0, float *S, float *z, int B, int H,
+                           int N, int d, int d_v, int chunk, int seg_len, la_dtype dtype,
+                           hipStream_t stream, int reps, float *ms);
 
 /* Bytes of stream-ordered temporary device memory a causal (form = 0) or global (form = 1)
  * call with these arguments takes (0 when none). seg_len as in la_causal_fwd_seg (0 = auto).

@@ -45,19 +45,23 @@ def test_version_and_strerror():
 
 
 def call(fn, q=A, k=2 * A, v=3 * A, out=4 * A, S=5 * A, z=6 * A, B=1, H=2, N=8, d=16, dv=16,
-         chunk=0, dtype=la.LA_BF16, seg=None):
+         chunk=0, dtype=la.LA_BF16, seg=None, S0="same", z0="same"):
     f = getattr(la.lib, fn)
+    if fn in ("la_causal_fwd_state", "la_causal_fwd_profiled"):
+        args = [q, k, v, out, S if S0 == "same" else S0, z if z0 == "same" else z0, S, z, B, H, N,
+                d, dv, chunk, 0 if seg is None else seg, dtype, None]
+        if fn == "la_causal_fwd_profiled":
+            args += [1, (ctypes.c_float * 3)()]
+        return f(*args)
     args = [q, k, v, out, S, z, B, H, N, d, dv, chunk]
-    if fn in ("la_causal_fwd_seg", "la_causal_fwd_profiled"):
+    if fn == "la_causal_fwd_seg":
         args.append(0 if seg is None else seg)
     args += [dtype, None]
-    if fn == "la_causal_fwd_profiled":
-        args += [1, (ctypes.c_float * 3)()]
     return f(*args)
 
 
-FORMS = ["la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_profiled", "la_global_fwd",
-         "la_decode_step"]
+FORMS = ["la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_profiled",
+         "la_global_fwd", "la_decode_step"]
 
 
 @pytest.mark.parametrize("fn", FORMS)
@@ -92,11 +96,24 @@ def test_form_specific_checks():
 
 def test_profiled_argument_checks():
     f = la.lib.la_causal_fwd_profiled
-    args = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 1, 2, 8, 16, 16, 0, 0, la.LA_BF16, None]
+    args = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 5 * A, 6 * A, 1, 2, 8, 16, 16, 0, 0, la.LA_BF16,
+            None]
     ms = (ctypes.c_float * 3)()
     assert f(*args, 1, None) == la.LA_EINVAL
     assert f(*args, 0, ms) == la.LA_EINVAL
     assert f(*args, 4097, ms) == la.LA_EINVAL
+
+
+def test_separate_state_checks():
+    fn = "la_causal_fwd_state"
+    S, z = 5 * A, 6 * A
+    assert call(fn, S0=S, z0=None) == la.LA_EINVAL              # half of a pair
+    assert call(fn, S0=None, z0=z) == la.LA_EINVAL
+    assert call(fn, S0=S + 16, z0=z) == la.LA_EINVAL            # partly overlaps S
+    assert call(fn, S0=S, z0=7 * A) == la.LA_EINVAL             # in place for S, not for z
+    assert call(fn, S0=A, z0=7 * A) == la.LA_EINVAL             # initial state overlaps q
+    assert call(fn, S0=7 * A, z0=7 * A) == la.LA_EINVAL         # S0 overlaps z0
+    assert call(fn, S0=7 * A + 8, z0=8 * A) == la.LA_EINVAL     # misaligned
 
 
 def test_chunk_and_segment_checks():

@@ -287,3 +287,43 @@ def test_causal_last_row_equals_global():
     og, Sg, zg = global_(q, k, v)
     check("last row", oc[:, :, -1:], og[:, :, -1:], TOL["bf16"])
     check("state", Sc, Sg, 1e-5)
+
+
+# ---------------------------------------------------------------- separate initial / final state
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 128, 3000), ("bf16", 64, 700), ("f32", 32, 300)])
+def test_separate_state(dtype, d, N):
+    """la_causal_fwd_state: zero initial state without a buffer; a carried initial state read
+    from one buffer and the final state written to another; the initial buffer unchanged."""
+    q, k, v = datagen.qkv(2, 3, N, d, d, 51 + d, 1 / math.sqrt(d), dtype)
+    n1 = N // 3
+    mod = la()
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    say(f"separate state dtype={dtype} d={d} N={N}")
+    # first piece from the zero state (nothing to read), final state out
+    out_a = torch.empty((2, 3, n1, d), dtype=q.dtype, device=DEV)
+    Sa = torch.full((2, 3, d, d), float("nan"), device=DEV)
+    za = torch.full((2, 3, d), float("nan"), device=DEV)
+    mod.la_causal_fwd_state(qd[:, :, :n1].contiguous(), kd[:, :, :n1].contiguous(),
+                            vd[:, :, :n1].contiguous(), out_a, None, None, Sa, za)
+    # second piece from that state into fresh buffers
+    out_b = torch.empty((2, 3, N - n1, d), dtype=q.dtype, device=DEV)
+    Sb = torch.full((2, 3, d, d), float("nan"), device=DEV)
+    zb = torch.full((2, 3, d), float("nan"), device=DEV)
+    Sa_before = Sa.clone()
+    mod.la_causal_fwd_state(qd[:, :, n1:].contiguous(), kd[:, :, n1:].contiguous(),
+                            vd[:, :, n1:].contiguous(), out_b, Sa, za, Sb, zb)
+    # outputs only (final state not returned)
+    out_c = torch.empty_like(out_b)
+    mod.la_causal_fwd_state(qd[:, :, n1:].contiguous(), kd[:, :, n1:].contiguous(),
+                            vd[:, :, n1:].contiguous(), out_c, Sa, za, None, None)
+    torch.cuda.synchronize()
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v))
+    _, S1, z1, _, _ = oracle.causal(f64(q[:, :, :n1]), f64(k[:, :, :n1]), f64(v[:, :, :n1]))
+    check("first piece out", f64(out_a), oo[:, :, :n1], TOL[dtype])
+    check("first piece S", f64(Sa), S1, TOL[dtype])
+    check("first piece z", f64(za)[..., None], z1[..., None], TOL[dtype])
+    check("second piece out", f64(out_b), oo[:, :, n1:], TOL[dtype])
+    check("final S", f64(Sb), So, TOL[dtype])
+    check("final z", f64(zb)[..., None], zo[..., None], TOL[dtype])
+    assert torch.equal(Sa, Sa_before), "the initial state buffer must not change"
+    assert torch.equal(out_b, out_c), "returning the final state must not change the outputs"
