@@ -38,6 +38,7 @@ template <int D> struct Cfg {
     static constexpr int RS = D + 16;           // row stride (elements) of the chunk arrays
     static constexpr int AS = C * RS + (C / 8 - 1) * 64; // chunk array size (elements)
     static constexpr int TS = C + 8;            // row stride (elements) of the score block
+    static constexpr int ZS = D + 8;            // row stride (elements) of the key-sum operand
     static constexpr int NCT = D / 64;          // 16-wide value-column tiles per wave (4 waves)
     static constexpr int NFT = D / 16;          // 16-row feature tiles of S
     static constexpr int NKB = D / 32;          // 32-feature k blocks
@@ -384,10 +385,14 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
 
 // ------------------------------------------------------------------------------------------
 // Causal kernel geometry: NCW = D/16 compute waves, each owning 16 value columns of S and one
-// 16-feature tile of z, plus 4 stage waves (NT threads).
+// 16-feature tile of z, plus NSW stage waves. Staging (three tensors per chunk, phi on two of
+// them) is the longer role per chunk at d = 128, so it gets as many waves as the register
+// budget of 16 waves per CU allows.
 template <int D> struct CausalCfg {
     static constexpr int NCW = D / 16;
-    static constexpr int THREADS = (NCW + 4) * 64;
+    static constexpr int NSW = D == 128 ? 8 : 4;
+    static constexpr int STAGE_THREADS = NSW * 64;
+    static constexpr int THREADS = (NCW + NSW) * 64;
 };
 
 template <int D> struct CausalLds {
@@ -395,7 +400,9 @@ template <int D> struct CausalLds {
     uint16_t sK[2][Cfg<D>::AS]; // phi(K), double-buffered (read in both phases)
     uint16_t sV[Cfg<D>::AS];    // V, read only in phase 2
     uint16_t sA[C * Cfg<D>::TS];
-    float sz[D];           // key sum before the chunk being computed
+    // key sum before the chunk being computed, as the A operand of phi(Q) z: row 0 = bf16(z),
+    // row 1 = bf16(z - row 0) (together ~16 significant bits), row 2 = 0 (read by lanes 2..15)
+    uint16_t szA[3][Cfg<D>::ZS];
     float srs[C];          // rowsum(A) per query row of the chunk
     float sqz[C];          // phi(q) . z per query row of the chunk
 };
@@ -407,6 +414,20 @@ struct CausalArgs {
     float *Sout, *zout;           // final state of the head (null: not written)
     int tb, te, nch;              // token range of the segment, chunks in it
 };
+
+// Writes the wave's 16 features of z (rows 4g..4g+3 of its tile; lane li == 0 of each group)
+// into the key-sum operand rows: bf16(z) and bf16(z - bf16(z)).
+template <int D>
+__device__ __forceinline__ void put_z(CausalLds<D> &sm, const f32x4 &z, int w, int li, int g)
+{
+    if (li == 0) {
+        const uint32_t h0 = pack_bf2(z[0], z[1]), h1 = pack_bf2(z[2], z[3]);
+        const uint32_t l0 = pack_bf2(z[0] - bf_lo(h0), z[1] - bf_hi(h0));
+        const uint32_t l1 = pack_bf2(z[2] - bf_lo(h1), z[3] - bf_hi(h1));
+        sts<u32x2>(&sm.szA[0][16 * w + 4 * g], u32x2{h0, h1});
+        sts<u32x2>(&sm.szA[1][16 * w + 4 * g], u32x2{l0, l1});
+    }
+}
 
 // Compute role (waves 0..NCW-1). Wave w owns value columns [16w, 16w+16) of S and the key-sum
 // features [16w, 16w+16). Barrier sequence: 1 in the prologue, 2 per chunk.
@@ -434,11 +455,10 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
         for (int r = 0; r < 4; ++r)
             zacc[0][r] = a.z0[16 * w + 4 * g + r];
     }
-    if (li == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            sm.sz[16 * w + 4 * g + r] = zacc[0][r];
-    }
+    put_z<D>(sm, zacc[0], w, li, g);
+    if (w == 0)
+        for (int i = threadIdx.x; i < D / 8; i += 64)
+            sts<u32x4>(&sm.szA[2][8 * i], u32x4{0u, 0u, 0u, 0u});
     __syncthreads();
 
     // phase-1 jobs: waves 0-3 compute the scores of query rows 16w..16w+15; the waves that
@@ -488,19 +508,16 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
                 sm.srs[16 * w + li] = rs;
         }
         if (qz) {
-            float s = 0.f;
+            // phi(Q) z for query rows 16iw..: one matrix-core product per 32 features with
+            // A = the key-sum rows (lane li reads row min(li, 2)); C rows 0 and 1 hold the
+            // two parts of the sum for the lane's query
+            const uint16_t *za = &sm.szA[li < 2 ? li : 2][8 * g];
+            f32x4 cz = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < K::NKB; ++kk) {
-                const u32x4 qw = lds<u32x4>(sQ + opl + blk<D>(16 * iw, 32 * kk));
-                const f32x4 z0 = *reinterpret_cast<const f32x4 *>(sm.sz + 32 * kk + 8 * g);
-                const f32x4 z1 = *reinterpret_cast<const f32x4 *>(sm.sz + 32 * kk + 8 * g + 4);
-                s += bf_lo(qw[0]) * z0[0] + bf_hi(qw[0]) * z0[1] + bf_lo(qw[1]) * z0[2] + bf_hi(qw[1]) * z0[3];
-                s += bf_lo(qw[2]) * z1[0] + bf_hi(qw[2]) * z1[1] + bf_lo(qw[3]) * z1[2] + bf_hi(qw[3]) * z1[3];
-            }
-            s += __shfl_xor(s, 16, 64);
-            s += __shfl_xor(s, 32, 64);
+            for (int kk = 0; kk < K::NKB; ++kk)
+                cz = mfma(lds<bf16x8>(za + 32 * kk), lds<bf16x8>(sQ + opl + blk<D>(16 * iw, 32 * kk)), cz);
             if (g == 0)
-                sm.sqz[16 * iw + li] = s;
+                sm.sqz[16 * iw + li] = cz[0] + cz[1];
         }
         __syncthreads();
         // ---- phase 2: num^T = V^T A^T + S^T Qf^T for the wave's columns; out; S, z += Kf^T [V 1]
@@ -522,11 +539,7 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
             store_out<D, 1>(acc, sm.srs, sm.sqz, a.oh + (size_t)t0 * D, nvalid, cw0, li, g);
             state_update<D, 1>(sacc, sK + trl, sm.sV + cw0 + trl);
             key_sum<D, 1>(zacc, sK + 16 * w + trl);
-            if (li == 0) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sm.sz[16 * w + 4 * g + r] = zacc[0][r];
-            }
+            put_z<D>(sm, zacc[0], w, li, g);
         }
         __syncthreads();
     }
@@ -544,14 +557,14 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
     }
 }
 
-// Stage role (4 waves after the compute waves, thread index ht = 0..255). Same barrier sequence
+// Stage role (the NSW waves after the compute waves, thread index ht). Same barrier sequence
 // as the compute role.
 template <int D>
 __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs &a, int ht)
 {
-    using K = Cfg<D>;
-    const Tile<D> tile(ht);
-    u32x4 rq[Tile<D>::TM], rk[Tile<D>::TM], rv[Tile<D>::TM];
+    using TL = Tile<D, CausalCfg<D>::STAGE_THREADS>;
+    const TL tile(ht);
+    u32x4 rq[TL::TM], rk[TL::TM], rv[TL::TM];
     const int tb = a.tb, te = a.te, nch = a.nch;
     // first token of chunk c' (clamped to the last chunk, so prefetches past the end re-read
     // it: every load is in bounds and unconditional)
@@ -603,7 +616,7 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
 //
 // Two roles share every SIMD. D/16 "compute" waves hold the float32 state S and key sum z in
 // accumulators (16 value columns of S and 16 features of z each) and run the matrix-core
-// products of chunk c. Four "stage" waves load the next chunks from HBM, apply phi and store
+// products of chunk c. NSW "stage" waves load the next chunks from HBM, apply phi and store
 // them row-major into LDS. Two barriers per chunk:
 //   phase 1  compute: scores A of chunk c (waves 0-3: query rows 16w..16w+15), rowsum(A) and
 //                     phi(q) . z per query row
