@@ -13,7 +13,8 @@ Two independent formulations live here:
 Inputs are float64 NumPy arrays holding exactly the values the GPU saw (bf16/fp32 upcast
 exactly); shapes q, k [B,H,N,d], v [B,H,N,dv], S [B,H,d,dv], z [B,H,d].
 ``mode`` = "elu1" applies phi(x) = ELU(x) + 1; "identity" takes q and k as already mapped
-(the convention of the pages' worked examples).
+(the convention of the pages' worked examples). ``normalize=False`` returns the numerator
+phi(q)^T S itself (the unnormalised form). ``rf_map`` gives positive random features.
 """
 from __future__ import annotations
 
@@ -52,6 +53,8 @@ def _bind(path):
     lib.oracle_causal.restype = None
     lib.oracle_global.restype = None
     lib.oracle_decode.restype = None
+    lib.oracle_rf_map.argtypes = [P, P, P, L, L, L]
+    lib.oracle_rf_map.restype = None
     lib.oracle_threads.restype = ctypes.c_int
     return lib
 
@@ -77,7 +80,11 @@ def threads(lib=None) -> int:
     return int((lib or _load()).oracle_threads())
 
 
-def causal(q, k, v, S0=None, z0=None, mode: str = "elu1", lib=None):
+def _mode(mode, normalize):
+    return _MODES[mode] | (0 if normalize else 2)
+
+
+def causal(q, k, v, S0=None, z0=None, mode: str = "elu1", normalize: bool = True, lib=None):
     """Causal recurrence. Returns (o, S_N, z_N, num, den).
 
     S0, z0 (optional) are the state before the first token (zeros if omitted)."""
@@ -91,11 +98,11 @@ def causal(q, k, v, S0=None, z0=None, mode: str = "elu1", lib=None):
     num = np.empty((B, H, N, dv))
     den = np.empty((B, H, N))
     (lib or _load()).oracle_causal(_p(q), _p(k), _p(v), _p(o), _p(num), _p(den), _p(S), _p(z),
-                                   B * H, N, d, dv, _MODES[mode])
+                                   B * H, N, d, dv, _mode(mode, normalize))
     return o, S, z, num, den
 
 
-def global_(q, k, v, mode: str = "elu1", lib=None):
+def global_(q, k, v, mode: str = "elu1", normalize: bool = True, lib=None):
     """Global (non-causal) form. Returns (o, S, z, num, den).
 
     q may hold a different number of rows Nq than k and v (each query row is read against the
@@ -108,7 +115,7 @@ def global_(q, k, v, mode: str = "elu1", lib=None):
     z = np.empty((B, H, d))
     if q is None:
         (lib or _load()).oracle_global(None, _p(k), _p(v), None, None, None, _p(S), _p(z),
-                                       B * H, N, 0, d, dv, _MODES[mode])
+                                       B * H, N, 0, d, dv, _mode(mode, normalize))
         return None, S, z, None, None
     q = _f64(q)
     Nq = q.shape[2]
@@ -117,11 +124,11 @@ def global_(q, k, v, mode: str = "elu1", lib=None):
     num = np.empty((B, H, Nq, dv))
     den = np.empty((B, H, Nq))
     (lib or _load()).oracle_global(_p(q), _p(k), _p(v), _p(o), _p(num), _p(den), _p(S), _p(z),
-                                   B * H, N, Nq, d, dv, _MODES[mode])
+                                   B * H, N, Nq, d, dv, _mode(mode, normalize))
     return o, S, z, num, den
 
 
-def decode_step(q, k, v, S, z, mode: str = "elu1", lib=None):
+def decode_step(q, k, v, S, z, mode: str = "elu1", normalize: bool = True, lib=None):
     """One recurrent step for every head; q, k [B,H,d] (or [B,H,1,d]), v [B,H,dv] (or
     [B,H,1,dv]). Returns (o [B,H,dv], S', z'); the inputs S, z are not modified."""
     S = _f64(S).copy()
@@ -132,5 +139,16 @@ def decode_step(q, k, v, S, z, mode: str = "elu1", lib=None):
     v = _f64(v).reshape(B, H, dv)
     o = np.empty((B, H, dv))
     (lib or _load()).oracle_decode(_p(q), _p(k), _p(v), _p(o), _p(S), _p(z), B * H, d, dv,
-                                   _MODES[mode])
+                                   _mode(mode, normalize))
     return o, S, z
+
+
+def rf_map(x, W, lib=None):
+    """Positive random features of x [..., d] for projections W [m, d]: [..., m]."""
+    x = _f64(x)
+    W = _f64(W)
+    m, d = W.shape
+    assert x.shape[-1] == d
+    f = np.empty(x.shape[:-1] + (m,))
+    (lib or _load()).oracle_rf_map(_p(x), _p(W), _p(f), int(np.prod(x.shape[:-1])), d, m)
+    return f

@@ -9,7 +9,7 @@
  *   feature map   phi(x) = ELU(x) + 1 with alpha = 1, i.e. x + 1 for x > 0 and exp(x) otherwise
  *                 ("Linear Attention: Accumulating KV in a Fixed-Size State", section
  *                 "Why replace softmax?"; "Linear Attention Math", section "Feature maps:
- *                 elu+1 and positive random features"). mode = 1 selects phi(x) = x, the
+ *                 elu+1 and positive random features"). mode bit 0 selects phi(x) = x, the
  *                 feature-space convention of the pages' worked examples ("Store Values
  *                 according to Key components": q and k already denote mapped vectors).
  *   causal form   S_t = S_{t-1} + phi(k_t) v_t^T,  z_t = z_{t-1} + phi(k_t),
@@ -22,6 +22,13 @@
  *   decode step   one step of the recurrence applied to a caller-held state: update, then read
  *                 ("Linear Attention Math", section "The recurrent form"; its last paragraph
  *                 states the O(1) per-token inference form).
+ *   unnormalised  mode bit 1 returns the numerator phi(q_t)^T S_t itself (the weighted sum
+ *                 before the division; "Linear Attention: Accumulating KV in a Fixed-Size
+ *                 State", section "Read the state with a Query", prints such sums).
+ *   random        oracle_rf_map: positive random features phi(x)_r = exp(w_r . x - |x|^2 / 2)
+ *   features      / sqrt(m) for given projections w_r ("Linear Attention Math", section
+ *                 "Feature maps: elu+1 and positive random features"); attention over them
+ *                 is the identity-phi form applied to the mapped rows.
  * There is no epsilon in the denominator (the denominator is a sum of strictly positive terms
  * under ELU+1; "Linear Attention: From Pairwise Reads to a Recurrent State", section "The
  * reassociation that works", notes that a clamp changes the operation).
@@ -39,7 +46,7 @@
 
 static double phi(double x, int mode)
 {
-    if (mode == 1)
+    if (mode & 1)
         return x;
     return x > 0.0 ? x + 1.0 : exp(x);
 }
@@ -80,13 +87,15 @@ void oracle_causal(const double *q, const double *k, const double *v, double *o,
             for (long i = 0; i < d; ++i)
                 for (long j = 0; j < dv; ++j)
                     nm[j] += qf[i] * Sh[i * dv + j];
+            if (den)
+                den[h * N + t] = dn;
+            if (mode & 2) /* unnormalised form: the numerator is the output */
+                dn = 1.0;
             for (long j = 0; j < dv; ++j) {
                 o[(h * N + t) * dv + j] = nm[j] / dn;
                 if (num)
                     num[(h * N + t) * dv + j] = nm[j];
             }
-            if (den)
-                den[h * N + t] = dn;
         }
         free(kf);
         free(qf);
@@ -133,13 +142,15 @@ void oracle_global(const double *q, const double *k, const double *v, double *o,
             for (long i = 0; i < d; ++i)
                 for (long j = 0; j < dv; ++j)
                     nm[j] += qf[i] * Sh[i * dv + j];
+            if (den)
+                den[h * Nq + t] = dn;
+            if (mode & 2)
+                dn = 1.0;
             for (long j = 0; j < dv; ++j) {
                 o[(h * Nq + t) * dv + j] = nm[j] / dn;
                 if (num)
                     num[(h * Nq + t) * dv + j] = nm[j];
             }
-            if (den)
-                den[h * Nq + t] = dn;
         }
         free(kf);
         free(qf);
@@ -175,8 +186,32 @@ void oracle_decode(const double *q, const double *k, const double *v, double *o,
             for (long j = 0; j < dv; ++j)
                 o[h * dv + j] += qfi * Sh[i * dv + j];
         }
+        if (mode & 2)
+            dn = 1.0;
         for (long j = 0; j < dv; ++j)
             o[h * dv + j] /= dn;
+    }
+}
+
+/* Positive random features of `rows` vectors x [rows, d] for the projections W [m, d]:
+ * f[i][r] = exp(sum_j W[r][j] x[i][j] - (1/2) sum_j x[i][j]^2) / sqrt(m), so that
+ * f(q) . f(k) is an unbiased estimate of exp(q . k) when the rows of W are standard normal
+ * ("Linear Attention Math", section "Feature maps: elu+1 and positive random features"). */
+void oracle_rf_map(const double *x, const double *W, double *f, long rows, long d, long m)
+{
+    const double scale = 1.0 / sqrt((double)m);
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < rows; ++i) {
+        const double *xi = x + i * d;
+        double sq = 0.0;
+        for (long j = 0; j < d; ++j)
+            sq += xi[j] * xi[j];
+        for (long r = 0; r < m; ++r) {
+            double dot = 0.0;
+            for (long j = 0; j < d; ++j)
+                dot += W[r * d + j] * xi[j];
+            f[i * m + r] = exp(dot - 0.5 * sq) * scale;
+        }
     }
 }
 

@@ -33,6 +33,9 @@ class Orc:
     def decode_step(self, *a, **kw):
         return oracle.decode_step(*a, lib=self.lib, **kw)
 
+    def rf_map(self, *a, **kw):
+        return oracle.rf_map(*a, lib=self.lib, **kw)
+
 
 def _enc(feat):
     """Raw input whose ELU+1 features are the given 0/1/3 feature values."""
@@ -284,7 +287,98 @@ def pin_invariants(orc: Orc, golden=None):
     _close(den, w.sum(axis=-1), 1e-12)
 
 
+# ------------------------------------------------------------- unnormalised form (pages 1, 4)
+def pin_unnormalised_reads(orc: Orc, golden):
+    """normalize=False returns the numerator phi(q)^T S itself: the printed reads of S3, the
+    printed numerator of the decode example, and the duplicate-value sums, in all three forms;
+    on random inputs the unnormalised output times the normalised form's denominator is the
+    normalised output's numerator."""
+    g = golden("w7_unnormalised_reads.json")
+    se, de = g["state_example"], g["decode_example"]
+    k, v = np.array(se["k"], float), np.array(se["v"], float)
+    for mode, enc in (("identity", lambda x: x), ("elu1", _enc)):
+        for qs, key in (([1, 0], "q=[1,0]"), ([0, 1], "q=[0,1]"), ([1, 1], "q=[1,1]")):
+            qq = k.copy()
+            qq[2] = qs
+            o, _, _, num, _ = orc.causal(_t(enc(qq)), _t(enc(k)), _t(v), mode=mode,
+                                         normalize=False)
+            _close(o[0, 0, 2], se["printed_reads"][key])
+            _close(num[0, 0, 2], se["printed_reads"][key])
+            og, *_ = orc.global_(_t(enc(np.array([qs], float))), _t(enc(k)), _t(v), mode=mode,
+                                 normalize=False)
+            _close(og[0, 0, 0], se["printed_reads"][key])
+        pk, dv_, pq = (np.array(de[x], float) for x in ("phi_k", "v", "phi_q"))
+        S = np.zeros((1, 1, 2, 2))
+        z = np.zeros((1, 1, 2))
+        for t in range(2):
+            o, S, z = orc.decode_step(enc(pq)[None, None], enc(pk[t])[None, None],
+                                      dv_[t][None, None], S, z, mode=mode, normalize=False)
+        _close(o[0, 0], de["printed_numerator"])
+    w5 = golden("w5_duplicate_value.json")
+    vv = np.array(w5["v"], float)
+    o, *_ = orc.causal(_t(np.full((2, 1), RAW_ONE)), _t(np.full((2, 1), RAW_ONE)),
+                       _t(np.stack([vv, vv])), normalize=False)
+    _close(o[0, 0, 0], w5["printed"]["once_unnormalised"])
+    _close(o[0, 0, 1], w5["printed"]["twice_unnormalised"])
+    q, kk, vr = _rand((1, 2, 13, 4, 3), 15)
+    on, _, _, _, den = orc.causal(q, kk, vr)
+    ou, Su, zu, _, _ = orc.causal(q, kk, vr, normalize=False)
+    _close(ou, on * den[..., None], 1e-13)
+    og, Sg, zg, _, _ = orc.global_(q, kk, vr)
+    _close(Su, Sg, 1e-12)
+    _close(zu, zg, 1e-12)
+
+
+# ------------------------------------------------------------- positive random features (page 4)
+def pin_rf_closed_form(orc: Orc, golden=None):
+    """f_r(x) = exp(w_r . x - |x|^2 / 2) / sqrt(m): hand-computed values for an asymmetric W
+    (a transposed W or a dropped term changes them), W = 0 gives exp(-|x|^2 / 2) / sqrt(m),
+    x = 0 gives 1 / sqrt(m), and every feature is strictly positive."""
+    W = np.array([[1.0, 2.0], [0.0, -1.0], [0.5, 0.0]])      # m = 3, d = 2
+    x = np.array([[1.0, 0.0], [0.0, 0.5], [-1.0, 1.0]])
+    s = 1.0 / math.sqrt(3.0)
+    want = np.array([
+        [math.exp(1.0 - 0.5), math.exp(0.0 - 0.5), math.exp(0.5 - 0.5)],
+        [math.exp(1.0 - 0.125), math.exp(-0.5 - 0.125), math.exp(0.0 - 0.125)],
+        [math.exp(1.0 - 1.0), math.exp(-1.0 - 1.0), math.exp(-0.5 - 1.0)],
+    ]) * s
+    _close(orc.rf_map(x, W), want, 1e-14)
+    g = np.random.default_rng(16)
+    xr = g.standard_normal((5, 7))
+    _close(orc.rf_map(xr, np.zeros((4, 7))),
+           np.repeat(np.exp(-0.5 * (xr ** 2).sum(-1))[:, None], 4, axis=1) / 2.0, 1e-14)
+    _close(orc.rf_map(np.zeros((2, 7)), g.standard_normal((9, 7))), np.full((2, 9), 1 / 3.0),
+           1e-15)
+    f = orc.rf_map(3.0 * xr, g.standard_normal((64, 7)))
+    assert np.all(f > 0) and np.all(np.isfinite(f))
+
+
+def pin_rf_unbiased(orc: Orc, golden=None):
+    """With standard normal projections, f(q) . f(k) averages to exp(q . k): the estimate over
+    2^17 seeded features lies within 5 standard errors of exp(q . k) for several pairs, and
+    identity-phi attention over the features of q and k lands near softmax attention over the
+    raw scores q . k (the kernel the features estimate)."""
+    g = np.random.default_rng(17)
+    d, m = 4, 1 << 17
+    W = g.standard_normal((m, d))
+    q = 0.5 * g.standard_normal((6, d))
+    k = 0.5 * g.standard_normal((6, d))
+    fq, fk = orc.rf_map(q, W), orc.rf_map(k, W)
+    for i in range(6):
+        terms = fq[i] * fk[i] * m                      # m per-feature estimates of exp(q.k)
+        est, se = terms.mean(), terms.std() / math.sqrt(m)
+        exact = math.exp(float(q[i] @ k[i]))
+        assert abs(est - exact) <= 5 * se, (i, est, exact, se)
+        assert abs(est - exact) <= 0.1 * exact, (i, est, exact)
+    v = g.standard_normal((6, 3))
+    o, *_ = orc.causal(_t(fq), _t(fk), _t(v), mode="identity")
+    sc = np.tril(np.exp(q @ k.T))
+    soft = (sc @ v) / sc.sum(-1, keepdims=True)
+    _close(o[0, 0], soft, 2e-2)
+
+
 ALL_PINS = [pin_phi_closed_form, pin_two_token_read, pin_not_softmax, pin_three_token,
             pin_decode_example, pin_outer_product, pin_duplicate_value, pin_global_example,
             pin_brute_force, pin_global_matmul, pin_causal_last_equals_global,
-            pin_decode_chain_equals_causal, pin_split_invariance, pin_invariants]
+            pin_decode_chain_equals_causal, pin_split_invariance, pin_invariants,
+            pin_unnormalised_reads, pin_rf_closed_form, pin_rf_unbiased]

@@ -34,6 +34,14 @@ MUTANTS = [
     ("decode_den_uses_key", "dn += phi(qh[i], mode) * zh[i];", "dn += phi(kh[i], mode) * zh[i];", 1),
     ("decode_read_before_write_scale", "Sh[i * dv + j] += kfi * vh[j];",
      "Sh[i * dv + j] += 0.5 * kfi * vh[j];", 1),
+    ("unnormalised_flag_ignored", "if (mode & 2) /* unnormalised form: the numerator is the output */\n                dn = 1.0;",
+     "", 1),
+    ("global_unnormalised_ignored", "            if (mode & 2)\n                dn = 1.0;", "", 1),
+    ("decode_unnormalised_ignored", "        if (mode & 2)\n            dn = 1.0;", "", 1),
+    ("rf_drops_half_norm", "exp(dot - 0.5 * sq)", "exp(dot)", 1),
+    ("rf_scale_by_m", "1.0 / sqrt((double)m)", "1.0 / (double)m", 1),
+    ("rf_transposed_projection", "dot += W[r * d + j] * xi[j];", "dot += W[j * m + r] * xi[j];", 1),
+    ("rf_sign_of_projection", "exp(dot - 0.5 * sq)", "exp(-dot - 0.5 * sq)", 1),
 ]
 
 
