@@ -156,6 +156,74 @@ def bench_global(args):
     return w, ms, byts
 
 
+def bench_favor(args):
+    """Positive random features: la_rf_features on q and on k (m = 128 projections), then
+    causal attention over the features (la_causal_fwd_ex with LA_PHI_IDENTITY), on the prefill
+    workload's inputs. Returns per-step and per-kernel times."""
+    import torch
+    import causal_linear_attention_la_amd as la
+    import datagen
+
+    rw = datagen.RF_WORKLOAD
+    w = datagen.WORKLOADS[rw["base"]]
+    m = rw["m"]
+    dev = torch.device("cuda:0")
+    W = datagen.projections(m, w.d, rw["seed"], "bf16").to(dev)
+    sets = []
+    for r in range(args.rotate):
+        q, k, v = datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed + 100 * r, w.scale, "bf16")
+        fq = torch.empty((w.B, w.H, w.N, m), dtype=torch.bfloat16, device=dev)
+        fk = torch.empty_like(fq)
+        out = torch.empty_like(v)
+        S = torch.empty(w.B, w.H, m, w.dv, device=dev)
+        z = torch.empty(w.B, w.H, m, device=dev)
+        sets.append((q, k, v, fq, fk, out, S, z))
+
+    def step(i):
+        q, k, v, fq, fk, out, S, z = sets[i % len(sets)]
+        la.la_rf_features(q, W, fq)
+        la.la_rf_features(k, W, fk)
+        la.la_causal_fwd_ex(fq, fk, v, out, None, None, S, z, flags=la.LA_PHI_IDENTITY)
+
+    ms, _ = time_calls(step, args.steps, args.warmup)
+
+    def rf_only(i):
+        q, _, _, fq, _, _, _, _ = sets[i % len(sets)]
+        la.la_rf_features(q, W, fq)
+
+    ms_rf, _ = time_calls(rf_only, args.steps, 2)
+    q, k, v, fq, fk, out, S, z = sets[0]
+    kern = la.la_causal_fwd_profiled(fq, fk, v, out, None, None, S, z, flags=la.LA_PHI_IDENTITY,
+                                     reps=args.steps)
+    rows = w.B * w.H * w.N
+    rf_bytes = rows * (w.d + m) * 2 + m * w.d * 2
+    return w, m, ms, ms_rf, rf_bytes, kern
+
+
+def favor_name():
+    import datagen
+    return datagen.RF_WORKLOAD["name"]
+
+
+def bench_variants(args):
+    """Causal prefill with q, k taken as features and no division (LA_PHI_IDENTITY |
+    LA_UNNORMALIZED) on the prefill workload: the cost of the form without phi and z."""
+    import torch
+    import causal_linear_attention_la_amd as la
+    import datagen
+
+    w = datagen.WORKLOADS[3]
+    dev = torch.device("cuda:0")
+    q, k, v = datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale, "bf16")
+    out = torch.empty_like(q)
+    S = torch.empty(w.B, w.H, w.d, w.dv, device=dev)
+    z = torch.empty(w.B, w.H, w.d, device=dev)
+    flags = la.LA_PHI_IDENTITY | la.LA_UNNORMALIZED
+    ms, _ = time_calls(lambda i: la.la_causal_fwd_ex(q, k, v, out, None, None, S, z, flags=flags),
+                       args.steps, 2)
+    return w, ms
+
+
 def cpu_baseline():
     """The float64 oracle, as it stands, on the prefill workload's 32 heads (full size; about
     10 s of CPU work on 8 host threads)."""
@@ -228,7 +296,8 @@ def main():
     ap.add_argument("--seg-len", dest="seg_len", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled over the steps")
     ap.add_argument("--decode-steps", dest="decode_steps", type=int, default=1000)
-    ap.add_argument("--only", choices=["prefill", "decode", "global", "copycal"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "global", "favor", "variants", "copycal"],
+                    default=None,
                     help="run one form only (for profiling); no JSON line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copycal", action="store_true",
@@ -249,12 +318,17 @@ def main():
     if args.only:
         if args.copycal:
             copy_calibration()
-        fn = {"prefill": bench_prefill, "decode": bench_decode, "global": bench_global}[args.only]
+        fn = {"prefill": bench_prefill, "decode": bench_decode, "global": bench_global,
+              "favor": bench_favor, "variants": bench_variants}[args.only]
         r = fn(args)
         extra = ""
         if args.only == "prefill":
             extra = " (kernels: " + ", ".join(f"{t * 1e3:.1f}" for t in r[7]) + " us)"
-        print(f"{args.only}: {r[1]:.4f} ms/step{extra}", flush=True)
+        if args.only == "favor":
+            extra = f" (features {r[3] * 1e3:.1f} us per tensor; attention kernels " + \
+                ", ".join(f"{t * 1e3:.1f}" for t in r[5]) + " us)"
+        ms = r[2] if args.only == "favor" else r[1]
+        print(f"{args.only}: {ms:.4f} ms/step{extra}", flush=True)
         return
 
     w, ms, ms_hot, wall, byts, flops, P, kern_ms = bench_prefill(args)
@@ -270,6 +344,11 @@ def main():
     print(f"decode: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     wg, ms_g, byts_g = bench_global(args)
     print(f"global: {ms_g * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+    wf, m_f, ms_f, ms_rf, rf_bytes, kern_f = bench_favor(args)
+    print(f"favor: {ms_f * 1e3:.1f} us/step (features {ms_rf * 1e3:.1f} us per tensor)",
+          file=sys.stderr, flush=True)
+    wv, ms_v = bench_variants(args)
+    print(f"identity+unnormalised causal: {ms_v * 1e3:.1f} us/call", file=sys.stderr, flush=True)
 
     rec = {
         "metric": METRIC,
@@ -309,6 +388,16 @@ def main():
         "global": {"workload": wg.name, "us_per_call": ms_g * 1e3,
                    "token_heads_per_s": wg.B * wg.H * wg.N / (ms_g * 1e-3),
                    "hbm_frac": byts_g / (ms_g * 1e-3) / HBM_PEAK},
+        "favor": {"workload": favor_name(), "m": m_f,
+                  "us_per_step": ms_f * 1e3,
+                  "token_heads_per_s": wf.B * wf.H * wf.N / (ms_f * 1e-3),
+                  "features_us_per_tensor": ms_rf * 1e3,
+                  "features_hbm_frac": rf_bytes / (ms_rf * 1e-3) / HBM_PEAK,
+                  "attention_kernels_us": {"segment_sums": kern_f[0] * 1e3,
+                                           "segment_scan": kern_f[1] * 1e3,
+                                           "causal": kern_f[2] * 1e3}},
+        "identity_unnormalized": {"workload": wv.name, "us_per_call": ms_v * 1e3,
+                                  "token_heads_per_s": wv.B * wv.H * wv.N / (ms_v * 1e-3)},
         "wall_s_timed_region": wall,
     }
     if not args.no_cpu:

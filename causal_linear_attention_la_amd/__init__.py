@@ -6,10 +6,15 @@ the library's HIP kernels. PyTorch supplies device memory and streams; nothing e
 
 The entry points keep the C names:
     la_causal_fwd(q, k, v, out, S=None, z=None, chunk=0, seg_len=0)
+    la_causal_fwd_ex(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk=0, seg_len=0, flags=0)
     la_global_fwd(q, k, v, out, S, z, chunk=0)         # q, out may be None: state only
+    la_global_fwd_ex(q, k, v, out, S, z, chunk=0, flags=0)
     la_decode_step(q, k, v, out, S, z)
+    la_decode_step_ex(q, k, v, out, S, z, flags=0)
+    la_rf_features(x, W, f)                            # positive random features
 with q, k [B,H,N,d], v, out [B,H,N,d_v] (bf16 or float32, contiguous, on the GPU),
-S [B,H,d,d_v] and z [B,H,d] float32. A non-zero status raises ``LAError``.
+S [B,H,d,d_v] and z [B,H,d] float32; flags is a bitwise or of LA_PHI_IDENTITY and
+LA_UNNORMALIZED. A non-zero status raises ``LAError``.
 
 If the shared library is missing or fails to load, importing this package raises: there is
 no fallback implementation.
@@ -32,10 +37,13 @@ LIB_PATH = Path(os.environ.get("LINATTN_LIB", _PKG / "liblinattn.so"))
 
 LA_F32, LA_BF16 = 0, 1
 LA_OK, LA_EINVAL, LA_ENOTSUP, LA_EHIP = 0, 1, 2, 3
+LA_PHI_IDENTITY, LA_UNNORMALIZED = 1, 2
 
 # Every symbol include/la.h declares.
-EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_profiled",
-           "la_global_fwd", "la_decode_step", "la_workspace_bytes", "la_strerror", "la_version")
+EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
+           "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
+           "la_decode_step_ex", "la_rf_features", "la_workspace_bytes", "la_strerror",
+           "la_version")
 
 
 class LAError(RuntimeError):
@@ -53,13 +61,18 @@ def _load(path: Path):
     core = [vp, vp, vp, vp, fp, fp, i, i, i, i, i, i]
     lib.la_causal_fwd.argtypes = core + [i, vp]
     lib.la_causal_fwd_seg.argtypes = core + [i, i, vp]
-    state = [vp, vp, vp, vp, fp, fp, fp, fp, i, i, i, i, i, i, i, i, vp]
-    lib.la_causal_fwd_state.argtypes = state
-    lib.la_causal_fwd_profiled.argtypes = state + [i, ctypes.POINTER(ctypes.c_float)]
+    state = [vp, vp, vp, vp, fp, fp, fp, fp, i, i, i, i, i, i, i]
+    lib.la_causal_fwd_state.argtypes = state + [i, vp]
+    lib.la_causal_fwd_ex.argtypes = state + [i, i, vp]
+    lib.la_causal_fwd_profiled.argtypes = state + [i, i, vp, i, ctypes.POINTER(ctypes.c_float)]
     lib.la_global_fwd.argtypes = core + [i, vp]
+    lib.la_global_fwd_ex.argtypes = core + [i, i, vp]
     lib.la_decode_step.argtypes = core + [i, vp]
-    for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_profiled",
-              "la_global_fwd", "la_decode_step"):
+    lib.la_decode_step_ex.argtypes = core + [i, vp]
+    lib.la_rf_features.argtypes = [vp, vp, vp, ctypes.c_long, i, i, i, vp]
+    for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
+              "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
+              "la_decode_step_ex", "la_rf_features"):
         getattr(lib, f).restype = ctypes.c_int
     lib.la_workspace_bytes.argtypes = [i] * 8 + [i]
     lib.la_workspace_bytes.restype = ctypes.c_size_t
@@ -158,16 +171,28 @@ def la_causal_fwd_state(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk: i
     return out
 
 
+def la_causal_fwd_ex(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk: int = 0,
+                     seg_len: int = 0, flags: int = 0):
+    """la_causal_fwd_state with variant flags (LA_PHI_IDENTITY, LA_UNNORMALIZED)."""
+    _check_tensors(q, k, v, out, S0, z0, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    st = lib.la_causal_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0), _ptr(S),
+                              _ptr(z), B, H, N, d, dv, chunk, seg_len, flags, _dtype_code(k),
+                              _stream(k))
+    _check(st, "la_causal_fwd_ex")
+    return out
+
+
 def la_causal_fwd_profiled(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk: int = 0,
-                           seg_len: int = 0, reps: int = 1):
-    """la_causal_fwd_state enqueued `reps` times back to back with HIP events around its
+                           seg_len: int = 0, flags: int = 0, reps: int = 1):
+    """la_causal_fwd_ex enqueued `reps` times back to back with HIP events around its
     kernels; waits for them and returns the average device milliseconds of (segment sums,
     segment scan, causal outputs)."""
     _check_tensors(q, k, v, out, S0, z0, S, z)
     B, H, N, d, dv = _dims(q, k, v)
     ms = (ctypes.c_float * 3)()
     st = lib.la_causal_fwd_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0),
-                                    _ptr(S), _ptr(z), B, H, N, d, dv, chunk, seg_len,
+                                    _ptr(S), _ptr(z), B, H, N, d, dv, chunk, seg_len, flags,
                                     _dtype_code(k), _stream(k), reps, ms)
     _check(st, "la_causal_fwd_profiled")
     return tuple(float(x) for x in ms)
@@ -183,6 +208,16 @@ def la_global_fwd(q, k, v, out, S, z, chunk: int = 0):
     return out
 
 
+def la_global_fwd_ex(q, k, v, out, S, z, chunk: int = 0, flags: int = 0):
+    """la_global_fwd with variant flags."""
+    _check_tensors(q, k, v, out, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    st = lib.la_global_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d,
+                              dv, chunk, flags, _dtype_code(k), _stream(k))
+    _check(st, "la_global_fwd_ex")
+    return out
+
+
 def la_decode_step(q, k, v, out, S, z):
     """One decode step; S, z are updated in place."""
     _check_tensors(q, k, v, out, S, z)
@@ -191,6 +226,31 @@ def la_decode_step(q, k, v, out, S, z):
                             0, _dtype_code(k), _stream(k))
     _check(st, "la_decode_step")
     return out
+
+
+def la_decode_step_ex(q, k, v, out, S, z, flags: int = 0):
+    """la_decode_step with variant flags."""
+    _check_tensors(q, k, v, out, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    st = lib.la_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d,
+                               dv, flags, _dtype_code(k), _stream(k))
+    _check(st, "la_decode_step_ex")
+    return out
+
+
+def la_rf_features(x, W, f):
+    """Positive random features f[..., r] = exp(W[r] . x - |x|^2 / 2) / sqrt(m) of the rows of
+    x [..., d] for projections W [m, d]; f [..., m] (all one dtype, contiguous, on the GPU)."""
+    _check_tensors(x, W, f)
+    m, d = W.shape
+    if x.shape[-1] != d or f.shape[-1] != m or x.shape[:-1] != f.shape[:-1]:
+        raise ValueError(f"shapes x {tuple(x.shape)}, W {tuple(W.shape)}, f {tuple(f.shape)} do not match")
+    if x.dtype != W.dtype or x.dtype != f.dtype:
+        raise ValueError("x, W and f must share one dtype")
+    rows = x.numel() // d if d else 0
+    st = lib.la_rf_features(_ptr(x), _ptr(W), _ptr(f), rows, d, m, _dtype_code(x), _stream(x))
+    _check(st, "la_rf_features")
+    return f
 
 
 def la_workspace_bytes(form: int, B: int, H: int, N: int, d: int, d_v: int, chunk: int = 0,

@@ -268,8 +268,9 @@ __device__ __forceinline__ void key_sum(f32x4 (&zacc)[ZT], const uint16_t *k)
 }
 
 // out rows [0, nvalid) of the chunk at `ob`: out = num / den, rounded to bf16.
-// The denominator of row i is sden[i] (+ sden2[i] when given).
-template <int D, int NCT>
+// The denominator of row i is sden[i] (+ sden2[i] when given); NORM = false stores num itself
+// (the unnormalised form) and reads no denominator.
+template <int D, int NCT, bool NORM = true>
 __device__ __forceinline__ void store_out(const f32x4 (&acc)[NCT][4], const float *sden,
                                           const float *sden2, uint16_t *__restrict__ ob, int nvalid,
                                           int cw0, int li, int g)
@@ -278,7 +279,7 @@ __device__ __forceinline__ void store_out(const f32x4 (&acc)[NCT][4], const floa
     for (int it = 0; it < 4; ++it) {
         const int i = 16 * it + li;
         if (i < nvalid) {
-            const float inv = __builtin_amdgcn_rcpf(sden2 ? sden[i] + sden2[i] : sden[i]);
+            const float inv = NORM ? __builtin_amdgcn_rcpf(sden2 ? sden[i] + sden2[i] : sden[i]) : 1.f;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const f32x4 a = acc[ct][it];
@@ -313,7 +314,7 @@ template <int D> struct AggCfg {
     static constexpr int THREADS = NW * 64;
 };
 
-template <int D>
+template <int D, bool PHI>
 __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__restrict__ k,
                                                            const uint16_t *__restrict__ v,
                                                            float *__restrict__ dstS,
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
     u32x4 rk[TL::TM], rv[TL::TM];
     tile.load(rk, kb + (size_t)tb * D, te - tb);
     tile.load(rv, vb + (size_t)tb * D, te - tb);
-    tile.store(sK[0], rk, te - tb, true);
+    tile.store(sK[0], rk, te - tb, PHI);
     tile.store(sV[0], rv, te - tb, false);
     {
         const int tn = chunk_t0(1);
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
         const int b = c & 1, nb = b ^ 1;
         if (c + 1 < nch) {
             const int n1 = min(C, te - (tb + (c + 1) * C));
-            tile.store(sK[nb], rk, n1, true);
+            tile.store(sK[nb], rk, n1, PHI);
             tile.store(sV[nb], rv, n1, false);
         }
         {
@@ -430,8 +431,10 @@ __device__ __forceinline__ void put_z(CausalLds<D> &sm, const f32x4 &z, int w, i
 }
 
 // Compute role (waves 0..NCW-1). Wave w owns value columns [16w, 16w+16) of S and the key-sum
-// features [16w, 16w+16). Barrier sequence: 1 in the prologue, 2 per chunk.
-template <int D>
+// features [16w, 16w+16). Barrier sequence: 1 in the prologue, 2 per chunk. NORM = false (the
+// unnormalised form) skips the denominator: no row sums of A and no phi(q) . z, while z is
+// still accumulated as part of the state.
+template <int D, bool NORM>
 __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArgs &a, int w,
                                                int li, int g)
 {
@@ -464,7 +467,7 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
     // phase-1 jobs: waves 0-3 compute the scores of query rows 16w..16w+15; the waves that
     // compute phi(q) . z for rows 16(w%4).. are waves 4-7 (D = 128) or the same waves (D = 64)
     const bool scores = w < 4;
-    const bool qz = NCW == 8 ? w >= 4 : true;
+    const bool qz = NORM && (NCW == 8 ? w >= 4 : true);
     const int iw = w & 3;
     for (int c = 0; c < a.nch; ++c) {
         const int b = c & 1;
@@ -498,14 +501,17 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
                     }
                     pk[2 * h] = pack_bf2(t[0], t[1]);
                     pk[2 * h + 1] = pack_bf2(t[2], t[3]);
-                    rs += (bf_lo(pk[2 * h]) + bf_hi(pk[2 * h])) + (bf_lo(pk[2 * h + 1]) + bf_hi(pk[2 * h + 1]));
+                    if (NORM)
+                        rs += (bf_lo(pk[2 * h]) + bf_hi(pk[2 * h])) + (bf_lo(pk[2 * h + 1]) + bf_hi(pk[2 * h + 1]));
                 }
                 sts<u32x4>(sm.sA + sa_ix(16 * w + li, mp, g), u32x4{pk[0], pk[1], pk[2], pk[3]});
             }
-            rs += __shfl_xor(rs, 16, 64);
-            rs += __shfl_xor(rs, 32, 64);
-            if (g == 0)
-                sm.srs[16 * w + li] = rs;
+            if (NORM) {
+                rs += __shfl_xor(rs, 16, 64);
+                rs += __shfl_xor(rs, 32, 64);
+                if (g == 0)
+                    sm.srs[16 * w + li] = rs;
+            }
         }
         if (qz) {
             // phi(Q) z for query rows 16iw..: one matrix-core product per 32 features with
@@ -536,10 +542,11 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
                 }
             }
             state_read<D, 1>(acc, sacc, sQ + sql);
-            store_out<D, 1>(acc, sm.srs, sm.sqz, a.oh + (size_t)t0 * D, nvalid, cw0, li, g);
+            store_out<D, 1, NORM>(acc, sm.srs, sm.sqz, a.oh + (size_t)t0 * D, nvalid, cw0, li, g);
             state_update<D, 1>(sacc, sK + trl, sm.sV + cw0 + trl);
             key_sum<D, 1>(zacc, sK + 16 * w + trl);
-            put_z<D>(sm, zacc[0], w, li, g);
+            if (NORM)
+                put_z<D>(sm, zacc[0], w, li, g);
         }
         __syncthreads();
     }
@@ -558,8 +565,8 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
 }
 
 // Stage role (the NSW waves after the compute waves, thread index ht). Same barrier sequence
-// as the compute role.
-template <int D>
+// as the compute role. PHI = false stages q and k as given (already mapped features).
+template <int D, bool PHI>
 __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs &a, int ht)
 {
     using TL = Tile<D, CausalCfg<D>::STAGE_THREADS>;
@@ -573,8 +580,8 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
     tile.load(rq, a.qh + (size_t)tb * D, te - tb);
     tile.load(rk, a.kh + (size_t)tb * D, te - tb);
     tile.load(rv, a.vh + (size_t)tb * D, te - tb);
-    tile.store(sm.sQ[0], rq, te - tb, true);
-    tile.store(sm.sK[0], rk, te - tb, true);
+    tile.store(sm.sQ[0], rq, te - tb, PHI);
+    tile.store(sm.sK[0], rk, te - tb, PHI);
     {
         const int tn = chunk_t0(1);
         tile.load(rq, a.qh + (size_t)tn * D, te - tn);
@@ -594,7 +601,7 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
             tile.load(rv, a.vh + (size_t)tn * D, te - tn);
         }
         if (c + 1 < nch)
-            tile.store(sm.sQ[nb], rq, n1, true);
+            tile.store(sm.sQ[nb], rq, n1, PHI);
         {
             const int tn = chunk_t0(c + 2);
             tile.load(rq, a.qh + (size_t)tn * D, te - tn);
@@ -602,7 +609,7 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
         __syncthreads();
         // phase 2: phi(K_{c+1}) -> LDS, load K_{c+2}
         if (c + 1 < nch)
-            tile.store(sm.sK[nb], rk, n1, true);
+            tile.store(sm.sK[nb], rk, n1, PHI);
         {
             const int tn = chunk_t0(c + 2);
             tile.load(rk, a.kh + (size_t)tn * D, te - tn);
@@ -626,8 +633,8 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
 //            stage:   phi(K_{c+1}) -> LDS, load K_{c+2}
 //   --- barrier ---
 // Roles are chosen by the wave-uniform wave index, so every wave executes the same sequence of
-// barriers.
-template <int D>
+// barriers. F: variant flags (F_IDENTITY: q, k are already features; F_UNNORM: no denominator).
+template <int D, int F>
 __global__ __launch_bounds__(CausalCfg<D>::THREADS) void k_causal(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ out, const float *__restrict__ preS, const float *__restrict__ prez,
@@ -653,14 +660,15 @@ __global__ __launch_bounds__(CausalCfg<D>::THREADS) void k_causal(
     a.te = min(N, a.tb + L);
     a.nch = (a.te - a.tb + C - 1) / C;
     if (wave < NCW)
-        causal_compute<D>(sm, a, wave, l & 15, l >> 4);
+        causal_compute<D, !(F & F_UNNORM)>(sm, a, wave, l & 15, l >> 4);
     else
-        causal_stage<D>(sm, a, tid - NCW * 64);
+        causal_stage<D, !(F & F_IDENTITY)>(sm, a, tid - NCW * 64);
 }
 
 // ------------------------------------------------------------------------------------------
-// Global read: out = phi(Q) S / phi(Q) z for one segment of tokens of one head.
-template <int D>
+// Global read: out = phi(Q) S / phi(Q) z for one segment of tokens of one head (F as for
+// k_causal).
+template <int D, int F>
 __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
                                               uint16_t *__restrict__ out,
                                               const float *__restrict__ S,
@@ -705,13 +713,13 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
     const int tlast = tb + ((te - tb - 1) / C) * C;
     for (int t0 = tb; t0 < te; t0 += C) {
         const int nvalid = min(C, te - t0);
-        tile.store(sQ, rq, nvalid, true);
+        tile.store(sQ, rq, nvalid, !(F & F_IDENTITY));
         __syncthreads();
         {
             const int tn = min(t0 + C, tlast);
             tile.load(rq, q + hoff + (size_t)tn * D, te - tn);
         }
-        {
+        if (!(F & F_UNNORM)) {
             // den[i] = Qf[i] . z: 4 threads per row, D/4 features each
             const int i = tid >> 2, qq = tid & 3;
             float s = 0.f;
@@ -748,30 +756,76 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
                     acc[ct][it] = mfma(sf[ct][m], bq, acc[ct][it]);
             }
         }
-        store_out<D, K::NCT>(acc, sden, nullptr, out + hoff + (size_t)t0 * D, nvalid, cw0, li, g);
+        store_out<D, K::NCT, !(F & F_UNNORM)>(acc, sden, nullptr, out + hoff + (size_t)t0 * D, nvalid,
+                                              cw0, li, g);
         __syncthreads();
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// Host dispatch over the compile-time variants. Every kernel is instantiated for D in {64, 128}
+// and each variant flag it uses.
+template <int D, int F> void launch_causal(dim3 grid, hipStream_t st, const uint16_t *q,
+                                           const uint16_t *k, const uint16_t *v, uint16_t *o,
+                                           const float *preS, const float *prez, long ps, long pzs,
+                                           float *Sout, float *zout, int N, int L, int P)
+{
+    hipLaunchKernelGGL((k_causal<D, F>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q, k, v, o, preS,
+                       prez, ps, pzs, Sout, zout, N, L, P);
+}
+
+template <int D> void launch_causal_f(int flags, dim3 grid, hipStream_t st, const uint16_t *q,
+                                      const uint16_t *k, const uint16_t *v, uint16_t *o,
+                                      const float *preS, const float *prez, long ps, long pzs,
+                                      float *Sout, float *zout, int N, int L, int P)
+{
+    switch (flags & (F_IDENTITY | F_UNNORM)) {
+    case 0: launch_causal<D, 0>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
+    case 1: launch_causal<D, 1>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
+    case 2: launch_causal<D, 2>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
+    default: launch_causal<D, 3>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
+    }
+}
+
+template <int D> void launch_gread_f(int flags, dim3 grid, hipStream_t st, const uint16_t *q,
+                                     uint16_t *o, const float *S, const float *z, int N, int L, int P)
+{
+    switch (flags & (F_IDENTITY | F_UNNORM)) {
+    case 0: hipLaunchKernelGGL((k_gread<D, 0>), grid, dim3(NT), 0, st, q, o, S, z, N, L, P); break;
+    case 1: hipLaunchKernelGGL((k_gread<D, 1>), grid, dim3(NT), 0, st, q, o, S, z, N, L, P); break;
+    case 2: hipLaunchKernelGGL((k_gread<D, 2>), grid, dim3(NT), 0, st, q, o, S, z, N, L, P); break;
+    default: hipLaunchKernelGGL((k_gread<D, 3>), grid, dim3(NT), 0, st, q, o, S, z, N, L, P); break;
+    }
+}
+
+template <int D> void launch_agg_f(int flags, dim3 grid, hipStream_t st, const uint16_t *k,
+                                   const uint16_t *v, float *dstS, float *dstz, long ss, long zs,
+                                   int N, int L, int nseg, int P)
+{
+    if (flags & F_IDENTITY)
+        hipLaunchKernelGGL((k_agg<D, false>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v, dstS,
+                           dstz, ss, zs, N, L, nseg, P);
+    else
+        hipLaunchKernelGGL((k_agg<D, true>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v, dstS,
+                           dstz, ss, zs, N, L, nseg, P);
+}
+
 } // namespace
 
-// ------------------------------------------------------------------------------------------
-hipError_t agg_mfma(int D, const void *k, const void *v, float *dstS, float *dstz, long sstride,
-                    long zstride, int BH, int N, int L, int nseg, int P, hipStream_t st)
+hipError_t agg_mfma(int D, int flags, const void *k, const void *v, float *dstS, float *dstz,
+                    long sstride, long zstride, int BH, int N, int L, int nseg, int P, hipStream_t st)
 {
     const dim3 grid((unsigned)(BH * nseg));
     const auto *kk = static_cast<const uint16_t *>(k);
     const auto *vv = static_cast<const uint16_t *>(v);
     if (D == 128)
-        hipLaunchKernelGGL(k_agg<128>, grid, dim3(AggCfg<128>::THREADS), 0, st, kk, vv, dstS, dstz, sstride, zstride, N,
-                           L, nseg, P);
+        launch_agg_f<128>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
     else
-        hipLaunchKernelGGL(k_agg<64>, grid, dim3(AggCfg<64>::THREADS), 0, st, kk, vv, dstS, dstz, sstride, zstride, N,
-                           L, nseg, P);
+        launch_agg_f<64>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
     return hipGetLastError();
 }
 
-hipError_t causal_mfma(int D, const void *q, const void *k, const void *v, void *out,
+hipError_t causal_mfma(int D, int flags, const void *q, const void *k, const void *v, void *out,
                        const float *preS, const float *prez, long pstride, long pzstride,
                        float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st)
 {
@@ -781,24 +835,24 @@ hipError_t causal_mfma(int D, const void *q, const void *k, const void *v, void 
     const auto *vv = static_cast<const uint16_t *>(v);
     auto *oo = static_cast<uint16_t *>(out);
     if (D == 128)
-        hipLaunchKernelGGL(k_causal<128>, grid, dim3(CausalCfg<128>::THREADS), 0, st, qq, kk, vv, oo, preS, prez, pstride,
-                           pzstride, Sout, zout, N, L, P);
+        launch_causal_f<128>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout,
+                             zout, N, L, P);
     else
-        hipLaunchKernelGGL(k_causal<64>, grid, dim3(CausalCfg<64>::THREADS), 0, st, qq, kk, vv, oo, preS, prez, pstride,
-                           pzstride, Sout, zout, N, L, P);
+        launch_causal_f<64>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout,
+                            zout, N, L, P);
     return hipGetLastError();
 }
 
-hipError_t global_read_mfma(int D, const void *q, void *out, const float *S, const float *z,
-                            int BH, int N, int L, int P, hipStream_t st)
+hipError_t global_read_mfma(int D, int flags, const void *q, void *out, const float *S,
+                            const float *z, int BH, int N, int L, int P, hipStream_t st)
 {
-    const dim3 grid((unsigned)(BH * P)), block(NT);
+    const dim3 grid((unsigned)(BH * P));
     const auto *qq = static_cast<const uint16_t *>(q);
     auto *oo = static_cast<uint16_t *>(out);
     if (D == 128)
-        hipLaunchKernelGGL(k_gread<128>, grid, block, 0, st, qq, oo, S, z, N, L, P);
+        launch_gread_f<128>(flags, grid, st, qq, oo, S, z, N, L, P);
     else
-        hipLaunchKernelGGL(k_gread<64>, grid, block, 0, st, qq, oo, S, z, N, L, P);
+        launch_gread_f<64>(flags, grid, st, qq, oo, S, z, N, L, P);
     return hipGetLastError();
 }
 

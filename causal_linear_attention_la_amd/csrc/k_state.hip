@@ -11,8 +11,9 @@
 //
 // Decode step ("Linear Attention Math", section "The recurrent form"): for each head,
 // S' = S + phi(k) v^T and z' = z + phi(k) are written back in place, then
-// out = phi(q)^T S' / phi(q)^T z'. One workgroup per head streams the float32 state once in
-// and once out with 16-byte accesses; the read phi(q)^T S' reuses the updated values while
+// out = phi(q)^T S' / phi(q)^T z' (F_IDENTITY: q, k are the features; F_UNNORM: no
+// division). One workgroup per head streams the float32 state once in and once out with
+// 16-byte accesses; the read phi(q)^T S' reuses the updated values while
 // they are in registers, so each state byte crosses HBM exactly twice. The state accesses are
 // non-temporal: the state is touched once per step, and on gfx950 an in-place stream with
 // non-temporal loads and stores sustains about 8 % more bandwidth than with cached ones.
@@ -89,8 +90,10 @@ __global__ __launch_bounds__(NT) void k_seg_total(const float *__restrict__ ws, 
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T *__restrict__ k,
                                                const T *__restrict__ v, T *__restrict__ out,
-                                               float *__restrict__ S, float *__restrict__ z)
+                                               float *__restrict__ S, float *__restrict__ z,
+                                               int flags)
 {
+    const bool ident = flags & F_IDENTITY;
     constexpr int CG = DV / 4, RP = NT / CG, RPT = (D + RP - 1) / RP;
     __shared__ float skf[D], sqf[D];
     __shared__ float red[RP][DV + 4];
@@ -111,8 +114,8 @@ __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T 
 
     float part = 0.f;
     if (tid < D) {
-        const float kf = phi_exact(Elem<T>::ld(k, bh * D + tid));
-        const float qf = phi_exact(Elem<T>::ld(q, bh * D + tid));
+        const float kf = feature(Elem<T>::ld(k, bh * D + tid), ident);
+        const float qf = feature(Elem<T>::ld(q, bh * D + tid), ident);
         skf[tid] = kf;
         sqf[tid] = qf;
         const float zn = z[bh * D + tid] + kf;
@@ -156,13 +159,13 @@ __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T 
 #pragma unroll
         for (int w = 0; w < NT / 64; ++w)
             den += sden[w];
-        Elem<T>::st(out, bh * DV + tid, num / den);
+        Elem<T>::st(out, bh * DV + tid, (flags & F_UNNORM) ? num : num / den);
     }
 }
 
 template <typename T>
-hipError_t decode_t(const void *q, const void *k, const void *v, void *out, float *S, float *z,
-                    int BH, int d, int dv, hipStream_t st)
+hipError_t decode_t(int flags, const void *q, const void *k, const void *v, void *out, float *S,
+                    float *z, int BH, int d, int dv, hipStream_t st)
 {
     const dim3 grid((unsigned)BH), block(NT);
     const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
@@ -170,7 +173,7 @@ hipError_t decode_t(const void *q, const void *k, const void *v, void *out, floa
     T *oo = static_cast<T *>(out);
 #define LA_DEC(DD, VV)                                                                          \
     if (d == DD && dv == VV) {                                                                  \
-        hipLaunchKernelGGL((k_decode<T, DD, VV>), grid, block, 0, st, qq, kk, vv, oo, S, z);    \
+        hipLaunchKernelGGL((k_decode<T, DD, VV>), grid, block, 0, st, qq, kk, vv, oo, S, z, flags); \
         return hipGetLastError();                                                               \
     }
 #define LA_DEC_ROW(DD) LA_DEC(DD, 16) LA_DEC(DD, 32) LA_DEC(DD, 64) LA_DEC(DD, 128)
@@ -203,11 +206,11 @@ hipError_t seg_total(const float *ws, float *S, float *z, int BH, int P, int d, 
     return hipGetLastError();
 }
 
-hipError_t decode_step(bool bf16, const void *q, const void *k, const void *v, void *out,
-                       float *S, float *z, int BH, int d, int dv, hipStream_t st)
+hipError_t decode_step(bool bf16, int flags, const void *q, const void *k, const void *v,
+                       void *out, float *S, float *z, int BH, int d, int dv, hipStream_t st)
 {
-    return bf16 ? decode_t<bf16_t>(q, k, v, out, S, z, BH, d, dv, st)
-                : decode_t<float>(q, k, v, out, S, z, BH, d, dv, st);
+    return bf16 ? decode_t<bf16_t>(flags, q, k, v, out, S, z, BH, d, dv, st)
+                : decode_t<float>(flags, q, k, v, out, S, z, BH, d, dv, st);
 }
 
 } // namespace la

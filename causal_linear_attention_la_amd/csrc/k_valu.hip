@@ -10,6 +10,8 @@
 // -- the recurrence of "Linear Attention Math", section "The recurrent form: a running KV
 // state", grouped by chunk. With causal = false the kernel is the global read
 // out_i = Qf_i^T S / Qf_i . z of section "The associativity trick, written out".
+// Flags: F_IDENTITY takes q and k as the features themselves; F_UNNORM stores num_i (no
+// division).
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -40,8 +42,9 @@ __global__ __launch_bounds__(NT) void k_agg_valu(const T *__restrict__ k, const 
                                                  float *__restrict__ dstS,
                                                  float *__restrict__ dstz, long sstride,
                                                  long zstride, int N, int d, int dv, int ch,
-                                                 int L, int nseg, int P)
+                                                 int L, int nseg, int P, int flags)
 {
+    const bool ident = flags & F_IDENTITY;
     extern __shared__ float sm[];
     const Lay lay(d, dv, ch);
     float *sS = sm + lay.oS, *sz = sm + lay.oz, *sK = sm + lay.oK, *sV = sm + lay.oV;
@@ -60,7 +63,7 @@ __global__ __launch_bounds__(NT) void k_agg_valu(const T *__restrict__ k, const 
         __syncthreads();
         for (int e = tid; e < ch * d; e += NT) {
             const int j = e / d;
-            sK[e] = j < nvalid ? phi_exact(Elem<T>::ld(kb, (size_t)(t0 + j) * d + e % d)) : 0.f;
+            sK[e] = j < nvalid ? feature(Elem<T>::ld(kb, (size_t)(t0 + j) * d + e % d), ident) : 0.f;
         }
         for (int e = tid; e < ch * dv; e += NT) {
             const int j = e / dv;
@@ -97,9 +100,10 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
                                                  long pzstride, int pslots,
                                                  float *__restrict__ Sout,
                                                  float *__restrict__ zout, int N, int d, int dv,
-                                                 int ch, int L, int P)
+                                                 int ch, int L, int P, int flags)
 {
     extern __shared__ float sm[];
+    const bool ident = flags & F_IDENTITY, norm = !(flags & F_UNNORM);
     const Lay lay(d, dv, ch);
     float *sS = sm + lay.oS, *sz = sm + lay.oz, *sQ = sm + lay.oQ, *sK = sm + lay.oK;
     float *sV = sm + lay.oV, *sA = sm + lay.oA, *sden = sm + lay.oden;
@@ -125,9 +129,9 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
         for (int e = tid; e < ch * d; e += NT) {
             const int j = e / d;
             const size_t gi = (size_t)(t0 + j) * d + e % d;
-            sQ[e] = j < nvalid ? phi_exact(Elem<T>::ld(qb, gi)) : 0.f;
+            sQ[e] = j < nvalid ? feature(Elem<T>::ld(qb, gi), ident) : 0.f;
             if (CAUSAL)
-                sK[e] = j < nvalid ? phi_exact(Elem<T>::ld(kb, gi)) : 0.f;
+                sK[e] = j < nvalid ? feature(Elem<T>::ld(kb, gi), ident) : 0.f;
         }
         if (CAUSAL)
             for (int e = tid; e < ch * dv; e += NT) {
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
             if (CAUSAL)
                 for (int j = 0; j <= i; ++j)
                     s += sA[i * ch + j] * sV[j * dv + c];
-            Elem<T>::st(ob, (size_t)(t0 + i) * dv + c, s / sden[i]);
+            Elem<T>::st(ob, (size_t)(t0 + i) * dv + c, norm ? s / sden[i] : s);
         }
         if (CAUSAL) {
             __syncthreads();
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
 
 } // namespace
 
-hipError_t agg_valu(bool bf16, const void *k, const void *v, float *dstS, float *dstz,
+hipError_t agg_valu(bool bf16, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int d, int dv, int chunk, int L,
                     int nseg, int P, hipStream_t st)
 {
@@ -211,16 +215,16 @@ hipError_t agg_valu(bool bf16, const void *k, const void *v, float *dstS, float 
     if (bf16)
         hipLaunchKernelGGL(k_agg_valu<bf16_t>, grid, block, lds, st, static_cast<const bf16_t *>(k),
                            static_cast<const bf16_t *>(v), dstS, dstz, sstride, zstride, N, d, dv,
-                           chunk, L, nseg, P);
+                           chunk, L, nseg, P, flags);
     else
         hipLaunchKernelGGL(k_agg_valu<float>, grid, block, lds, st, static_cast<const float *>(k),
                            static_cast<const float *>(v), dstS, dstz, sstride, zstride, N, d, dv,
-                           chunk, L, nseg, P);
+                           chunk, L, nseg, P, flags);
     return hipGetLastError();
 }
 
 template <typename T, bool CAUSAL>
-hipError_t out_valu_t(const void *q, const void *k, const void *v, void *out, const float *preS,
+hipError_t out_valu_t(int flags, const void *q, const void *k, const void *v, void *out, const float *preS,
                       const float *prez, long pstride, long pzstride, int pslots, float *Sout,
                       float *zout, int BH, int N, int d, int dv, int chunk, int L, int P,
                       hipStream_t st)
@@ -233,18 +237,18 @@ hipError_t out_valu_t(const void *q, const void *k, const void *v, void *out, co
     hipLaunchKernelGGL((k_out_valu<T, CAUSAL>), dim3((unsigned)(BH * P)), dim3(NT), lds, st,
                        static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), static_cast<T *>(out), preS, prez, pstride,
-                       pzstride, pslots, Sout, zout, N, d, dv, chunk, L, P);
+                       pzstride, pslots, Sout, zout, N, d, dv, chunk, L, P, flags);
     return hipGetLastError();
 }
 
-hipError_t out_valu(bool bf16, bool causal, const void *q, const void *k, const void *v,
+hipError_t out_valu(bool bf16, bool causal, int flags, const void *q, const void *k, const void *v,
                     void *out, const float *preS, const float *prez, long pstride,
                     long pzstride, int pslots, float *Sout, float *zout, int BH, int N, int d,
                     int dv, int chunk, int L, int P, hipStream_t st)
 {
     auto f = bf16 ? (causal ? out_valu_t<bf16_t, true> : out_valu_t<bf16_t, false>)
                   : (causal ? out_valu_t<float, true> : out_valu_t<float, false>);
-    return f(q, k, v, out, preS, prez, pstride, pzstride, pslots, Sout, zout, BH, N, d, dv, chunk,
+    return f(flags, q, k, v, out, preS, prez, pstride, pzstride, pslots, Sout, zout, BH, N, d, dv, chunk,
              L, P, st);
 }
 

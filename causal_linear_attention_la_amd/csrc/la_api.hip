@@ -21,6 +21,8 @@ constexpr long kCUs = 256;
 
 bool dim_ok(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
 
+constexpr int kRfMaxFeatures = 4096; // projections per random-feature map
+
 struct Span {
     uintptr_t lo, hi; // [lo, hi); empty when lo == hi
 };
@@ -238,8 +240,10 @@ hipError_t mark(Stamps *ts, int i, hipStream_t st)
     return ts ? hipEventRecord(ts->ev[i], st) : hipSuccess;
 }
 
+bool flags_ok(int flags) { return (flags & ~(LA_PHI_IDENTITY | LA_UNNORMALIZED)) == 0; }
+
 int run_causal(const void *q, const void *k, const void *v, void *out, const float *S0,
-               const float *z0, float *S, float *z, int N, int d, int dv, bool bf16,
+               const float *z0, float *S, float *z, int N, int d, int dv, bool bf16, int flags,
                const Plan &pl, hipStream_t st, Stamps *ts = nullptr)
 {
     const int BH = (int)pl.BH, P = pl.P, L = pl.L;
@@ -252,9 +256,10 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
     long ps = (long)d * dv, pzs = d;
     if (P > 1 && e == hipSuccess) {
         // sums of segments 0..P-2, then the exclusive prefix over segments in place
-        e = pl.mfma ? la::agg_mfma(d, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L, P - 1, P, st)
-                    : la::agg_valu(bf16, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, d, dv,
-                                   pl.chunk, L, P - 1, P, st);
+        e = pl.mfma ? la::agg_mfma(d, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L,
+                                   P - 1, P, st)
+                    : la::agg_valu(bf16, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N,
+                                   d, dv, pl.chunk, L, P - 1, P, st);
         if (e == hipSuccess)
             e = mark(ts, 1, st);
         if (e == hipSuccess)
@@ -268,16 +273,17 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
     if (e == hipSuccess)
         e = mark(ts, 2, st);
     if (e == hipSuccess)
-        e = pl.mfma ? la::causal_mfma(d, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N, L, P, st)
-                    : la::out_valu(bf16, true, q, k, v, out, preS, prez, ps, pzs, P > 1 ? P : 1, S,
-                                   z, BH, N, d, dv, pl.chunk, L, P, st);
+        e = pl.mfma ? la::causal_mfma(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N, L,
+                                      P, st)
+                    : la::out_valu(bf16, true, flags, q, k, v, out, preS, prez, ps, pzs,
+                                   P > 1 ? P : 1, S, z, BH, N, d, dv, pl.chunk, L, P, st);
     if (e == hipSuccess)
         e = mark(ts, 3, st);
     return e == hipSuccess ? LA_OK : LA_EHIP;
 }
 
 int run_global(const void *q, const void *k, const void *v, void *out, float *S, float *z, int N,
-               int d, int dv, bool bf16, const Plan &pl, hipStream_t st)
+               int d, int dv, bool bf16, int flags, const Plan &pl, hipStream_t st)
 {
     const int BH = (int)pl.BH, P = pl.P, L = pl.L;
     const long E = (long)d * dv + d;
@@ -286,20 +292,21 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
         return LA_EHIP;
     hipError_t e;
     if (P > 1) {
-        e = pl.mfma ? la::agg_mfma(d, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L, P, P, st)
-                    : la::agg_valu(bf16, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, d, dv,
-                                   pl.chunk, L, P, P, st);
+        e = pl.mfma ? la::agg_mfma(d, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L,
+                                   P, P, st)
+                    : la::agg_valu(bf16, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N,
+                                   d, dv, pl.chunk, L, P, P, st);
         if (e == hipSuccess)
             e = la::seg_total(ws.ptr, S, z, BH, P, d, dv, st);
     } else {
-        e = pl.mfma ? la::agg_mfma(d, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1, st)
-                    : la::agg_valu(bf16, k, v, S, z, (long)d * dv, d, BH, N, d, dv, pl.chunk, L, 1,
-                                   1, st);
+        e = pl.mfma ? la::agg_mfma(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1, st)
+                    : la::agg_valu(bf16, flags, k, v, S, z, (long)d * dv, d, BH, N, d, dv,
+                                   pl.chunk, L, 1, 1, st);
     }
     if (e == hipSuccess && q)
-        e = pl.mfma ? la::global_read_mfma(d, q, out, S, z, BH, N, L, P, st)
-                    : la::out_valu(bf16, false, q, nullptr, nullptr, out, S, z, (long)d * dv, d, 1,
-                                   nullptr, nullptr, BH, N, d, dv, pl.chunk, L, P, st);
+        e = pl.mfma ? la::global_read_mfma(d, flags, q, out, S, z, BH, N, L, P, st)
+                    : la::out_valu(bf16, false, flags, q, nullptr, nullptr, out, S, z, (long)d * dv,
+                                   d, 1, nullptr, nullptr, BH, N, d, dv, pl.chunk, L, P, st);
     return e == hipSuccess ? LA_OK : LA_EHIP;
 }
 
@@ -307,18 +314,27 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
 
 extern "C" {
 
-int la_causal_fwd_state(const void *q, const void *k, const void *v, void *out, const float *S0,
-                        const float *z0, float *S, float *z, int B, int H, int N, int d, int d_v,
-                        int chunk, int seg_len, la_dtype dtype, hipStream_t stream)
+int la_causal_fwd_ex(const void *q, const void *k, const void *v, void *out, const float *S0,
+                     const float *z0, float *S, float *z, int B, int H, int N, int d, int d_v,
+                     int chunk, int seg_len, int flags, la_dtype dtype, hipStream_t stream)
 {
+    if (!flags_ok(flags))
+        return LA_EINVAL;
     Plan pl;
     const int s = validate(CAUSAL, q, k, v, out, S0, z0, S, z, B, H, N, d, d_v, chunk, seg_len,
                            dtype, &pl);
     if (s != LA_OK)
         return s;
-    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, pl, stream);
+    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, pl, stream);
 }
 
+int la_causal_fwd_state(const void *q, const void *k, const void *v, void *out, const float *S0,
+                        const float *z0, float *S, float *z, int B, int H, int N, int d, int d_v,
+                        int chunk, int seg_len, la_dtype dtype, hipStream_t stream)
+{
+    return la_causal_fwd_ex(q, k, v, out, S0, z0, S, z, B, H, N, d, d_v, chunk, seg_len, 0, dtype,
+                            stream);
+}
 int la_causal_fwd_seg(const void *q, const void *k, const void *v, void *out, float *S, float *z,
                       int B, int H, int N, int d, int d_v, int chunk, int seg_len, la_dtype dtype,
                       hipStream_t stream)
@@ -329,10 +345,10 @@ int la_causal_fwd_seg(const void *q, const void *k, const void *v, void *out, fl
 
 int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *out,
                            const float *S0, const float *z0, float *S, float *z, int B, int H,
-                           int N, int d, int d_v, int chunk, int seg_len, la_dtype dtype,
+                           int N, int d, int d_v, int chunk, int seg_len, int flags, la_dtype dtype,
                            hipStream_t stream, int reps, float *ms)
 {
-    if (!ms || reps < 1 || reps > 4096)
+    if (!ms || reps < 1 || reps > 4096 || !flags_ok(flags))
         return LA_EINVAL;
     Plan pl;
     const int s = validate(CAUSAL, q, k, v, out, S0, z0, S, z, B, H, N, d, d_v, chunk, seg_len,
@@ -344,8 +360,8 @@ int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *ou
         if (t.init() != hipSuccess)
             return LA_EHIP;
     for (Stamps &t : ts) {
-        const int r = run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, pl,
-                                 stream, &t);
+        const int r = run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags,
+                                 pl, stream, &t);
         if (r != LA_OK)
             return r;
     }
@@ -370,15 +386,40 @@ int la_causal_fwd(const void *q, const void *k, const void *v, void *out, float 
     return la_causal_fwd_seg(q, k, v, out, S, z, B, H, N, d, d_v, chunk, 0, dtype, stream);
 }
 
-int la_global_fwd(const void *q, const void *k, const void *v, void *out, float *S, float *z,
-                  int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype, hipStream_t stream)
+int la_global_fwd_ex(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                     int B, int H, int N, int d, int d_v, int chunk, int flags, la_dtype dtype,
+                     hipStream_t stream)
 {
+    if (!flags_ok(flags))
+        return LA_EINVAL;
     Plan pl;
     const int s = validate(GLOBAL, q, k, v, out, nullptr, nullptr, S, z, B, H, N, d, d_v, chunk, 0,
                            dtype, &pl);
     if (s != LA_OK)
         return s;
-    return run_global(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, pl, stream);
+    return run_global(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, flags, pl, stream);
+}
+
+int la_global_fwd(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                  int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype, hipStream_t stream)
+{
+    return la_global_fwd_ex(q, k, v, out, S, z, B, H, N, d, d_v, chunk, 0, dtype, stream);
+}
+
+int la_decode_step_ex(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                      int B, int H, int N, int d, int d_v, int flags, la_dtype dtype,
+                      hipStream_t stream)
+{
+    if (!flags_ok(flags))
+        return LA_EINVAL;
+    Plan pl;
+    const int s = validate(DECODE, q, k, v, out, nullptr, nullptr, S, z, B, H, N, d, d_v, 0, 0,
+                           dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    const hipError_t e = la::decode_step(dtype == LA_BF16, flags, q, k, v, out, S, z, (int)pl.BH,
+                                         d, d_v, stream);
+    return e == hipSuccess ? LA_OK : LA_EHIP;
 }
 
 int la_decode_step(const void *q, const void *k, const void *v, void *out, float *S, float *z,
@@ -386,12 +427,25 @@ int la_decode_step(const void *q, const void *k, const void *v, void *out, float
                    hipStream_t stream)
 {
     (void)chunk;
-    Plan pl;
-    const int s = validate(DECODE, q, k, v, out, nullptr, nullptr, S, z, B, H, N, d, d_v, 0, 0,
-                           dtype, &pl);
-    if (s != LA_OK)
-        return s;
-    const hipError_t e = la::decode_step(dtype == LA_BF16, q, k, v, out, S, z, (int)pl.BH, d, d_v, stream);
+    return la_decode_step_ex(q, k, v, out, S, z, B, H, N, d, d_v, 0, dtype, stream);
+}
+
+int la_rf_features(const void *x, const void *W, void *f, long rows, int d, int m,
+                   la_dtype dtype, hipStream_t stream)
+{
+    if (!x || !W || !f || !aligned16(x) || !aligned16(W) || !aligned16(f))
+        return LA_EINVAL;
+    if (dtype != LA_F32 && dtype != LA_BF16)
+        return LA_EINVAL;
+    if (rows <= 0 || d <= 0 || m <= 0)
+        return LA_EINVAL;
+    if (d > la::rf_max_d() || m > kRfMaxFeatures || rows > (long)INT32_MAX)
+        return LA_ENOTSUP;
+    const size_t es = dtype == LA_BF16 ? 2 : 4;
+    const Span sf = span(f, (size_t)rows * m * es);
+    if (overlap(sf, span(x, (size_t)rows * d * es)) || overlap(sf, span(W, (size_t)m * d * es)))
+        return LA_EINVAL;
+    const hipError_t e = la::rf_features(dtype == LA_BF16, x, W, f, rows, d, m, stream);
     return e == hipSuccess ? LA_OK : LA_EHIP;
 }
 
@@ -413,10 +467,10 @@ const char *la_strerror(int status)
         return "success";
     case LA_EINVAL:
         return "invalid argument (null, misaligned or overlapping buffer, non-positive size, "
-               "decode with N != 1, or unknown dtype)";
+               "decode with N != 1, unknown dtype or unknown flag bits)";
     case LA_ENOTSUP:
         return "unsupported shape or chunk (d and d_v must be 16, 32, 64 or 128; chunk 0, 16, "
-               "32 or 64 as the shape allows)";
+               "32 or 64 as the shape allows; random features: d <= 256, m <= 4096)";
     case LA_EHIP:
         return "HIP runtime error (allocation or kernel launch failed)";
     default:

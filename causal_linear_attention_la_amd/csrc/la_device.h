@@ -42,6 +42,8 @@ __device__ __forceinline__ uint16_t to_bf(float x)
 // the accurate form is used where the arithmetic stays in float32.
 __device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 __device__ __forceinline__ float phi_exact(float x) { return x > 0.f ? x + 1.f : expf(x); }
+// The feature of one element: phi_exact(x), or x itself when q and k are already features.
+__device__ __forceinline__ float feature(float x, bool identity) { return identity ? x : phi_exact(x); }
 
 // ---- generic element access for the vector-ALU kernels -----------------------------------
 template <typename T> struct Elem;

@@ -11,30 +11,34 @@
 
 namespace la {
 
+// Variant flags (the same bits as the ABI's LA_PHI_IDENTITY and LA_UNNORMALIZED).
+constexpr int F_IDENTITY = 1; // q and k are taken as already-mapped features (phi = identity)
+constexpr int F_UNNORM = 2;   // out = phi(q)^T S, no division by phi(q)^T z
+
 // ---- matrix-core family: bf16, d == d_v in {64, 128}, chunk 64 ---------------------------
 // Segment sums dS = phi(K_seg)^T V_seg, dz = phi(K_seg)^T 1 of segments p < nseg of every
 // head, written to dstS + (bh * P + p) * sstride and dstz + (bh * P + p) * zstride.
-hipError_t agg_mfma(int D, const void *k, const void *v, float *dstS, float *dstz,
+hipError_t agg_mfma(int D, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int L, int nseg, int P,
                     hipStream_t st);
 // Causal outputs of all P segments. Segment p starts from the state at preS/prez +
 // (bh * P + p) * stride (zero state if preS is null). The last segment writes the final
 // state to Sout/zout when they are non-null.
-hipError_t causal_mfma(int D, const void *q, const void *k, const void *v, void *out,
+hipError_t causal_mfma(int D, int flags, const void *q, const void *k, const void *v, void *out,
                        const float *preS, const float *prez, long pstride, long pzstride,
                        float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st);
 // Global read: out = phi(Q) S / phi(Q) z for every token, S/z per head ([BH, D, D], [BH, D]).
-hipError_t global_read_mfma(int D, const void *q, void *out, const float *S, const float *z,
-                            int BH, int N, int L, int P, hipStream_t st);
+hipError_t global_read_mfma(int D, int flags, const void *q, void *out, const float *S,
+                            const float *z, int BH, int N, int L, int P, hipStream_t st);
 
 // ---- vector-ALU family: any d, d_v in {16, 32, 64, 128}, float32 or bf16, chunk 16/32 ----
-hipError_t agg_valu(bool bf16, const void *k, const void *v, float *dstS, float *dstz,
+hipError_t agg_valu(bool bf16, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int d, int dv, int chunk, int L,
                     int nseg, int P, hipStream_t st);
 // Segment p of head bh starts from the state in slot bh * pslots + min(p, pslots - 1) of
 // preS/prez (zero state if preS is null). causal = false gives the global read (pslots = 1:
 // every segment reads the head's full state; nothing is updated).
-hipError_t out_valu(bool bf16, bool causal, const void *q, const void *k, const void *v,
+hipError_t out_valu(bool bf16, bool causal, int flags, const void *q, const void *k, const void *v,
                     void *out, const float *preS, const float *prez, long pstride,
                     long pzstride, int pslots, float *Sout, float *zout, int BH, int N, int d,
                     int dv, int chunk, int L, int P, hipStream_t st);
@@ -51,8 +55,17 @@ hipError_t seg_exclusive_scan(float *ws, const float *S0, const float *z0, int B
 hipError_t seg_total(const float *ws, float *S, float *z, int BH, int P, int d, int dv,
                      hipStream_t st);
 
+// ---- positive random features ------------------------------------------------------------
+// f[i][r] = exp(W[r] . x[i] - |x[i]|^2 / 2) / sqrt(m) for rows i, projections r < m. The
+// matrix-core kernel serves bf16 with rf_mfma_ok(d, m); a float32-arithmetic kernel takes any
+// d <= rf_max_d() and m.
+bool rf_mfma_ok(bool bf16, int d, int m);
+int rf_max_d();
+hipError_t rf_features(bool bf16, const void *x, const void *W, void *f, long rows, int d, int m,
+                       hipStream_t st);
+
 // ---- decode ------------------------------------------------------------------------------
-hipError_t decode_step(bool bf16, const void *q, const void *k, const void *v, void *out,
+hipError_t decode_step(bool bf16, int flags, const void *q, const void *k, const void *v, void *out,
                        float *S, float *z, int BH, int d, int dv, hipStream_t st);
 
 } // namespace la

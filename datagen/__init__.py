@@ -68,6 +68,20 @@ def qkv_cuda(B: int, H: int, N: int, d: int, dv: int, seed: int, scale: float = 
     return tuple(out)
 
 
+def projections(m: int, d: int, seed: int, dtype: str = "bf16") -> torch.Tensor:
+    """Random-feature projections W [m, d]: IID standard normal rows, rounded to ``dtype``
+    (the draw the unbiasedness of positive random features assumes)."""
+    return normal((m, d), seed, 1.0, dtype)
+
+
+def positive(shape, seed: int, scale: float = 1.0, dtype: str = "bf16", floor: float = 0.05):
+    """IID |N(0, scale^2)| + floor, rounded to ``dtype``: strictly positive inputs for the
+    forms that take q and k as features as given."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = np.abs(g.standard_normal(size=tuple(shape), dtype=np.float64)) * scale + floor
+    return torch.from_numpy(x).to(DTYPES[dtype])
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a bf16/fp32 tensor (both embed exactly in float64)."""
     return t.detach().to("cpu").to(torch.float64).numpy()
@@ -107,3 +121,9 @@ WORKLOADS = {
     5: Workload("decode_b256h32_d128_bf16_state4096", "decode", 256, 32, 1, 128, 128, "bf16",
                 1.0 / math.sqrt(128), 1005, steps=1000, prior=4096),
 }
+
+# Positive random features over the causal workload's inputs: q and k of workload 3 mapped
+# with m = 128 standard normal projections (seed 1006), then causal attention over the
+# features.
+RF_WORKLOAD = {"name": "favor_causal_b2h16n8192_d128_m128_bf16", "base": 3, "m": 128,
+               "seed": 1006}

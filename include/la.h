@@ -62,6 +62,21 @@ typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 enum { LA_OK = 0, LA_EINVAL = 1, LA_ENOTSUP = 2, LA_EHIP = 3 };
 
 /*
+ * Variant flags of the *_ex entry points (bitwise or; any other bit set: LA_EINVAL).
+ *   LA_PHI_IDENTITY  q and k are taken as already-mapped features: phi(x) = x. This is the
+ *                    convention of the pages' worked examples ("Linear Attention:
+ *                    Accumulating KV in a Fixed-Size State", section "Store Values according
+ *                    to Key components") and the form that attention over precomputed
+ *                    features (la_rf_features) takes. Features that are not positive can make
+ *                    a denominator zero or negative; nothing is clamped.
+ *   LA_UNNORMALIZED  out = phi(q_i)^T S_i, the weighted sum before the division by the score
+ *                    sum (same page, sections "Read the state with a Query" and "Divide by
+ *                    the sum of scores"). z is still accumulated and returned as part of the
+ *                    state, so a state can be read both ways.
+ */
+enum { LA_PHI_IDENTITY = 1, LA_UNNORMALIZED = 2 };
+
+/*
  * Causal prefill: out[b,h,i] = phi(q_i)^T S_i / phi(q_i)^T z_i over tokens j <= i, starting
  * from an optional carried state.
  *   S, z   both NULL: start from the zero state; the final state is not returned.
@@ -108,6 +123,14 @@ int la_causal_fwd_state(const void *q, const void *k, const void *v, void *out, 
                         int chunk, int seg_len, la_dtype dtype, hipStream_t stream);
 
 /*
+ * la_causal_fwd_state with variant flags (LA_PHI_IDENTITY, LA_UNNORMALIZED; 0 gives
+ * la_causal_fwd_state itself). Arguments, layout, ownership and errors as there.
+ */
+int la_causal_fwd_ex(const void *q, const void *k, const void *v, void *out, const float *S0,
+                     const float *z0, float *S, float *z, int B, int H, int N, int d, int d_v,
+                     int chunk, int seg_len, int flags, la_dtype dtype, hipStream_t stream);
+
+/*
  * Global (non-causal): S = phi(K)^T V and z = phi(K)^T 1 per (b, h) over all N tokens, then
  * out[b,h,i] = phi(q_i)^T S / phi(q_i)^T z for every token.
  *   S, z   required; written (not read) with the full-sequence state.
@@ -119,6 +142,11 @@ int la_causal_fwd_state(const void *q, const void *k, const void *v, void *out, 
 int la_global_fwd(const void *q, const void *k, const void *v, void *out, float *S, float *z,
                   int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype,
                   hipStream_t stream);
+
+/* la_global_fwd with variant flags (as for la_causal_fwd_ex; 0 gives la_global_fwd). */
+int la_global_fwd_ex(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                     int B, int H, int N, int d, int d_v, int chunk, int flags, la_dtype dtype,
+                     hipStream_t stream);
 
 /*
  * One recurrent decode step for B*H heads: N must be 1; q, k [B,H,1,d], v, out [B,H,1,d_v].
@@ -132,8 +160,13 @@ int la_decode_step(const void *q, const void *k, const void *v, void *out, float
                    int B, int H, int N, int d, int d_v, int chunk, la_dtype dtype,
                    hipStream_t stream);
 
+/* la_decode_step with variant flags (as for la_causal_fwd_ex; 0 gives la_decode_step). */
+int la_decode_step_ex(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                      int B, int H, int N, int d, int d_v, int flags, la_dtype dtype,
+                      hipStream_t stream);
+
 /*
- * Profiling form of la_causal_fwd_state: the same call enqueued `reps` times back to back on
+ * Profiling form of la_causal_fwd_ex: the same call enqueued `reps` times back to back on
  * `stream` (with S0 == S each call reads the state the previous one left; the work per call
  * is identical either way), with a HIP event recorded on that stream before and after each of
  * every call's kernels. The function then waits for the last event and writes the average
@@ -142,12 +175,32 @@ int la_decode_step(const void *q, const void *k, const void *v, void *out, float
  *   ms[2] causal outputs and final state; a phase the call did not launch (P = 1) gets 0.
  *   reps   1..4096; ms host array of 3 floats. reps out of range or ms NULL -> LA_EINVAL.
  * Blocks the calling thread until the work is done; for measurement, not for pipelines.
- * Errors as for la_causal_fwd_state; a failure while creating or reading events -> LA_EHIP.
+ * Errors as for la_causal_fwd_ex; a failure while creating or reading events -> LA_EHIP.
  */
 int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *out,
                            const float *S0, const float *z0, float *S, float *z, int B, int H,
-                           int N, int d, int d_v, int chunk, int seg_len, la_dtype dtype,
-                           hipStream_t stream, int reps, float *ms);
+                           int N, int d, int d_v, int chunk, int seg_len, int flags,
+                           la_dtype dtype, hipStream_t stream, int reps, float *ms);
+
+/*
+ * Positive random features: for rows x_i [rows, d] and projections W [m, d] (rows w_r),
+ *     f[i][r] = exp(w_r . x_i - |x_i|^2 / 2) / sqrt(m),      f [rows, m]
+ * so that f(q) . f(k) is an unbiased estimate of exp(q . k) when the w_r are drawn standard
+ * normal ("Linear Attention Math", section "Feature maps: elu+1 and positive random
+ * features"; "线性注意力从头到尾讲清楚", section 9, Performer's FAVOR+). The caller draws W
+ * (seeded, orthogonalised or not): the library draws no random numbers. Attention over the
+ * features is la_causal_fwd_ex / la_global_fwd_ex / la_decode_step_ex with LA_PHI_IDENTITY
+ * and d = m (q and k both mapped with the same W).
+ *   x, W, f  device memory, contiguous row-major, all of `dtype`; 16-byte aligned; f must not
+ *            overlap x or W. For B*H*N tokens of a [B, H, N, d] tensor, rows = B*H*N.
+ *   Arithmetic: float32 dots (bf16 operands of matrix-core products for bf16 with d in
+ *   {64, 128} and m in {64, 128, 256}), float32 exponent, output rounded to nearest even.
+ * Errors: NULL or misaligned pointer, rows, d or m <= 0, unknown dtype or a forbidden overlap:
+ * LA_EINVAL; d > 256, m > 4096 or rows > 2^31 - 1: LA_ENOTSUP; launch failure: LA_EHIP.
+ * Asynchronous on `stream` like the other entry points; no temporary memory.
+ */
+int la_rf_features(const void *x, const void *W, void *f, long rows, int d, int m,
+                   la_dtype dtype, hipStream_t stream);
 
 /* Bytes of stream-ordered temporary device memory a causal (form = 0) or global (form = 1)
  * call with these arguments takes (0 when none). seg_len as in la_causal_fwd_seg (0 = auto).

@@ -45,28 +45,37 @@ def test_version_and_strerror():
 
 
 def call(fn, q=A, k=2 * A, v=3 * A, out=4 * A, S=5 * A, z=6 * A, B=1, H=2, N=8, d=16, dv=16,
-         chunk=0, dtype=la.LA_BF16, seg=None, S0="same", z0="same"):
+         chunk=0, dtype=la.LA_BF16, seg=None, S0="same", z0="same", flags=0):
     f = getattr(la.lib, fn)
-    if fn in ("la_causal_fwd_state", "la_causal_fwd_profiled"):
+    if fn in ("la_causal_fwd_state", "la_causal_fwd_ex", "la_causal_fwd_profiled"):
         args = [q, k, v, out, S if S0 == "same" else S0, z if z0 == "same" else z0, S, z, B, H, N,
-                d, dv, chunk, 0 if seg is None else seg, dtype, None]
+                d, dv, chunk, 0 if seg is None else seg]
+        if fn != "la_causal_fwd_state":
+            args.append(flags)
+        args += [dtype, None]
         if fn == "la_causal_fwd_profiled":
             args += [1, (ctypes.c_float * 3)()]
         return f(*args)
+    if fn == "la_decode_step_ex":
+        return f(q, k, v, out, S, z, B, H, N, d, dv, flags, dtype, None)
     args = [q, k, v, out, S, z, B, H, N, d, dv, chunk]
     if fn == "la_causal_fwd_seg":
         args.append(0 if seg is None else seg)
+    if fn == "la_global_fwd_ex":
+        args.append(flags)
     args += [dtype, None]
     return f(*args)
 
 
-FORMS = ["la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_profiled",
-         "la_global_fwd", "la_decode_step"]
+FORMS = ["la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
+         "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
+         "la_decode_step_ex"]
+FLAGGED = ["la_causal_fwd_ex", "la_causal_fwd_profiled", "la_global_fwd_ex", "la_decode_step_ex"]
 
 
 @pytest.mark.parametrize("fn", FORMS)
 def test_null_and_size_checks(fn):
-    N = 1 if fn == "la_decode_step" else 8
+    N = 1 if fn.startswith("la_decode_step") else 8
     assert call(fn, k=None, N=N) == la.LA_EINVAL
     assert call(fn, v=None, N=N) == la.LA_EINVAL
     assert call(fn, B=0, N=N) == la.LA_EINVAL
@@ -94,10 +103,41 @@ def test_form_specific_checks():
     assert call("la_global_fwd", z=None) == la.LA_EINVAL
 
 
+@pytest.mark.parametrize("fn", FLAGGED)
+def test_flag_checks(fn):
+    N = 1 if fn.startswith("la_decode_step") else 8
+    for bad in (4, 8, 1 << 30, -1):
+        assert call(fn, N=N, flags=bad) == la.LA_EINVAL
+    # valid flags still go through the other checks first
+    for ok in (0, la.LA_PHI_IDENTITY, la.LA_UNNORMALIZED, la.LA_PHI_IDENTITY | la.LA_UNNORMALIZED):
+        assert call(fn, N=N, flags=ok, k=None) == la.LA_EINVAL
+        assert call(fn, N=N, flags=ok, d=48) == la.LA_ENOTSUP
+
+
+def rf(x=A, W=2 * A, f=3 * A, rows=64, d=64, m=128, dtype=la.LA_BF16):
+    return la.lib.la_rf_features(x, W, f, rows, d, m, dtype, None)
+
+
+def test_rf_argument_checks():
+    assert rf(x=None) == la.LA_EINVAL
+    assert rf(W=None) == la.LA_EINVAL
+    assert rf(f=None) == la.LA_EINVAL
+    assert rf(x=A + 8) == la.LA_EINVAL                          # misaligned
+    assert rf(rows=0) == la.LA_EINVAL
+    assert rf(d=-1) == la.LA_EINVAL
+    assert rf(m=0) == la.LA_EINVAL
+    assert rf(dtype=5) == la.LA_EINVAL
+    assert rf(f=A + 64) == la.LA_EINVAL                         # f overlaps x
+    assert rf(f=2 * A - 16) == la.LA_EINVAL                     # f overlaps W
+    assert rf(d=257) == la.LA_ENOTSUP
+    assert rf(m=4097) == la.LA_ENOTSUP
+    assert rf(rows=1 << 31, f=1 << 46) == la.LA_ENOTSUP
+
+
 def test_profiled_argument_checks():
     f = la.lib.la_causal_fwd_profiled
-    args = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 5 * A, 6 * A, 1, 2, 8, 16, 16, 0, 0, la.LA_BF16,
-            None]
+    args = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 5 * A, 6 * A, 1, 2, 8, 16, 16, 0, 0, 0,
+            la.LA_BF16, None]
     ms = (ctypes.c_float * 3)()
     assert f(*args, 1, None) == la.LA_EINVAL
     assert f(*args, 0, ms) == la.LA_EINVAL
