@@ -14,7 +14,8 @@ Inputs are float64 NumPy arrays holding exactly the values the GPU saw (bf16/fp3
 exactly); shapes q, k [B,H,N,d], v [B,H,N,dv], S [B,H,d,dv], z [B,H,d].
 ``mode`` = "elu1" applies phi(x) = ELU(x) + 1; "identity" takes q and k as already mapped
 (the convention of the pages' worked examples). ``normalize=False`` returns the numerator
-phi(q)^T S itself (the unnormalised form). ``rf_map`` gives positive random features.
+phi(q)^T S itself (the unnormalised form). ``gamma`` (causal and decode) decays the carried
+state per head (the retention recurrence). ``rf_map`` gives positive random features.
 """
 from __future__ import annotations
 
@@ -47,9 +48,9 @@ def _bind(path):
     lib = ctypes.CDLL(str(path))
     P = ctypes.POINTER(ctypes.c_double)
     L = ctypes.c_long
-    lib.oracle_causal.argtypes = [P, P, P, P, P, P, P, P, L, L, L, L, ctypes.c_int]
+    lib.oracle_causal.argtypes = [P, P, P, P, P, P, P, P, L, L, L, L, ctypes.c_int, P]
     lib.oracle_global.argtypes = [P, P, P, P, P, P, P, P, L, L, L, L, L, ctypes.c_int]
-    lib.oracle_decode.argtypes = [P, P, P, P, P, P, L, L, L, ctypes.c_int]
+    lib.oracle_decode.argtypes = [P, P, P, P, P, P, L, L, L, ctypes.c_int, P]
     lib.oracle_causal.restype = None
     lib.oracle_global.restype = None
     lib.oracle_decode.restype = None
@@ -84,10 +85,20 @@ def _mode(mode, normalize):
     return _MODES[mode] | (0 if normalize else 2)
 
 
-def causal(q, k, v, S0=None, z0=None, mode: str = "elu1", normalize: bool = True, lib=None):
+def _gamma(gamma, B, H):
+    """Per-head decay [H] (or a scalar) -> one value per (b, h) head, or None."""
+    if gamma is None:
+        return None
+    g = np.broadcast_to(np.asarray(gamma, dtype=np.float64), (H,))
+    return np.ascontiguousarray(np.tile(g, B))
+
+
+def causal(q, k, v, S0=None, z0=None, mode: str = "elu1", normalize: bool = True, gamma=None,
+           lib=None):
     """Causal recurrence. Returns (o, S_N, z_N, num, den).
 
-    S0, z0 (optional) are the state before the first token (zeros if omitted)."""
+    S0, z0 (optional) are the state before the first token (zeros if omitted). gamma (optional,
+    scalar or [H]) is the per-head decay of the carried state."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
     dv = v.shape[-1]
@@ -97,8 +108,9 @@ def causal(q, k, v, S0=None, z0=None, mode: str = "elu1", normalize: bool = True
     o = np.empty((B, H, N, dv))
     num = np.empty((B, H, N, dv))
     den = np.empty((B, H, N))
+    g = _gamma(gamma, B, H)
     (lib or _load()).oracle_causal(_p(q), _p(k), _p(v), _p(o), _p(num), _p(den), _p(S), _p(z),
-                                   B * H, N, d, dv, _mode(mode, normalize))
+                                   B * H, N, d, dv, _mode(mode, normalize), _p(g))
     return o, S, z, num, den
 
 
@@ -128,9 +140,11 @@ def global_(q, k, v, mode: str = "elu1", normalize: bool = True, lib=None):
     return o, S, z, num, den
 
 
-def decode_step(q, k, v, S, z, mode: str = "elu1", normalize: bool = True, lib=None):
+def decode_step(q, k, v, S, z, mode: str = "elu1", normalize: bool = True, gamma=None,
+                lib=None):
     """One recurrent step for every head; q, k [B,H,d] (or [B,H,1,d]), v [B,H,dv] (or
-    [B,H,1,dv]). Returns (o [B,H,dv], S', z'); the inputs S, z are not modified."""
+    [B,H,1,dv]). Returns (o [B,H,dv], S', z'); the inputs S, z are not modified. gamma as for
+    causal."""
     S = _f64(S).copy()
     z = _f64(z).copy()
     B, H, d, dv = S.shape
@@ -138,8 +152,9 @@ def decode_step(q, k, v, S, z, mode: str = "elu1", normalize: bool = True, lib=N
     k = _f64(k).reshape(B, H, d)
     v = _f64(v).reshape(B, H, dv)
     o = np.empty((B, H, dv))
+    g = _gamma(gamma, B, H)
     (lib or _load()).oracle_decode(_p(q), _p(k), _p(v), _p(o), _p(S), _p(z), B * H, d, dv,
-                                   _mode(mode, normalize))
+                                   _mode(mode, normalize), _p(g))
     return o, S, z
 
 

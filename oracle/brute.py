@@ -25,18 +25,26 @@ def phi(x, mode: str = "elu1"):
     return np.where(x > 0.0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def weights(q, k, causal: bool, mode: str = "elu1"):
-    """w[..., i, j] = phi(q_i) . phi(k_j), zeroed for j > i when causal."""
+def weights(q, k, causal: bool, mode: str = "elu1", gamma=None):
+    """w[..., i, j] = phi(q_i) . phi(k_j), zeroed for j > i when causal. With a per-head decay
+    gamma [H] (causal only), w[..., i, j] is further multiplied by gamma^(i - j): the parallel
+    form of the retention recurrence (the decay mask over pairs)."""
     w = np.matmul(phi(q, mode), np.swapaxes(phi(k, mode), -1, -2))
     if causal:
         n = w.shape[-1]
         w = w * np.tril(np.ones((n, n)))
+        if gamma is not None:
+            H = w.shape[-3]
+            g = np.broadcast_to(np.asarray(gamma, dtype=np.float64), (H,))
+            lag = np.tril(np.arange(n)[:, None] - np.arange(n)[None, :])   # i - j >= 0
+            dmask = np.stack([np.tril(gh ** lag) for gh in g])               # [H, n, n]
+            w = w * dmask
     return w
 
 
-def attend(q, k, v, causal: bool, mode: str = "elu1"):
+def attend(q, k, v, causal: bool, mode: str = "elu1", gamma=None):
     """Returns (o, num, den) of the pairwise form."""
-    w = weights(q, k, causal, mode)
+    w = weights(q, k, causal, mode, gamma)
     num = np.matmul(w, np.asarray(v, dtype=np.float64))
     den = w.sum(axis=-1)
     return num / den[..., None], num, den

@@ -25,6 +25,11 @@
  *   unnormalised  mode bit 1 returns the numerator phi(q_t)^T S_t itself (the weighted sum
  *                 before the division; "Linear Attention: Accumulating KV in a Fixed-Size
  *                 State", section "Read the state with a Query", prints such sums).
+ *   decay         optional per-head gamma (NULL: none): S_t = gamma S_{t-1} + phi(k_t) v_t^T
+ *                 and z_t = gamma z_{t-1} + phi(k_t) in the causal form and the decode step,
+ *                 the retention recurrence ("Linear Attention Math", section "Cousins: RetNet,
+ *                 Mamba, RWKV": linear attention with an explicit decay of the carried state;
+ *                 with mode bit 1 and the identity map it is that recurrence as stated).
  *   random        oracle_rf_map: positive random features phi(x)_r = exp(w_r . x - |x|^2 / 2)
  *   features      / sqrt(m) for given projections w_r ("Linear Attention Math", section
  *                 "Feature maps: elu+1 and positive random features"); attention over them
@@ -55,7 +60,8 @@ static double phi(double x, int mode)
  * sequence) and the state after the last token on return. num and den (may be NULL) receive
  * the numerator phi(q_t)^T S_t [BH, N, dv] and the denominator phi(q_t)^T z_t [BH, N]. */
 void oracle_causal(const double *q, const double *k, const double *v, double *o, double *num,
-                   double *den, double *S, double *z, long BH, long N, long d, long dv, int mode)
+                   double *den, double *S, double *z, long BH, long N, long d, long dv, int mode,
+                   const double *gamma)
 {
 #pragma omp parallel for schedule(dynamic, 1)
     for (long h = 0; h < BH; ++h) {
@@ -68,6 +74,13 @@ void oracle_causal(const double *q, const double *k, const double *v, double *o,
             const double *kt = k + (h * N + t) * d;
             const double *qt = q + (h * N + t) * d;
             const double *vt = v + (h * N + t) * dv;
+            /* decay: the state carried from the earlier tokens is scaled by gamma first */
+            if (gamma) {
+                for (long i = 0; i < d * dv; ++i)
+                    Sh[i] *= gamma[h];
+                for (long i = 0; i < d; ++i)
+                    zh[i] *= gamma[h];
+            }
             /* write: add the outer product phi(k_t) v_t^T and phi(k_t) to the key sum */
             for (long i = 0; i < d; ++i) {
                 kf[i] = phi(kt[i], mode);
@@ -161,7 +174,7 @@ void oracle_global(const double *q, const double *k, const double *v, double *o,
 /* One decode step for every head: q, k [BH, d]; v, o [BH, dv]; S, z updated in place
  * (S <- S + phi(k) v^T, z <- z + phi(k)), then o = phi(q)^T S / phi(q)^T z. */
 void oracle_decode(const double *q, const double *k, const double *v, double *o, double *S,
-                   double *z, long BH, long d, long dv, int mode)
+                   double *z, long BH, long d, long dv, int mode, const double *gamma)
 {
 #pragma omp parallel for schedule(static)
     for (long h = 0; h < BH; ++h) {
@@ -170,6 +183,12 @@ void oracle_decode(const double *q, const double *k, const double *v, double *o,
         const double *kh = k + h * d;
         const double *qh = q + h * d;
         const double *vh = v + h * dv;
+        if (gamma) {
+            for (long i = 0; i < d * dv; ++i)
+                Sh[i] *= gamma[h];
+            for (long i = 0; i < d; ++i)
+                zh[i] *= gamma[h];
+        }
         for (long i = 0; i < d; ++i) {
             double kfi = phi(kh[i], mode);
             for (long j = 0; j < dv; ++j)

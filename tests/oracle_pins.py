@@ -377,8 +377,79 @@ def pin_rf_unbiased(orc: Orc, golden=None):
     _close(o[0, 0], soft, 2e-2)
 
 
+# ------------------------------------------------------------- decayed recurrence (page 4)
+def pin_decay_worked(orc: Orc, golden):
+    """Hand-derived three-token example of the decayed recurrence (gamma = 0.5), causal and
+    as decode steps, unnormalised with the identity map (the retention form as stated)."""
+    g = golden("w8_decay_derived.json")
+    k, v, dr = np.array(g["k"], float), np.array(g["v"], float), g["derived"]
+    for mode, enc in (("identity", lambda x: x), ("elu1", _enc)):
+        o, S, z, _, _ = orc.causal(_t(enc(k)), _t(enc(k)), _t(v), mode=mode, normalize=False,
+                                   gamma=g["gamma"])
+        _close(S[0, 0], dr["S3"])
+        _close(z[0, 0], dr["z3"])
+        _close(o[0, 0], dr["causal_outputs_unnormalised_q_equal_k"])
+        for qs, key in (([1, 0], "q=[1,0]"), ([0, 1], "q=[0,1]"), ([1, 1], "q=[1,1]")):
+            Sd, zd = np.zeros((1, 1, 2, 2)), np.zeros((1, 1, 2))
+            for t in range(3):
+                qq = np.array(qs if t == 2 else k[t], float)
+                od, Sd, zd = orc.decode_step(enc(qq)[None, None], enc(k[t])[None, None],
+                                             v[t][None, None], Sd, zd, mode=mode,
+                                             normalize=False, gamma=g["gamma"])
+                if t < 2:
+                    _close(Sd[0, 0], dr[f"S{t + 1}"])
+            _close(od[0, 0], dr["reads_unnormalised"][key])
+
+
+def pin_decay_parallel_form(orc: Orc, golden=None):
+    """Recurrence with per-head decay == the parallel form sum_{j<=i} gamma^(i-j) w_ij v_j
+    (normalised and not, ELU+1 and identity), with a different gamma per head, including
+    gamma = 0 and gamma = 1."""
+    from oracle.compare import max_row_rel_err
+    gam = np.array([0.9, 0.5, 1.0, 0.0])
+    q, k, v = _rand((2, 4, 21, 5, 3), 18, scale=1.2)
+    for mode, (qq, kk) in (("elu1", (q, k)), ("identity", (np.abs(q) + 0.1, np.abs(k) + 0.1))):
+        for norm in (True, False):
+            o, _, _, num, den = orc.causal(qq, kk, v, mode=mode, normalize=norm, gamma=gam)
+            ob, numb, denb = brute.attend(qq, kk, v, causal=True, mode=mode, gamma=gam)
+            assert max_row_rel_err(num, numb) < 1e-12, (mode, norm)
+            assert max_row_rel_err(den[..., None], denb[..., None]) < 1e-12
+            assert max_row_rel_err(o, ob if norm else numb) < 1e-12
+
+
+def pin_decay_special_cases(orc: Orc, golden=None):
+    """gamma = 1 is the undecayed form exactly; gamma = 0 keeps only the current token
+    (normalised output v_t, unnormalised (phi(q_t) . phi(k_t)) v_t); decode steps chain to
+    the causal form, and a carried state splits the sequence, under decay."""
+    q, k, v = _rand((2, 3, 17, 4, 3), 19)
+    a = orc.causal(q, k, v)
+    b = orc.causal(q, k, v, gamma=1.0)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    o0, *_ = orc.causal(q, k, v, gamma=0.0)
+    _close(o0, v, 1e-14)
+    u0, *_ = orc.causal(q, k, v, normalize=False, gamma=0.0)
+    s = (brute.phi(q) * brute.phi(k)).sum(-1)
+    _close(u0, s[..., None] * v, 1e-13)
+    gam = np.array([0.8, 0.6, 0.95])
+    oc, Sc, zc, _, _ = orc.causal(q, k, v, gamma=gam)
+    S, z = np.zeros((2, 3, 4, 3)), np.zeros((2, 3, 4))
+    for t in range(17):
+        od, S, z = orc.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], S, z, gamma=gam)
+        _close(od, oc[:, :, t], 1e-12)
+    _close(S, Sc, 1e-12)
+    _close(z, zc, 1e-12)
+    n1 = 6
+    oa, Sa, za, _, _ = orc.causal(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], gamma=gam)
+    ob, Sb, zb, _, _ = orc.causal(q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], S0=Sa, z0=za,
+                                  gamma=gam)
+    _close(np.concatenate([oa, ob], axis=2), oc, 1e-12)
+    _close(Sb, Sc, 1e-12)
+
+
 ALL_PINS = [pin_phi_closed_form, pin_two_token_read, pin_not_softmax, pin_three_token,
             pin_decode_example, pin_outer_product, pin_duplicate_value, pin_global_example,
             pin_brute_force, pin_global_matmul, pin_causal_last_equals_global,
             pin_decode_chain_equals_causal, pin_split_invariance, pin_invariants,
-            pin_unnormalised_reads, pin_rf_closed_form, pin_rf_unbiased]
+            pin_unnormalised_reads, pin_rf_closed_form, pin_rf_unbiased, pin_decay_worked,
+            pin_decay_parallel_form, pin_decay_special_cases]

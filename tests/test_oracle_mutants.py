@@ -42,6 +42,14 @@ MUTANTS = [
     ("rf_scale_by_m", "1.0 / sqrt((double)m)", "1.0 / (double)m", 1),
     ("rf_transposed_projection", "dot += W[r * d + j] * xi[j];", "dot += W[j * m + r] * xi[j];", 1),
     ("rf_sign_of_projection", "exp(dot - 0.5 * sq)", "exp(-dot - 0.5 * sq)", 1),
+    ("decay_after_write", "            if (gamma) {\n                for (long i = 0; i < d * dv; ++i)\n                    Sh[i] *= gamma[h];",
+     "            if (0) {\n                for (long i = 0; i < d * dv; ++i)\n                    Sh[i] *= gamma[h];", 1),
+    ("decay_skips_key_sum", "                for (long i = 0; i < d; ++i)\n                    zh[i] *= gamma[h];",
+     "                for (long i = 0; i < d; ++i)\n                    zh[i] *= 1.0;", 1),
+    ("decay_first_head_only", "Sh[i] *= gamma[h];", "Sh[i] *= gamma[0];", 0),
+    ("decay_squared", "Sh[i] *= gamma[h];", "Sh[i] *= gamma[h] * gamma[h];", 0),
+    ("decode_decay_missing", "        if (gamma) {\n            for (long i = 0; i < d * dv; ++i)",
+     "        if (0) {\n            for (long i = 0; i < d * dv; ++i)", 1),
 ]
 
 
