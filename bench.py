@@ -200,6 +200,11 @@ def bench_favor(args):
     return w, m, ms, ms_rf, rf_bytes, kern
 
 
+def retention_name():
+    import datagen
+    return datagen.DECAY_WORKLOAD["name"]
+
+
 def favor_name():
     import datagen
     return datagen.RF_WORKLOAD["name"]
@@ -214,14 +219,92 @@ def bench_variants(args):
 
     w = datagen.WORKLOADS[3]
     dev = torch.device("cuda:0")
+    sets = []
+    for r in range(args.rotate):
+        q, k, v = datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed + 100 * r, w.scale, "bf16")
+        out = torch.empty_like(q)
+        S = torch.empty(w.B, w.H, w.d, w.dv, device=dev)
+        z = torch.empty(w.B, w.H, w.d, device=dev)
+        sets.append((q, k, v, out, S, z))
+    flags = la.LA_PHI_IDENTITY | la.LA_UNNORMALIZED
+
+    def step(i):
+        q, k, v, out, S, z = sets[i % len(sets)]
+        la.la_causal_fwd_ex(q, k, v, out, None, None, S, z, flags=flags)
+
+    ms, _ = time_calls(step, args.steps, args.warmup)
+    return w, ms
+
+
+def bench_retention(args):
+    """The decayed recurrence in its retention form (LA_PHI_IDENTITY | LA_UNNORMALIZED, per-head
+    gamma = 1 - 2^-(5+h)) on the prefill workload's inputs: la_causal_fwd_decay per step."""
+    import torch
+    import causal_linear_attention_la_amd as la
+    import datagen
+
+    w = datagen.WORKLOADS[datagen.DECAY_WORKLOAD["base"]]
+    dev = torch.device("cuda:0")
+    gamma = datagen.decay_rates(w.H).to(dev)
+    sets = []
+    for r in range(args.rotate):
+        q, k, v = datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed + 100 * r, w.scale, "bf16")
+        out = torch.empty_like(q)
+        S = torch.empty(w.B, w.H, w.d, w.dv, device=dev)
+        z = torch.empty(w.B, w.H, w.d, device=dev)
+        sets.append((q, k, v, out, S, z))
+    flags = la.LA_PHI_IDENTITY | la.LA_UNNORMALIZED
+
+    def step(i):
+        q, k, v, out, S, z = sets[i % len(sets)]
+        la.la_causal_fwd_decay(q, k, v, out, gamma, None, None, S, z, flags=flags)
+
+    ms, _ = time_calls(step, args.steps, args.warmup)
+    return w, ms
+
+
+def bench_serving(args):
+    """Prefill then decode for the same sequences: la_causal_fwd_state over an N-token prompt
+    (B=2 H=16 N=8192 d=128) writes S, z; then K decode steps (la_decode_step, one token per
+    sequence per step) continue from that state. The K steps are captured once in a HIP graph
+    and replayed (no per-step launch from Python). One serving step = prefill + K decode
+    steps; throughput counts prompt and generated tokens (per sequence, times heads)."""
+    import torch
+    import causal_linear_attention_la_amd as la
+    import datagen
+
+    w = datagen.WORKLOADS[3]
+    K = args.serve_steps
+    dev = torch.device("cuda:0")
     q, k, v = datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale, "bf16")
     out = torch.empty_like(q)
     S = torch.empty(w.B, w.H, w.d, w.dv, device=dev)
     z = torch.empty(w.B, w.H, w.d, device=dev)
-    flags = la.LA_PHI_IDENTITY | la.LA_UNNORMALIZED
-    ms, _ = time_calls(lambda i: la.la_causal_fwd_ex(q, k, v, out, None, None, S, z, flags=flags),
-                       args.steps, 2)
-    return w, ms
+    toks = datagen.qkv_cuda(K, w.B * w.H, 1, w.d, w.dv, w.seed + 7, w.scale, "bf16")
+    toks = [x.view(K, w.B, w.H, -1) for x in toks]
+    dout = torch.empty(K, w.B, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+
+    def decode_all():
+        for t in range(K):
+            la.la_decode_step(toks[0][t], toks[1][t], toks[2][t], dout[t], S, z)
+
+    # capture on a side stream (the library launches on the current stream)
+    la.la_causal_fwd_state(q, k, v, out, None, None, S, z)
+    decode_all()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_all()
+    torch.cuda.synchronize()
+
+    def step(i):
+        la.la_causal_fwd_state(q, k, v, out, None, None, S, z)
+        graph.replay()
+
+    ms, _ = time_calls(step, max(3, args.steps // 5), 2)
+    ms_pre, _ = time_calls(lambda i: la.la_causal_fwd_state(q, k, v, out, None, None, S, z),
+                           max(3, args.steps // 5), 1)
+    return w, K, ms, ms_pre
 
 
 def cpu_baseline():
@@ -296,7 +379,10 @@ def main():
     ap.add_argument("--seg-len", dest="seg_len", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled over the steps")
     ap.add_argument("--decode-steps", dest="decode_steps", type=int, default=1000)
-    ap.add_argument("--only", choices=["prefill", "decode", "global", "favor", "variants", "copycal"],
+    ap.add_argument("--serve-steps", dest="serve_steps", type=int, default=256,
+                    help="decode steps after the prefill in the serving leg")
+    ap.add_argument("--only", choices=["prefill", "decode", "global", "favor", "variants",
+                                       "retention", "serving", "copycal"],
                     default=None,
                     help="run one form only (for profiling); no JSON line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -319,7 +405,8 @@ def main():
         if args.copycal:
             copy_calibration()
         fn = {"prefill": bench_prefill, "decode": bench_decode, "global": bench_global,
-              "favor": bench_favor, "variants": bench_variants}[args.only]
+              "favor": bench_favor, "variants": bench_variants, "retention": bench_retention,
+              "serving": bench_serving}[args.only]
         r = fn(args)
         extra = ""
         if args.only == "prefill":
@@ -327,7 +414,7 @@ def main():
         if args.only == "favor":
             extra = f" (features {r[3] * 1e3:.1f} us per tensor; attention kernels " + \
                 ", ".join(f"{t * 1e3:.1f}" for t in r[5]) + " us)"
-        ms = r[2] if args.only == "favor" else r[1]
+        ms = r[2] if args.only in ("favor", "serving") else r[1]
         print(f"{args.only}: {ms:.4f} ms/step{extra}", flush=True)
         return
 
@@ -349,6 +436,11 @@ def main():
           file=sys.stderr, flush=True)
     wv, ms_v = bench_variants(args)
     print(f"identity+unnormalised causal: {ms_v * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+    wr, ms_r = bench_retention(args)
+    print(f"retention causal: {ms_r * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+    ws_, K_s, ms_s, ms_sp = bench_serving(args)
+    print(f"serving: {ms_s * 1e3:.1f} us per prefill + {K_s} decode steps", file=sys.stderr,
+          flush=True)
 
     rec = {
         "metric": METRIC,
@@ -398,6 +490,12 @@ def main():
                                            "causal": kern_f[2] * 1e3}},
         "identity_unnormalized": {"workload": wv.name, "us_per_call": ms_v * 1e3,
                                   "token_heads_per_s": wv.B * wv.H * wv.N / (ms_v * 1e-3)},
+        "retention": {"workload": retention_name(), "us_per_call": ms_r * 1e3,
+                      "token_heads_per_s": wr.B * wr.H * wr.N / (ms_r * 1e-3)},
+        "serving": {"workload": f"prefill {ws_.name} then {K_s} decode steps (HIP graph)",
+                    "us_per_serving_step": ms_s * 1e3, "prefill_us": ms_sp * 1e3,
+                    "decode_us_per_step": (ms_s - ms_sp) * 1e3 / K_s,
+                    "token_heads_per_s": ws_.B * ws_.H * (ws_.N + K_s) / (ms_s * 1e-3)},
         "wall_s_timed_region": wall,
     }
     if not args.no_cpu:

@@ -11,6 +11,9 @@ The entry points keep the C names:
     la_global_fwd_ex(q, k, v, out, S, z, chunk=0, flags=0)
     la_decode_step(q, k, v, out, S, z)
     la_decode_step_ex(q, k, v, out, S, z, flags=0)
+    la_causal_fwd_decay(q, k, v, out, gamma, S0=None, z0=None, S=None, z=None, chunk=0,
+                        seg_len=0, flags=0)            # per-head decay gamma [H] (retention)
+    la_decode_step_decay(q, k, v, out, S, z, gamma, flags=0)
     la_rf_features(x, W, f)                            # positive random features
 with q, k [B,H,N,d], v, out [B,H,N,d_v] (bf16 or float32, contiguous, on the GPU),
 S [B,H,d,d_v] and z [B,H,d] float32; flags is a bitwise or of LA_PHI_IDENTITY and
@@ -42,8 +45,8 @@ LA_PHI_IDENTITY, LA_UNNORMALIZED = 1, 2
 # Every symbol include/la.h declares.
 EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
            "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
-           "la_decode_step_ex", "la_rf_features", "la_workspace_bytes", "la_strerror",
-           "la_version")
+           "la_decode_step_ex", "la_causal_fwd_decay", "la_decode_step_decay", "la_rf_features",
+           "la_workspace_bytes", "la_strerror", "la_version")
 
 
 class LAError(RuntimeError):
@@ -70,9 +73,11 @@ def _load(path: Path):
     lib.la_decode_step.argtypes = core + [i, vp]
     lib.la_decode_step_ex.argtypes = core + [i, vp]
     lib.la_rf_features.argtypes = [vp, vp, vp, ctypes.c_long, i, i, i, vp]
+    lib.la_causal_fwd_decay.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp] + [i] * 9 + [vp]
+    lib.la_decode_step_decay.argtypes = [vp, vp, vp, vp, fp, fp, fp] + [i] * 7 + [vp]
     for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
               "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
-              "la_decode_step_ex", "la_rf_features"):
+              "la_decode_step_ex", "la_rf_features", "la_causal_fwd_decay", "la_decode_step_decay"):
         getattr(lib, f).restype = ctypes.c_int
     lib.la_workspace_bytes.argtypes = [i] * 8 + [i]
     lib.la_workspace_bytes.restype = ctypes.c_size_t
@@ -235,6 +240,32 @@ def la_decode_step_ex(q, k, v, out, S, z, flags: int = 0):
     st = lib.la_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d,
                                dv, flags, _dtype_code(k), _stream(k))
     _check(st, "la_decode_step_ex")
+    return out
+
+
+def la_causal_fwd_decay(q, k, v, out, gamma, S0=None, z0=None, S=None, z=None, chunk: int = 0,
+                        seg_len: int = 0, flags: int = 0):
+    """Causal prefill of the decayed recurrence; gamma: float32 [H] on the device."""
+    _check_tensors(q, k, v, out, gamma, S0, z0, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    if gamma.dtype != torch.float32 or gamma.numel() != H:
+        raise ValueError("gamma must be a float32 tensor of H values")
+    st = lib.la_causal_fwd_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0), _ptr(S),
+                                 _ptr(z), _ptr(gamma), B, H, N, d, dv, chunk, seg_len, flags,
+                                 _dtype_code(k), _stream(k))
+    _check(st, "la_causal_fwd_decay")
+    return out
+
+
+def la_decode_step_decay(q, k, v, out, S, z, gamma, flags: int = 0):
+    """One decode step of the decayed recurrence; S, z are updated in place."""
+    _check_tensors(q, k, v, out, S, z, gamma)
+    B, H, N, d, dv = _dims(q, k, v)
+    if gamma.dtype != torch.float32 or gamma.numel() != H:
+        raise ValueError("gamma must be a float32 tensor of H values")
+    st = lib.la_decode_step_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z),
+                                  _ptr(gamma), B, H, N, d, dv, flags, _dtype_code(k), _stream(k))
+    _check(st, "la_decode_step_decay")
     return out
 
 

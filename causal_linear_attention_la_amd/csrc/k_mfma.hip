@@ -267,6 +267,76 @@ __device__ __forceinline__ void key_sum(f32x4 (&zacc)[ZT], const uint16_t *k)
             zacc[zt] = mfma(frag_tok<D>(k + blk<D>(32 * m, 16 * zt)), ones, zacc[zt]);
 }
 
+// ---- decay of the carried state (the retention recurrence S_t = gamma S_{t-1} + ...) ------
+// gamma^n = exp2(n lg) with lg = log2(gamma) clamped to -1000, so gamma = 0 gives 1 for n = 0
+// and 0 for n > 0 without an infinity (no 0 * inf).
+__device__ __forceinline__ float decay_lg(const float *gamma, int bh, int H)
+{
+    return gamma ? fmaxf(log2f(gamma[bh % H]), -1000.f) : 0.f;
+}
+__device__ __forceinline__ float dpow(float lg, int n) { return __builtin_amdgcn_exp2f(lg * (float)n); }
+
+// Token weights gamma^(nvalid - 1 - tok) of 32-token block m in the k-slot order of frag_tok:
+// slot 4h + y is token 32m + 16h + 4g + y. Tokens past nvalid (zero rows) get weight 1.
+__device__ __forceinline__ void tok_weights(float (&wt)[8], float lg, int nvalid, int m, int g)
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+            wt[4 * h + y] = dpow(lg, max(nvalid - 1 - (32 * m + 16 * h + 4 * g + y), 0));
+}
+
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 x, const float (&w)[8])
+{
+    const u32x4 u = __builtin_bit_cast(u32x4, x);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = pack_bf2(bf_lo(u[i]) * w[2 * i], bf_hi(u[i]) * w[2 * i + 1]);
+    return __builtin_bit_cast(bf16x8, o);
+}
+
+// S = gamma^nvalid S + Kf^T diag(w) V and z = gamma^nvalid z + Kf^T w over one chunk, with
+// the token weights w of tok_weights: the chunk's tokens decayed to its last one.
+template <int D, int NCT, int ZT>
+__device__ __forceinline__ void state_update_decay(f32x4 (&sacc)[Cfg<D>::NFT][NCT], f32x4 (&zacc)[ZT],
+                                                   const uint16_t *k, const uint16_t *v,
+                                                   const uint16_t *kz, float lg, int nvalid, int g)
+{
+    using K = Cfg<D>;
+    const float fc = dpow(lg, nvalid);
+#pragma unroll
+    for (int ft = 0; ft < K::NFT; ++ft)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            sacc[ft][ct] *= fc;
+#pragma unroll
+    for (int zt = 0; zt < ZT; ++zt)
+        zacc[zt] *= fc;
+#pragma unroll
+    for (int m = 0; m < C / 32; ++m) {
+        float wt[8];
+        tok_weights(wt, lg, nvalid, m, g);
+        bf16x8 bv[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+            bv[ct] = scale_frag(frag_tok<D>(v + blk<D>(32 * m, 16 * ct)), wt);
+#pragma unroll
+        for (int ft = 0; ft < K::NFT; ++ft) {
+            const bf16x8 ak = frag_tok<D>(k + blk<D>(32 * m, 16 * ft));
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                sacc[ft][ct] = mfma(ak, bv[ct], sacc[ft][ct]);
+        }
+        const u32x4 wb = {pack_bf2(wt[0], wt[1]), pack_bf2(wt[2], wt[3]), pack_bf2(wt[4], wt[5]),
+                          pack_bf2(wt[6], wt[7])};
+#pragma unroll
+        for (int zt = 0; zt < ZT; ++zt)
+            zacc[zt] = mfma(frag_tok<D>(kz + blk<D>(32 * m, 16 * zt)), __builtin_bit_cast(bf16x8, wb), zacc[zt]);
+    }
+}
+
 // out rows [0, nvalid) of the chunk at `ob`: out = num / den, rounded to bf16.
 // The denominator of row i is sden[i] (+ sden2[i] when given); NORM = false stores num itself
 // (the unnormalised form) and reads no denominator.
@@ -314,13 +384,14 @@ template <int D> struct AggCfg {
     static constexpr int THREADS = NW * 64;
 };
 
-template <int D, bool PHI>
+template <int D, bool PHI, bool DECAY>
 __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__restrict__ k,
                                                            const uint16_t *__restrict__ v,
                                                            float *__restrict__ dstS,
                                                            float *__restrict__ dstz, long sstride,
                                                            long zstride, int N, int L, int nseg,
-                                                           int P)
+                                                           int P, const float *__restrict__ gamma,
+                                                           int H)
 {
     using K = Cfg<D>;
     using TL = Tile<D, AggCfg<D>::THREADS>;
@@ -337,6 +408,7 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
     const int trl = tr_lane<D>(li, g);
     const TL tile(tid);
     auto chunk_t0 = [&](int cc) { return tb + min(cc, nch - 1) * C; };
+    const float lg = DECAY ? decay_lg(gamma, bh, H) : 0.f;
 
     f32x4 sacc[K::NFT][1];
     f32x4 zacc[1];
@@ -365,8 +437,13 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
             tile.load(rk, kb + (size_t)tn * D, te - tn);
             tile.load(rv, vb + (size_t)tn * D, te - tn);
         }
-        state_update<D, 1>(sacc, sK[b] + trl, sV[b] + cw0 + trl);
-        key_sum<D, 1>(zacc, sK[b] + cw0 + trl);
+        if (DECAY) {
+            state_update_decay<D, 1, 1>(sacc, zacc, sK[b] + trl, sV[b] + cw0 + trl, sK[b] + cw0 + trl,
+                                        lg, min(C, te - (tb + c * C)), g);
+        } else {
+            state_update<D, 1>(sacc, sK[b] + trl, sV[b] + cw0 + trl);
+            key_sum<D, 1>(zacc, sK[b] + cw0 + trl);
+        }
         __syncthreads();
     }
 
@@ -414,6 +491,7 @@ struct CausalArgs {
     const float *S0, *z0;         // state before the segment (null: zero)
     float *Sout, *zout;           // final state of the head (null: not written)
     int tb, te, nch;              // token range of the segment, chunks in it
+    float lg;                     // log2 of the head's decay (0: none)
 };
 
 // Writes the wave's 16 features of z (rows 4g..4g+3 of its tile; lane li == 0 of each group)
@@ -434,7 +512,7 @@ __device__ __forceinline__ void put_z(CausalLds<D> &sm, const f32x4 &z, int w, i
 // features [16w, 16w+16). Barrier sequence: 1 in the prologue, 2 per chunk. NORM = false (the
 // unnormalised form) skips the denominator: no row sums of A and no phi(q) . z, while z is
 // still accumulated as part of the state.
-template <int D, bool NORM>
+template <int D, bool NORM, bool DECAY>
 __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArgs &a, int w,
                                                int li, int g)
 {
@@ -499,6 +577,14 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
                             if (4 * g + r > li)
                                 t[r] = 0.f;
                     }
+                    if (DECAY && jt <= w) {
+                        // A[i][j] *= gamma^(i - j) for j <= i (the decay mask)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int lag = 16 * (w - jt) + li - 4 * g - r;
+                            t[r] = lag >= 0 ? t[r] * dpow(a.lg, lag) : 0.f;
+                        }
+                    }
                     pk[2 * h] = pack_bf2(t[0], t[1]);
                     pk[2 * h + 1] = pack_bf2(t[2], t[3]);
                     if (NORM)
@@ -522,8 +608,8 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
 #pragma unroll
             for (int kk = 0; kk < K::NKB; ++kk)
                 cz = mfma(lds<bf16x8>(za + 32 * kk), lds<bf16x8>(sQ + opl + blk<D>(16 * iw, 32 * kk)), cz);
-            if (g == 0)
-                sm.sqz[16 * iw + li] = cz[0] + cz[1];
+            if (g == 0) // the carried key sum reaches query row i decayed by gamma^(i + 1)
+                sm.sqz[16 * iw + li] = (cz[0] + cz[1]) * (DECAY ? dpow(a.lg, 16 * iw + li + 1) : 1.f);
         }
         __syncthreads();
         // ---- phase 2: num^T = V^T A^T + S^T Qf^T for the wave's columns; out; S, z += Kf^T [V 1]
@@ -532,6 +618,14 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
 #pragma unroll
             for (int it = 0; it < 4; ++it)
                 acc[0][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (DECAY) {
+                // the carried state reaches query row i decayed by gamma^(i + 1): read it
+                // first and scale the rows before the within-chunk part is added
+                state_read<D, 1>(acc, sacc, sQ + sql);
+#pragma unroll
+                for (int it = 0; it < 4; ++it)
+                    acc[0][it] *= dpow(a.lg, 16 * it + li + 1);
+            }
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const bf16x8 av = frag_tok<D>(sm.sV + cw0 + trl + blk<D>(32 * m, 0));
@@ -541,10 +635,16 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
                     acc[0][it] = mfma(av, ba, acc[0][it]);
                 }
             }
-            state_read<D, 1>(acc, sacc, sQ + sql);
+            if (!DECAY)
+                state_read<D, 1>(acc, sacc, sQ + sql);
             store_out<D, 1, NORM>(acc, sm.srs, sm.sqz, a.oh + (size_t)t0 * D, nvalid, cw0, li, g);
-            state_update<D, 1>(sacc, sK + trl, sm.sV + cw0 + trl);
-            key_sum<D, 1>(zacc, sK + 16 * w + trl);
+            if (DECAY) {
+                state_update_decay<D, 1, 1>(sacc, zacc, sK + trl, sm.sV + cw0 + trl, sK + 16 * w + trl,
+                                            a.lg, nvalid, g);
+            } else {
+                state_update<D, 1>(sacc, sK + trl, sm.sV + cw0 + trl);
+                key_sum<D, 1>(zacc, sK + 16 * w + trl);
+            }
             if (NORM)
                 put_z<D>(sm, zacc[0], w, li, g);
         }
@@ -634,12 +734,12 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
 //   --- barrier ---
 // Roles are chosen by the wave-uniform wave index, so every wave executes the same sequence of
 // barriers. F: variant flags (F_IDENTITY: q, k are already features; F_UNNORM: no denominator).
-template <int D, int F>
+template <int D, int F, bool DECAY>
 __global__ __launch_bounds__(CausalCfg<D>::THREADS) void k_causal(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ out, const float *__restrict__ preS, const float *__restrict__ prez,
     long pstride, long pzstride, float *__restrict__ Sout, float *__restrict__ zout, int N, int L,
-    int P)
+    int P, const float *__restrict__ gamma, int H)
 {
     constexpr int NCW = CausalCfg<D>::NCW;
     __shared__ __attribute__((aligned(16))) CausalLds<D> sm;
@@ -659,8 +759,9 @@ __global__ __launch_bounds__(CausalCfg<D>::THREADS) void k_causal(
     a.tb = p * L;
     a.te = min(N, a.tb + L);
     a.nch = (a.te - a.tb + C - 1) / C;
+    a.lg = DECAY ? decay_lg(gamma, bh, H) : 0.f;
     if (wave < NCW)
-        causal_compute<D, !(F & F_UNNORM)>(sm, a, wave, l & 15, l >> 4);
+        causal_compute<D, !(F & F_UNNORM), DECAY>(sm, a, wave, l & 15, l >> 4);
     else
         causal_stage<D, !(F & F_IDENTITY)>(sm, a, tid - NCW * 64);
 }
@@ -768,22 +869,28 @@ __global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
 template <int D, int F> void launch_causal(dim3 grid, hipStream_t st, const uint16_t *q,
                                            const uint16_t *k, const uint16_t *v, uint16_t *o,
                                            const float *preS, const float *prez, long ps, long pzs,
-                                           float *Sout, float *zout, int N, int L, int P)
+                                           float *Sout, float *zout, int N, int L, int P,
+                                           const float *gamma, int H)
 {
-    hipLaunchKernelGGL((k_causal<D, F>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q, k, v, o, preS,
-                       prez, ps, pzs, Sout, zout, N, L, P);
+    if (gamma)
+        hipLaunchKernelGGL((k_causal<D, F, true>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q, k, v,
+                           o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
+    else
+        hipLaunchKernelGGL((k_causal<D, F, false>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q, k,
+                           v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
 }
 
 template <int D> void launch_causal_f(int flags, dim3 grid, hipStream_t st, const uint16_t *q,
                                       const uint16_t *k, const uint16_t *v, uint16_t *o,
                                       const float *preS, const float *prez, long ps, long pzs,
-                                      float *Sout, float *zout, int N, int L, int P)
+                                      float *Sout, float *zout, int N, int L, int P,
+                                      const float *gamma, int H)
 {
     switch (flags & (F_IDENTITY | F_UNNORM)) {
-    case 0: launch_causal<D, 0>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
-    case 1: launch_causal<D, 1>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
-    case 2: launch_causal<D, 2>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
-    default: launch_causal<D, 3>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
+    case 0: launch_causal<D, 0>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
+    case 1: launch_causal<D, 1>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
+    case 2: launch_causal<D, 2>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
+    default: launch_causal<D, 3>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
     }
 }
 
@@ -798,36 +905,49 @@ template <int D> void launch_gread_f(int flags, dim3 grid, hipStream_t st, const
     }
 }
 
+template <int D, bool PHI> void launch_agg(dim3 grid, hipStream_t st, const uint16_t *k,
+                                           const uint16_t *v, float *dstS, float *dstz, long ss,
+                                           long zs, int N, int L, int nseg, int P,
+                                           const float *gamma, int H)
+{
+    if (gamma)
+        hipLaunchKernelGGL((k_agg<D, PHI, true>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v, dstS,
+                           dstz, ss, zs, N, L, nseg, P, gamma, H);
+    else
+        hipLaunchKernelGGL((k_agg<D, PHI, false>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v, dstS,
+                           dstz, ss, zs, N, L, nseg, P, gamma, H);
+}
+
 template <int D> void launch_agg_f(int flags, dim3 grid, hipStream_t st, const uint16_t *k,
                                    const uint16_t *v, float *dstS, float *dstz, long ss, long zs,
-                                   int N, int L, int nseg, int P)
+                                   int N, int L, int nseg, int P, const float *gamma, int H)
 {
     if (flags & F_IDENTITY)
-        hipLaunchKernelGGL((k_agg<D, false>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v, dstS,
-                           dstz, ss, zs, N, L, nseg, P);
+        launch_agg<D, false>(grid, st, k, v, dstS, dstz, ss, zs, N, L, nseg, P, gamma, H);
     else
-        hipLaunchKernelGGL((k_agg<D, true>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v, dstS,
-                           dstz, ss, zs, N, L, nseg, P);
+        launch_agg<D, true>(grid, st, k, v, dstS, dstz, ss, zs, N, L, nseg, P, gamma, H);
 }
 
 } // namespace
 
 hipError_t agg_mfma(int D, int flags, const void *k, const void *v, float *dstS, float *dstz,
-                    long sstride, long zstride, int BH, int N, int L, int nseg, int P, hipStream_t st)
+                    long sstride, long zstride, int BH, int N, int L, int nseg, int P,
+                    const float *gamma, int H, hipStream_t st)
 {
     const dim3 grid((unsigned)(BH * nseg));
     const auto *kk = static_cast<const uint16_t *>(k);
     const auto *vv = static_cast<const uint16_t *>(v);
     if (D == 128)
-        launch_agg_f<128>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
+        launch_agg_f<128>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
     else
-        launch_agg_f<64>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
+        launch_agg_f<64>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
     return hipGetLastError();
 }
 
 hipError_t causal_mfma(int D, int flags, const void *q, const void *k, const void *v, void *out,
                        const float *preS, const float *prez, long pstride, long pzstride,
-                       float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st)
+                       float *Sout, float *zout, int BH, int N, int L, int P, const float *gamma,
+                       int H, hipStream_t st)
 {
     const dim3 grid((unsigned)(BH * P));
     const auto *qq = static_cast<const uint16_t *>(q);
@@ -836,10 +956,10 @@ hipError_t causal_mfma(int D, int flags, const void *q, const void *k, const voi
     auto *oo = static_cast<uint16_t *>(out);
     if (D == 128)
         launch_causal_f<128>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout,
-                             zout, N, L, P);
+                             zout, N, L, P, gamma, H);
     else
         launch_causal_f<64>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout,
-                            zout, N, L, P);
+                            zout, N, L, P, gamma, H);
     return hipGetLastError();
 }
 

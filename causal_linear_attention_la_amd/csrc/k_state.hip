@@ -31,7 +31,8 @@ constexpr int SB = 16;
 
 __global__ __launch_bounds__(NT) void k_seg_scan(float *__restrict__ ws, const float *__restrict__ S0,
                                                  const float *__restrict__ z0, int P, int d,
-                                                 int dv, int blocks_per_head)
+                                                 int dv, int blocks_per_head,
+                                                 const float *__restrict__ gamma, int H, int L)
 {
     const int E = d * dv + d;
     const int bh = blockIdx.x / blocks_per_head;
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(NT) void k_seg_scan(float *__restrict__ ws, const f
     if (S0)
         run = e < d * dv ? S0[(size_t)bh * d * dv + e] : z0[(size_t)bh * d + (e - d * dv)];
     float *slot = ws + (size_t)bh * P * E + e;
+    const float fL = gamma ? decay_pow(decay_log2(gamma, bh, H), L) : 1.f;
     for (int p0 = 0; p0 < P - 1; p0 += SB) {
         float t[SB];
 #pragma unroll
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(NT) void k_seg_scan(float *__restrict__ ws, const f
         for (int i = 0; i < SB; ++i)
             if (p0 + i < P - 1) {
                 slot[(size_t)(p0 + i) * E] = run;
-                run += t[i];
+                run = gamma ? fmaf(run, fL, t[i]) : run + t[i];
             }
     }
     slot[(size_t)(P - 1) * E] = run;
@@ -91,7 +93,7 @@ template <typename T, int D, int DV>
 __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T *__restrict__ k,
                                                const T *__restrict__ v, T *__restrict__ out,
                                                float *__restrict__ S, float *__restrict__ z,
-                                               int flags)
+                                               int flags, const float *__restrict__ gamma, int H)
 {
     const bool ident = flags & F_IDENTITY;
     constexpr int CG = DV / 4, RP = NT / CG, RPT = (D + RP - 1) / RP;
@@ -102,6 +104,8 @@ __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T 
     const int tid = threadIdx.x, cg = tid % CG, rp = tid / CG;
     const size_t bh = blockIdx.x;
     f32x4 *Sh = reinterpret_cast<f32x4 *>(S + bh * D * DV);
+    // decay of the carried state (1 without gamma): S' = gd S + phi(k) v^T, z' = gd z + phi(k)
+    const float gd = gamma ? gamma[bh % H] : 1.f;
 
     // the head's state rows, all loads in flight before any use
     f32x4 s[RPT];
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T 
         const float qf = feature(Elem<T>::ld(q, bh * D + tid), ident);
         skf[tid] = kf;
         sqf[tid] = qf;
-        const float zn = z[bh * D + tid] + kf;
+        const float zn = fmaf(gd, z[bh * D + tid], kf);
         z[bh * D + tid] = zn;
         part = qf * zn;
     }
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T 
             f32x4 sn;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                sn[c] = s[i][c] + kf * vv[c];
+                sn[c] = fmaf(gd, s[i][c], kf * vv[c]);
                 acc[c] += qf * sn[c];
             }
             __builtin_nontemporal_store(sn, Sh + r * CG + cg);
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T 
 
 template <typename T>
 hipError_t decode_t(int flags, const void *q, const void *k, const void *v, void *out, float *S,
-                    float *z, int BH, int d, int dv, hipStream_t st)
+                    float *z, int BH, int d, int dv, const float *gamma, int H, hipStream_t st)
 {
     const dim3 grid((unsigned)BH), block(NT);
     const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
@@ -173,7 +177,8 @@ hipError_t decode_t(int flags, const void *q, const void *k, const void *v, void
     T *oo = static_cast<T *>(out);
 #define LA_DEC(DD, VV)                                                                          \
     if (d == DD && dv == VV) {                                                                  \
-        hipLaunchKernelGGL((k_decode<T, DD, VV>), grid, block, 0, st, qq, kk, vv, oo, S, z, flags); \
+        hipLaunchKernelGGL((k_decode<T, DD, VV>), grid, block, 0, st, qq, kk, vv, oo, S, z, flags, \
+                           gamma, H);                                                           \
         return hipGetLastError();                                                               \
     }
 #define LA_DEC_ROW(DD) LA_DEC(DD, 16) LA_DEC(DD, 32) LA_DEC(DD, 64) LA_DEC(DD, 128)
@@ -189,11 +194,11 @@ hipError_t decode_t(int flags, const void *q, const void *k, const void *v, void
 } // namespace
 
 hipError_t seg_exclusive_scan(float *ws, const float *S0, const float *z0, int BH, int P, int d,
-                              int dv, hipStream_t st)
+                              int dv, const float *gamma, int H, int L, hipStream_t st)
 {
     const int E = d * dv + d, bph = (E + NT - 1) / NT;
     hipLaunchKernelGGL(k_seg_scan, dim3((unsigned)(BH * bph)), dim3(NT), 0, st, ws, S0, z0, P, d,
-                       dv, bph);
+                       dv, bph, gamma, H, L);
     return hipGetLastError();
 }
 
@@ -207,10 +212,11 @@ hipError_t seg_total(const float *ws, float *S, float *z, int BH, int P, int d, 
 }
 
 hipError_t decode_step(bool bf16, int flags, const void *q, const void *k, const void *v,
-                       void *out, float *S, float *z, int BH, int d, int dv, hipStream_t st)
+                       void *out, float *S, float *z, int BH, int d, int dv, const float *gamma,
+                       int H, hipStream_t st)
 {
-    return bf16 ? decode_t<bf16_t>(flags, q, k, v, out, S, z, BH, d, dv, st)
-                : decode_t<float>(flags, q, k, v, out, S, z, BH, d, dv, st);
+    return bf16 ? decode_t<bf16_t>(flags, q, k, v, out, S, z, BH, d, dv, gamma, H, st)
+                : decode_t<float>(flags, q, k, v, out, S, z, BH, d, dv, gamma, H, st);
 }
 
 } // namespace la

@@ -11,7 +11,10 @@
 // state", grouped by chunk. With causal = false the kernel is the global read
 // out_i = Qf_i^T S / Qf_i . z of section "The associativity trick, written out".
 // Flags: F_IDENTITY takes q and k as the features themselves; F_UNNORM stores num_i (no
-// division).
+// division). With a per-head decay gamma (causal only; the retention recurrence
+// S_t = gamma S_{t-1} + Kf_t V_t^T), A[i][j] carries gamma^(i - j), the carried S and z reach
+// row i scaled by gamma^(i + 1), and the update is S = gamma^n S + sum_j gamma^(n - 1 - j)
+// Kf_j V_j^T over the chunk's n tokens.
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -42,7 +45,8 @@ __global__ __launch_bounds__(NT) void k_agg_valu(const T *__restrict__ k, const 
                                                  float *__restrict__ dstS,
                                                  float *__restrict__ dstz, long sstride,
                                                  long zstride, int N, int d, int dv, int ch,
-                                                 int L, int nseg, int P, int flags)
+                                                 int L, int nseg, int P, int flags,
+                                                 const float *__restrict__ gamma, int H)
 {
     const bool ident = flags & F_IDENTITY;
     extern __shared__ float sm[];
@@ -53,6 +57,7 @@ __global__ __launch_bounds__(NT) void k_agg_valu(const T *__restrict__ k, const 
     const int tb = p * L, te = min(N, tb + L);
     const T *kb = k + (size_t)bh * N * d;
     const T *vb = v + (size_t)bh * N * dv;
+    const float lg = decay_log2(gamma, bh, H);
 
     for (int e = tid; e < d * dv; e += NT)
         sS[e] = 0.f;
@@ -70,18 +75,35 @@ __global__ __launch_bounds__(NT) void k_agg_valu(const T *__restrict__ k, const 
             sV[e] = j < nvalid ? Elem<T>::ld(vb, (size_t)(t0 + j) * dv + e % dv) : 0.f;
         }
         __syncthreads();
-        for (int e = tid; e < d * dv; e += NT) {
-            const int f = e / dv, c = e % dv;
-            float s = 0.f;
-            for (int j = 0; j < ch; ++j)
-                s += sK[j * d + f] * sV[j * dv + c];
-            sS[e] += s;
-        }
-        for (int f = tid; f < d; f += NT) {
-            float s = 0.f;
-            for (int j = 0; j < ch; ++j)
-                s += sK[j * d + f];
-            sz[f] += s;
+        if (gamma) {
+            const float fc = decay_pow(lg, nvalid);
+            for (int e = tid; e < d * dv; e += NT) {
+                const int f = e / dv, c = e % dv;
+                float s = 0.f;
+                for (int j = 0; j < nvalid; ++j)
+                    s += decay_pow(lg, nvalid - 1 - j) * sK[j * d + f] * sV[j * dv + c];
+                sS[e] = fc * sS[e] + s;
+            }
+            for (int f = tid; f < d; f += NT) {
+                float s = 0.f;
+                for (int j = 0; j < nvalid; ++j)
+                    s += decay_pow(lg, nvalid - 1 - j) * sK[j * d + f];
+                sz[f] = fc * sz[f] + s;
+            }
+        } else {
+            for (int e = tid; e < d * dv; e += NT) {
+                const int f = e / dv, c = e % dv;
+                float s = 0.f;
+                for (int j = 0; j < ch; ++j)
+                    s += sK[j * d + f] * sV[j * dv + c];
+                sS[e] += s;
+            }
+            for (int f = tid; f < d; f += NT) {
+                float s = 0.f;
+                for (int j = 0; j < ch; ++j)
+                    s += sK[j * d + f];
+                sz[f] += s;
+            }
         }
     }
     __syncthreads();
@@ -100,7 +122,8 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
                                                  long pzstride, int pslots,
                                                  float *__restrict__ Sout,
                                                  float *__restrict__ zout, int N, int d, int dv,
-                                                 int ch, int L, int P, int flags)
+                                                 int ch, int L, int P, int flags,
+                                                 const float *__restrict__ gamma, int H)
 {
     extern __shared__ float sm[];
     const bool ident = flags & F_IDENTITY, norm = !(flags & F_UNNORM);
@@ -114,6 +137,7 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
     const T *kb = CAUSAL ? k + (size_t)bh * N * d : nullptr;
     const T *vb = CAUSAL ? v + (size_t)bh * N * dv : nullptr;
     T *ob = out + (size_t)bh * N * dv;
+    const float lg = decay_log2(gamma, bh, H);
 
     const long slot = (long)bh * pslots + min(p, pslots - 1);
     const float *S0 = preS ? preS + slot * pstride : nullptr;
@@ -146,13 +170,15 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
                 if (j <= i)
                     for (int f = 0; f < d; ++f)
                         s += sQ[i * d + f] * sK[j * d + f];
-                sA[e] = s;
+                sA[e] = gamma && j <= i ? s * decay_pow(lg, i - j) : s;
             }
         __syncthreads();
         for (int i = tid; i < ch; i += NT) {
             float s = 0.f;
             for (int f = 0; f < d; ++f)
                 s += sQ[i * d + f] * sz[f];
+            if (gamma)
+                s *= decay_pow(lg, i + 1);
             if (CAUSAL)
                 for (int j = 0; j <= i; ++j)
                     s += sA[i * ch + j];
@@ -166,12 +192,30 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
             float s = 0.f;
             for (int f = 0; f < d; ++f)
                 s += sQ[i * d + f] * sS[f * dv + c];
+            if (gamma)
+                s *= decay_pow(lg, i + 1);
             if (CAUSAL)
                 for (int j = 0; j <= i; ++j)
                     s += sA[i * ch + j] * sV[j * dv + c];
             Elem<T>::st(ob, (size_t)(t0 + i) * dv + c, norm ? s / sden[i] : s);
         }
-        if (CAUSAL) {
+        if (CAUSAL && gamma) {
+            __syncthreads();
+            const float fc = decay_pow(lg, nvalid);
+            for (int e = tid; e < d * dv; e += NT) {
+                const int f = e / dv, c = e % dv;
+                float s = 0.f;
+                for (int j = 0; j < nvalid; ++j)
+                    s += decay_pow(lg, nvalid - 1 - j) * sK[j * d + f] * sV[j * dv + c];
+                sS[e] = fc * sS[e] + s;
+            }
+            for (int f = tid; f < d; f += NT) {
+                float s = 0.f;
+                for (int j = 0; j < nvalid; ++j)
+                    s += decay_pow(lg, nvalid - 1 - j) * sK[j * d + f];
+                sz[f] = fc * sz[f] + s;
+            }
+        } else if (CAUSAL) {
             __syncthreads();
             for (int e = tid; e < d * dv; e += NT) {
                 const int f = e / dv, c = e % dv;
@@ -201,7 +245,7 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
 
 hipError_t agg_valu(bool bf16, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int d, int dv, int chunk, int L,
-                    int nseg, int P, hipStream_t st)
+                    int nseg, int P, const float *gamma, int H, hipStream_t st)
 {
     const Lay lay(d, dv, chunk);
     const size_t lds = sizeof(float) * lay.total;
@@ -215,11 +259,11 @@ hipError_t agg_valu(bool bf16, int flags, const void *k, const void *v, float *d
     if (bf16)
         hipLaunchKernelGGL(k_agg_valu<bf16_t>, grid, block, lds, st, static_cast<const bf16_t *>(k),
                            static_cast<const bf16_t *>(v), dstS, dstz, sstride, zstride, N, d, dv,
-                           chunk, L, nseg, P, flags);
+                           chunk, L, nseg, P, flags, gamma, H);
     else
         hipLaunchKernelGGL(k_agg_valu<float>, grid, block, lds, st, static_cast<const float *>(k),
                            static_cast<const float *>(v), dstS, dstz, sstride, zstride, N, d, dv,
-                           chunk, L, nseg, P, flags);
+                           chunk, L, nseg, P, flags, gamma, H);
     return hipGetLastError();
 }
 
@@ -227,7 +271,7 @@ template <typename T, bool CAUSAL>
 hipError_t out_valu_t(int flags, const void *q, const void *k, const void *v, void *out, const float *preS,
                       const float *prez, long pstride, long pzstride, int pslots, float *Sout,
                       float *zout, int BH, int N, int d, int dv, int chunk, int L, int P,
-                      hipStream_t st)
+                      const float *gamma, int H, hipStream_t st)
 {
     const size_t lds = sizeof(float) * Lay(d, dv, chunk).total;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_out_valu<T, CAUSAL>),
@@ -237,19 +281,19 @@ hipError_t out_valu_t(int flags, const void *q, const void *k, const void *v, vo
     hipLaunchKernelGGL((k_out_valu<T, CAUSAL>), dim3((unsigned)(BH * P)), dim3(NT), lds, st,
                        static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), static_cast<T *>(out), preS, prez, pstride,
-                       pzstride, pslots, Sout, zout, N, d, dv, chunk, L, P, flags);
+                       pzstride, pslots, Sout, zout, N, d, dv, chunk, L, P, flags, gamma, H);
     return hipGetLastError();
 }
 
 hipError_t out_valu(bool bf16, bool causal, int flags, const void *q, const void *k, const void *v,
                     void *out, const float *preS, const float *prez, long pstride,
                     long pzstride, int pslots, float *Sout, float *zout, int BH, int N, int d,
-                    int dv, int chunk, int L, int P, hipStream_t st)
+                    int dv, int chunk, int L, int P, const float *gamma, int H, hipStream_t st)
 {
     auto f = bf16 ? (causal ? out_valu_t<bf16_t, true> : out_valu_t<bf16_t, false>)
                   : (causal ? out_valu_t<float, true> : out_valu_t<float, false>);
     return f(flags, q, k, v, out, preS, prez, pstride, pzstride, pslots, Sout, zout, BH, N, d, dv, chunk,
-             L, P, st);
+             L, P, gamma, H, st);
 }
 
 // Largest dynamic LDS the vector-ALU kernels take (d = d_v = 128, chunk 32): 118,912 bytes.

@@ -242,9 +242,26 @@ hipError_t mark(Stamps *ts, int i, hipStream_t st)
 
 bool flags_ok(int flags) { return (flags & ~(LA_PHI_IDENTITY | LA_UNNORMALIZED)) == 0; }
 
+// The decay vector: non-null, 4-byte aligned, H floats that no written buffer overlaps (sizes
+// are checked by validate; here only what the pointer itself needs, with positive sizes).
+bool gamma_ok(const float *gamma, int H, const void *out, const float *S, const float *z, int B,
+              int N, int d, int dv, int dtype)
+{
+    if (!gamma || (reinterpret_cast<uintptr_t>(gamma) & 3u) != 0)
+        return false;
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || dv <= 0)
+        return true; // validate reports the size error
+    const size_t es = dtype == LA_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * (size_t)H;
+    const Span sg = span(gamma, (size_t)H * 4);
+    return !overlap(sg, span(out, BH * N * dv * es)) && !overlap(sg, span(S, BH * d * dv * 4)) &&
+           !overlap(sg, span(z, BH * d * 4));
+}
+
+// gamma (optional): per-head decay of the carried state, device float32 [H].
 int run_causal(const void *q, const void *k, const void *v, void *out, const float *S0,
                const float *z0, float *S, float *z, int N, int d, int dv, bool bf16, int flags,
-               const Plan &pl, hipStream_t st, Stamps *ts = nullptr)
+               const float *gamma, int H, const Plan &pl, hipStream_t st, Stamps *ts = nullptr)
 {
     const int BH = (int)pl.BH, P = pl.P, L = pl.L;
     const long E = (long)d * dv + d;
@@ -257,13 +274,13 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
     if (P > 1 && e == hipSuccess) {
         // sums of segments 0..P-2, then the exclusive prefix over segments in place
         e = pl.mfma ? la::agg_mfma(d, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L,
-                                   P - 1, P, st)
+                                   P - 1, P, gamma, H, st)
                     : la::agg_valu(bf16, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N,
-                                   d, dv, pl.chunk, L, P - 1, P, st);
+                                   d, dv, pl.chunk, L, P - 1, P, gamma, H, st);
         if (e == hipSuccess)
             e = mark(ts, 1, st);
         if (e == hipSuccess)
-            e = la::seg_exclusive_scan(ws.ptr, S0, z0, BH, P, d, dv, st);
+            e = la::seg_exclusive_scan(ws.ptr, S0, z0, BH, P, d, dv, gamma, H, L, st);
         preS = ws.ptr;
         prez = ws.ptr + (long)d * dv;
         ps = pzs = E;
@@ -274,9 +291,9 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
         e = mark(ts, 2, st);
     if (e == hipSuccess)
         e = pl.mfma ? la::causal_mfma(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N, L,
-                                      P, st)
+                                      P, gamma, H, st)
                     : la::out_valu(bf16, true, flags, q, k, v, out, preS, prez, ps, pzs,
-                                   P > 1 ? P : 1, S, z, BH, N, d, dv, pl.chunk, L, P, st);
+                                   P > 1 ? P : 1, S, z, BH, N, d, dv, pl.chunk, L, P, gamma, H, st);
     if (e == hipSuccess)
         e = mark(ts, 3, st);
     return e == hipSuccess ? LA_OK : LA_EHIP;
@@ -293,20 +310,22 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
     hipError_t e;
     if (P > 1) {
         e = pl.mfma ? la::agg_mfma(d, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L,
-                                   P, P, st)
+                                   P, P, nullptr, 1, st)
                     : la::agg_valu(bf16, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N,
-                                   d, dv, pl.chunk, L, P, P, st);
+                                   d, dv, pl.chunk, L, P, P, nullptr, 1, st);
         if (e == hipSuccess)
             e = la::seg_total(ws.ptr, S, z, BH, P, d, dv, st);
     } else {
-        e = pl.mfma ? la::agg_mfma(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1, st)
+        e = pl.mfma ? la::agg_mfma(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1, nullptr,
+                                   1, st)
                     : la::agg_valu(bf16, flags, k, v, S, z, (long)d * dv, d, BH, N, d, dv,
-                                   pl.chunk, L, 1, 1, st);
+                                   pl.chunk, L, 1, 1, nullptr, 1, st);
     }
     if (e == hipSuccess && q)
         e = pl.mfma ? la::global_read_mfma(d, flags, q, out, S, z, BH, N, L, P, st)
                     : la::out_valu(bf16, false, flags, q, nullptr, nullptr, out, S, z, (long)d * dv,
-                                   d, 1, nullptr, nullptr, BH, N, d, dv, pl.chunk, L, P, st);
+                                   d, 1, nullptr, nullptr, BH, N, d, dv, pl.chunk, L, P, nullptr, 1,
+                                   st);
     return e == hipSuccess ? LA_OK : LA_EHIP;
 }
 
@@ -325,7 +344,24 @@ int la_causal_fwd_ex(const void *q, const void *k, const void *v, void *out, con
                            dtype, &pl);
     if (s != LA_OK)
         return s;
-    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, pl, stream);
+    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, nullptr, 1,
+                      pl, stream);
+}
+
+int la_causal_fwd_decay(const void *q, const void *k, const void *v, void *out, const float *S0,
+                        const float *z0, float *S, float *z, const float *gamma, int B, int H,
+                        int N, int d, int d_v, int chunk, int seg_len, int flags, la_dtype dtype,
+                        hipStream_t stream)
+{
+    if (!flags_ok(flags) || !gamma_ok(gamma, H, out, S, z, B, N, d, d_v, dtype))
+        return LA_EINVAL;
+    Plan pl;
+    const int s = validate(CAUSAL, q, k, v, out, S0, z0, S, z, B, H, N, d, d_v, chunk, seg_len,
+                           dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, gamma, H, pl,
+                      stream);
 }
 
 int la_causal_fwd_state(const void *q, const void *k, const void *v, void *out, const float *S0,
@@ -361,7 +397,7 @@ int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *ou
             return LA_EHIP;
     for (Stamps &t : ts) {
         const int r = run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags,
-                                 pl, stream, &t);
+                                 nullptr, 1, pl, stream, &t);
         if (r != LA_OK)
             return r;
     }
@@ -418,7 +454,23 @@ int la_decode_step_ex(const void *q, const void *k, const void *v, void *out, fl
     if (s != LA_OK)
         return s;
     const hipError_t e = la::decode_step(dtype == LA_BF16, flags, q, k, v, out, S, z, (int)pl.BH,
-                                         d, d_v, stream);
+                                         d, d_v, nullptr, 1, stream);
+    return e == hipSuccess ? LA_OK : LA_EHIP;
+}
+
+int la_decode_step_decay(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                         const float *gamma, int B, int H, int N, int d, int d_v, int flags,
+                         la_dtype dtype, hipStream_t stream)
+{
+    if (!flags_ok(flags) || !gamma_ok(gamma, H, out, S, z, B, N, d, d_v, dtype))
+        return LA_EINVAL;
+    Plan pl;
+    const int s = validate(DECODE, q, k, v, out, nullptr, nullptr, S, z, B, H, N, d, d_v, 0, 0,
+                           dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    const hipError_t e = la::decode_step(dtype == LA_BF16, flags, q, k, v, out, S, z, (int)pl.BH,
+                                         d, d_v, gamma, H, stream);
     return e == hipSuccess ? LA_OK : LA_EHIP;
 }
 

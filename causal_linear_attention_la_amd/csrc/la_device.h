@@ -45,6 +45,15 @@ __device__ __forceinline__ float phi_exact(float x) { return x > 0.f ? x + 1.f :
 // The feature of one element: phi_exact(x), or x itself when q and k are already features.
 __device__ __forceinline__ float feature(float x, bool identity) { return identity ? x : phi_exact(x); }
 
+// ---- decay of the carried state (the retention recurrence) -----------------------------
+// log2 of the decay gamma of head bh % H (0 when gamma is null: no decay), clamped to -1000 so
+// that gamma = 0 gives gamma^0 = 1 and gamma^n = 0 for n > 0 through exp2 without infinities.
+__device__ __forceinline__ float decay_log2(const float *gamma, long bh, int H)
+{
+    return gamma ? fmaxf(log2f(gamma[bh % H]), -1000.f) : 0.f;
+}
+__device__ __forceinline__ float decay_pow(float lg, int n) { return exp2f(lg * (float)n); }
+
 // ---- generic element access for the vector-ALU kernels -----------------------------------
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -18,15 +18,18 @@ constexpr int F_UNNORM = 2;   // out = phi(q)^T S, no division by phi(q)^T z
 // ---- matrix-core family: bf16, d == d_v in {64, 128}, chunk 64 ---------------------------
 // Segment sums dS = phi(K_seg)^T V_seg, dz = phi(K_seg)^T 1 of segments p < nseg of every
 // head, written to dstS + (bh * P + p) * sstride and dstz + (bh * P + p) * zstride.
+// gamma (optional, device [H] float32): per-head decay of the carried state; the sums are then
+// decayed to each segment's last token.
 hipError_t agg_mfma(int D, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int L, int nseg, int P,
-                    hipStream_t st);
+                    const float *gamma, int H, hipStream_t st);
 // Causal outputs of all P segments. Segment p starts from the state at preS/prez +
 // (bh * P + p) * stride (zero state if preS is null). The last segment writes the final
 // state to Sout/zout when they are non-null.
 hipError_t causal_mfma(int D, int flags, const void *q, const void *k, const void *v, void *out,
                        const float *preS, const float *prez, long pstride, long pzstride,
-                       float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st);
+                       float *Sout, float *zout, int BH, int N, int L, int P, const float *gamma,
+                       int H, hipStream_t st);
 // Global read: out = phi(Q) S / phi(Q) z for every token, S/z per head ([BH, D, D], [BH, D]).
 hipError_t global_read_mfma(int D, int flags, const void *q, void *out, const float *S,
                             const float *z, int BH, int N, int L, int P, hipStream_t st);
@@ -34,23 +37,25 @@ hipError_t global_read_mfma(int D, int flags, const void *q, void *out, const fl
 // ---- vector-ALU family: any d, d_v in {16, 32, 64, 128}, float32 or bf16, chunk 16/32 ----
 hipError_t agg_valu(bool bf16, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int d, int dv, int chunk, int L,
-                    int nseg, int P, hipStream_t st);
+                    int nseg, int P, const float *gamma, int H, hipStream_t st);
 // Segment p of head bh starts from the state in slot bh * pslots + min(p, pslots - 1) of
 // preS/prez (zero state if preS is null). causal = false gives the global read (pslots = 1:
 // every segment reads the head's full state; nothing is updated).
 hipError_t out_valu(bool bf16, bool causal, int flags, const void *q, const void *k, const void *v,
                     void *out, const float *preS, const float *prez, long pstride,
                     long pzstride, int pslots, float *Sout, float *zout, int BH, int N, int d,
-                    int dv, int chunk, int L, int P, hipStream_t st);
+                    int dv, int chunk, int L, int P, const float *gamma, int H, hipStream_t st);
 
 // Dynamic LDS bytes of the vector-ALU kernels for this shape.
 size_t valu_lds_bytes(int d, int dv, int chunk);
 
 // ---- segment joins -----------------------------------------------------------------------
 // In place: slots 0..P-2 hold segment sums on entry; on return slot p (0..P-1) holds the
-// state before segment p (the sum of earlier segments plus the optional initial state).
+// state before segment p (the sum of earlier segments plus the optional initial state). With a
+// decay gamma (device [H]) the running state is scaled by gamma^L before each segment's sum is
+// added (all scanned segments hold L tokens).
 hipError_t seg_exclusive_scan(float *ws, const float *S0, const float *z0, int BH, int P,
-                              int d, int dv, hipStream_t st);
+                              int d, int dv, const float *gamma, int H, int L, hipStream_t st);
 // S, z = sum of the P slots (fixed order p = 0..P-1).
 hipError_t seg_total(const float *ws, float *S, float *z, int BH, int P, int d, int dv,
                      hipStream_t st);
@@ -66,6 +71,7 @@ hipError_t rf_features(bool bf16, const void *x, const void *W, void *f, long ro
 
 // ---- decode ------------------------------------------------------------------------------
 hipError_t decode_step(bool bf16, int flags, const void *q, const void *k, const void *v, void *out,
-                       float *S, float *z, int BH, int d, int dv, hipStream_t st);
+                       float *S, float *z, int BH, int d, int dv, const float *gamma, int H,
+                       hipStream_t st);
 
 } // namespace la

@@ -82,6 +82,12 @@ def positive(shape, seed: int, scale: float = 1.0, dtype: str = "bf16", floor: f
     return torch.from_numpy(x).to(DTYPES[dtype])
 
 
+def decay_rates(H: int) -> torch.Tensor:
+    """Per-head decays for the decayed recurrence, one per head on a multi-scale ladder:
+    gamma_h = 1 - 2^-(5 + h) (0.96875 for head 0, closer to 1 for each later head), float32."""
+    return torch.tensor([1.0 - 2.0 ** -(5 + h) for h in range(H)], dtype=torch.float32)
+
+
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 copy of a bf16/fp32 tensor (both embed exactly in float64)."""
     return t.detach().to("cpu").to(torch.float64).numpy()
@@ -127,3 +133,7 @@ WORKLOADS = {
 # features.
 RF_WORKLOAD = {"name": "favor_causal_b2h16n8192_d128_m128_bf16", "base": 3, "m": 128,
                "seed": 1006}
+
+# The decayed recurrence in its retention form (identity map, no denominator) over the causal
+# workload's inputs, per-head decays from decay_rates(16).
+DECAY_WORKLOAD = {"name": "retention_causal_b2h16n8192_d128_bf16", "base": 3}

@@ -131,6 +131,28 @@ int la_causal_fwd_ex(const void *q, const void *k, const void *v, void *out, con
                      int chunk, int seg_len, int flags, la_dtype dtype, hipStream_t stream);
 
 /*
+ * Causal prefill with a per-head decay of the carried state, the retention recurrence of
+ * "Linear Attention Math", section "Cousins: RetNet, Mamba, RWKV" (linear attention plus an
+ * explicit decay gamma < 1 of the state, scalar or per head):
+ *     S_i = gamma_h S_{i-1} + phi(k_i) v_i^T,   z_i = gamma_h z_{i-1} + phi(k_i),
+ *     out_i = phi(q_i)^T S_i / phi(q_i)^T z_i    (LA_UNNORMALIZED: phi(q_i)^T S_i)
+ * RetNet's retention as stated there is flags = LA_PHI_IDENTITY | LA_UNNORMALIZED (its gated
+ * normalisation is a separate learned layer, not part of this call). Equivalently, token j
+ * reaches the read of token i with weight gamma^(i - j) (the parallel form); the chunked
+ * evaluation applies that mask within a chunk and gamma^(i + 1 - t0) to the carried state.
+ *   gamma  device memory, H float32 values (one per head, shared by the batch), 4-byte
+ *          aligned, read only; values in [0, 1] (0 keeps only the current token, 1 is
+ *          la_causal_fwd_ex). Values are not inspected on the host; one above 1 can overflow.
+ *          NULL, misaligned, or overlapping out, S or z: LA_EINVAL.
+ * Every other argument, the layout, ownership and errors as for la_causal_fwd_ex (S0, z0: the
+ * state before token 0; S, z: the state after token N-1, both in the decayed recurrence).
+ */
+int la_causal_fwd_decay(const void *q, const void *k, const void *v, void *out, const float *S0,
+                        const float *z0, float *S, float *z, const float *gamma, int B, int H,
+                        int N, int d, int d_v, int chunk, int seg_len, int flags, la_dtype dtype,
+                        hipStream_t stream);
+
+/*
  * Global (non-causal): S = phi(K)^T V and z = phi(K)^T 1 per (b, h) over all N tokens, then
  * out[b,h,i] = phi(q_i)^T S / phi(q_i)^T z for every token.
  *   S, z   required; written (not read) with the full-sequence state.
@@ -164,6 +186,15 @@ int la_decode_step(const void *q, const void *k, const void *v, void *out, float
 int la_decode_step_ex(const void *q, const void *k, const void *v, void *out, float *S, float *z,
                       int B, int H, int N, int d, int d_v, int flags, la_dtype dtype,
                       hipStream_t stream);
+
+/*
+ * One decode step of the decayed recurrence (as for la_causal_fwd_decay): S <- gamma_h S +
+ * phi(k) v^T, z <- gamma_h z + phi(k), then the read. gamma as for la_causal_fwd_decay; the
+ * other arguments as for la_decode_step_ex.
+ */
+int la_decode_step_decay(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                         const float *gamma, int B, int H, int N, int d, int d_v, int flags,
+                         la_dtype dtype, hipStream_t stream);
 
 /*
  * Profiling form of la_causal_fwd_ex: the same call enqueued `reps` times back to back on

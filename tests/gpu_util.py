@@ -67,3 +67,19 @@ def check(name, got, want, tol):
     assert r["nonfinite"] == 0, name
     assert r["row_max"] <= tol, (name, r)
     return r
+
+
+def check_bounded(name, got, want, bound, tol):
+    """Forward-error check for sums of signed terms: per row (last axis), the largest error is
+    compared with the largest entry of `bound`, the same sum taken over absolute values (the
+    scale every rounding error is proportional to). Used where a row's terms may cancel, so
+    that the row itself can be far smaller than the terms that make it up."""
+    got, want, bound = (np.asarray(x, dtype=np.float64) for x in (got, want, bound))
+    assert got.shape == want.shape == bound.shape, (got.shape, want.shape, bound.shape)
+    err = np.abs(got - want).max(axis=-1)
+    scale = np.maximum(bound.max(axis=-1), np.finfo(np.float64).tiny)
+    r = float((err / scale).max()) if err.size else 0.0
+    say(f"  {name}: bounded row_max={r:.3e} nonfinite={int((~np.isfinite(got)).sum())} tol={tol:g}")
+    assert np.all(np.isfinite(got)), name
+    assert r <= tol, (name, r)
+    return r

@@ -114,6 +114,30 @@ def test_flag_checks(fn):
         assert call(fn, N=N, flags=ok, d=48) == la.LA_ENOTSUP
 
 
+def decay(fn, q=A, k=2 * A, v=3 * A, out=4 * A, S=5 * A, z=6 * A, gamma=7 * A, B=1, H=2, N=8,
+          d=16, dv=16, flags=0, dtype=la.LA_BF16):
+    f = getattr(la.lib, fn)
+    if fn == "la_causal_fwd_decay":
+        return f(q, k, v, out, S, z, S, z, gamma, B, H, N, d, dv, 0, 0, flags, dtype, None)
+    return f(q, k, v, out, S, z, gamma, B, H, 1 if N == 8 else N, d, dv, flags, dtype, None)
+
+
+@pytest.mark.parametrize("fn", ["la_causal_fwd_decay", "la_decode_step_decay"])
+def test_decay_argument_checks(fn):
+    assert decay(fn, gamma=None) == la.LA_EINVAL
+    assert decay(fn, gamma=7 * A + 2) == la.LA_EINVAL           # not 4-byte aligned
+    assert decay(fn, gamma=4 * A + 32) == la.LA_EINVAL          # inside out (64 bytes at N = 1)
+    assert decay(fn, gamma=5 * A) == la.LA_EINVAL               # inside S
+    assert decay(fn, gamma=6 * A + 4) == la.LA_EINVAL           # inside z
+    assert decay(fn, flags=4) == la.LA_EINVAL
+    assert decay(fn, k=None) == la.LA_EINVAL
+    assert decay(fn, B=0) == la.LA_EINVAL
+    assert decay(fn, d=48) == la.LA_ENOTSUP
+    assert decay(fn, out=A + 16) == la.LA_EINVAL                # out overlaps q
+    if fn == "la_decode_step_decay":
+        assert decay(fn, N=2) == la.LA_EINVAL
+
+
 def rf(x=A, W=2 * A, f=3 * A, rows=64, d=64, m=128, dtype=la.LA_BF16):
     return la.lib.la_rf_features(x, W, f, rows, d, m, dtype, None)
 
