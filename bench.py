@@ -462,7 +462,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
-                     "kernel": "k_causal<128> (causal outputs + final state; reads q, k, v and "
+                     "kernel": "k_causal<128, 0, false> (causal outputs + final state; reads q, k, v and "
                                "the segment prefix states, writes out and S, z)",
                      "kernel_us": kern_ms[2] * 1e3,
                      "algorithmic_bytes_per_launch": byts,

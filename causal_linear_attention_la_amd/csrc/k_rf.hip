@@ -9,11 +9,16 @@
 // the library draws no random numbers.
 //
 // Matrix-core kernel (bf16, d in {64, 128}, m in {64, 128, 256}): the dots W x_i are one
-// [m x d] x [d x rows] product. Wave w of a 4-wave workgroup keeps the bf16 fragments of its
-// m/4 projections in registers for the whole launch and sweeps blocks of 64 rows; the x rows are
-// read straight from HBM as the B operand (lane li reads row li, 16 bytes per k block), so no
-// LDS is needed. |x_i|^2 is summed in float32 from the same registers. The exponent runs as
-// exp2 with log2(e) folded into one fused multiply-add per feature.
+// [m x d] x [d x rows] product. Each workgroup copies W into LDS once, in fragment order (the
+// 16 bytes lane l reads for projection tile mt and k block kk sit at ((mt * NKB + kk) * 64 + l)
+// * 16, so every operand read is one contiguous, conflict-free 1 KiB). The projections are
+// placed in the tiles so that lane group g of the product holds features (m/4) g .. (m/4) g +
+// m/4 - 1 of its row: two tiles give 8 consecutive features, one 16-byte store. Each wave then
+// sweeps tiles of 16 rows: it reads the rows straight from HBM as the B operand (lane li reads
+// row li, 16 bytes per k block; the next tile is loaded while the current one is computed), so
+// every row is read from HBM once and by one wave, and computes all m features of its rows.
+// |x_i|^2 is summed in float32 from the same registers. The exponent runs as exp2 with log2(e)
+// folded into one fused multiply-add per feature.
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -21,8 +26,6 @@
 
 namespace la {
 namespace {
-
-constexpr int RB = 64; // rows per block of the sweep
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
 {
@@ -36,66 +39,80 @@ __global__ __launch_bounds__(256) void k_rf_mfma(const uint16_t *__restrict__ x,
                                                  float neg_half_log2m)
 {
     constexpr int NKB = D / 32;     // k blocks of 32 features
-    constexpr int MT = M / 64;      // 16-projection tiles per wave
+    constexpr int MT = M / 16;      // 16-projection tiles
     constexpr float LOG2E = 1.44269504088896341f;
-    const int l = threadIdx.x & 63, li = l & 15, g = l >> 4;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int f0 = w * (M / 4);
+    __shared__ __attribute__((aligned(16))) uint16_t sW[M * D];
+    const int tid = threadIdx.x, l = tid & 63, li = l & 15, g = l >> 4;
 
-    // A operand: projection row f0 + 16 mt + li, k-slots 8g..8g+7 of block kk
-    bf16x8 wa[MT][NKB];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    const long ntile = (rows + 15) / 16;
+    const long nwave = (long)gridDim.x * 4;
+    const long w0 = (long)blockIdx.x * 4 + (tid >> 6);
+    // B operand of a 16-row tile: row 16 t + li (clamped to the last row: every load is in
+    // bounds), k-slots 8g..8g+7 of block kk
+    auto load = [&](u32x4 (&dst)[NKB], long t) {
+        const long r = min(16 * t + li, rows - 1);
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk)
-            wa[mt][kk] = *reinterpret_cast<const bf16x8 *>(W + (size_t)(f0 + 16 * mt + li) * D + 32 * kk + 8 * g);
+            dst[kk] = *reinterpret_cast<const u32x4 *>(x + r * D + 32 * kk + 8 * g);
+    };
+    u32x4 xb[NKB], xn[NKB];
+    load(xb, min(w0, ntile - 1));
+    // W (row-major [M][D]) -> LDS in fragment order: granule (row r, columns 8c..8c+7) is lane
+    // (c % 4) * 16 + (row of r in its tile) of fragment (tile of r, kk = c / 4)
+    for (int e = tid; e < M * D / 8; e += 256) {
+        const int r = e / (D / 8), c = e % (D / 8);
+        // projection r = (M/4) g + 4 mt + j sits in row 4g + j of tile mt, so that lane group g
+        // of the product holds the M/4 consecutive features (M/4) g .. of its row
+        const int gq = r / (M / 4), mt = (r % (M / 4)) / 4, j = r % 4;
+        const int frag = mt * NKB + c / 4, lane = (c % 4) * 16 + 4 * gq + j;
+        *reinterpret_cast<u32x4 *>(sW + (frag * 64 + lane) * 8) =
+            *reinterpret_cast<const u32x4 *>(W + (size_t)r * D + 8 * c);
+    }
+    __syncthreads();
 
-    const long nblk = (rows + RB - 1) / RB;
-    for (long blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
-        const long r0 = blk * RB;
-        // B operand of the four 16-row tiles: row r0 + 16s + li (clamped to the last row, so
-        // every load is in bounds), k-slots 8g..8g+7 of block kk
-        u32x4 xb[4][NKB];
+    for (long t = w0; t < ntile; t += nwave) {
+        load(xn, min(t + nwave, ntile - 1)); // next tile (a re-read of the last one at the end)
+        float n = 0.f;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const long r = min(r0 + 16 * s + li, rows - 1);
+        for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < NKB; ++kk)
-                xb[s][kk] = *reinterpret_cast<const u32x4 *>(x + r * D + 32 * kk + 8 * g);
-        }
+            for (int h = 0; h < 4; ++h) {
+                const float a = bf_lo(xb[kk][h]), b = bf_hi(xb[kk][h]);
+                n = fmaf(a, a, n);
+                n = fmaf(b, b, n);
+            }
+        n += __shfl_xor(n, 16, 64);
+        n += __shfl_xor(n, 32, 64);
+        // exponent in base 2: (dot - n / 2) log2(e) - log2(m) / 2
+        const float bias = fmaf(-0.5f * LOG2E, n, neg_half_log2m);
+        const long r = 16 * t + li;
+        // two projection tiles per step: enough independent work per wave without holding
+        // every W fragment in registers at once
+#pragma unroll 1
+        for (int s = 0; s < MT / 2; ++s) {
+            uint32_t o[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            float n = 0.f;
-#pragma unroll
-            for (int kk = 0; kk < NKB; ++kk)
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const float a = bf_lo(xb[s][kk][h]), b = bf_hi(xb[s][kk][h]);
-                    n = fmaf(a, a, n);
-                    n = fmaf(b, b, n);
-                }
-            n += __shfl_xor(n, 16, 64);
-            n += __shfl_xor(n, 32, 64);
-            // exponent in base 2: (dot - n / 2) log2(e) - log2(m) / 2
-            const float bias = fmaf(-0.5f * LOG2E, n, neg_half_log2m);
-            const long r = r0 + 16 * s + li;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
+            for (int h = 0; h < 2; ++h) {
+                const int mt = 2 * s + h;
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < NKB; ++kk)
-                    c = mfma16(wa[mt][kk], __builtin_bit_cast(bf16x8, xb[s][kk]), c);
-                // c[j] = w_{f0 + 16 mt + 4g + j} . x_r
+                    c = mfma16(*reinterpret_cast<const bf16x8 *>(sW + ((mt * NKB + kk) * 64 + l) * 8),
+                               __builtin_bit_cast(bf16x8, xb[kk]), c);
+                // c[j] = w_{(M/4) g + 4 mt + j} . x_r
                 float e[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     e[j] = __builtin_amdgcn_exp2f(fmaf(c[j], LOG2E, bias));
-                if (r < rows) {
-                    const u32x2 o = {pack_bf2(e[0], e[1]), pack_bf2(e[2], e[3])};
-                    *reinterpret_cast<u32x2 *>(f + r * M + f0 + 16 * mt + 4 * g) = o;
-                }
+                o[2 * h] = pack_bf2(e[0], e[1]);
+                o[2 * h + 1] = pack_bf2(e[2], e[3]);
             }
+            if (r < rows)
+                *reinterpret_cast<u32x4 *>(f + r * M + (M / 4) * g + 8 * s) = u32x4{o[0], o[1], o[2], o[3]};
         }
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk)
+            xb[kk] = xn[kk];
     }
 }
 
@@ -140,8 +157,13 @@ __global__ __launch_bounds__(256) void k_rf_generic(const T *__restrict__ x, con
 template <int D, int M>
 void launch_rf(const void *x, const void *W, void *f, long rows, hipStream_t st)
 {
-    const long nblk = (rows + RB - 1) / RB;
-    const unsigned grid = (unsigned)(nblk < 2048 ? nblk : 2048);
+    // workgroups: two per CU (one when W takes more than 32 KiB of LDS). Every workgroup copies
+    // W from L2 first, all at the same time; measured on MI355X (d = m = 128), more workgroups
+    // than this make the copies cost more than the extra waves bring.
+    const long ntile = (rows + 15) / 16;
+    const long cap = 256L * (M * D * 2 > 32768 ? 1 : 2);
+    const long want = (ntile + 3) / 4;
+    const unsigned grid = (unsigned)(want < cap ? want : cap);
     hipLaunchKernelGGL((k_rf_mfma<D, M>), dim3(grid), dim3(256), 0, st,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(W),
                        static_cast<uint16_t *>(f), rows, -0.5f * log2f((float)M));
