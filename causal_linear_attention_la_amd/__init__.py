@@ -15,6 +15,8 @@ The entry points keep the C names:
                         seg_len=0, flags=0)            # per-head decay gamma [H] (retention)
     la_decode_step_decay(q, k, v, out, S, z, gamma, flags=0)
     la_rf_features(x, W, f)                            # positive random features
+    la_causal_fwd_rf(q, k, v, out, W, S0=None, z0=None, S=None, z=None, chunk=0, seg_len=0,
+                     flags=0)                          # causal over random features of q, k
 with q, k [B,H,N,d], v, out [B,H,N,d_v] (bf16 or float32, contiguous, on the GPU),
 S [B,H,d,d_v] and z [B,H,d] float32; flags is a bitwise or of LA_PHI_IDENTITY and
 LA_UNNORMALIZED. A non-zero status raises ``LAError``.
@@ -46,7 +48,7 @@ LA_PHI_IDENTITY, LA_UNNORMALIZED = 1, 2
 EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
            "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
            "la_decode_step_ex", "la_causal_fwd_decay", "la_decode_step_decay", "la_rf_features",
-           "la_workspace_bytes", "la_strerror", "la_version")
+           "la_causal_fwd_rf", "la_workspace_bytes", "la_strerror", "la_version")
 
 
 class LAError(RuntimeError):
@@ -75,9 +77,11 @@ def _load(path: Path):
     lib.la_rf_features.argtypes = [vp, vp, vp, ctypes.c_long, i, i, i, vp]
     lib.la_causal_fwd_decay.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp] + [i] * 9 + [vp]
     lib.la_decode_step_decay.argtypes = [vp, vp, vp, vp, fp, fp, fp] + [i] * 7 + [vp]
+    lib.la_causal_fwd_rf.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, fp] + [i] * 10 + [vp]
     for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
               "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
-              "la_decode_step_ex", "la_rf_features", "la_causal_fwd_decay", "la_decode_step_decay"):
+              "la_decode_step_ex", "la_rf_features", "la_causal_fwd_decay", "la_decode_step_decay",
+              "la_causal_fwd_rf"):
         getattr(lib, f).restype = ctypes.c_int
     lib.la_workspace_bytes.argtypes = [i] * 8 + [i]
     lib.la_workspace_bytes.restype = ctypes.c_size_t
@@ -266,6 +270,22 @@ def la_decode_step_decay(q, k, v, out, S, z, gamma, flags: int = 0):
     st = lib.la_decode_step_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z),
                                   _ptr(gamma), B, H, N, d, dv, flags, _dtype_code(k), _stream(k))
     _check(st, "la_decode_step_decay")
+    return out
+
+
+def la_causal_fwd_rf(q, k, v, out, W, S0=None, z0=None, S=None, z=None, chunk: int = 0,
+                     seg_len: int = 0, flags: int = 0):
+    """Causal prefill over positive random features of q and k (projections W [m, d]); the
+    state S [B,H,m,d_v], z [B,H,m] as for la_causal_fwd_state."""
+    _check_tensors(q, k, v, out, W, S0, z0, S, z)
+    B, H, N, d, dv = _dims(q, k, v)
+    m = W.shape[0]
+    if W.dim() != 2 or W.shape[1] != d or W.dtype != k.dtype:
+        raise ValueError(f"W must be [m, {d}] of the input dtype")
+    st = lib.la_causal_fwd_rf(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(W), _ptr(S0), _ptr(z0),
+                              _ptr(S), _ptr(z), B, H, N, d, dv, m, chunk, seg_len, flags,
+                              _dtype_code(k), _stream(k))
+    _check(st, "la_causal_fwd_rf")
     return out
 
 

@@ -181,6 +181,121 @@ template <int D, int NTH = NT> struct Tile {
     }
 };
 
+// ---- positive random features in the staging ------------------------------------------
+// The random-feature form maps q and k while they are staged: f_r(x) = exp(w_r . x - |x|^2 / 2)
+// / sqrt(D) for D projections w_r (W bf16 [D][D], m = d = D; "Linear Attention Math", section
+// "Feature maps: elu+1 and positive random features"). A staging wave takes 16 rows of a
+// chunk as matrix-core B operands straight from HBM, multiplies them by W held in LDS and
+// writes the bf16 features into the chunk array, where the attention reads them as it reads
+// phi(Q), phi(K). The work of one chunk of Q (or K) is 4 row tiles x 2 feature halves.
+template <int D> struct Rf {
+    static constexpr int NKB = D / 32; // k blocks of 32 input features
+    static constexpr int TPH = D / 32; // 16-projection tiles per feature half
+    static constexpr int GF = D / 8;   // consecutive features one lane group holds in a half
+};
+
+// W -> LDS in matrix-core fragment order (the 16 bytes lane l reads for tile mt, k block kk
+// sit at ((mt * NKB + kk) * 64 + l) * 16: contiguous, conflict-free 1 KiB reads), with the
+// projections placed so that in the product for half h lane group g holds features
+// h D/2 + g D/8 .. + D/8 - 1 of its row: projection h D/2 + g D/8 + 4t + j is row 4g + j of tile
+// h TPH + t.
+template <int D, int NTH>
+__device__ __forceinline__ void rf_put_w(uint16_t *sW, const uint16_t *__restrict__ W, int tid)
+{
+    using R = Rf<D>;
+    for (int e = tid; e < D * D / 8; e += NTH) {
+        const int p = e / (D / 8), c = e % (D / 8);
+        const int h = p / (D / 2), rem = p % (D / 2);
+        const int gq = rem / R::GF, t = (rem % R::GF) / 4, j = p % 4;
+        const int frag = (h * R::TPH + t) * R::NKB + c / 4, lane = (c % 4) * 16 + 4 * gq + j;
+        sts<u32x4>(sW + (frag * 64 + lane) * 8,
+                   *reinterpret_cast<const u32x4 *>(W + (size_t)p * D + 8 * c));
+    }
+}
+
+// Rows 16 rt + li of the chunk at `chunk` (clamped to its last valid row, so every load is in
+// bounds) as B operands: k-slots 8g..8g+7 of k block kk.
+template <int D>
+__device__ __forceinline__ void rf_load(u32x4 (&x)[D / 32], const uint16_t *chunk, int rt, int nvalid,
+                                        int li, int g)
+{
+    const uint32_t r = (uint32_t)min(16 * rt + li, nvalid - 1);
+    const char *b = reinterpret_cast<const char *>(chunk);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        x[kk] = *reinterpret_cast<const u32x4 *>(b + (r * (uint32_t)(2 * D) + 64u * kk + 16u * g));
+}
+
+// Features of half h of rows 16 rt + li into the chunk array s (rows >= nvalid become 0).
+template <int D>
+__device__ __forceinline__ void rf_put(uint16_t *s, const uint16_t *sW, const u32x4 (&x)[D / 32],
+                                       int rt, int h, int nvalid, int l, int li, int g)
+{
+    using R = Rf<D>;
+    constexpr float LOG2E = 1.44269504088896341f;
+    constexpr float NEG_HALF_LOG2M = D == 128 ? -3.5f : -3.0f; // -log2(sqrt(D))
+    float n = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < R::NKB; ++kk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float a = bf_lo(x[kk][i]), b = bf_hi(x[kk][i]);
+            n = fmaf(a, a, n);
+            n = fmaf(b, b, n);
+        }
+    n += __shfl_xor(n, 16, 64);
+    n += __shfl_xor(n, 32, 64);
+    // exponent in base 2: (w . x - |x|^2 / 2) log2(e) - log2(D) / 2
+    const float bias = fmaf(-0.5f * LOG2E, n, NEG_HALF_LOG2M);
+    const int row = 16 * rt + li;
+    const bool ok = row < nvalid;
+    // the half's TPH tiles as independent accumulation chains, interleaved over k blocks
+    f32x4 c[R::TPH];
+#pragma unroll
+    for (int t = 0; t < R::TPH; ++t)
+        c[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < R::NKB; ++kk) {
+        bf16x8 wa[R::TPH];
+#pragma unroll
+        for (int t = 0; t < R::TPH; ++t)
+            wa[t] = lds<bf16x8>(sW + (((h * R::TPH + t) * R::NKB + kk) * 64 + l) * 8);
+#pragma unroll
+        for (int t = 0; t < R::TPH; ++t)
+            c[t] = mfma(wa[t], __builtin_bit_cast(bf16x8, x[kk]), c[t]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < R::TPH / 2; ++s2) {
+        uint32_t o[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            float e[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                e[j] = __builtin_amdgcn_exp2f(fmaf(c[2 * s2 + hh][j], LOG2E, bias));
+            o[2 * hh] = pack_bf2(e[0], e[1]);
+            o[2 * hh + 1] = pack_bf2(e[2], e[3]);
+        }
+        sts<u32x4>(s + nix<D>(row, h * (D / 2) + g * R::GF + 8 * s2),
+                   ok ? u32x4{o[0], o[1], o[2], o[3]} : u32x4{0u, 0u, 0u, 0u});
+    }
+}
+
+// The staging work of one wave for a chunk of Q or K: its row tile (wave % 4) and its feature
+// half (NW = 8 staging waves: wave / 4) or both halves (NW = 4).
+template <int D, int NW>
+__device__ __forceinline__ void rf_put_share(uint16_t *s, const uint16_t *sW, const u32x4 (&x)[D / 32],
+                                             int sw, int nvalid, int l)
+{
+    const int li = l & 15, g = l >> 4;
+    if (NW == 8) {
+        rf_put<D>(s, sW, x, sw & 3, sw >> 2, nvalid, l, li, g);
+    } else {
+        rf_put<D>(s, sW, x, sw & 3, 0, nvalid, l, li, g);
+        rf_put<D>(s, sW, x, sw & 3, 1, nvalid, l, li, g);
+    }
+}
+
 // An offset hidden from the compiler. The 8-byte state-read pieces of one lane sit 32 or 64
 // bytes apart; with their offsets visible the compiler merges them into ds_read2_b64, which
 // gfx950 serves with bank conflicts that separate 8-byte reads do not have. Reads off distinct
@@ -384,19 +499,20 @@ template <int D> struct AggCfg {
     static constexpr int THREADS = NW * 64;
 };
 
-template <int D, bool PHI, bool DECAY>
+template <int D, bool PHI, bool DECAY, bool RF>
 __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__restrict__ k,
                                                            const uint16_t *__restrict__ v,
                                                            float *__restrict__ dstS,
                                                            float *__restrict__ dstz, long sstride,
                                                            long zstride, int N, int L, int nseg,
                                                            int P, const float *__restrict__ gamma,
-                                                           int H)
+                                                           int H, const uint16_t *__restrict__ W)
 {
     using K = Cfg<D>;
     using TL = Tile<D, AggCfg<D>::THREADS>;
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][K::AS];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][K::AS];
+    __shared__ __attribute__((aligned(16))) uint16_t sW[RF ? D * D : 8];
 
     const int tid = threadIdx.x, w = wave_id(), l = tid & 63, li = l & 15, g = l >> 4;
     const int p = blockIdx.x % nseg, bh = blockIdx.x / nseg;
@@ -414,14 +530,32 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
     f32x4 zacc[1];
     zero_acc<D, 1, 1>(sacc, zacc);
 
-    u32x4 rk[TL::TM], rv[TL::TM];
-    tile.load(rk, kb + (size_t)tb * D, te - tb);
+    // K staging: phi (or as given) through the tile map, or random features (RF) with each
+    // wave taking its row tile and feature half of every chunk
+    u32x4 rk[RF ? D / 32 : TL::TM], rv[TL::TM];
+    auto load_k = [&](const uint16_t *base, int nvalid) {
+        if constexpr (RF)
+            rf_load<D>(rk, base, w & 3, nvalid, li, g);
+        else
+            tile.load(rk, base, nvalid);
+    };
+    auto put_k = [&](uint16_t *dst, int nvalid) {
+        if constexpr (RF)
+            rf_put_share<D, AggCfg<D>::NW>(dst, sW, rk, w, nvalid, l);
+        else
+            tile.store(dst, rk, nvalid, PHI);
+    };
+    if (RF) {
+        rf_put_w<D, AggCfg<D>::THREADS>(sW, W, tid);
+        __syncthreads();
+    }
+    load_k(kb + (size_t)tb * D, te - tb);
     tile.load(rv, vb + (size_t)tb * D, te - tb);
-    tile.store(sK[0], rk, te - tb, PHI);
+    put_k(sK[0], te - tb);
     tile.store(sV[0], rv, te - tb, false);
     {
         const int tn = chunk_t0(1);
-        tile.load(rk, kb + (size_t)tn * D, te - tn);
+        load_k(kb + (size_t)tn * D, te - tn);
         tile.load(rv, vb + (size_t)tn * D, te - tn);
     }
     __syncthreads();
@@ -429,12 +563,12 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
         const int b = c & 1, nb = b ^ 1;
         if (c + 1 < nch) {
             const int n1 = min(C, te - (tb + (c + 1) * C));
-            tile.store(sK[nb], rk, n1, PHI);
+            put_k(sK[nb], n1);
             tile.store(sV[nb], rv, n1, false);
         }
         {
             const int tn = chunk_t0(c + 2);
-            tile.load(rk, kb + (size_t)tn * D, te - tn);
+            load_k(kb + (size_t)tn * D, te - tn);
             tile.load(rv, vb + (size_t)tn * D, te - tn);
         }
         if (DECAY) {
@@ -666,26 +800,43 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
 
 // Stage role (the NSW waves after the compute waves, thread index ht). Same barrier sequence
 // as the compute role. PHI = false stages q and k as given (already mapped features).
-template <int D, bool PHI>
-__device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs &a, int ht)
+template <int D, bool PHI, bool RF>
+__device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const uint16_t *sW, const CausalArgs &a,
+                                             int ht)
 {
     using TL = Tile<D, CausalCfg<D>::STAGE_THREADS>;
+    constexpr int NSW = CausalCfg<D>::NSW;
     const TL tile(ht);
-    u32x4 rq[TL::TM], rk[TL::TM], rv[TL::TM];
+    // q and k in the tile map (phi or as given), or as B operands of the random-feature
+    // product (RF: stage wave sw takes row tile sw % 4 and its feature half)
+    u32x4 rq[RF ? D / 32 : TL::TM], rk[RF ? D / 32 : TL::TM], rv[TL::TM];
+    const int sw = ht >> 6, l = ht & 63;
+    auto load_qk = [&](u32x4 (&r)[RF ? D / 32 : TL::TM], const uint16_t *base, int nvalid) {
+        if constexpr (RF)
+            rf_load<D>(r, base, sw & 3, nvalid, l & 15, l >> 4);
+        else
+            tile.load(r, base, nvalid);
+    };
+    auto put_qk = [&](uint16_t *dst, const u32x4 (&r)[RF ? D / 32 : TL::TM], int nvalid) {
+        if constexpr (RF)
+            rf_put_share<D, NSW>(dst, sW, r, sw, nvalid, l);
+        else
+            tile.store(dst, r, nvalid, PHI);
+    };
     const int tb = a.tb, te = a.te, nch = a.nch;
     // first token of chunk c' (clamped to the last chunk, so prefetches past the end re-read
     // it: every load is in bounds and unconditional)
     auto chunk_t0 = [&](int cc) { return tb + min(cc, nch - 1) * C; };
 
-    tile.load(rq, a.qh + (size_t)tb * D, te - tb);
-    tile.load(rk, a.kh + (size_t)tb * D, te - tb);
+    load_qk(rq, a.qh + (size_t)tb * D, te - tb);
+    load_qk(rk, a.kh + (size_t)tb * D, te - tb);
     tile.load(rv, a.vh + (size_t)tb * D, te - tb);
-    tile.store(sm.sQ[0], rq, te - tb, PHI);
-    tile.store(sm.sK[0], rk, te - tb, PHI);
+    put_qk(sm.sQ[0], rq, te - tb);
+    put_qk(sm.sK[0], rk, te - tb);
     {
         const int tn = chunk_t0(1);
-        tile.load(rq, a.qh + (size_t)tn * D, te - tn);
-        tile.load(rk, a.kh + (size_t)tn * D, te - tn);
+        load_qk(rq, a.qh + (size_t)tn * D, te - tn);
+        load_qk(rk, a.kh + (size_t)tn * D, te - tn);
     }
     __syncthreads();
 
@@ -701,18 +852,18 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
             tile.load(rv, a.vh + (size_t)tn * D, te - tn);
         }
         if (c + 1 < nch)
-            tile.store(sm.sQ[nb], rq, n1, PHI);
+            put_qk(sm.sQ[nb], rq, n1);
         {
             const int tn = chunk_t0(c + 2);
-            tile.load(rq, a.qh + (size_t)tn * D, te - tn);
+            load_qk(rq, a.qh + (size_t)tn * D, te - tn);
         }
         __syncthreads();
         // phase 2: phi(K_{c+1}) -> LDS, load K_{c+2}
         if (c + 1 < nch)
-            tile.store(sm.sK[nb], rk, n1, PHI);
+            put_qk(sm.sK[nb], rk, n1);
         {
             const int tn = chunk_t0(c + 2);
-            tile.load(rk, a.kh + (size_t)tn * D, te - tn);
+            load_qk(rk, a.kh + (size_t)tn * D, te - tn);
         }
         __syncthreads();
     }
@@ -734,15 +885,18 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const CausalArgs 
 //   --- barrier ---
 // Roles are chosen by the wave-uniform wave index, so every wave executes the same sequence of
 // barriers. F: variant flags (F_IDENTITY: q, k are already features; F_UNNORM: no denominator).
-template <int D, int F, bool DECAY>
+// RF: q and k are mapped to positive random features by W while staged (one more barrier,
+// after W is copied into LDS).
+template <int D, int F, bool DECAY, bool RF>
 __global__ __launch_bounds__(CausalCfg<D>::THREADS) void k_causal(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ out, const float *__restrict__ preS, const float *__restrict__ prez,
     long pstride, long pzstride, float *__restrict__ Sout, float *__restrict__ zout, int N, int L,
-    int P, const float *__restrict__ gamma, int H)
+    int P, const float *__restrict__ gamma, int H, const uint16_t *__restrict__ W)
 {
     constexpr int NCW = CausalCfg<D>::NCW;
     __shared__ __attribute__((aligned(16))) CausalLds<D> sm;
+    __shared__ __attribute__((aligned(16))) uint16_t sW[RF ? D * D : 8];
     const int tid = threadIdx.x, wave = wave_id(), l = tid & 63;
     const int p = blockIdx.x % P, bh = blockIdx.x / P;
     const size_t hoff = (size_t)bh * N * D;
@@ -760,10 +914,14 @@ __global__ __launch_bounds__(CausalCfg<D>::THREADS) void k_causal(
     a.te = min(N, a.tb + L);
     a.nch = (a.te - a.tb + C - 1) / C;
     a.lg = DECAY ? decay_lg(gamma, bh, H) : 0.f;
+    if (RF) {
+        rf_put_w<D, CausalCfg<D>::THREADS>(sW, W, tid);
+        __syncthreads();
+    }
     if (wave < NCW)
         causal_compute<D, !(F & F_UNNORM), DECAY>(sm, a, wave, l & 15, l >> 4);
     else
-        causal_stage<D, !(F & F_IDENTITY)>(sm, a, tid - NCW * 64);
+        causal_stage<D, !(F & F_IDENTITY), RF>(sm, sW, a, tid - NCW * 64);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -872,12 +1030,13 @@ template <int D, int F> void launch_causal(dim3 grid, hipStream_t st, const uint
                                            float *Sout, float *zout, int N, int L, int P,
                                            const float *gamma, int H)
 {
+    const uint16_t *W = nullptr;
     if (gamma)
-        hipLaunchKernelGGL((k_causal<D, F, true>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q, k, v,
-                           o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
+        hipLaunchKernelGGL((k_causal<D, F, true, false>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q,
+                           k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H, W);
     else
-        hipLaunchKernelGGL((k_causal<D, F, false>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q, k,
-                           v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
+        hipLaunchKernelGGL((k_causal<D, F, false, false>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q,
+                           k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H, W);
 }
 
 template <int D> void launch_causal_f(int flags, dim3 grid, hipStream_t st, const uint16_t *q,
@@ -910,12 +1069,13 @@ template <int D, bool PHI> void launch_agg(dim3 grid, hipStream_t st, const uint
                                            long zs, int N, int L, int nseg, int P,
                                            const float *gamma, int H)
 {
+    const uint16_t *W = nullptr;
     if (gamma)
-        hipLaunchKernelGGL((k_agg<D, PHI, true>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v, dstS,
-                           dstz, ss, zs, N, L, nseg, P, gamma, H);
+        hipLaunchKernelGGL((k_agg<D, PHI, true, false>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v,
+                           dstS, dstz, ss, zs, N, L, nseg, P, gamma, H, W);
     else
-        hipLaunchKernelGGL((k_agg<D, PHI, false>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v, dstS,
-                           dstz, ss, zs, N, L, nseg, P, gamma, H);
+        hipLaunchKernelGGL((k_agg<D, PHI, false, false>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v,
+                           dstS, dstz, ss, zs, N, L, nseg, P, gamma, H, W);
 }
 
 template <int D> void launch_agg_f(int flags, dim3 grid, hipStream_t st, const uint16_t *k,
@@ -960,6 +1120,56 @@ hipError_t causal_mfma(int D, int flags, const void *q, const void *k, const voi
     else
         launch_causal_f<64>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout,
                             zout, N, L, P, gamma, H);
+    return hipGetLastError();
+}
+
+hipError_t agg_rf_mfma(int D, const void *k, const void *v, const void *W, float *dstS, float *dstz,
+                       long sstride, long zstride, int BH, int N, int L, int nseg, int P,
+                       hipStream_t st)
+{
+    const dim3 grid((unsigned)(BH * nseg));
+    const auto *kk = static_cast<const uint16_t *>(k);
+    const auto *vv = static_cast<const uint16_t *>(v);
+    const auto *ww = static_cast<const uint16_t *>(W);
+    const float *gamma = nullptr;
+    if (D == 128)
+        hipLaunchKernelGGL((k_agg<128, false, false, true>), grid, dim3(AggCfg<128>::THREADS), 0, st,
+                           kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, 1, ww);
+    else
+        hipLaunchKernelGGL((k_agg<64, false, false, true>), grid, dim3(AggCfg<64>::THREADS), 0, st,
+                           kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, 1, ww);
+    return hipGetLastError();
+}
+
+hipError_t causal_rf_mfma(int D, int flags, const void *q, const void *k, const void *v,
+                          const void *W, void *out, const float *preS, const float *prez,
+                          long pstride, long pzstride, float *Sout, float *zout, int BH, int N,
+                          int L, int P, hipStream_t st)
+{
+    const dim3 grid((unsigned)(BH * P));
+    const auto *qq = static_cast<const uint16_t *>(q);
+    const auto *kk = static_cast<const uint16_t *>(k);
+    const auto *vv = static_cast<const uint16_t *>(v);
+    const auto *ww = static_cast<const uint16_t *>(W);
+    auto *oo = static_cast<uint16_t *>(out);
+    const float *gamma = nullptr;
+#define LA_RFC(DD, FF)                                                                          \
+    hipLaunchKernelGGL((k_causal<DD, FF, false, true>), grid, dim3(CausalCfg<DD>::THREADS), 0, st, \
+                       qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout, zout, N, L, P, gamma, 1, \
+                       ww)
+    const bool unnorm = flags & F_UNNORM;
+    if (D == 128) {
+        if (unnorm)
+            LA_RFC(128, F_UNNORM);
+        else
+            LA_RFC(128, 0);
+    } else {
+        if (unnorm)
+            LA_RFC(64, F_UNNORM);
+        else
+            LA_RFC(64, 0);
+    }
+#undef LA_RFC
     return hipGetLastError();
 }
 

@@ -329,6 +329,116 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
     return e == hipSuccess ? LA_OK : LA_EHIP;
 }
 
+// The random-feature causal call: q, k [B,H,N,d] are mapped with W [m, d] to features
+// [B,H,N,m] and the causal identity-map form runs over them (S [B,H,m,d_v], z [B,H,m]). When
+// m == d == d_v in {64, 128} and the matrix-core kernels apply, the map runs inside their
+// staging (no feature tensor is written); otherwise the features go through pool memory.
+int validate_rf(const void *q, const void *k, const void *v, void *out, const void *W,
+                const float *S0, const float *z0, float *S, float *z, int B, int H, int N, int d,
+                int dv, int m, int chunk, int seg_len, int flags, int dtype, Plan *plan)
+{
+    if (!flags_ok(flags) || (flags & LA_PHI_IDENTITY))
+        return LA_EINVAL;
+    if (!q || !k || !v || !out || !W)
+        return LA_EINVAL;
+    if ((S == nullptr) != (z == nullptr) || (S0 == nullptr) != (z0 == nullptr))
+        return LA_EINVAL;
+    const void *ptrs[] = {q, k, v, out, W, S0, z0, S, z};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p))
+            return LA_EINVAL;
+    if (dtype != LA_F32 && dtype != LA_BF16)
+        return LA_EINVAL;
+    if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || dv <= 0 || m <= 0 || chunk < 0 || seg_len < 0)
+        return LA_EINVAL;
+    if (d > la::rf_max_d())
+        return LA_ENOTSUP;
+    // the attention runs over m features
+    const int s = make_plan(CAUSAL, B, H, N, m, dv, chunk, seg_len, dtype, plan);
+    if (s != LA_OK)
+        return s;
+    if ((size_t)N * (size_t)d > (size_t)INT32_MAX || (size_t)B * H * N > (size_t)INT32_MAX)
+        return LA_ENOTSUP;
+    const size_t es = dtype == LA_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * (size_t)H;
+    const Span sq = span(q, BH * N * d * es), sk = span(k, BH * N * d * es);
+    const Span sv = span(v, BH * N * dv * es), so = span(out, BH * N * dv * es);
+    const Span sw = span(W, (size_t)m * d * es);
+    const Span sS = span(S, BH * m * dv * 4), sz = span(z, BH * m * 4);
+    const Span sS0 = span(S0, BH * m * dv * 4), sz0 = span(z0, BH * m * 4);
+    for (Span in : {sq, sk, sv, sw})
+        if (overlap(so, in))
+            return LA_EINVAL;
+    for (Span st : {sS, sz, sS0, sz0})
+        for (Span o : {sq, sk, sv, so, sw})
+            if (overlap(st, o))
+                return LA_EINVAL;
+    if (overlap(sS, sz) || overlap(sS0, sz0))
+        return LA_EINVAL;
+    if (S0 && S0 != S && (overlap(sS0, sS) || overlap(sS0, sz)))
+        return LA_EINVAL;
+    if (z0 && z0 != z && (overlap(sz0, sS) || overlap(sz0, sz)))
+        return LA_EINVAL;
+    if (S0 && ((S0 == S) != (z0 == z)))
+        return LA_EINVAL;
+    return LA_OK;
+}
+
+int run_causal_rf(const void *q, const void *k, const void *v, void *out, const void *W,
+                  const float *S0, const float *z0, float *S, float *z, int N, int d, int dv,
+                  int m, bool bf16, int flags, const Plan &pl, hipStream_t st)
+{
+    const int BH = (int)pl.BH, P = pl.P, L = pl.L;
+    if (pl.mfma && m == d && d == dv) {
+        const long E = (long)d * dv + d;
+        Workspace ws;
+        if (ws.init(pl.ws_bytes, st) != hipSuccess)
+            return LA_EHIP;
+        hipError_t e = hipSuccess;
+        const float *preS = S0, *prez = z0;
+        long ps = (long)d * dv, pzs = d;
+        if (P > 1) {
+            e = la::agg_rf_mfma(d, k, v, W, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L, P - 1, P, st);
+            if (e == hipSuccess)
+                e = la::seg_exclusive_scan(ws.ptr, S0, z0, BH, P, d, dv, nullptr, 1, L, st);
+            preS = ws.ptr;
+            prez = ws.ptr + (long)d * dv;
+            ps = pzs = E;
+        }
+        if (e == hipSuccess)
+            e = la::causal_rf_mfma(d, flags, q, k, v, W, out, preS, prez, ps, pzs, S, z, BH, N, L, P,
+                                   st);
+        return e == hipSuccess ? LA_OK : LA_EHIP;
+    }
+    // features through pool memory, then the identity-map causal form over them
+    const size_t es = bf16 ? 2 : 4;
+    const size_t fbytes = (size_t)BH * N * m * es;
+    struct Bytes {
+        void *ptr = nullptr;
+        hipStream_t st = nullptr;
+        ~Bytes()
+        {
+            if (ptr)
+                (void)hipFreeAsync(ptr, st);
+        }
+    } feat;
+    hipMemPool_t pool;
+    if (pool_for_current_device(&pool) != hipSuccess)
+        return LA_EHIP;
+    feat.st = st;
+    if (hipMallocFromPoolAsync(&feat.ptr, 2 * fbytes, pool, st) != hipSuccess)
+        return LA_EHIP;
+    char *fq = static_cast<char *>(feat.ptr), *fk = fq + fbytes;
+    const long rows = (long)BH * N;
+    hipError_t e = la::rf_features(bf16, q, W, fq, rows, d, m, st);
+    if (e == hipSuccess)
+        e = la::rf_features(bf16, k, W, fk, rows, d, m, st);
+    if (e != hipSuccess)
+        return LA_EHIP;
+    return run_causal(fq, fk, v, out, S0, z0, S, z, N, m, dv, bf16, flags | LA_PHI_IDENTITY, nullptr,
+                      1, pl, st);
+}
+
 } // namespace
 
 extern "C" {
@@ -480,6 +590,20 @@ int la_decode_step(const void *q, const void *k, const void *v, void *out, float
 {
     (void)chunk;
     return la_decode_step_ex(q, k, v, out, S, z, B, H, N, d, d_v, 0, dtype, stream);
+}
+
+int la_causal_fwd_rf(const void *q, const void *k, const void *v, void *out, const void *W,
+                     const float *S0, const float *z0, float *S, float *z, int B, int H, int N,
+                     int d, int d_v, int m, int chunk, int seg_len, int flags, la_dtype dtype,
+                     hipStream_t stream)
+{
+    Plan pl;
+    const int s = validate_rf(q, k, v, out, W, S0, z0, S, z, B, H, N, d, d_v, m, chunk, seg_len,
+                              flags, dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    return run_causal_rf(q, k, v, out, W, S0, z0, S, z, N, d, d_v, m, dtype == LA_BF16, flags, pl,
+                         stream);
 }
 
 int la_rf_features(const void *x, const void *W, void *f, long rows, int d, int m,

@@ -30,6 +30,15 @@ hipError_t causal_mfma(int D, int flags, const void *q, const void *k, const voi
                        const float *preS, const float *prez, long pstride, long pzstride,
                        float *Sout, float *zout, int BH, int N, int L, int P, const float *gamma,
                        int H, hipStream_t st);
+// Random-feature forms of the two: q, k are mapped to exp(W x - |x|^2 / 2) / sqrt(D) while
+// staged (W bf16 [D][D]; m = d = d_v = D); the attention is the identity-map form over them.
+hipError_t agg_rf_mfma(int D, const void *k, const void *v, const void *W, float *dstS, float *dstz,
+                       long sstride, long zstride, int BH, int N, int L, int nseg, int P,
+                       hipStream_t st);
+hipError_t causal_rf_mfma(int D, int flags, const void *q, const void *k, const void *v,
+                          const void *W, void *out, const float *preS, const float *prez,
+                          long pstride, long pzstride, float *Sout, float *zout, int BH, int N,
+                          int L, int P, hipStream_t st);
 // Global read: out = phi(Q) S / phi(Q) z for every token, S/z per head ([BH, D, D], [BH, D]).
 hipError_t global_read_mfma(int D, int flags, const void *q, void *out, const float *S,
                             const float *z, int BH, int N, int L, int P, hipStream_t st);

@@ -233,6 +233,31 @@ int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *ou
 int la_rf_features(const void *x, const void *W, void *f, long rows, int d, int m,
                    la_dtype dtype, hipStream_t stream);
 
+/*
+ * Causal prefill over positive random features (Performer's FAVOR+ form, "Linear Attention
+ * Math", section "Feature maps: elu+1 and positive random features"): with f as for
+ * la_rf_features (one projection matrix W for q and k),
+ *     out_i = f(q_i)^T S_i / f(q_i)^T z_i,  S_i = sum_{j <= i} f(k_j) v_j^T,  z_i = sum f(k_j)
+ * (LA_UNNORMALIZED: f(q_i)^T S_i). Equal to la_rf_features on q and k followed by
+ * la_causal_fwd_ex with LA_PHI_IDENTITY and d = m.
+ *   q, k   [B, H, N, d];  v, out [B, H, N, d_v];  W [m, d] (rows = projections); all of dtype
+ *   S0, z0 / S, z   the state over the m features: [B, H, m, d_v] and [B, H, m] float32, with
+ *          the rules of la_causal_fwd_state (NULL pairs allowed as there)
+ *   flags  0 or LA_UNNORMALIZED (LA_PHI_IDENTITY, or any other bit: LA_EINVAL)
+ *   chunk, seg_len  as for la_causal_fwd_seg, for the attention over m features
+ * When m == d == d_v in {64, 128}, dtype is bf16 and the matrix-core chunk applies, the map runs
+ * inside the attention kernels' staging (W in LDS; no feature tensor is written to memory);
+ * otherwise the features of q and k are written to stream-ordered temporary memory
+ * (2 B H N m elements of dtype) and read back.
+ * Errors: as for la_causal_fwd_state (with S, z sized by m), plus W NULL, misaligned or
+ * overlapping out or the state: LA_EINVAL; d > 256, or m, d_v not in {16, 32, 64, 128}:
+ * LA_ENOTSUP.
+ */
+int la_causal_fwd_rf(const void *q, const void *k, const void *v, void *out, const void *W,
+                     const float *S0, const float *z0, float *S, float *z, int B, int H, int N,
+                     int d, int d_v, int m, int chunk, int seg_len, int flags, la_dtype dtype,
+                     hipStream_t stream);
+
 /* Bytes of stream-ordered temporary device memory a causal (form = 0) or global (form = 1)
  * call with these arguments takes (0 when none). seg_len as in la_causal_fwd_seg (0 = auto).
  * Returns 0 for invalid or unsupported arguments as well. */

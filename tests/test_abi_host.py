@@ -158,6 +158,30 @@ def test_rf_argument_checks():
     assert rf(rows=1 << 31, f=1 << 46) == la.LA_ENOTSUP
 
 
+def crf(q=A, k=2 * A, v=3 * A, out=4 * A, W=7 * A, S=5 * A, z=6 * A, B=1, H=2, N=8, d=64, dv=64,
+        m=64, chunk=0, seg=0, flags=0, dtype=la.LA_BF16):
+    return la.lib.la_causal_fwd_rf(q, k, v, out, W, S, z, S, z, B, H, N, d, dv, m, chunk, seg, flags,
+                                   dtype, None)
+
+
+def test_causal_rf_argument_checks():
+    assert crf(W=None) == la.LA_EINVAL
+    assert crf(W=7 * A + 8) == la.LA_EINVAL                     # misaligned
+    assert crf(W=4 * A + 16) == la.LA_EINVAL                    # W overlaps out
+    assert crf(S=7 * A) == la.LA_EINVAL                         # state overlaps W
+    assert crf(flags=la.LA_PHI_IDENTITY) == la.LA_EINVAL        # the map is the features
+    assert crf(flags=4) == la.LA_EINVAL
+    assert crf(q=None) == la.LA_EINVAL
+    assert crf(m=0) == la.LA_EINVAL
+    assert crf(B=0) == la.LA_EINVAL
+    assert crf(S=None) == la.LA_EINVAL                          # one of S, z
+    assert crf(out=A + 16) == la.LA_EINVAL                      # out overlaps q
+    assert crf(d=257) == la.LA_ENOTSUP
+    assert crf(m=48) == la.LA_ENOTSUP                           # the attention runs over m
+    assert crf(dv=256) == la.LA_ENOTSUP
+    assert crf(chunk=64, dtype=la.LA_F32) == la.LA_ENOTSUP
+
+
 def test_profiled_argument_checks():
     f = la.lib.la_causal_fwd_profiled
     args = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 5 * A, 6 * A, 1, 2, 8, 16, 16, 0, 0, 0,

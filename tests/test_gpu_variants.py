@@ -281,3 +281,70 @@ def test_favor_workload_full():
     oo, So, zo, _, _ = oracle.causal(fq, fk, f64(v), mode="identity")
     check("out", o, oo, TOL["bf16"])
     check("S", S, So, TOL["bf16"])
+
+
+# ---------------------------------------------------------------- random features in one call
+def causal_rf(q, k, v, W, flags=0, S0=None, z0=None, chunk=0, seg_len=0):
+    B, H, N, d = q.shape
+    dv, m = v.shape[-1], W.shape[0]
+    out = torch.empty((B, H, N, dv), dtype=q.dtype, device=DEV)
+    S = torch.full((B, H, m, dv), float("nan"), device=DEV)
+    z = torch.full((B, H, m), float("nan"), device=DEV)
+    S0d = None if S0 is None else torch.as_tensor(S0, dtype=torch.float32).to(DEV)
+    z0d = None if z0 is None else torch.as_tensor(z0, dtype=torch.float32).to(DEV)
+    la().la_causal_fwd_rf(to_dev(q), to_dev(k), to_dev(v), out, to_dev(W), S0d, z0d, S, z,
+                          chunk=chunk, seg_len=seg_len, flags=flags)
+    torch.cuda.synchronize()
+    return f64(out), f64(S), f64(z)
+
+
+@pytest.mark.parametrize("d,m,dv,N,seg,flags", [
+    (128, 128, 128, 3000, 0, 0), (128, 128, 128, 1000, 192, UNNORM), (64, 64, 64, 1111, 0, 0),
+    (64, 64, 64, 65, 0, UNNORM), (128, 128, 128, 1, 0, 0), (128, 64, 128, 700, 0, 0),
+    (128, 64, 64, 500, 0, 0), (64, 128, 64, 300, 0, 0)])
+def test_causal_rf(d, m, dv, N, seg, flags):
+    """la_causal_fwd_rf against the oracle's features and recurrence, with a carried initial
+    state: m == d == d_v maps inside the attention kernels, other shapes go through memory."""
+    q, k, v = datagen.qkv(2, 2, N, d, dv, 1500 + d + m + N, 1 / math.sqrt(d), "bf16")
+    W = datagen.projections(m, d, 1600 + m, "bf16")
+    fq, fk = oracle.rf_map(f64(q), f64(W)), oracle.rf_map(f64(k), f64(W))
+    mode, norm = MODE[IDENT | flags]
+    # a carried state from 64 earlier tokens
+    qp, kp, vp = datagen.qkv(2, 2, 64, d, dv, 1700 + d, 1 / math.sqrt(d), "bf16")
+    _, S0, z0, _, _ = oracle.causal(oracle.rf_map(f64(qp), f64(W)), oracle.rf_map(f64(kp), f64(W)),
+                                    f64(vp), mode="identity")
+    S0, z0 = S0.astype(np.float32), z0.astype(np.float32)
+    say(f"causal rf d={d} m={m} dv={dv} N={N} seg={seg} flags={flags}")
+    o, S, z = causal_rf(q, k, v, W, flags=flags, S0=S0, z0=z0, seg_len=seg)
+    oo, So, zo, _, _ = oracle.causal(fq, fk, f64(v), S0=S0, z0=z0, mode=mode, normalize=norm)
+    check("out", o, oo, TOL["bf16"])
+    check("S", S, So, TOL["bf16"])
+    check("z", z, zo, TOL["bf16"])
+
+
+def test_causal_rf_fused_equals_two_pass():
+    """The map inside the staging gives the features the separate feature kernel writes, so
+    the one-call form and the two-pass form agree to far below the bf16 tolerance."""
+    q, k, v = datagen.qkv(2, 4, 2500, 128, 128, 1801, 1 / math.sqrt(128), "bf16")
+    W = datagen.projections(128, 128, 1802, "bf16")
+    say("causal rf fused vs two-pass")
+    o1, S1, z1 = causal_rf(q, k, v, W)
+    fq, fk = rf_gpu(q, W), rf_gpu(k, W)
+    o2, S2, z2 = causal_ex(fq, fk, v, IDENT)
+    check("out", o1, o2, 1e-3)
+    check("S", S1, S2, 1e-5)
+    check("z", z1, z2, 1e-5)
+
+
+def test_causal_rf_workload_full():
+    """The random-feature workload in one call, in the launch configuration of the bench."""
+    rw = datagen.RF_WORKLOAD
+    w = datagen.WORKLOADS[rw["base"]]
+    q, k, v = datagen.qkv(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale, "bf16")
+    W = datagen.projections(rw["m"], w.d, rw["seed"], "bf16")
+    say(f"causal rf workload {rw['name']}")
+    o, S, z = causal_rf(q, k, v, W)
+    fq, fk = oracle.rf_map(f64(q), f64(W)), oracle.rf_map(f64(k), f64(W))
+    oo, So, zo, _, _ = oracle.causal(fq, fk, f64(v), mode="identity")
+    check("out", o, oo, TOL["bf16"])
+    check("S", S, So, TOL["bf16"])
