@@ -493,7 +493,7 @@ def main():
                   "two_pass_us_per_step": ms_f2 * 1e3,
                   "features_us_per_tensor": ms_rf * 1e3,
                   "features_hbm_frac": rf_bytes / (ms_rf * 1e-3) / HBM_PEAK,
-                  "attention_kernels_us": {"segment_sums": kern_f[0] * 1e3,
+                  "two_pass_attention_kernels_us": {"segment_sums": kern_f[0] * 1e3,
                                            "segment_scan": kern_f[1] * 1e3,
                                            "causal": kern_f[2] * 1e3}},
         "identity_unnormalized": {"workload": wv.name, "us_per_call": ms_v * 1e3,

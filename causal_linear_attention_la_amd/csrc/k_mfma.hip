@@ -510,8 +510,13 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
 {
     using K = Cfg<D>;
     using TL = Tile<D, AggCfg<D>::THREADS>;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][K::AS];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][K::AS];
+    // double-buffered chunks; single-buffered with the random-feature map (its W takes
+    // 32 KiB of LDS): measured on MI355X, two barriers per chunk over 71 KiB beat one barrier
+    // per chunk over 110 KiB there (the staging of a random-feature chunk is matrix work of
+    // its own, and it overlaps better with the other workgroups than within one)
+    constexpr int NB = RF ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[NB][K::AS];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[NB][K::AS];
     __shared__ __attribute__((aligned(16))) uint16_t sW[RF ? D * D : 8];
 
     const int tid = threadIdx.x, w = wave_id(), l = tid & 63, li = l & 15, g = l >> 4;
@@ -549,6 +554,15 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
         rf_put_w<D, AggCfg<D>::THREADS>(sW, W, tid);
         __syncthreads();
     }
+    auto update = [&](int b, int c) {
+        if (DECAY) {
+            state_update_decay<D, 1, 1>(sacc, zacc, sK[b] + trl, sV[b] + cw0 + trl, sK[b] + cw0 + trl,
+                                        lg, min(C, te - (tb + c * C)), g);
+        } else {
+            state_update<D, 1>(sacc, sK[b] + trl, sV[b] + cw0 + trl);
+            key_sum<D, 1>(zacc, sK[b] + cw0 + trl);
+        }
+    };
     load_k(kb + (size_t)tb * D, te - tb);
     tile.load(rv, vb + (size_t)tb * D, te - tb);
     put_k(sK[0], te - tb);
@@ -560,25 +574,32 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
     }
     __syncthreads();
     for (int c = 0; c < nch; ++c) {
-        const int b = c & 1, nb = b ^ 1;
-        if (c + 1 < nch) {
-            const int n1 = min(C, te - (tb + (c + 1) * C));
-            put_k(sK[nb], n1);
-            tile.store(sV[nb], rv, n1, false);
-        }
-        {
+        if (NB == 2) {
+            // stage chunk c + 1 into the other buffer, then sum chunk c
+            if (c + 1 < nch) {
+                const int n1 = min(C, te - (tb + (c + 1) * C));
+                put_k(sK[(c & 1) ^ 1], n1);
+                tile.store(sV[(c & 1) ^ 1], rv, n1, false);
+            }
             const int tn = chunk_t0(c + 2);
             load_k(kb + (size_t)tn * D, te - tn);
             tile.load(rv, vb + (size_t)tn * D, te - tn);
-        }
-        if (DECAY) {
-            state_update_decay<D, 1, 1>(sacc, zacc, sK[b] + trl, sV[b] + cw0 + trl, sK[b] + cw0 + trl,
-                                        lg, min(C, te - (tb + c * C)), g);
+            update(c & 1, c);
+            __syncthreads();
         } else {
-            state_update<D, 1>(sacc, sK[b] + trl, sV[b] + cw0 + trl);
-            key_sum<D, 1>(zacc, sK[b] + cw0 + trl);
+            // single buffer: sum chunk c, then stage chunk c + 1 (two barriers per chunk)
+            update(0, c);
+            __syncthreads();
+            if (c + 1 < nch) {
+                const int n1 = min(C, te - (tb + (c + 1) * C));
+                put_k(sK[0], n1);
+                tile.store(sV[0], rv, n1, false);
+            }
+            const int tn = chunk_t0(c + 2);
+            load_k(kb + (size_t)tn * D, te - tn);
+            tile.load(rv, vb + (size_t)tn * D, te - tn);
+            __syncthreads();
         }
-        __syncthreads();
     }
 
     float *S = dstS + ((long)bh * P + p) * sstride;
