@@ -313,26 +313,60 @@ def bench_serving(args):
     return w, K, ms, ms_pre
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline():
-    """The float64 oracle, as it stands, on the prefill workload's 32 heads (full size; about
-    10 s of CPU work on 8 host threads)."""
+    """The float64 oracle, as it stands, on the prefill workload's 32 heads (full size) on all
+    host threads, and on 4 of its heads single-threaded; median of 3 wall-clock runs each."""
     import datagen
     import oracle
 
     w = datagen.WORKLOADS[3]
-    heads = 32
+    heads = w.B * w.H
     q, k, v = datagen.qkv(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale, "bf16")
     qd, kd, vd = (datagen.to_f64(x) for x in (q, k, v))
-    times = []
-    for _ in range(3):
-        t0 = time.perf_counter()
-        oracle.causal(qd, kd, vd)
-        times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return {"value": w.B * w.H * w.N / t, "unit": "tokens/s (B*H*N/s)", "cores": oracle.threads(),
+
+    def med(fn):
+        times = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        return statistics.median(times)
+
+    t = med(lambda: oracle.causal(qd, kd, vd))
+    cores = oracle.threads()
+    prev = oracle.set_threads(1)
+    try:
+        t1 = med(lambda: oracle.causal(qd[:1, :4], kd[:1, :4], vd[:1, :4]))
+    finally:
+        oracle.set_threads(prev)
+    return {"value": w.B * w.H * w.N / t, "unit": "tokens/s (B*H*N/s)", "cores": cores,
             "kind": "oracle",
             "sample": f"causal B={w.B} H={w.H} N={w.N} d=128 ({heads} heads, the whole workload), "
-                      f"float64 token-serial recurrence, median of 3 runs of {t:.2f} s"}
+                      f"float64 token-serial recurrence, median of 3 runs of {t:.2f} s",
+            "single_thread": {"value": 4 * w.N / t1, "unit": "tokens/s (B*H*N/s)", "cores": 1,
+                              "sample": f"4 of the {heads} heads, median of 3 runs of {t1:.2f} s"},
+            "host_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def copy_bandwidth(nbytes=256 << 20, reps=20):
+    """Read + write bandwidth of a plain elementwise copy (dst = src * 1, float32) of `nbytes`
+    on the box: the practical streaming rate the HBM-bound kernels are compared with."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = [torch.empty_like(src) for _ in range(2)]
+    ms, _ = time_calls(lambda i: torch.mul(src, 1.0, out=dst[i % 2]), reps, 3)
+    return 2 * nbytes / (ms * 1e-3)
 
 
 def copy_calibration(nbytes=256 << 20, reps=5):
@@ -431,6 +465,7 @@ def main():
     th = w.B * w.H * w.N
     value = th / (ms * 1e-3)
     achieved = byts / (kern_ms[2] * 1e-3)
+    copy_bw = copy_bandwidth()
     traffic = recorded_traffic()
     issued = mfma_issued_prefill(w.B, w.H, w.N, P)
     wd, ms_d, byts_d = bench_decode(args)
@@ -468,10 +503,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
-                     "kernel": "k_causal<128, 0, false> (causal outputs + final state; reads q, k, v and "
+                     "kernel": "k_causal<128, 0, false, false> (causal outputs + final state; reads q, k, v and "
                                "the segment prefix states, writes out and S, z)",
                      "kernel_us": kern_ms[2] * 1e3,
                      "algorithmic_bytes_per_launch": byts,
+                     "copy_GBps": copy_bw / 1e9, "frac_of_copy": achieved / copy_bw,
                      "call_us": ms * 1e3, "call_frac": byts / (ms * 1e-3) / HBM_PEAK,
                      "call_kernels_us": {"segment_sums": kern_ms[0] * 1e3,
                                          "segment_scan": kern_ms[1] * 1e3,

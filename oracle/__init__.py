@@ -81,6 +81,16 @@ def threads(lib=None) -> int:
     return int((lib or _load()).oracle_threads())
 
 
+def set_threads(n: int) -> int:
+    """Sets the OpenMP thread count of later oracle calls from this thread; returns the
+    previous count (for timing the oracle single-threaded and on all host cores)."""
+    _load()
+    gomp = ctypes.CDLL("libgomp.so.1")
+    prev = int(gomp.omp_get_max_threads())
+    gomp.omp_set_num_threads(int(n))
+    return prev
+
+
 def _mode(mode, normalize):
     return _MODES[mode] | (0 if normalize else 2)
 
