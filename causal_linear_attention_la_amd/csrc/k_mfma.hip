@@ -707,6 +707,17 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
         const int t0 = a.tb + c * C, nvalid = min(C, a.te - t0);
         const uint16_t *sQ = sm.sQ[b], *sK = sm.sK[b];
         // ---- phase 1
+        // every compute wave reads the carried state for its value columns here (phi(Q_c) and
+        // S are ready): phase 2, with the within-chunk product, the output and the state
+        // update, is the longer phase of the two (measured on MI355X: the compute waves arrive
+        // last at its barrier, the stage waves at phase 1's), so this work is moved out of it.
+        // The decayed form keeps it in phase 2, where its registers fit without spilling.
+        f32x4 acc[1][4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            acc[0][it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (!DECAY)
+            state_read<D, 1>(acc, sacc, sQ + sql);
         if (scores) {
             bf16x8 qb[K::NKB];
 #pragma unroll
@@ -767,12 +778,8 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
                 sm.sqz[16 * iw + li] = (cz[0] + cz[1]) * (DECAY ? dpow(a.lg, 16 * iw + li + 1) : 1.f);
         }
         __syncthreads();
-        // ---- phase 2: num^T = V^T A^T + S^T Qf^T for the wave's columns; out; S, z += Kf^T [V 1]
+        // ---- phase 2: num^T += V^T A^T for the wave's columns; out; S, z += Kf^T [V 1]
         {
-            f32x4 acc[1][4];
-#pragma unroll
-            for (int it = 0; it < 4; ++it)
-                acc[0][it] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (DECAY) {
                 // the carried state reaches query row i decayed by gamma^(i + 1): read it
                 // first and scale the rows before the within-chunk part is added
@@ -790,8 +797,6 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
                     acc[0][it] = mfma(av, ba, acc[0][it]);
                 }
             }
-            if (!DECAY)
-                state_read<D, 1>(acc, sacc, sQ + sql);
             store_out<D, 1, NORM>(acc, sm.srs, sm.sqz, a.oh + (size_t)t0 * D, nvalid, cw0, li, g);
             if (DECAY) {
                 state_update_decay<D, 1, 1>(sacc, zacc, sK + trl, sm.sV + cw0 + trl, sK + 16 * w + trl,
