@@ -102,9 +102,8 @@ def bench_prefill(args):
     kern_ms = list(la.la_causal_fwd_profiled(q, k, v, out, None, None, S, z, chunk=args.chunk,
                                              seg_len=args.seg_len, reps=args.steps))
     byts, flops = algo_prefill(w.B, w.H, w.N, w.d, w.dv)
-    # segments per head the library chose: its temporary memory is one state per segment
-    ws = la.la_workspace_bytes(0, w.B, w.H, w.N, w.d, w.dv, args.chunk, args.seg_len)
-    P = max(1, ws // (w.B * w.H * (w.d * w.dv + w.d) * 4))
+    # segments per head the library chose
+    P = la.la_segments(0, w.B, w.H, w.N, w.d, w.dv, args.chunk, args.seg_len)
     return w, ms, ms_hot, wall, byts, flops, P, kern_ms
 
 

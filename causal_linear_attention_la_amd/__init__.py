@@ -48,7 +48,7 @@ LA_PHI_IDENTITY, LA_UNNORMALIZED = 1, 2
 EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
            "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
            "la_decode_step_ex", "la_causal_fwd_decay", "la_decode_step_decay", "la_rf_features",
-           "la_causal_fwd_rf", "la_workspace_bytes", "la_strerror", "la_version")
+           "la_causal_fwd_rf", "la_workspace_bytes", "la_segments", "la_strerror", "la_version")
 
 
 class LAError(RuntimeError):
@@ -85,6 +85,8 @@ def _load(path: Path):
         getattr(lib, f).restype = ctypes.c_int
     lib.la_workspace_bytes.argtypes = [i] * 8 + [i]
     lib.la_workspace_bytes.restype = ctypes.c_size_t
+    lib.la_segments.argtypes = [i] * 9
+    lib.la_segments.restype = ctypes.c_int
     lib.la_strerror.argtypes = [i]
     lib.la_strerror.restype = ctypes.c_char_p
     lib.la_version.argtypes = []
@@ -302,6 +304,11 @@ def la_rf_features(x, W, f):
     st = lib.la_rf_features(_ptr(x), _ptr(W), _ptr(f), rows, d, m, _dtype_code(x), _stream(x))
     _check(st, "la_rf_features")
     return f
+
+
+def la_segments(form: int, B: int, H: int, N: int, d: int, d_v: int, chunk: int = 0,
+                seg_len: int = 0, dtype: int = LA_BF16) -> int:
+    return int(lib.la_segments(form, B, H, N, d, d_v, chunk, seg_len, dtype))
 
 
 def la_workspace_bytes(form: int, B: int, H: int, N: int, d: int, d_v: int, chunk: int = 0,

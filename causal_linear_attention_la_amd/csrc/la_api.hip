@@ -636,6 +636,17 @@ size_t la_workspace_bytes(int form, int B, int H, int N, int d, int d_v, int chu
     return pl.ws_bytes;
 }
 
+int la_segments(int form, int B, int H, int N, int d, int d_v, int chunk, int seg_len,
+                la_dtype dtype)
+{
+    if (form != 0 && form != 1)
+        return 0;
+    Plan pl;
+    if (make_plan(form == 0 ? CAUSAL : GLOBAL, B, H, N, d, d_v, chunk, seg_len, dtype, &pl) != LA_OK)
+        return 0;
+    return pl.P;
+}
+
 const char *la_strerror(int status)
 {
     switch (status) {

@@ -264,6 +264,12 @@ int la_causal_fwd_rf(const void *q, const void *k, const void *v, void *out, con
 size_t la_workspace_bytes(int form, int B, int H, int N, int d, int d_v, int chunk,
                           int seg_len, la_dtype dtype);
 
+/* Segments per (b, h) head that a causal (form = 0) or global (form = 1) call with these
+ * arguments splits the sequence into (they run in parallel; see la_causal_fwd_seg). Returns 0
+ * for invalid or unsupported arguments. */
+int la_segments(int form, int B, int H, int N, int d, int d_v, int chunk, int seg_len,
+                la_dtype dtype);
+
 /* Static, NUL-terminated description of a status code; never NULL. */
 const char *la_strerror(int status);
 

@@ -220,8 +220,13 @@ def test_workspace_bytes():
     # causal B=2 H=16 N=8192 d=128 bf16: chunk 64; the d = 128 matrix-core kernel takes one
     # workgroup per CU, so 256 / 32 = 8 segments of 1024 tokens per head
     E = 128 * 128 + 128
+    assert la.la_segments(0, 2, 16, 8192, 128, 128) == 8
     assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128) == 32 * 8 * E * 4
+    assert la.la_segments(0, 2, 16, 8192, 128, 128, 64, 512) == 16
     assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128, 64, 512) == 32 * 16 * E * 4
+    assert la.la_segments(0, 2, 16, 8192, 128, 128, 64, 192) == 43
+    assert la.la_segments(1, 1, 8, 100000, 128, 128) == 63
+    assert la.la_segments(0, 1, 1, 64, 48, 16) == 0
     # d = 64: two workgroups per CU, 512 / 32 = 16 segments of 128 tokens
     E64 = 64 * 64 + 64
     assert la.la_workspace_bytes(0, 4, 8, 2048, 64, 64) == 32 * 16 * E64 * 4
