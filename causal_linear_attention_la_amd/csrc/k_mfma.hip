@@ -1,5 +1,8 @@
 // k_mfma.hip -- matrix-core kernels of liblinattn: bf16 inputs, d == d_v = D in {64, 128},
 // chunks of C = 64 tokens, gfx950 MFMA v_mfma_f32_16x16x32_bf16 with float32 accumulation.
+// Variants are compile-time parameters of the same kernels: the identity map and the
+// unnormalised read (flags), a per-head decay of the carried state (the retention recurrence)
+// and positive random features computed in the staging.
 //
 // Chunked causal evaluation (the within-chunk part plus the state carried from earlier chunks,
 // as "Linear Attention: From Pairwise Reads to a Recurrent State", section "A recurrence need
@@ -902,13 +905,15 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const uint16_t *s
 // accumulators (16 value columns of S and 16 features of z each) and run the matrix-core
 // products of chunk c. NSW "stage" waves load the next chunks from HBM, apply phi and store
 // them row-major into LDS. Two barriers per chunk:
-//   phase 1  compute: scores A of chunk c (waves 0-3: query rows 16w..16w+15), rowsum(A) and
-//                     phi(q) . z per query row
+//   phase 1  compute: num = phi(Q_c) S (all compute waves, their value columns); scores A of
+//                     chunk c (waves 0-3: query rows 16w..16w+15), rowsum(A) and phi(q) . z
+//                     per query row
 //            stage:   V_c -> LDS, load V_{c+1}; phi(Q_{c+1}) -> LDS, load Q_{c+2}
 //   --- barrier ---
-//   phase 2  compute: num = A V_c + phi(Q_c) S; out = num / den; S, z += phi(K_c)^T [V_c 1]
+//   phase 2  compute: num += A V_c; out = num / den; S, z += phi(K_c)^T [V_c 1]
 //            stage:   phi(K_{c+1}) -> LDS, load K_{c+2}
 //   --- barrier ---
+// (with a decay, num = phi(Q_c) S is read in phase 2, scaled per row, before A V_c is added)
 // Roles are chosen by the wave-uniform wave index, so every wave executes the same sequence of
 // barriers. F: variant flags (F_IDENTITY: q, k are already features; F_UNNORM: no denominator).
 // RF: q and k are mapped to positive random features by W while staged (one more barrier,
