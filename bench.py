@@ -385,13 +385,18 @@ TRAFFIC_SOURCES = ("causal_linear_attention_la_amd/csrc/k_mfma.hip",
 
 
 def sources_digest():
-    """SHA-256 over the sources that decide the causal kernel's memory traffic (the kernel and
-    the launch plan that sizes its segments)."""
+    """SHA-256 over the code of the sources that decide the causal kernel's memory traffic (the
+    kernel and the launch plan that sizes its segments): // comments, trailing blanks and empty
+    lines are dropped first, so an edit of the comments keeps a measurement valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 
