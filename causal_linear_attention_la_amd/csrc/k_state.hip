@@ -29,35 +29,49 @@ constexpr int NT = 256;
 // segments costs P / SB memory round trips instead of P.
 constexpr int SB = 16;
 
+// Four consecutive floats per thread (16-byte accesses): d and d_v are multiples of 16 and every
+// state buffer is 16-byte aligned (the entry points reject anything else), so a group of four
+// never straddles the end of S.
 __global__ __launch_bounds__(NT) void k_seg_scan(float *__restrict__ ws, const float *__restrict__ S0,
-                                                 const float *__restrict__ z0, int P, int d,
-                                                 int dv, int blocks_per_head,
-                                                 const float *__restrict__ gamma, int H, int L)
+                                                  const float *__restrict__ z0, int P, int d,
+                                                  int dv, int blocks_per_head,
+                                                  const float *__restrict__ gamma, int H, int L)
 {
     const int E = d * dv + d;
     const int bh = blockIdx.x / blocks_per_head;
-    const int e = (blockIdx.x % blocks_per_head) * NT + threadIdx.x;
+    const int e = 4 * ((blockIdx.x % blocks_per_head) * NT + threadIdx.x);
     if (e >= E)
         return;
-    float run = 0.f;
+    float4 run = {0.f, 0.f, 0.f, 0.f};
     if (S0)
-        run = e < d * dv ? S0[(size_t)bh * d * dv + e] : z0[(size_t)bh * d + (e - d * dv)];
+        run = e < d * dv ? *reinterpret_cast<const float4 *>(S0 + (size_t)bh * d * dv + e)
+                         : *reinterpret_cast<const float4 *>(z0 + (size_t)bh * d + (e - d * dv));
     float *slot = ws + (size_t)bh * P * E + e;
     const float fL = gamma ? decay_pow(decay_log2(gamma, bh, H), L) : 1.f;
     for (int p0 = 0; p0 < P - 1; p0 += SB) {
-        float t[SB];
+        float4 t[SB];
 #pragma unroll
         for (int i = 0; i < SB; ++i)
             if (p0 + i < P - 1)
-                t[i] = slot[(size_t)(p0 + i) * E];
+                t[i] = *reinterpret_cast<const float4 *>(slot + (size_t)(p0 + i) * E);
 #pragma unroll
         for (int i = 0; i < SB; ++i)
             if (p0 + i < P - 1) {
-                slot[(size_t)(p0 + i) * E] = run;
-                run = gamma ? fmaf(run, fL, t[i]) : run + t[i];
+                *reinterpret_cast<float4 *>(slot + (size_t)(p0 + i) * E) = run;
+                if (gamma) {
+                    run.x = fmaf(run.x, fL, t[i].x);
+                    run.y = fmaf(run.y, fL, t[i].y);
+                    run.z = fmaf(run.z, fL, t[i].z);
+                    run.w = fmaf(run.w, fL, t[i].w);
+                } else {
+                    run.x += t[i].x;
+                    run.y += t[i].y;
+                    run.z += t[i].z;
+                    run.w += t[i].w;
+                }
             }
     }
-    slot[(size_t)(P - 1) * E] = run;
+    *reinterpret_cast<float4 *>(slot + (size_t)(P - 1) * E) = run;
 }
 
 __global__ __launch_bounds__(NT) void k_seg_total(const float *__restrict__ ws, float *__restrict__ S,
@@ -196,7 +210,11 @@ hipError_t decode_t(int flags, const void *q, const void *k, const void *v, void
 hipError_t seg_exclusive_scan(float *ws, const float *S0, const float *z0, int BH, int P, int d,
                               int dv, const float *gamma, int H, int L, hipStream_t st)
 {
-    const int E = d * dv + d, bph = (E + NT - 1) / NT;
+    const int E = d * dv + d;
+    auto a16 = [](const void *p) { return ((uintptr_t)p & 15) == 0; };
+    if (d % 4 || dv % 4 || !a16(ws) || (S0 && (!a16(S0) || !a16(z0))))
+        return hipErrorInvalidValue;
+    const int bph = (E / 4 + NT - 1) / NT;
     hipLaunchKernelGGL(k_seg_scan, dim3((unsigned)(BH * bph)), dim3(NT), 0, st, ws, S0, z0, P, d,
                        dv, bph, gamma, H, L);
     return hipGetLastError();

@@ -1,5 +1,5 @@
 // la_api.hip -- the C ABI of liblinattn (declared in include/la.h): argument validation,
-// kernel selection, sequence split and stream-ordered workspace.
+// kernel selection, sequence split and per-stream scratch memory.
 #include "la.h"
 #include "la_launch.h"
 
@@ -158,57 +158,115 @@ int validate(Form form, const void *q, const void *k, const void *v, void *out, 
     return LA_OK;
 }
 
-// Private stream-ordered pool per device, kept for the life of the process so that temporary
-// segment states are recycled between calls instead of returned to the driver each time.
-hipError_t pool_for_current_device(hipMemPool_t *out)
-{
-    static std::mutex mu;
-    static hipMemPool_t pools[64] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return e;
-    if (dev < 0 || dev >= 64)
-        return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!pools[dev]) {
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.handleTypes = hipMemHandleTypeNone;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t p = nullptr;
-        e = hipMemPoolCreate(&p, &props);
+// Scratch blocks kept per (device, stream) for the life of the process. A call takes a free
+// block of its stream and gives it back when it has enqueued its kernels: the next call on
+// that stream runs after it in stream order, so a block is reused with no wait on the host or
+// the device. (Taking and returning stream-ordered pool memory in every call made the call
+// wait on the host for the stream to drain, measured on MI355X: the host could not run ahead
+// of the device.) Calls on different streams never share a block. When no free block of the
+// stream is large enough, the largest free one is returned (after the stream has drained: the
+// previous call may still be reading it) and a new one is allocated, so this waits only when
+// a stream's shapes grow.
+struct BlockCache {
+    struct Block {
+        int dev;
+        hipStream_t st;
+        void *ptr;
+        size_t bytes;
+        bool busy;
+    };
+    std::mutex mu;
+    std::vector<Block> blocks;
+
+    hipError_t take(int dev, hipStream_t st, size_t bytes, void **out)
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        Block *fit = nullptr, *small = nullptr;
+        for (Block &b : blocks) {
+            if (b.dev != dev || b.st != st || b.busy)
+                continue;
+            if (b.bytes >= bytes) {
+                if (!fit || b.bytes < fit->bytes)
+                    fit = &b;
+            } else if (!small || b.bytes > small->bytes) {
+                small = &b;
+            }
+        }
+        if (fit) {
+            fit->busy = true;
+            *out = fit->ptr;
+            return hipSuccess;
+        }
+        if (small) {
+            hipError_t e = hipStreamSynchronize(st);
+            if (e == hipSuccess)
+                e = hipFree(small->ptr);
+            if (e != hipSuccess)
+                return e;
+            blocks.erase(blocks.begin() + (small - blocks.data()));
+        }
+        void *p = nullptr;
+        const hipError_t e = hipMalloc(&p, bytes);
         if (e != hipSuccess)
             return e;
-        uint64_t keep = UINT64_MAX;
-        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
-        if (e != hipSuccess)
-            return e;
-        pools[dev] = p;
+        blocks.push_back(Block{dev, st, p, bytes, true});
+        *out = p;
+        return hipSuccess;
     }
-    *out = pools[dev];
-    return hipSuccess;
+    void give_back(void *ptr)
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (Block &b : blocks)
+            if (b.ptr == ptr)
+                b.busy = false;
+    }
+};
+
+BlockCache &block_cache()
+{
+    static BlockCache *c = new BlockCache(); // never destroyed: blocks live until the process ends
+    return *c;
 }
 
+// Scratch device memory of one call, released when the call has enqueued its work.
 struct Workspace {
     float *ptr = nullptr;
     hipStream_t st = nullptr;
+    bool pooled = false; // from the device's stream-ordered pool (stream under capture)
     hipError_t init(size_t bytes, hipStream_t stream)
     {
         st = stream;
         if (!bytes)
             return hipSuccess;
-        hipMemPool_t pool;
-        hipError_t e = pool_for_current_device(&pool);
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(stream, &cs);
         if (e != hipSuccess)
             return e;
-        return hipMallocFromPoolAsync(reinterpret_cast<void **>(&ptr), bytes, pool, stream);
+        if (cs != hipStreamCaptureStatusNone) {
+            // allocation and free nodes in the captured graph, so every replay owns its
+            // scratch (the device's default pool: measured to capture on ROCm where a private
+            // pool does not)
+            e = hipMallocAsync(reinterpret_cast<void **>(&ptr), bytes, stream);
+            pooled = e == hipSuccess;
+            return e;
+        }
+        int dev = 0;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess)
+            return e;
+        void *p = nullptr;
+        e = block_cache().take(dev, stream, bytes, &p);
+        ptr = static_cast<float *>(p);
+        return e;
     }
     ~Workspace()
     {
-        if (ptr)
+        if (!ptr)
+            return;
+        if (pooled)
             (void)hipFreeAsync(ptr, st);
+        else
+            block_cache().give_back(ptr);
     }
 };
 
@@ -332,7 +390,7 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
 // The random-feature causal call: q, k [B,H,N,d] are mapped with W [m, d] to features
 // [B,H,N,m] and the causal identity-map form runs over them (S [B,H,m,d_v], z [B,H,m]). When
 // m == d == d_v in {64, 128} and the matrix-core kernels apply, the map runs inside their
-// staging (no feature tensor is written); otherwise the features go through pool memory.
+// staging (no feature tensor is written); otherwise the features go through scratch memory.
 int validate_rf(const void *q, const void *k, const void *v, void *out, const void *W,
                 const float *S0, const float *z0, float *S, float *z, int B, int H, int N, int d,
                 int dv, int m, int chunk, int seg_len, int flags, int dtype, Plan *plan)
@@ -410,25 +468,13 @@ int run_causal_rf(const void *q, const void *k, const void *v, void *out, const 
                                    st);
         return e == hipSuccess ? LA_OK : LA_EHIP;
     }
-    // features through pool memory, then the identity-map causal form over them
+    // features through scratch memory, then the identity-map causal form over them
     const size_t es = bf16 ? 2 : 4;
     const size_t fbytes = (size_t)BH * N * m * es;
-    struct Bytes {
-        void *ptr = nullptr;
-        hipStream_t st = nullptr;
-        ~Bytes()
-        {
-            if (ptr)
-                (void)hipFreeAsync(ptr, st);
-        }
-    } feat;
-    hipMemPool_t pool;
-    if (pool_for_current_device(&pool) != hipSuccess)
+    Workspace feat;
+    if (feat.init(2 * fbytes, st) != hipSuccess)
         return LA_EHIP;
-    feat.st = st;
-    if (hipMallocFromPoolAsync(&feat.ptr, 2 * fbytes, pool, st) != hipSuccess)
-        return LA_EHIP;
-    char *fq = static_cast<char *>(feat.ptr), *fk = fq + fbytes;
+    char *fq = reinterpret_cast<char *>(feat.ptr), *fk = fq + fbytes;
     const long rows = (long)BH * N;
     hipError_t e = la::rf_features(bf16, q, W, fq, rows, d, m, st);
     if (e == hipSuccess)

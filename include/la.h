@@ -29,13 +29,19 @@
  * and state). d and d_v must each be one of 16, 32, 64, 128. Pointers must be 16-byte aligned.
  * q, k and v must not overlap out; S and z must not overlap each other or q, k, v, out.
  *
- * Ownership and concurrency: all memory belongs to the caller. The library never frees or
- * retains a pointer past the call and keeps no mutable global state. Work is enqueued on
- * `stream` (NULL = the null stream) and the call returns without waiting; the results are
- * ready when the stream reaches that point. Calls on different streams may run concurrently.
- * The causal and global forms take stream-ordered temporary device memory (hipMallocAsync /
- * hipFreeAsync on `stream`) for per-segment partial states; its size is returned by
- * la_workspace_bytes().
+ * Ownership and concurrency: all memory passed in belongs to the caller; the library never
+ * frees or retains a caller pointer past the call. Work is enqueued on `stream` (NULL = the
+ * null stream) and the call returns without waiting; the results are ready when the stream
+ * reaches that point. Calls on different streams may run concurrently.
+ * Scratch: the causal and global forms need temporary device memory for per-segment partial
+ * states (size: la_workspace_bytes()). The library keeps it in blocks cached per (device,
+ * stream handle) until the process ends: a call reuses a free block of its stream, which is
+ * safe without any wait because later calls on one stream run after it in stream order.
+ * A new block is allocated (hipMalloc) when a stream first needs one or needs a larger one;
+ * only then may the call wait for that stream to drain. Under stream capture the memory comes
+ * from the device's default stream-ordered pool instead (hipMallocAsync / hipFreeAsync:
+ * allocation nodes in the graph). A stream handle must not be destroyed while library work on
+ * it is pending and then reused by a new stream.
  *
  * Errors: every call validates all arguments before enqueuing anything and returns a status.
  *   LA_OK       enqueued
@@ -247,8 +253,8 @@ int la_rf_features(const void *x, const void *W, void *f, long rows, int d, int 
  *   chunk, seg_len  as for la_causal_fwd_seg, for the attention over m features
  * When m == d == d_v in {64, 128}, dtype is bf16 and the matrix-core chunk applies, the map runs
  * inside the attention kernels' staging (W in LDS; no feature tensor is written to memory);
- * otherwise the features of q and k are written to stream-ordered temporary memory
- * (2 B H N m elements of dtype) and read back.
+ * otherwise the features of q and k are written to scratch memory (2 B H N m elements of
+ * dtype, taken as described at the top of this file) and read back.
  * Errors: as for la_causal_fwd_state (with S, z sized by m), plus W NULL, misaligned or
  * overlapping out or the state: LA_EINVAL; d > 256, or m, d_v not in {16, 32, 64, 128}:
  * LA_ENOTSUP.
@@ -258,7 +264,7 @@ int la_causal_fwd_rf(const void *q, const void *k, const void *v, void *out, con
                      int d, int d_v, int m, int chunk, int seg_len, int flags, la_dtype dtype,
                      hipStream_t stream);
 
-/* Bytes of stream-ordered temporary device memory a causal (form = 0) or global (form = 1)
+/* Bytes of scratch device memory a causal (form = 0) or global (form = 1)
  * call with these arguments takes (0 when none). seg_len as in la_causal_fwd_seg (0 = auto).
  * Returns 0 for invalid or unsupported arguments as well. */
 size_t la_workspace_bytes(int form, int B, int H, int N, int d, int d_v, int chunk,
