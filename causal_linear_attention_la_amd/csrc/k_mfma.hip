@@ -40,8 +40,8 @@ constexpr int NT = 256; // threads of the segment-sum and global-read kernels; s
 template <int D> struct Cfg {
     static constexpr int RS = D + 16;           // row stride (elements) of the chunk arrays
     static constexpr int AS = C * RS + (C / 8 - 1) * 64; // chunk array size (elements)
-    static constexpr int TS = C + 8;            // row stride (elements) of the score block
-    static constexpr int ZS = D + 8;            // row stride (elements) of the key-sum operand
+    static constexpr int TS = C + 16;           // row stride (elements) of the score block
+    static constexpr int ZS = D + 16;           // row stride (elements) of the key-sum operand
     static constexpr int NCT = D / 64;          // 16-wide value-column tiles per wave (4 waves)
     static constexpr int NFT = D / 16;          // 16-row feature tiles of S
     static constexpr int NKB = D / 32;          // 32-feature k blocks
@@ -112,13 +112,16 @@ template <int D> __device__ __forceinline__ bf16x8 frag_tok(const uint16_t *p)
     return __builtin_bit_cast(bf16x8, x);
 }
 
-// Score block: [query row][key], row stride TS. Within each 32-key block, key 16h + 4q + y is
-// stored at position 8q + 4h + y, so a 16-byte read at position 8g holds the keys in the
-// k-slot order of frag_tok (slot 4h + y = key 16h + 4g + y), and one lane's two 4-key score
-// pieces of a tile pair form one 16-byte store.
+// Score block: [query row][key], row stride TS = C + 16. Within each 32-key block, key
+// 16h + 4q + y is stored at position 8q + 4h + y, so a 16-byte read at position 8g holds the
+// keys in the k-slot order of frag_tok (slot 4h + y = key 16h + 4g + y), and one lane's two
+// 4-key score pieces of a tile pair form one 16-byte store. The 16-byte granules of rows with
+// bit 2 set are swapped in pairs (granule index xor 1): with the stride this makes both the
+// score stores (8 lanes per pass) and the A V reads (16 lanes per pass) free of bank conflicts
+// (the unswizzled stride C + 8 left every A V read with two-way conflicts).
 __device__ __forceinline__ int sa_ix(int row, int kblock, int g)
 {
-    return row * (C + 8) + 32 * kblock + 8 * g;
+    return row * (C + 16) + 32 * kblock + 8 * (g ^ ((row >> 2) & 1));
 }
 
 // phi(x) = ELU(x) + 1 = exp(min(x, 0)) + max(x, 0) on 8 packed bf16 values, rounded to bf16
