@@ -569,31 +569,19 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
             key_sum<D, 1>(zacc, sK[b] + cw0 + trl);
         }
     };
-    load_k(kb + (size_t)tb * D, te - tb);
-    tile.load(rv, vb + (size_t)tb * D, te - tb);
-    put_k(sK[0], te - tb);
-    tile.store(sV[0], rv, te - tb, false);
-    {
-        const int tn = chunk_t0(1);
-        load_k(kb + (size_t)tn * D, te - tn);
-        tile.load(rv, vb + (size_t)tn * D, te - tn);
-    }
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-        if (NB == 2) {
-            // stage chunk c + 1 into the other buffer, then sum chunk c
-            if (c + 1 < nch) {
-                const int n1 = min(C, te - (tb + (c + 1) * C));
-                put_k(sK[(c & 1) ^ 1], n1);
-                tile.store(sV[(c & 1) ^ 1], rv, n1, false);
-            }
-            const int tn = chunk_t0(c + 2);
+    if constexpr (RF) {
+        // single buffer: sum chunk c, then stage chunk c + 1 (two barriers per chunk)
+        load_k(kb + (size_t)tb * D, te - tb);
+        tile.load(rv, vb + (size_t)tb * D, te - tb);
+        put_k(sK[0], te - tb);
+        tile.store(sV[0], rv, te - tb, false);
+        {
+            const int tn = chunk_t0(1);
             load_k(kb + (size_t)tn * D, te - tn);
             tile.load(rv, vb + (size_t)tn * D, te - tn);
-            update(c & 1, c);
-            __syncthreads();
-        } else {
-            // single buffer: sum chunk c, then stage chunk c + 1 (two barriers per chunk)
+        }
+        __syncthreads();
+        for (int c = 0; c < nch; ++c) {
             update(0, c);
             __syncthreads();
             if (c + 1 < nch) {
@@ -605,6 +593,42 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
             load_k(kb + (size_t)tn * D, te - tn);
             tile.load(rv, vb + (size_t)tn * D, te - tn);
             __syncthreads();
+        }
+    } else {
+        // Double-buffered LDS and two register sets: at the top of iteration c, chunk c is in
+        // LDS buffer c & 1, chunk c + 1 is loading into register set (c + 1) & 1 and set c & 1
+        // is free. The loads of chunk c + 2 go out first, so they are in flight while chunk c + 1
+        // is staged (wait, phi, LDS stores) and chunk c is summed: the loads never wait behind
+        // the staging. (Issuing them after the staging left each workgroup with no load in
+        // flight for the length of its staging, measured on MI355X: 27.3 us for the sums of the
+        // 2 x 16 x 8192 x 128 prefill against 19.7 us for a plain read of the same bytes.)
+        constexpr int TM = TL::TM;
+        u32x4 k0[TM], v0[TM], k1[TM], v1[TM];
+        auto ld = [&](u32x4 (&rkk)[TM], u32x4 (&rvv)[TM], int cc) {
+            const int tn = chunk_t0(cc);
+            tile.load(rkk, kb + (size_t)tn * D, te - tn);
+            tile.load(rvv, vb + (size_t)tn * D, te - tn);
+        };
+        auto put = [&](int bsel, const u32x4 (&rkk)[TM], const u32x4 (&rvv)[TM], int n) {
+            tile.store(sK[bsel], rkk, n, PHI);
+            tile.store(sV[bsel], rvv, n, false);
+        };
+        ld(k0, v0, 0);
+        put(0, k0, v0, te - tb);
+        ld(k1, v1, 1);
+        __syncthreads();
+        auto step = [&](int c, u32x4 (&fk)[TM], u32x4 (&fv)[TM], const u32x4 (&nk)[TM],
+                        const u32x4 (&nv)[TM]) {
+            ld(fk, fv, c + 2);
+            if (c + 1 < nch)
+                put((c & 1) ^ 1, nk, nv, min(C, te - (tb + (c + 1) * C)));
+            update(c & 1, c);
+            __syncthreads();
+        };
+        for (int c = 0; c < nch; c += 2) {
+            step(c, k0, v0, k1, v1);
+            if (c + 1 < nch)
+                step(c + 1, k1, v1, k0, v0);
         }
     }
 
