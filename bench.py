@@ -325,7 +325,8 @@ def cpu_model():
 
 def cpu_baseline():
     """The float64 oracle, as it stands, on the prefill workload's 32 heads (full size) on all
-    host threads, and on 4 of its heads single-threaded; median of 3 wall-clock runs each."""
+    host threads, and on 4 of its heads single-threaded: each repeated for about 10 s and 5 s
+    of wall-clock time (at least 3 runs), median run."""
     import datagen
     import oracle
 
@@ -334,27 +335,27 @@ def cpu_baseline():
     q, k, v = datagen.qkv(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale, "bf16")
     qd, kd, vd = (datagen.to_f64(x) for x in (q, k, v))
 
-    def med(fn):
+    def med(fn, seconds):
         times = []
-        for _ in range(3):
+        while len(times) < 3 or sum(times) < seconds:
             t0 = time.perf_counter()
             fn()
             times.append(time.perf_counter() - t0)
-        return statistics.median(times)
+        return statistics.median(times), len(times)
 
-    t = med(lambda: oracle.causal(qd, kd, vd))
+    t, n = med(lambda: oracle.causal(qd, kd, vd), 10.0)
     cores = oracle.threads()
     prev = oracle.set_threads(1)
     try:
-        t1 = med(lambda: oracle.causal(qd[:1, :4], kd[:1, :4], vd[:1, :4]))
+        t1, n1 = med(lambda: oracle.causal(qd[:1, :4], kd[:1, :4], vd[:1, :4]), 5.0)
     finally:
         oracle.set_threads(prev)
     return {"value": w.B * w.H * w.N / t, "unit": "tokens/s (B*H*N/s)", "cores": cores,
             "kind": "oracle",
             "sample": f"causal B={w.B} H={w.H} N={w.N} d=128 ({heads} heads, the whole workload), "
-                      f"float64 token-serial recurrence, median of 3 runs of {t:.2f} s",
+                      f"float64 token-serial recurrence, median of {n} runs of {t:.2f} s",
             "single_thread": {"value": 4 * w.N / t1, "unit": "tokens/s (B*H*N/s)", "cores": 1,
-                              "sample": f"4 of the {heads} heads, median of 3 runs of {t1:.2f} s"},
+                              "sample": f"4 of the {heads} heads, median of {n1} runs of {t1:.2f} s"},
             "host_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
 
 
