@@ -18,7 +18,11 @@
 // row li, 16 bytes per k block; the next tile is loaded while the current one is computed), so
 // every row is read from HBM once and by one wave, and computes all m features of its rows.
 // |x_i|^2 is summed in float32 from the same registers. The exponent runs as exp2 with log2(e)
-// folded into one fused multiply-add per feature.
+// folded into one fused multiply-add per feature. A wave's 16 x m feature tile goes through a
+// wave-private LDS tile before it is stored, so each store instruction writes whole rows (1 KiB
+// of consecutive memory) rather than 16-byte pieces of 16 rows: stored straight from the
+// product, the pieces kept the texture addresser waiting on the L1 and the kernel took 37 us
+// per 2 x 16 x 8192 x 128 tensor instead of 29 (measured on MI355X).
 #include "la_device.h"
 #include "la_launch.h"
 
@@ -41,8 +45,12 @@ __global__ __launch_bounds__(256) void k_rf_mfma(const uint16_t *__restrict__ x,
     constexpr int NKB = D / 32;     // k blocks of 32 features
     constexpr int MT = M / 16;      // 16-projection tiles
     constexpr float LOG2E = 1.44269504088896341f;
+    constexpr int FS = M + 8;       // row stride (elements) of a wave's feature tile
+    constexpr int LPR = M / 8;      // lanes per row when a tile is stored (16 bytes each)
     __shared__ __attribute__((aligned(16))) uint16_t sW[M * D];
+    __shared__ __attribute__((aligned(16))) uint16_t sF[4][16 * FS];
     const int tid = threadIdx.x, l = tid & 63, li = l & 15, g = l >> 4;
+    uint16_t *tileF = sF[tid >> 6];
 
     const long ntile = (rows + 15) / 16;
     const long nwave = (long)gridDim.x * 4;
@@ -85,7 +93,6 @@ __global__ __launch_bounds__(256) void k_rf_mfma(const uint16_t *__restrict__ x,
         n += __shfl_xor(n, 32, 64);
         // exponent in base 2: (dot - n / 2) log2(e) - log2(m) / 2
         const float bias = fmaf(-0.5f * LOG2E, n, neg_half_log2m);
-        const long r = 16 * t + li;
         // two projection tiles per step: enough independent work per wave without holding
         // every W fragment in registers at once
 #pragma unroll 1
@@ -107,8 +114,15 @@ __global__ __launch_bounds__(256) void k_rf_mfma(const uint16_t *__restrict__ x,
                 o[2 * h] = pack_bf2(e[0], e[1]);
                 o[2 * h + 1] = pack_bf2(e[2], e[3]);
             }
-            if (r < rows)
-                *reinterpret_cast<u32x4 *>(f + r * M + (M / 4) * g + 8 * s) = u32x4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<u32x4 *>(tileF + li * FS + (M / 4) * g + 8 * s) = u32x4{o[0], o[1], o[2], o[3]};
+        }
+        // the tile back as whole rows (this wave's LDS only: its accesses stay in order)
+#pragma unroll
+        for (int i = 0; i < 16 / (64 / LPR); ++i) {
+            const int row = (64 / LPR) * i + l / LPR, col = 8 * (l % LPR);
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(tileF + row * FS + col);
+            if (16 * t + row < rows)
+                *reinterpret_cast<u32x4 *>(f + (16 * t + row) * M + col) = v;
         }
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk)
