@@ -984,98 +984,117 @@ __global__ __launch_bounds__(CausalCfg<D>::THREADS) void k_causal(
 
 // ------------------------------------------------------------------------------------------
 // Global read: out = phi(Q) S / phi(Q) z for one segment of tokens of one head (F as for
-// k_causal).
+// k_causal). The workgroup copies S (bf16, in matrix-core fragment order) and z into LDS once;
+// after that each wave works alone on 16-row tiles of the segment (tiles w, w + 4, ...) with
+// no further barrier. A wave loads its 16 rows of Q straight from HBM as the B operand of
+// num^T = S^T phi(Q)^T (lane li holds row li; the next tile's rows load while the current one
+// is computed), applies phi in registers, takes phi(q) . z for its row from the same registers,
+// and writes the 16 x D output tile to a wave-private LDS tile that it stores as whole rows
+// (1 KiB per store instruction). (The earlier form staged Q through LDS with two barriers per
+// chunk and stored 64-byte pieces of 16 rows per instruction.)
+template <int D> struct GreadCfg {
+    static constexpr int NKB = D / 32;   // 32-feature k blocks
+    static constexpr int NCT = D / 16;   // 16-column value tiles
+    static constexpr int OS = D + 4;     // row stride (elements) of a wave's output tile
+};
+
+// (at most 168 VGPRs: three waves per SIMD, so three workgroups share a CU)
 template <int D, int F>
-__global__ __launch_bounds__(NT) void k_gread(const uint16_t *__restrict__ q,
+__global__ __launch_bounds__(NT, 3) void k_gread(const uint16_t *__restrict__ q,
                                               uint16_t *__restrict__ out,
                                               const float *__restrict__ S,
                                               const float *__restrict__ z, int N, int L, int P)
 {
-    using K = Cfg<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[K::AS];
+    using G = GreadCfg<D>;
+    constexpr int NKB = G::NKB, NCT = G::NCT, OS = G::OS, LPR = D / 8, RPI = 64 / LPR;
+    constexpr bool PHI = !(F & F_IDENTITY), NORM = !(F & F_UNNORM);
+    __shared__ __attribute__((aligned(16))) uint16_t sS[D * D];      // S^T fragments
+    __shared__ __attribute__((aligned(16))) uint16_t sT[4][16 * OS];  // per-wave output tiles
     __shared__ float sz[D];
-    __shared__ float sden[C];
 
     const int tid = threadIdx.x, w = wave_id(), l = tid & 63, li = l & 15, g = l >> 4;
     const int p = blockIdx.x % P, bh = blockIdx.x / P;
     const int tb = p * L, te = min(N, tb + L);
     const size_t hoff = (size_t)bh * N * D;
-    const int cw0 = w * (D / 4);
-    const int sql = nix<D>(li, 4 * g);
-    const Tile<D> tile(tid);
 
-    bf16x8 sf[K::NCT][K::NKB];
+    // S^T -> LDS: fragment fr = ct * NKB + kb, lane ll = lli + 16 lg holds S[32 kb + 8 lg + j]
+    // [16 ct + lli], j < 8 (the A operand: row = value column, k-slots = 8 features)
     {
         const float *Sh = S + (size_t)bh * D * D;
+        for (int e = tid; e < D * D / 8; e += NT) {
+            const int ll = e & 63, fr = e >> 6;
+            const int ct = fr / NKB, kb = fr % NKB, lli = ll & 15, lg = ll >> 4;
+            float x[8];
 #pragma unroll
-        for (int ct = 0; ct < K::NCT; ++ct)
-#pragma unroll
-            for (int m = 0; m < K::NKB; ++m) {
-                float x[8];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    x[r] = Sh[(32 * m + 4 * g + r) * D + cw0 + 16 * ct + li];
-                    x[4 + r] = Sh[(32 * m + 16 + 4 * g + r) * D + cw0 + 16 * ct + li];
-                }
-                const u32x4 wv = {pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]),
-                                  pack_bf2(x[6], x[7])};
-                sf[ct][m] = __builtin_bit_cast(bf16x8, wv);
-            }
-    }
-    if (tid < D)
-        sz[tid] = z[(size_t)bh * D + tid];
-
-    u32x4 rq[Tile<D>::TM];
-    tile.load(rq, q + hoff + (size_t)tb * D, te - tb);
-    const int tlast = tb + ((te - tb - 1) / C) * C;
-    for (int t0 = tb; t0 < te; t0 += C) {
-        const int nvalid = min(C, te - t0);
-        tile.store(sQ, rq, nvalid, !(F & F_IDENTITY));
-        __syncthreads();
-        {
-            const int tn = min(t0 + C, tlast);
-            tile.load(rq, q + hoff + (size_t)tn * D, te - tn);
+            for (int j = 0; j < 8; ++j)
+                x[j] = Sh[(32 * kb + 8 * lg + j) * D + 16 * ct + lli];
+            sts<u32x4>(sS + 8 * e, u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]),
+                                        pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])});
         }
-        if (!(F & F_UNNORM)) {
-            // den[i] = Qf[i] . z: 4 threads per row, D/4 features each
-            const int i = tid >> 2, qq = tid & 3;
-            float s = 0.f;
+        if (tid < D)
+            sz[tid] = z[(size_t)bh * D + tid];
+    }
+    __syncthreads();
+
+    const int ntile = (te - tb + 15) / 16;
+    if (w >= ntile)
+        return;
+    // B operand of tile t: row tb + 16 t + li (clamped to the segment's last row: every load is
+    // in bounds), features 32 kb + 8 g .. + 7
+    auto ldq = [&](u32x4 (&r)[NKB], int t) {
+        const int row = min(tb + 16 * t + li, te - 1);
 #pragma unroll
-            for (int e = 0; e < D / 32; ++e) {
-                const int f = qq * (D / 4) + 8 * e;
-                const u32x4 qw = lds<u32x4>(sQ + nix<D>(i, f));
+        for (int kb = 0; kb < NKB; ++kb)
+            r[kb] = *reinterpret_cast<const u32x4 *>(q + hoff + (size_t)row * D + 32 * kb + 8 * g);
+    };
+    uint16_t *tile = sT[w];
+    u32x4 qa[NKB], qn[NKB];
+    ldq(qa, w);
+    for (int t = w; t < ntile; t += 4) {
+        ldq(qn, min(t + 4, ntile - 1)); // next tile (a re-read of the last one at the end)
+        bf16x8 qb[NKB];
+        float den = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const u32x4 y = PHI ? phi8(qa[kb]) : qa[kb];
+            qb[kb] = __builtin_bit_cast(bf16x8, y);
+            if (NORM) {
+                const float4 z0 = *reinterpret_cast<const float4 *>(sz + 32 * kb + 8 * g);
+                const float4 z1 = *reinterpret_cast<const float4 *>(sz + 32 * kb + 8 * g + 4);
+                const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
                 for (int h = 0; h < 4; ++h)
-                    s += bf_lo(qw[h]) * sz[f + 2 * h] + bf_hi(qw[h]) * sz[f + 2 * h + 1];
-            }
-            s += __shfl_xor(s, 1, 64);
-            s += __shfl_xor(s, 2, 64);
-            if (qq == 0)
-                sden[i] = s;
-        }
-        __syncthreads();
-        f32x4 acc[K::NCT][4];
-#pragma unroll
-        for (int ct = 0; ct < K::NCT; ++ct)
-#pragma unroll
-            for (int it = 0; it < 4; ++it)
-                acc[ct][it] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < K::NKB; ++m) {
-            const uint16_t *q0b = sQ + sql + hidden(32 * m), *q1b = sQ + sql + hidden(32 * m + 16);
-#pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const u32x2 q0 = lds<u32x2>(q0b + blk<D>(16 * it, 0));
-                const u32x2 q1 = lds<u32x2>(q1b + blk<D>(16 * it, 0));
-                const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
-#pragma unroll
-                for (int ct = 0; ct < K::NCT; ++ct)
-                    acc[ct][it] = mfma(sf[ct][m], bq, acc[ct][it]);
+                    den = fmaf(bf_lo(y[h]), zz[2 * h], fmaf(bf_hi(y[h]), zz[2 * h + 1], den));
             }
         }
-        store_out<D, K::NCT, !(F & F_UNNORM)>(acc, sden, nullptr, out + hoff + (size_t)t0 * D, nvalid,
-                                              cw0, li, g);
-        __syncthreads();
+        float inv = 1.f;
+        if (NORM) {
+            den += __shfl_xor(den, 16, 64);
+            den += __shfl_xor(den, 32, 64);
+            inv = __builtin_amdgcn_rcpf(den);
+        }
+#pragma unroll 2
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                c = mfma(lds<bf16x8>(sS + ((ct * NKB + kb) * 64 + l) * 8), qb[kb], c);
+            // c[r] = num[query row li][value column 16 ct + 4 g + r]
+            sts<u32x2>(tile + li * OS + 16 * ct + 4 * g,
+                       u32x2{pack_bf2(c[0] * inv, c[1] * inv), pack_bf2(c[2] * inv, c[3] * inv)});
+        }
+        // the tile back as whole rows (this wave's LDS only: its accesses stay in order)
+        const int r0 = tb + 16 * t;
+#pragma unroll
+        for (int i = 0; i < 16 / RPI; ++i) {
+            const int row = RPI * i + l / LPR, col = 8 * (l % LPR);
+            const u32x4 x = lds<u32x4>(tile + row * OS + col);
+            if (r0 + row < te)
+                *reinterpret_cast<u32x4 *>(out + hoff + (size_t)(r0 + row) * D + col) = x;
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            qa[kb] = qn[kb];
     }
 }
 
@@ -1234,6 +1253,17 @@ hipError_t causal_rf_mfma(int D, int flags, const void *q, const void *k, const 
 hipError_t global_read_mfma(int D, int flags, const void *q, void *out, const float *S,
                             const float *z, int BH, int N, int L, int P, hipStream_t st)
 {
+    // the read needs no segment sums, so it takes its own split: about three workgroups per
+    // CU (its LDS allows three), 16-row tiles of the sequence
+    {
+        const long want = 3 * 256;
+        if ((long)BH * P < want) {
+            const long pr = (want + BH - 1) / BH;
+            const int Lr = (int)(((N + pr - 1) / pr + 15) / 16 * 16);
+            L = Lr;
+            P = (N + Lr - 1) / Lr;
+        }
+    }
     const dim3 grid((unsigned)(BH * P));
     const auto *qq = static_cast<const uint16_t *>(q);
     auto *oo = static_cast<uint16_t *>(out);
