@@ -35,7 +35,7 @@ namespace la {
 namespace {
 
 constexpr int C = 64;   // tokens per chunk
-constexpr int NT = 256; // threads of the segment-sum and global-read kernels; stage threads
+constexpr int NT = 256; // threads of the global-read kernel
 
 template <int D> struct Cfg {
     static constexpr int RS = D + 16;           // row stride (elements) of the chunk arrays
@@ -142,7 +142,7 @@ __device__ __forceinline__ u32x4 phi8(u32x4 x)
     return y;
 }
 
-// Staging of one [C, D] chunk by NT threads: consecutive lanes own consecutive 16-byte feature
+// Staging of one [C, D] chunk by NTH threads: consecutive lanes own consecutive 16-byte feature
 // groups of one row (FG lanes per row), so a wave's global load reads whole rows (1 KiB
 // contiguous) and 8 lanes of a staging store cover 128 contiguous bytes of one row. Thread t
 // owns rows t / FG + RPI * i, i < TM.
