@@ -102,3 +102,37 @@ def test_scratch_under_graph_capture():
         _run(mod, q2, k2, v2, 512)
         torch.cuda.synchronize()
 
+
+
+def test_scratch_host_threads():
+    """Four host threads, each with its own stream, enqueue causal calls at the same time (the
+    binding releases the interpreter lock during the C call); every result matches the oracle."""
+    import threading
+    mod = la()
+    cases = [_inputs(1, 2, 1024 + 128 * i, 64, 700 + i) for i in range(4)]
+    dev_in = [tuple(to_dev(x) for x in c) for c in cases]
+    torch.cuda.synchronize()
+    results = [None] * 4
+    errors = []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [_run(mod, *dev_in[i], 128) for _ in range(3)]
+            s.synchronize()
+            results[i] = outs
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    say("scratch host threads: 4 threads x 3 calls, d=64, seg_len=128")
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, (q, k, v) in enumerate(cases):
+        for j, (out, S, z) in enumerate(results[i]):
+            _check_oracle(f"thread {i} call {j}", q, k, v, out, S, z)
