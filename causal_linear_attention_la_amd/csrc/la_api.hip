@@ -13,10 +13,12 @@ constexpr int LA_VERSION = (0 << 16) | (1 << 8) | 0;
 
 enum Form { CAUSAL = 0, GLOBAL = 1, DECODE = 2 };
 
-// Target number of workgroups per launch on an MI355X (256 CUs): as many as run at once. The
-// d = 128 matrix-core causal kernel holds a whole CU (its LDS), so its segments are sized for
-// one wave of 256 workgroups; the other kernels fit two per CU. More segments than that only
-// add segment-state traffic (66 KB read and written per extra segment at d = 128).
+// Target number of workgroups per launch on an MI355X (256 CUs). The d = 128 matrix-core
+// kernels get one wave of 256 workgroups: the causal kernel holds a whole CU (its LDS), and the
+// segment sums, though two fit per CU, stream faster one per CU (measured on MI355X for the
+// global form B=1 H=8 N=100000: 63 segments per head, two per CU, 200.6 us per call; 32
+// segments, one per CU, 195.5 us). The other kernels fit two per CU. More segments than that
+// only add segment-state traffic (66 KB read and written per extra segment at d = 128).
 constexpr long kCUs = 256;
 
 bool dim_ok(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
@@ -91,7 +93,7 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
             return LA_ENOTSUP;
         pl.L = seg_len;
     } else {
-        const long target = (form == CAUSAL && pl.mfma && d == 128) ? kCUs : 2 * kCUs;
+        const long target = (pl.mfma && d == 128) ? kCUs : 2 * kCUs;
         long want = (target + (long)BH - 1) / (long)BH; // segments per head
         if (want > nchunks)
             want = nchunks;

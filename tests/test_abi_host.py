@@ -225,7 +225,8 @@ def test_workspace_bytes():
     assert la.la_segments(0, 2, 16, 8192, 128, 128, 64, 512) == 16
     assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128, 64, 512) == 32 * 16 * E * 4
     assert la.la_segments(0, 2, 16, 8192, 128, 128, 64, 192) == 43
-    assert la.la_segments(1, 1, 8, 100000, 128, 128) == 63
+    # global B=1 H=8 N=100000 d=128: one segment per CU as well, 256 / 8 = 32 per head
+    assert la.la_segments(1, 1, 8, 100000, 128, 128) == 32
     assert la.la_segments(0, 1, 1, 64, 48, 16) == 0
     # d = 64: two workgroups per CU, 512 / 32 = 16 segments of 128 tokens
     E64 = 64 * 64 + 64
