@@ -239,6 +239,28 @@ def test_workspace_bytes():
     assert la.la_workspace_bytes(0, 1, 1, 64, 48, 16) == 0
 
 
+def test_size_limits():
+    # 32-bit index arithmetic: N * max(d, d_v) and B * H * segments must stay below 2^31
+    n_max = (2**31 - 1) // 128
+    assert la.la_segments(0, 1, 1, n_max, 128, 128) > 0
+    assert la.la_workspace_bytes(0, 1, 1, n_max, 128, 128) > 0
+    assert la.la_segments(0, 1, 1, n_max + 1, 128, 128) == 0
+    assert la.la_segments(1, 1, 1, n_max + 1, 128, 128) == 0
+    assert la.la_segments(0, 1, 1, 2**31 // 64 - 1, 64, 128) == 0     # d_v decides
+    bh_max = (2**31 - 1) // 8
+    assert la.la_segments(0, 1, bh_max, 64, 16, 16) > 0               # B * H at the limit
+    assert la.la_segments(0, 1, bh_max + 1, 64, 16, 16) == 0
+    assert la.la_segments(0, 2**16, 2**12 + 1, 64, 16, 16) == 0       # B * H > (2^31 - 1) / 8
+    # the entry points report the same limit as unsupported (fake pointers 1 TiB apart, so no
+    # overlap check fires first; nothing is dereferenced)
+    T = 1 << 40
+    for fn in ("la_causal_fwd", "la_causal_fwd_state", "la_global_fwd"):
+        assert call(fn, q=T, k=2 * T, v=3 * T, out=4 * T, S=5 * T, z=6 * T, B=1, H=1,
+                    N=n_max + 1, d=128, dv=128) == la.LA_ENOTSUP
+        assert call(fn, q=T, k=2 * T, v=3 * T, out=4 * T, S=5 * T, z=6 * T, B=2**16, H=2**12 + 1,
+                    N=64, d=16, dv=16) == la.LA_ENOTSUP
+
+
 def test_binding_rejects_host_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 1, 4, 16)
