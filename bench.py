@@ -369,6 +369,16 @@ def copy_bandwidth(nbytes=256 << 20, reps=20):
     return 2 * nbytes / (ms * 1e-3)
 
 
+def rmw_bandwidth(nbytes, reps=10):
+    """Read + write bandwidth of an in-place read-modify-write (x *= 1, float32) over `nbytes`:
+    the pattern of a decode step, which reads and rewrites its state in place."""
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    ms, _ = time_calls(lambda i: x.mul_(1.0), reps, 3)
+    del x
+    return 2 * nbytes / (ms * 1e-3)
+
+
 def copy_calibration(nbytes=256 << 20, reps=5):
     """A plain elementwise copy kernel of known size (dst = src * 1, float32), for scaling the
     HBM byte counters FETCH_SIZE and WRITE_SIZE: each launch reads and writes nbytes."""
@@ -474,6 +484,9 @@ def main():
     traffic = recorded_traffic()
     issued = mfma_issued_prefill(w.B, w.H, w.N, P)
     wd, ms_d, byts_d = bench_decode(args)
+    # reference for the decode step: an in-place read-modify-write over a buffer of its state's
+    # size (S and z in float32, 541 MB for the decode workload)
+    rmw_bw = rmw_bandwidth(wd.B * wd.H * (wd.d * wd.dv + wd.d) * 4)
     print(f"decode: {ms_d * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     wg, ms_g, byts_g = bench_global(args)
     print(f"global: {ms_g * 1e3:.1f} us/call", file=sys.stderr, flush=True)
@@ -523,7 +536,9 @@ def main():
         "hot_cache_ms_per_step": ms_hot,
         "decode": {"workload": wd.name, "us_per_step": ms_d * 1e3,
                    "GB_per_s": byts_d / (ms_d * 1e-3) / 1e9,
-                   "hbm_frac": byts_d / (ms_d * 1e-3) / HBM_PEAK, "steps": args.decode_steps},
+                   "hbm_frac": byts_d / (ms_d * 1e-3) / HBM_PEAK,
+                   "rmw_GBps": rmw_bw / 1e9, "frac_of_rmw": byts_d / (ms_d * 1e-3) / rmw_bw,
+                   "steps": args.decode_steps},
         "global": {"workload": wg.name, "us_per_call": ms_g * 1e3,
                    "token_heads_per_s": wg.B * wg.H * wg.N / (ms_g * 1e-3),
                    "hbm_frac": byts_g / (ms_g * 1e-3) / HBM_PEAK},
