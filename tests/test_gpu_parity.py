@@ -280,6 +280,21 @@ def test_global_state_only():
     check("z", z[..., None], zo[..., None], TOL["bf16"])
 
 
+def test_global_one_segment_per_head():
+    """B * H = 256 heads at d = 128: one segment per head, the sums written straight into S, z
+    (the path the decode prior of the bench takes); outputs, and the state-only call."""
+    assert la().la_segments(1, 16, 16, 777, 128, 128) == 1
+    q, k, v = datagen.qkv(16, 16, 777, 128, 128, 51, 1 / math.sqrt(128), "bf16")
+    say("global one segment per head B=16 H=16 N=777 d=128")
+    o, S, z = global_(q, k, v)
+    oo, So, zo, _, _ = oracle.global_(f64(q), f64(k), f64(v))
+    check("out", o, oo, TOL["bf16"])
+    check("S", S, So, TOL["bf16"])
+    check("z", z[..., None], zo[..., None], TOL["bf16"])
+    _, S2, z2 = global_(None, k, v)
+    assert np.array_equal(S2, S) and np.array_equal(z2, z)
+
+
 def test_causal_last_row_equals_global():
     q, k, v = datagen.qkv(1, 2, 1500, 64, 64, 41, 1 / 8, "bf16")
     say("causal last row vs global")
