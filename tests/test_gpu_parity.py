@@ -280,6 +280,34 @@ def test_global_state_only():
     check("z", z[..., None], zo[..., None], TOL["bf16"])
 
 
+@pytest.mark.parametrize("B,H,N,d,flags", [(2, 4, 3000, 128, 0), (1, 8, 2048, 64, 0), (2, 2, 1500, 128, 3)])
+def test_profiled_matches_plain(B, H, N, d, flags):
+    """la_causal_fwd_profiled (the entry point the bench times its kernels through) runs the
+    same kernels as la_causal_fwd_ex: bit-identical outputs and state, and positive times."""
+    m = la()
+    q, k, v = datagen.qkv(B, H, N, d, d, 61 + N, 1 / math.sqrt(d), "bf16")
+    if flags & 1:  # identity map over positive features
+        q, k = q.abs() + 0.05, k.abs() + 0.05
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    say(f"profiled vs plain B={B} H={H} N={N} d={d} flags={flags}")
+    outs = []
+    for profiled in (False, True):
+        out = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        S = torch.full((B, H, d, d), float("nan"), device=DEV)
+        z = torch.full((B, H, d), float("nan"), device=DEV)
+        if profiled:
+            ms = m.la_causal_fwd_profiled(qd, kd, vd, out, None, None, S, z, flags=flags, reps=3)
+            assert len(ms) == 3 and all(math.isfinite(t) and t >= 0 for t in ms), ms
+            assert ms[2] > 0, ms
+        else:
+            m.la_causal_fwd_ex(qd, kd, vd, out, None, None, S, z, flags=flags)
+        torch.cuda.synchronize()
+        outs.append((out.cpu(), S.cpu(), z.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
 def test_global_one_segment_per_head():
     """B * H = 256 heads at d = 128: one segment per head, the sums written straight into S, z
     (the path the decode prior of the bench takes); outputs, and the state-only call."""
