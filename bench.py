@@ -450,7 +450,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the heads of this "
-              "workload shard across GPUs without communication, see DESIGN.md", file=sys.stderr)
+              "workload are independent, so across GPUs each would take a slice of the B*H "
+              "heads with no communication", file=sys.stderr)
         sys.exit(2)
 
     import torch
