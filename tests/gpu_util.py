@@ -8,7 +8,7 @@ import numpy as np
 import torch
 
 import datagen
-from oracle.compare import report
+from oracle.compare import bounded_row_err, report
 
 DEV = torch.device("cuda:0")
 
@@ -74,12 +74,7 @@ def check_bounded(name, got, want, bound, tol):
     compared with the largest entry of `bound`, the same sum taken over absolute values (the
     scale every rounding error is proportional to). Used where a row's terms may cancel, so
     that the row itself can be far smaller than the terms that make it up."""
-    got, want, bound = (np.asarray(x, dtype=np.float64) for x in (got, want, bound))
-    assert got.shape == want.shape == bound.shape, (got.shape, want.shape, bound.shape)
-    err = np.abs(got - want).max(axis=-1)
-    scale = np.maximum(bound.max(axis=-1), np.finfo(np.float64).tiny)
-    r = float((err / scale).max()) if err.size else 0.0
-    say(f"  {name}: bounded row_max={r:.3e} nonfinite={int((~np.isfinite(got)).sum())} tol={tol:g}")
-    assert np.all(np.isfinite(got)), name
+    r = bounded_row_err(got, want, bound)
+    say(f"  {name}: bounded row_max={r:.3e} nonfinite={int((~np.isfinite(np.asarray(got, dtype=np.float64))).sum())} tol={tol:g}")
     assert r <= tol, (name, r)
     return r
