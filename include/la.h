@@ -17,7 +17,8 @@
  *           -- "Linear Attention Math", section "The recurrent form" (O(1) per token);
  *              "线性注意力从头到尾讲清楚", section 7 (only S_t and z_t are kept).
  * No epsilon is added to the denominator ("Linear Attention: From Pairwise Reads to a
- * Recurrent State", section "The reassociation that works": a clamp changes the operation).
+ * Recurrent State", section "The reassociation that works—and the one that does not": a clamp
+ * changes the operation).
  *
  * Layout: every tensor is contiguous, row-major, in device memory.
  *   q, k  [B, H, N, d]       dtype given by `dtype`
@@ -138,7 +139,7 @@ int la_causal_fwd_ex(const void *q, const void *k, const void *v, void *out, con
 
 /*
  * Causal prefill with a per-head decay of the carried state, the retention recurrence of
- * "Linear Attention Math", section "Cousins: RetNet, Mamba, RWKV" (linear attention plus an
+ * "Linear Attention Math", section "The kernel cousins: SSMs and RetNet" (linear attention plus an
  * explicit decay gamma < 1 of the state, scalar or per head):
  *     S_i = gamma_h S_{i-1} + phi(k_i) v_i^T,   z_i = gamma_h z_{i-1} + phi(k_i),
  *     out_i = phi(q_i)^T S_i / phi(q_i)^T z_i    (LA_UNNORMALIZED: phi(q_i)^T S_i)

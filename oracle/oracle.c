@@ -27,8 +27,8 @@
  *                 State", section "Read the state with a Query", prints such sums).
  *   decay         optional per-head gamma (NULL: none): S_t = gamma S_{t-1} + phi(k_t) v_t^T
  *                 and z_t = gamma z_{t-1} + phi(k_t) in the causal form and the decode step,
- *                 the retention recurrence ("Linear Attention Math", section "Cousins: RetNet,
- *                 Mamba, RWKV": linear attention with an explicit decay of the carried state;
+ *                 the retention recurrence ("Linear Attention Math", section "The kernel
+ *                 cousins: SSMs and RetNet": linear attention with an explicit decay of the carried state;
  *                 with mode bit 1 and the identity map it is that recurrence as stated).
  *   random        oracle_rf_map: positive random features phi(x)_r = exp(w_r . x - |x|^2 / 2)
  *   features      / sqrt(m) for given projections w_r ("Linear Attention Math", section
