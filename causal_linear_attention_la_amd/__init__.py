@@ -151,8 +151,43 @@ def _dims(q, k, v):
     if k.dim() == 3:  # decode tensors given as [B, H, d]
         B, H, d = k.shape
         return B, H, 1, d, v.shape[-1]
+    if k.dim() != 4 or v.dim() != 4:
+        raise ValueError(f"k and v must be [B, H, N, d] tensors, got {tuple(k.shape)} and "
+                         f"{tuple(v.shape)}")
     B, H, N, d = k.shape
     return B, H, N, d, v.shape[-1]
+
+
+def _expect(name, t, shape, dtype):
+    """Raises ValueError unless tensor t (if given) has exactly this shape and dtype: the C ABI
+    sees only pointers and sizes, so a mismatched buffer would be read or written past its
+    end."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _layout(q, k, v, out, states=(), rows=None):
+    """Checks q, k [B,H,N,d], v, out [B,H,N,d_v] (decode: N = 1 given as [B,H,d] and
+    [B,H,d_v], or [B,H,1,.]) of one input dtype, and each float32 state pair (S, z) in
+    ``states`` against [B,H,rows,d_v] and [B,H,rows] (rows = d unless given). Returns
+    (B, H, N, d, d_v) as k and v give them."""
+    B, H, N, d, dv = _dims(q, k, v)
+    dt = k.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"unsupported dtype {dt}")
+    lead = tuple(k.shape[:-1])
+    _expect("v", v, lead + (dv,), dt)
+    _expect("q", q, tuple(k.shape), dt)
+    _expect("out", out, lead + (dv,), dt)
+    r = d if rows is None else rows
+    for S, z in states:
+        _expect("S", S, (B, H, r, dv), torch.float32)
+        _expect("z", z, (B, H, r), torch.float32)
+    return B, H, N, d, dv
 
 
 def _check(status, fn):
@@ -162,8 +197,8 @@ def _check(status, fn):
 
 def la_causal_fwd(q, k, v, out, S=None, z=None, chunk: int = 0, seg_len: int = 0):
     """Causal prefill (see include/la.h). S, z: optional float32 in/out state."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S, z),))
     _check_tensors(q, k, v, out, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
     st = lib.la_causal_fwd_seg(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d,
                                dv, chunk, seg_len, _dtype_code(k), _stream(k))
     _check(st, "la_causal_fwd")
@@ -174,8 +209,8 @@ def la_causal_fwd_state(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk: i
                         seg_len: int = 0):
     """Causal prefill with the initial state (S0, z0; None: zero) and the final state (S, z;
     None: not returned) in separate float32 tensors (see include/la.h)."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S0, z0), (S, z)))
     _check_tensors(q, k, v, out, S0, z0, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
     st = lib.la_causal_fwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0), _ptr(S),
                                  _ptr(z), B, H, N, d, dv, chunk, seg_len, _dtype_code(k), _stream(k))
     _check(st, "la_causal_fwd_state")
@@ -185,8 +220,8 @@ def la_causal_fwd_state(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk: i
 def la_causal_fwd_ex(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk: int = 0,
                      seg_len: int = 0, flags: int = 0):
     """la_causal_fwd_state with variant flags (LA_PHI_IDENTITY, LA_UNNORMALIZED)."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S0, z0), (S, z)))
     _check_tensors(q, k, v, out, S0, z0, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
     st = lib.la_causal_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0), _ptr(S),
                               _ptr(z), B, H, N, d, dv, chunk, seg_len, flags, _dtype_code(k),
                               _stream(k))
@@ -199,8 +234,8 @@ def la_causal_fwd_profiled(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk
     """la_causal_fwd_ex enqueued `reps` times back to back with HIP events around its
     kernels; waits for them and returns the average device milliseconds of (segment sums,
     segment scan, causal outputs)."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S0, z0), (S, z)))
     _check_tensors(q, k, v, out, S0, z0, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
     ms = (ctypes.c_float * 3)()
     st = lib.la_causal_fwd_profiled(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0),
                                     _ptr(S), _ptr(z), B, H, N, d, dv, chunk, seg_len, flags,
@@ -211,8 +246,8 @@ def la_causal_fwd_profiled(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk
 
 def la_global_fwd(q, k, v, out, S, z, chunk: int = 0):
     """Global (non-causal) form; S, z are written. q and out may both be None."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S, z),))
     _check_tensors(q, k, v, out, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
     st = lib.la_global_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d, dv,
                            chunk, _dtype_code(k), _stream(k))
     _check(st, "la_global_fwd")
@@ -221,8 +256,8 @@ def la_global_fwd(q, k, v, out, S, z, chunk: int = 0):
 
 def la_global_fwd_ex(q, k, v, out, S, z, chunk: int = 0, flags: int = 0):
     """la_global_fwd with variant flags."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S, z),))
     _check_tensors(q, k, v, out, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
     st = lib.la_global_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d,
                               dv, chunk, flags, _dtype_code(k), _stream(k))
     _check(st, "la_global_fwd_ex")
@@ -231,8 +266,8 @@ def la_global_fwd_ex(q, k, v, out, S, z, chunk: int = 0, flags: int = 0):
 
 def la_decode_step(q, k, v, out, S, z):
     """One decode step; S, z are updated in place."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S, z),))
     _check_tensors(q, k, v, out, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
     st = lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d, dv,
                             0, _dtype_code(k), _stream(k))
     _check(st, "la_decode_step")
@@ -241,8 +276,8 @@ def la_decode_step(q, k, v, out, S, z):
 
 def la_decode_step_ex(q, k, v, out, S, z, flags: int = 0):
     """la_decode_step with variant flags."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S, z),))
     _check_tensors(q, k, v, out, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
     st = lib.la_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d,
                                dv, flags, _dtype_code(k), _stream(k))
     _check(st, "la_decode_step_ex")
@@ -252,10 +287,10 @@ def la_decode_step_ex(q, k, v, out, S, z, flags: int = 0):
 def la_causal_fwd_decay(q, k, v, out, gamma, S0=None, z0=None, S=None, z=None, chunk: int = 0,
                         seg_len: int = 0, flags: int = 0):
     """Causal prefill of the decayed recurrence; gamma: float32 [H] on the device."""
-    _check_tensors(q, k, v, out, gamma, S0, z0, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
-    if gamma.dtype != torch.float32 or gamma.numel() != H:
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S0, z0), (S, z)))
+    if gamma is None or gamma.dtype != torch.float32 or gamma.numel() != H:
         raise ValueError("gamma must be a float32 tensor of H values")
+    _check_tensors(q, k, v, out, gamma, S0, z0, S, z)
     st = lib.la_causal_fwd_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0), _ptr(S),
                                  _ptr(z), _ptr(gamma), B, H, N, d, dv, chunk, seg_len, flags,
                                  _dtype_code(k), _stream(k))
@@ -265,10 +300,10 @@ def la_causal_fwd_decay(q, k, v, out, gamma, S0=None, z0=None, S=None, z=None, c
 
 def la_decode_step_decay(q, k, v, out, S, z, gamma, flags: int = 0):
     """One decode step of the decayed recurrence; S, z are updated in place."""
-    _check_tensors(q, k, v, out, S, z, gamma)
-    B, H, N, d, dv = _dims(q, k, v)
-    if gamma.dtype != torch.float32 or gamma.numel() != H:
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S, z),))
+    if gamma is None or gamma.dtype != torch.float32 or gamma.numel() != H:
         raise ValueError("gamma must be a float32 tensor of H values")
+    _check_tensors(q, k, v, out, S, z, gamma)
     st = lib.la_decode_step_decay(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z),
                                   _ptr(gamma), B, H, N, d, dv, flags, _dtype_code(k), _stream(k))
     _check(st, "la_decode_step_decay")
@@ -279,11 +314,12 @@ def la_causal_fwd_rf(q, k, v, out, W, S0=None, z0=None, S=None, z=None, chunk: i
                      seg_len: int = 0, flags: int = 0):
     """Causal prefill over positive random features of q and k (projections W [m, d]); the
     state S [B,H,m,d_v], z [B,H,m] as for la_causal_fwd_state."""
-    _check_tensors(q, k, v, out, W, S0, z0, S, z)
-    B, H, N, d, dv = _dims(q, k, v)
+    if W is None or W.dim() != 2:
+        raise ValueError("W must be a [m, d] tensor")
     m = W.shape[0]
-    if W.dim() != 2 or W.shape[1] != d or W.dtype != k.dtype:
-        raise ValueError(f"W must be [m, {d}] of the input dtype")
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S0, z0), (S, z)), rows=m)
+    _expect("W", W, (m, d), k.dtype)
+    _check_tensors(q, k, v, out, W, S0, z0, S, z)
     st = lib.la_causal_fwd_rf(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(W), _ptr(S0), _ptr(z0),
                               _ptr(S), _ptr(z), B, H, N, d, dv, m, chunk, seg_len, flags,
                               _dtype_code(k), _stream(k))
@@ -294,12 +330,14 @@ def la_causal_fwd_rf(q, k, v, out, W, S0=None, z0=None, S=None, z=None, chunk: i
 def la_rf_features(x, W, f):
     """Positive random features f[..., r] = exp(W[r] . x - |x|^2 / 2) / sqrt(m) of the rows of
     x [..., d] for projections W [m, d]; f [..., m] (all one dtype, contiguous, on the GPU)."""
-    _check_tensors(x, W, f)
+    if W.dim() != 2:
+        raise ValueError("W must be a [m, d] tensor")
     m, d = W.shape
     if x.shape[-1] != d or f.shape[-1] != m or x.shape[:-1] != f.shape[:-1]:
         raise ValueError(f"shapes x {tuple(x.shape)}, W {tuple(W.shape)}, f {tuple(f.shape)} do not match")
     if x.dtype != W.dtype or x.dtype != f.dtype:
         raise ValueError("x, W and f must share one dtype")
+    _check_tensors(x, W, f)
     rows = x.numel() // d if d else 0
     st = lib.la_rf_features(_ptr(x), _ptr(W), _ptr(f), rows, d, m, _dtype_code(x), _stream(x))
     _check(st, "la_rf_features")

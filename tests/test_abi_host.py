@@ -271,3 +271,96 @@ def test_binding_rejects_host_tensors():
 def test_error_type_carries_status():
     e = la.LAError(la.LA_ENOTSUP, "la_causal_fwd")
     assert e.status == la.LA_ENOTSUP and "unsupported" in str(e)
+
+
+def _host(*shape, dtype=None):
+    torch = pytest.importorskip("torch")
+    return torch.zeros(*shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_checks_every_tensor_layout():
+    """The C ABI sees pointers and sizes only, so the binding checks each tensor's shape and
+    dtype against (B, H, N, d, d_v, dtype) before any call: a wrong one raises ValueError
+    naming the tensor (host tensors of the right layout get as far as the device check)."""
+    torch = pytest.importorskip("torch")
+    f32 = torch.float32
+    B, H, N, d, dv = 2, 3, 8, 16, 32
+    q, k, v, out = _host(B, H, N, d), _host(B, H, N, d), _host(B, H, N, dv), _host(B, H, N, dv)
+    S, z = _host(B, H, d, dv, dtype=f32), _host(B, H, d, dtype=f32)
+    with pytest.raises(ValueError, match="device tensors only"):
+        la.la_causal_fwd(q, k, v, out, S, z)
+    bad = [
+        ("q", dict(q=_host(B, H, N + 1, d))),
+        ("q", dict(q=_host(B, H, N, d, dtype=f32))),
+        ("v", dict(v=_host(B, H, N - 1, dv))),
+        ("out", dict(out=_host(B, H, N, dv, dtype=f32))),
+        ("out", dict(out=_host(B, H, N, d))),
+        ("S", dict(S=_host(B, H, d, dv))),
+        ("S", dict(S=_host(B, H, dv, d, dtype=f32))),
+        ("z", dict(z=_host(B, H, dv, dtype=f32))),
+    ]
+    for name, kw in bad:
+        a = dict(q=q, k=k, v=v, out=out, S=S, z=z)
+        a.update(kw)
+        with pytest.raises(ValueError, match=f"^{name} must"):
+            la.la_causal_fwd(**a)
+        with pytest.raises(ValueError, match=f"^{name} must"):
+            la.la_causal_fwd_ex(a["q"], a["k"], a["v"], a["out"], None, None, a["S"], a["z"])
+        with pytest.raises(ValueError, match=f"^{name} must"):
+            la.la_global_fwd(a["q"], a["k"], a["v"], a["out"], a["S"], a["z"])
+    # separate initial state
+    with pytest.raises(ValueError, match="^S must"):
+        la.la_causal_fwd_state(q, k, v, out, _host(B, H, d, d, dtype=f32), z, S, z)
+    with pytest.raises(ValueError, match="^z must"):
+        la.la_causal_fwd_state(q, k, v, out, S, _host(B, H, d), S, z)
+    # k and v must be 4-D outside decode
+    with pytest.raises(ValueError, match="k and v"):
+        la.la_causal_fwd(q, _host(B, H, N, d, 1), v, out)
+    with pytest.raises(TypeError):
+        la.la_causal_fwd(q.half(), k.half(), v.half(), out.half())
+
+
+def test_binding_checks_decode_layout():
+    torch = pytest.importorskip("torch")
+    f32 = torch.float32
+    B, H, d, dv = 4, 2, 16, 16
+    q, k, v, out = _host(B, H, d), _host(B, H, d), _host(B, H, dv), _host(B, H, dv)
+    S, z = _host(B, H, d, dv, dtype=f32), _host(B, H, d, dtype=f32)
+    gamma = _host(H, dtype=f32)
+    with pytest.raises(ValueError, match="device tensors only"):
+        la.la_decode_step(q, k, v, out, S, z)
+    with pytest.raises(ValueError, match="device tensors only"):
+        la.la_decode_step(q[:, :, None], k[:, :, None], v[:, :, None], out[:, :, None], S, z)
+    with pytest.raises(ValueError, match="^out must"):
+        la.la_decode_step(q, k, v, _host(B, H, dv, dtype=f32), S, z)
+    with pytest.raises(ValueError, match="^S must"):
+        la.la_decode_step_ex(q, k, v, out, _host(B, H, d, dv), z)
+    with pytest.raises(ValueError, match="^q must"):
+        la.la_decode_step(_host(B, H, 1, d), k, v, out, S, z)
+    with pytest.raises(ValueError, match="gamma"):
+        la.la_decode_step_decay(q, k, v, out, S, z, _host(H))
+    with pytest.raises(ValueError, match="gamma"):
+        la.la_decode_step_decay(q, k, v, out, S, z, _host(H + 1, dtype=f32))
+    with pytest.raises(ValueError, match="device tensors only"):
+        la.la_decode_step_decay(q, k, v, out, S, z, gamma)
+
+
+def test_binding_checks_random_feature_layout():
+    torch = pytest.importorskip("torch")
+    f32 = torch.float32
+    B, H, N, d, dv, m = 1, 2, 8, 16, 16, 32
+    q, k, v, out = _host(B, H, N, d), _host(B, H, N, d), _host(B, H, N, dv), _host(B, H, N, dv)
+    W = _host(m, d)
+    S, z = _host(B, H, m, dv, dtype=f32), _host(B, H, m, dtype=f32)
+    with pytest.raises(ValueError, match="device tensors only"):
+        la.la_causal_fwd_rf(q, k, v, out, W, None, None, S, z)
+    with pytest.raises(ValueError, match="^S must"):
+        la.la_causal_fwd_rf(q, k, v, out, W, None, None, _host(B, H, d, dv, dtype=f32), z)
+    with pytest.raises(ValueError, match="^W must"):
+        la.la_causal_fwd_rf(q, k, v, out, _host(m, d, dtype=f32), None, None, S, z)
+    with pytest.raises(ValueError, match="^W must"):
+        la.la_causal_fwd_rf(q, k, v, out, _host(m, d + 1), None, None, S, z)
+    with pytest.raises(ValueError, match="do not match"):
+        la.la_rf_features(q, W, _host(B, H, N, m + 1))
+    with pytest.raises(ValueError, match="one dtype"):
+        la.la_rf_features(q, W, _host(B, H, N, m, dtype=f32))
