@@ -389,11 +389,11 @@ __device__ __forceinline__ void key_sum(f32x4 (&zacc)[ZT], const uint16_t *k)
 }
 
 // ---- decay of the carried state (the retention recurrence S_t = gamma S_{t-1} + ...) ------
-// gamma^n = exp2(n lg) with lg = log2(gamma) clamped to -1000, so gamma = 0 gives 1 for n = 0
-// and 0 for n > 0 without an infinity (no 0 * inf).
+// gamma^n = exp2(n lg) with lg = decay_log2 (log2(gamma) clamped to -1000, so gamma = 0 gives 1
+// for n = 0 and 0 for n > 0 without an infinity; NaN for a negative or NaN gamma).
 __device__ __forceinline__ float decay_lg(const float *gamma, int bh, int H)
 {
-    return gamma ? fmaxf(log2f(gamma[bh % H]), -1000.f) : 0.f;
+    return decay_log2(gamma, bh, H);
 }
 __device__ __forceinline__ float dpow(float lg, int n) { return __builtin_amdgcn_exp2f(lg * (float)n); }
 

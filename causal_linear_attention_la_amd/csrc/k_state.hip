@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T 
     const size_t bh = blockIdx.x;
     f32x4 *Sh = reinterpret_cast<f32x4 *>(S + bh * D * DV);
     // decay of the carried state (1 without gamma): S' = gd S + phi(k) v^T, z' = gd z + phi(k)
-    const float gd = gamma ? gamma[bh % H] : 1.f;
+    const float gd = decay_gamma(gamma, (long)bh, H);
 
     // the head's state rows, all loads in flight before any use
     f32x4 s[RPT];

@@ -46,11 +46,22 @@ __device__ __forceinline__ float phi_exact(float x) { return x > 0.f ? x + 1.f :
 __device__ __forceinline__ float feature(float x, bool identity) { return identity ? x : phi_exact(x); }
 
 // ---- decay of the carried state (the retention recurrence) -----------------------------
-// log2 of the decay gamma of head bh % H (0 when gamma is null: no decay), clamped to -1000 so
-// that gamma = 0 gives gamma^0 = 1 and gamma^n = 0 for n > 0 through exp2 without infinities.
+// The decay gamma of head bh % H as every form reads it: 1 when gamma is null (no decay), NaN
+// when the value is negative or NaN (outside the contract; the NaN then reaches every output
+// and the state of that head, in the prefill and the decode forms alike -- nothing is clamped).
+__device__ __forceinline__ float decay_gamma(const float *gamma, long bh, int H)
+{
+    if (!gamma)
+        return 1.f;
+    const float g = gamma[bh % H];
+    return g >= 0.f ? g : __builtin_nanf("");
+}
+// log2 of that decay (0: none), clamped below at -1000 so that gamma = 0 gives gamma^0 = 1 and
+// gamma^n = 0 for n > 0 through exp2 without infinities; NaN stays NaN.
 __device__ __forceinline__ float decay_log2(const float *gamma, long bh, int H)
 {
-    return gamma ? fmaxf(log2f(gamma[bh % H]), -1000.f) : 0.f;
+    const float g = decay_gamma(gamma, bh, H);
+    return g != g ? g : fmaxf(log2f(g), -1000.f);
 }
 __device__ __forceinline__ float decay_pow(float lg, int n) { return exp2f(lg * (float)n); }
 

@@ -179,3 +179,38 @@ def test_retention_workload_full():
                                      gamma=gam.astype(np.float64))
     check("out", o, oo, TOL["bf16"])
     check("S", S, So, TOL["bf16"])
+
+
+@pytest.mark.parametrize("dtype,d,chunk,seg", [("bf16", 128, 0, 64), ("f32", 32, 16, 0)])
+def test_decay_out_of_range_is_nan(dtype, d, chunk, seg):
+    """A negative or NaN gamma (outside the [0, 1] contract) makes every output and the state
+    of its head NaN, in the prefill and in the decode step alike; the other heads are
+    unaffected."""
+    gam = [0.9, -0.5, float("nan"), 0.5]
+    good = [0, 3]
+    B, H, N = 2, len(gam), 300
+    q, k, v = datagen.qkv(B, H, N + 1, d, d, 990 + d, 1 / math.sqrt(d), dtype)
+    pre = [x[:, :, :N].contiguous() for x in (q, k, v)]
+    say(f"decay out of range dtype={dtype} d={d} chunk={chunk} seg={seg}")
+    o, S, z = causal_decay(*pre, gam, 0, chunk=chunk, seg_len=seg)
+    for h in (1, 2):
+        assert np.isnan(o[:, h]).all() and np.isnan(S[:, h]).all() and np.isnan(z[:, h]).all(), h
+    sub = [f64(x[:, good]) for x in pre]
+    oo, So, zo, _, _ = oracle.causal(*sub, gamma=[gam[h] for h in good])
+    check("good heads out", o[:, good], oo, TOL[dtype])
+    check("good heads S", S[:, good], So, TOL[dtype])
+    # one decode step from the prefill's state
+    Sd = torch.from_numpy(S.astype(np.float32)).to(DEV)
+    zd = torch.from_numpy(z.astype(np.float32)).to(DEV)
+    qt, kt, vt = (to_dev(x[:, :, N].contiguous()) for x in (q, k, v))
+    out = torch.empty((B, H, d), dtype=qt.dtype, device=DEV)
+    la().la_decode_step_decay(qt, kt, vt, out, Sd, zd, torch.tensor(gam, dtype=torch.float32,
+                                                                     device=DEV))
+    torch.cuda.synchronize()
+    od, Sn = f64(out), f64(Sd)
+    for h in (1, 2):
+        assert np.isnan(od[:, h]).all() and np.isnan(Sn[:, h]).all(), h
+    oo2, So2, _, _, _ = oracle.causal(*[f64(x[:, good]) for x in (q, k, v)],
+                                      gamma=[gam[h] for h in good])
+    check("good heads decode", od[:, good], oo2[:, :, N], TOL[dtype])
+    check("good heads decode S", Sn[:, good], So2, TOL[dtype])
