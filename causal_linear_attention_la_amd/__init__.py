@@ -17,6 +17,10 @@ The entry points keep the C names:
     la_rf_features(x, W, f)                            # positive random features
     la_causal_fwd_rf(q, k, v, out, W, S0=None, z0=None, S=None, z=None, chunk=0, seg_len=0,
                      flags=0)                          # causal over random features of q, k
+    la_causal_fwd_ws(q, k, v, out, ws, S0=None, z0=None, S=None, z=None, gamma=None, chunk=0,
+                     seg_len=0, flags=0)               # caller-supplied workspace ws
+    la_global_fwd_ws(q, k, v, out, S, z, ws, chunk=0, flags=0)
+    la_release_cache()                                 # frees the library's cached scratch
 with q, k [B,H,N,d], v, out [B,H,N,d_v] (bf16 or float32, contiguous, on the GPU),
 S [B,H,d,d_v] and z [B,H,d] float32; flags is a bitwise or of LA_PHI_IDENTITY and
 LA_UNNORMALIZED. A non-zero status raises ``LAError``.
@@ -48,7 +52,8 @@ LA_PHI_IDENTITY, LA_UNNORMALIZED = 1, 2
 EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
            "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
            "la_decode_step_ex", "la_causal_fwd_decay", "la_decode_step_decay", "la_rf_features",
-           "la_causal_fwd_rf", "la_workspace_bytes", "la_segments", "la_strerror", "la_version")
+           "la_causal_fwd_rf", "la_causal_fwd_ws", "la_global_fwd_ws", "la_release_cache",
+           "la_workspace_bytes", "la_segments", "la_strerror", "la_version")
 
 
 class LAError(RuntimeError):
@@ -78,10 +83,14 @@ def _load(path: Path):
     lib.la_causal_fwd_decay.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp] + [i] * 9 + [vp]
     lib.la_decode_step_decay.argtypes = [vp, vp, vp, vp, fp, fp, fp] + [i] * 7 + [vp]
     lib.la_causal_fwd_rf.argtypes = [vp, vp, vp, vp, vp, fp, fp, fp, fp] + [i] * 10 + [vp]
+    sz = ctypes.c_size_t
+    lib.la_causal_fwd_ws.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp] + [i] * 9 + [vp, sz, vp]
+    lib.la_global_fwd_ws.argtypes = core + [i, i, vp, sz, vp]
+    lib.la_release_cache.argtypes = []
     for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
               "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
               "la_decode_step_ex", "la_rf_features", "la_causal_fwd_decay", "la_decode_step_decay",
-              "la_causal_fwd_rf"):
+              "la_causal_fwd_rf", "la_causal_fwd_ws", "la_global_fwd_ws", "la_release_cache"):
         getattr(lib, f).restype = ctypes.c_int
     lib.la_workspace_bytes.argtypes = [i] * 8 + [i]
     lib.la_workspace_bytes.restype = ctypes.c_size_t
@@ -308,6 +317,54 @@ def la_decode_step_decay(q, k, v, out, S, z, gamma, flags: int = 0):
                                   _ptr(gamma), B, H, N, d, dv, flags, _dtype_code(k), _stream(k))
     _check(st, "la_decode_step_decay")
     return out
+
+
+def _workspace(ws, need):
+    """ws: a device tensor of at least `need` bytes (contiguous), or None when need is 0."""
+    if ws is None:
+        if need:
+            raise ValueError(f"this call needs a workspace of {need} bytes")
+        return None, 0
+    nbytes = ws.numel() * ws.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, the call needs {need}")
+    return ws, nbytes
+
+
+def la_causal_fwd_ws(q, k, v, out, ws, S0=None, z0=None, S=None, z=None, gamma=None,
+                     chunk: int = 0, seg_len: int = 0, flags: int = 0):
+    """Causal prefill with a caller-supplied workspace `ws` (a device tensor of at least
+    la_workspace_bytes(0, ...) bytes; None when that is 0): la_causal_fwd_ex, or
+    la_causal_fwd_decay when gamma is given. Allocates nothing and never waits."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S0, z0), (S, z)))
+    if gamma is not None and (gamma.dtype != torch.float32 or gamma.numel() != H):
+        raise ValueError("gamma must be a float32 tensor of H values")
+    need = la_workspace_bytes(0, B, H, N, d, dv, chunk, seg_len, _dtype_code(k))
+    ws, nbytes = _workspace(ws, need)
+    _check_tensors(q, k, v, out, S0, z0, S, z, gamma, ws)
+    st = lib.la_causal_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0), _ptr(S),
+                              _ptr(z), _ptr(gamma), B, H, N, d, dv, chunk, seg_len, flags,
+                              _dtype_code(k), _ptr(ws), nbytes, _stream(k))
+    _check(st, "la_causal_fwd_ws")
+    return out
+
+
+def la_global_fwd_ws(q, k, v, out, S, z, ws, chunk: int = 0, flags: int = 0):
+    """Global form with a caller-supplied workspace `ws` (at least la_workspace_bytes(1, ...)
+    bytes; None when that is 0). q and out may both be None."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S, z),))
+    need = la_workspace_bytes(1, B, H, N, d, dv, chunk, 0, _dtype_code(k))
+    ws, nbytes = _workspace(ws, need)
+    _check_tensors(q, k, v, out, S, z, ws)
+    st = lib.la_global_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d,
+                              dv, chunk, flags, _dtype_code(k), _ptr(ws), nbytes, _stream(k))
+    _check(st, "la_global_fwd_ws")
+    return out
+
+
+def la_release_cache():
+    """Frees the scratch blocks the convenience entry points cached (waits for their last use)."""
+    _check(lib.la_release_cache(), "la_release_cache")
 
 
 def la_causal_fwd_rf(q, k, v, out, W, S0=None, z0=None, S=None, z=None, chunk: int = 0,

@@ -160,81 +160,130 @@ int validate(Form form, const void *q, const void *k, const void *v, void *out, 
     return LA_OK;
 }
 
-// Scratch blocks kept per (device, stream) for the life of the process. A call takes a free
-// block of its stream and gives it back when it has enqueued its kernels: the next call on
-// that stream runs after it in stream order, so a block is reused with no wait on the host or
-// the device. (Taking and returning stream-ordered pool memory in every call made the call
-// wait on the host for the stream to drain, measured on MI355X: the host could not run ahead
-// of the device.) Calls on different streams never share a block. When no free block of the
-// stream is large enough, the largest free one is returned (after the stream has drained: the
-// previous call may still be reading it) and a new one is allocated, so this waits only when
-// a stream's shapes grow.
+// Scratch blocks of the convenience entry points (those without a workspace argument), kept for
+// the life of the process (or until la_release_cache). A call takes any free block of its
+// device that is large enough and makes its stream wait, on the device, for the block's last
+// use (hipStreamWaitEvent on an event recorded after that use's kernels; no wait when that use
+// was on the same stream, which stream order already covers); the host never waits. When no
+// free block is large enough a new one is allocated (hipMalloc). Reuse therefore depends on
+// completion, not on which stream handle a block was last used with: per-thread default
+// streams, streams destroyed and handles reused, and blocks of streams that no longer exist are
+// all handled the same way. (Taking and returning stream-ordered pool memory in every call made
+// the call wait on the host for the stream to drain, measured on MI355X: the host could not run
+// ahead of the device.) HIP calls are made outside the lock.
 struct BlockCache {
     struct Block {
         int dev;
-        hipStream_t st;
         void *ptr;
         size_t bytes;
+        hipEvent_t last; // recorded after the kernels of the call that last used the block
+        bool used;       // `last` has been recorded at least once
         bool busy;
     };
     std::mutex mu;
-    std::vector<Block> blocks;
+    std::vector<Block *> blocks; // never shrinks except in release()
 
-    hipError_t take(int dev, hipStream_t st, size_t bytes, void **out)
+    hipError_t take(int dev, hipStream_t st, size_t bytes, Block **out)
     {
-        std::lock_guard<std::mutex> lock(mu);
-        Block *fit = nullptr, *small = nullptr;
-        for (Block &b : blocks) {
-            if (b.dev != dev || b.st != st || b.busy)
-                continue;
-            if (b.bytes >= bytes) {
-                if (!fit || b.bytes < fit->bytes)
-                    fit = &b;
-            } else if (!small || b.bytes > small->bytes) {
-                small = &b;
-            }
+        Block *fit = nullptr;
+        {
+            std::lock_guard<std::mutex> lock(mu);
+            for (Block *b : blocks)
+                if (b->dev == dev && !b->busy && b->bytes >= bytes && (!fit || b->bytes < fit->bytes))
+                    fit = b;
+            if (fit)
+                fit->busy = true;
         }
         if (fit) {
-            fit->busy = true;
-            *out = fit->ptr;
+            const hipError_t e = fit->used ? hipStreamWaitEvent(st, fit->last, 0) : hipSuccess;
+            if (e != hipSuccess) {
+                std::lock_guard<std::mutex> lock(mu);
+                fit->busy = false;
+                return e;
+            }
+            *out = fit;
             return hipSuccess;
         }
-        if (small) {
-            hipError_t e = hipStreamSynchronize(st);
-            if (e == hipSuccess)
-                e = hipFree(small->ptr);
+        Block *b = new Block{dev, nullptr, bytes, nullptr, false, true};
+        hipError_t e = hipMalloc(&b->ptr, bytes);
+        if (e == hipSuccess) {
+            e = hipEventCreateWithFlags(&b->last, hipEventDisableTiming);
             if (e != hipSuccess)
-                return e;
-            blocks.erase(blocks.begin() + (small - blocks.data()));
+                (void)hipFree(b->ptr);
         }
-        void *p = nullptr;
-        const hipError_t e = hipMalloc(&p, bytes);
-        if (e != hipSuccess)
+        if (e != hipSuccess) {
+            delete b;
             return e;
-        blocks.push_back(Block{dev, st, p, bytes, true});
-        *out = p;
+        }
+        std::lock_guard<std::mutex> lock(mu);
+        blocks.push_back(b);
+        *out = b;
         return hipSuccess;
     }
-    void give_back(void *ptr)
+    // After the call's kernels are enqueued on `st`: mark the block's last use there and free it
+    // for other calls. If the mark cannot be recorded the block stays busy for good (its last
+    // use would be unknown).
+    hipError_t give_back(Block *b, hipStream_t st)
     {
+        const hipError_t e = hipEventRecord(b->last, st);
         std::lock_guard<std::mutex> lock(mu);
-        for (Block &b : blocks)
-            if (b.ptr == ptr)
-                b.busy = false;
+        if (e == hipSuccess) {
+            b->used = true;
+            b->busy = false;
+        }
+        return e;
+    }
+    // Frees every block not in use by a call, after the work that last used it.
+    hipError_t release()
+    {
+        std::vector<Block *> mine;
+        {
+            std::lock_guard<std::mutex> lock(mu);
+            std::vector<Block *> keep;
+            for (Block *b : blocks)
+                (b->busy ? keep : mine).push_back(b);
+            blocks.swap(keep);
+        }
+        hipError_t err = hipSuccess;
+        for (Block *b : mine) {
+            int cur = 0;
+            hipError_t e = hipGetDevice(&cur);
+            if (e == hipSuccess && cur != b->dev)
+                e = hipSetDevice(b->dev);
+            if (e == hipSuccess && b->used)
+                e = hipEventSynchronize(b->last);
+            if (e == hipSuccess)
+                e = hipEventDestroy(b->last);
+            if (e == hipSuccess)
+                e = hipFree(b->ptr);
+            if (cur != b->dev)
+                (void)hipSetDevice(cur);
+            if (e != hipSuccess) {
+                err = e;
+                std::lock_guard<std::mutex> lock(mu);
+                blocks.push_back(b); // not freed: keep it (and its pointer) known
+            } else {
+                delete b;
+            }
+        }
+        return err;
     }
 };
 
 BlockCache &block_cache()
 {
-    static BlockCache *c = new BlockCache(); // never destroyed: blocks live until the process ends
+    static BlockCache *c = new BlockCache(); // never destroyed: blocks live until release()
     return *c;
 }
 
-// Scratch device memory of one call, released when the call has enqueued its work.
+// Scratch device memory of one convenience call: a cached block (or, under stream capture,
+// stream-ordered pool memory, so that every replay of the graph owns its scratch), released by
+// finish() once the call's kernels are enqueued.
 struct Workspace {
     float *ptr = nullptr;
     hipStream_t st = nullptr;
-    bool pooled = false; // from the device's stream-ordered pool (stream under capture)
+    BlockCache::Block *blk = nullptr;
+    bool pooled = false;
     hipError_t init(size_t bytes, hipStream_t stream)
     {
         st = stream;
@@ -245,9 +294,8 @@ struct Workspace {
         if (e != hipSuccess)
             return e;
         if (cs != hipStreamCaptureStatusNone) {
-            // allocation and free nodes in the captured graph, so every replay owns its
-            // scratch (the device's default pool: measured to capture on ROCm where a private
-            // pool does not)
+            // allocation and free nodes in the captured graph (the device's default pool:
+            // measured to capture on ROCm where a private pool does not)
             e = hipMallocAsync(reinterpret_cast<void **>(&ptr), bytes, stream);
             pooled = e == hipSuccess;
             return e;
@@ -256,20 +304,24 @@ struct Workspace {
         e = hipGetDevice(&dev);
         if (e != hipSuccess)
             return e;
-        void *p = nullptr;
-        e = block_cache().take(dev, stream, bytes, &p);
-        ptr = static_cast<float *>(p);
+        e = block_cache().take(dev, stream, bytes, &blk);
+        if (e == hipSuccess)
+            ptr = static_cast<float *>(blk->ptr);
         return e;
     }
-    ~Workspace()
+    hipError_t finish()
     {
-        if (!ptr)
-            return;
+        hipError_t e = hipSuccess;
         if (pooled)
-            (void)hipFreeAsync(ptr, st);
-        else
-            block_cache().give_back(ptr);
+            e = hipFreeAsync(ptr, st);
+        else if (blk)
+            e = block_cache().give_back(blk, st);
+        ptr = nullptr;
+        blk = nullptr;
+        pooled = false;
+        return e;
     }
+    ~Workspace() { (void)finish(); }
 };
 
 // HIP events marking the phase boundaries of one causal call (profiling form only).
@@ -318,31 +370,30 @@ bool gamma_ok(const float *gamma, int H, const void *out, const float *S, const 
            !overlap(sg, span(z, BH * d * 4));
 }
 
-// gamma (optional): per-head decay of the carried state, device float32 [H].
+// gamma (optional): per-head decay of the carried state, device float32 [H]. wsp: pl.ws_bytes
+// of device scratch (unused when the plan has one segment).
 int run_causal(const void *q, const void *k, const void *v, void *out, const float *S0,
                const float *z0, float *S, float *z, int N, int d, int dv, bool bf16, int flags,
-               const float *gamma, int H, const Plan &pl, hipStream_t st, Stamps *ts = nullptr)
+               const float *gamma, int H, const Plan &pl, float *wsp, hipStream_t st,
+               Stamps *ts = nullptr)
 {
     const int BH = (int)pl.BH, P = pl.P, L = pl.L;
     const long E = (long)d * dv + d;
-    Workspace ws;
-    if (ws.init(pl.ws_bytes, st) != hipSuccess)
-        return LA_EHIP;
     hipError_t e = mark(ts, 0, st);
     const float *preS = S0, *prez = z0; // P == 1: the initial state (or none) is the prefix
     long ps = (long)d * dv, pzs = d;
     if (P > 1 && e == hipSuccess) {
         // sums of segments 0..P-2, then the exclusive prefix over segments in place
-        e = pl.mfma ? la::agg_mfma(d, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L,
+        e = pl.mfma ? la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
                                    P - 1, P, gamma, H, st)
-                    : la::agg_valu(bf16, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N,
+                    : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
                                    d, dv, pl.chunk, L, P - 1, P, gamma, H, st);
         if (e == hipSuccess)
             e = mark(ts, 1, st);
         if (e == hipSuccess)
-            e = la::seg_exclusive_scan(ws.ptr, S0, z0, BH, P, d, dv, gamma, H, L, st);
-        preS = ws.ptr;
-        prez = ws.ptr + (long)d * dv;
+            e = la::seg_exclusive_scan(wsp, S0, z0, BH, P, d, dv, gamma, H, L, st);
+        preS = wsp;
+        prez = wsp + (long)d * dv;
         ps = pzs = E;
     } else if (e == hipSuccess) {
         e = mark(ts, 1, st);
@@ -360,21 +411,18 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
 }
 
 int run_global(const void *q, const void *k, const void *v, void *out, float *S, float *z, int N,
-               int d, int dv, bool bf16, int flags, const Plan &pl, hipStream_t st)
+               int d, int dv, bool bf16, int flags, const Plan &pl, float *wsp, hipStream_t st)
 {
     const int BH = (int)pl.BH, P = pl.P, L = pl.L;
     const long E = (long)d * dv + d;
-    Workspace ws;
-    if (ws.init(pl.ws_bytes, st) != hipSuccess)
-        return LA_EHIP;
     hipError_t e;
     if (P > 1) {
-        e = pl.mfma ? la::agg_mfma(d, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L,
+        e = pl.mfma ? la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
                                    P, P, nullptr, 1, st)
-                    : la::agg_valu(bf16, flags, k, v, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N,
+                    : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
                                    d, dv, pl.chunk, L, P, P, nullptr, 1, st);
         if (e == hipSuccess)
-            e = la::seg_total(ws.ptr, S, z, BH, P, d, dv, st);
+            e = la::seg_total(wsp, S, z, BH, P, d, dv, st);
     } else {
         e = pl.mfma ? la::agg_mfma(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1, nullptr,
                                    1, st)
@@ -387,6 +435,60 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
                                    d, 1, nullptr, nullptr, BH, N, d, dv, pl.chunk, L, P, nullptr, 1,
                                    st);
     return e == hipSuccess ? LA_OK : LA_EHIP;
+}
+
+// The convenience forms: scratch from the library's cache (or the stream-ordered pool under
+// capture), released once the call's kernels are enqueued.
+int run_causal_cached(const void *q, const void *k, const void *v, void *out, const float *S0,
+                      const float *z0, float *S, float *z, int N, int d, int dv, bool bf16,
+                      int flags, const float *gamma, int H, const Plan &pl, hipStream_t st,
+                      Stamps *ts = nullptr)
+{
+    Workspace ws;
+    if (ws.init(pl.ws_bytes, st) != hipSuccess)
+        return LA_EHIP;
+    const int r = run_causal(q, k, v, out, S0, z0, S, z, N, d, dv, bf16, flags, gamma, H, pl, ws.ptr,
+                             st, ts);
+    const hipError_t e = ws.finish();
+    return r != LA_OK ? r : (e == hipSuccess ? LA_OK : LA_EHIP);
+}
+
+int run_global_cached(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                      int N, int d, int dv, bool bf16, int flags, const Plan &pl, hipStream_t st)
+{
+    Workspace ws;
+    if (ws.init(pl.ws_bytes, st) != hipSuccess)
+        return LA_EHIP;
+    const int r = run_global(q, k, v, out, S, z, N, d, dv, bf16, flags, pl, ws.ptr, st);
+    const hipError_t e = ws.finish();
+    return r != LA_OK ? r : (e == hipSuccess ? LA_OK : LA_EHIP);
+}
+
+// A caller-supplied workspace: large enough for the plan, 16-byte aligned (or NULL when the plan
+// needs none), and apart from every buffer the call reads or writes.
+bool workspace_ok(const void *ws, size_t ws_bytes, const Plan &pl, const std::vector<Span> &bufs)
+{
+    if (!pl.ws_bytes)
+        return true;
+    if (!ws || !aligned16(ws) || ws_bytes < pl.ws_bytes)
+        return false;
+    const Span w = span(ws, pl.ws_bytes);
+    for (Span b : bufs)
+        if (overlap(w, b))
+            return false;
+    return true;
+}
+
+// The buffers of a causal or global call, as validate() sized them.
+std::vector<Span> call_spans(const void *q, const void *k, const void *v, const void *out,
+                             const float *S0, const float *z0, const float *S, const float *z,
+                             const float *gamma, int B, int H, int N, int d, int dv, int dtype)
+{
+    const size_t es = dtype == LA_BF16 ? 2 : 4;
+    const size_t BH = (size_t)B * (size_t)H;
+    return {span(q, BH * N * d * es),   span(k, BH * N * d * es),   span(v, BH * N * dv * es),
+            span(out, BH * N * dv * es), span(S0, BH * d * dv * 4), span(z0, BH * d * 4),
+            span(S, BH * d * dv * 4),   span(z, BH * d * 4),        span(gamma, (size_t)H * 4)};
 }
 
 // The random-feature causal call: q, k [B,H,N,d] are mapped with W [m, d] to features
@@ -468,7 +570,8 @@ int run_causal_rf(const void *q, const void *k, const void *v, void *out, const 
         if (e == hipSuccess)
             e = la::causal_rf_mfma(d, flags, q, k, v, W, out, preS, prez, ps, pzs, S, z, BH, N, L, P,
                                    st);
-        return e == hipSuccess ? LA_OK : LA_EHIP;
+        const hipError_t ef = ws.finish();
+        return e == hipSuccess && ef == hipSuccess ? LA_OK : LA_EHIP;
     }
     // features through scratch memory, then the identity-map causal form over them
     const size_t es = bf16 ? 2 : 4;
@@ -483,8 +586,10 @@ int run_causal_rf(const void *q, const void *k, const void *v, void *out, const 
         e = la::rf_features(bf16, k, W, fk, rows, d, m, st);
     if (e != hipSuccess)
         return LA_EHIP;
-    return run_causal(fq, fk, v, out, S0, z0, S, z, N, m, dv, bf16, flags | LA_PHI_IDENTITY, nullptr,
-                      1, pl, st);
+    const int r = run_causal_cached(fq, fk, v, out, S0, z0, S, z, N, m, dv, bf16,
+                                    flags | LA_PHI_IDENTITY, nullptr, 1, pl, st);
+    const hipError_t ef = feat.finish();
+    return r != LA_OK ? r : (ef == hipSuccess ? LA_OK : LA_EHIP);
 }
 
 } // namespace
@@ -502,8 +607,8 @@ int la_causal_fwd_ex(const void *q, const void *k, const void *v, void *out, con
                            dtype, &pl);
     if (s != LA_OK)
         return s;
-    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, nullptr, 1,
-                      pl, stream);
+    return run_causal_cached(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, nullptr,
+                             1, pl, stream);
 }
 
 int la_causal_fwd_decay(const void *q, const void *k, const void *v, void *out, const float *S0,
@@ -518,8 +623,8 @@ int la_causal_fwd_decay(const void *q, const void *k, const void *v, void *out, 
                            dtype, &pl);
     if (s != LA_OK)
         return s;
-    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, gamma, H, pl,
-                      stream);
+    return run_causal_cached(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, gamma,
+                             H, pl, stream);
 }
 
 int la_causal_fwd_state(const void *q, const void *k, const void *v, void *out, const float *S0,
@@ -554,8 +659,8 @@ int la_causal_fwd_profiled(const void *q, const void *k, const void *v, void *ou
         if (t.init() != hipSuccess)
             return LA_EHIP;
     for (Stamps &t : ts) {
-        const int r = run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags,
-                                 nullptr, 1, pl, stream, &t);
+        const int r = run_causal_cached(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16,
+                                        flags, nullptr, 1, pl, stream, &t);
         if (r != LA_OK)
             return r;
     }
@@ -591,7 +696,50 @@ int la_global_fwd_ex(const void *q, const void *k, const void *v, void *out, flo
                            dtype, &pl);
     if (s != LA_OK)
         return s;
-    return run_global(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, flags, pl, stream);
+    return run_global_cached(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, flags, pl, stream);
+}
+
+int la_causal_fwd_ws(const void *q, const void *k, const void *v, void *out, const float *S0,
+                     const float *z0, float *S, float *z, const float *gamma, int B, int H, int N,
+                     int d, int d_v, int chunk, int seg_len, int flags, la_dtype dtype, void *ws,
+                     size_t ws_bytes, hipStream_t stream)
+{
+    if (!flags_ok(flags) || (gamma && !gamma_ok(gamma, H, out, S, z, B, N, d, d_v, dtype)))
+        return LA_EINVAL;
+    Plan pl;
+    const int s = validate(CAUSAL, q, k, v, out, S0, z0, S, z, B, H, N, d, d_v, chunk, seg_len,
+                           dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    if (!workspace_ok(ws, ws_bytes, pl,
+                      call_spans(q, k, v, out, S0, z0, S, z, gamma, B, H, N, d, d_v, dtype)))
+        return LA_EINVAL;
+    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, gamma,
+                      gamma ? H : 1, pl, static_cast<float *>(ws), stream);
+}
+
+int la_global_fwd_ws(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                     int B, int H, int N, int d, int d_v, int chunk, int flags, la_dtype dtype,
+                     void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (!flags_ok(flags))
+        return LA_EINVAL;
+    Plan pl;
+    const int s = validate(GLOBAL, q, k, v, out, nullptr, nullptr, S, z, B, H, N, d, d_v, chunk, 0,
+                           dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    if (!workspace_ok(ws, ws_bytes, pl,
+                      call_spans(q, k, v, out, nullptr, nullptr, S, z, nullptr, B, H, N, d, d_v,
+                                 dtype)))
+        return LA_EINVAL;
+    return run_global(q, k, v, out, S, z, N, d, d_v, dtype == LA_BF16, flags, pl,
+                      static_cast<float *>(ws), stream);
+}
+
+int la_release_cache(void)
+{
+    return block_cache().release() == hipSuccess ? LA_OK : LA_EHIP;
 }
 
 int la_global_fwd(const void *q, const void *k, const void *v, void *out, float *S, float *z,

@@ -35,14 +35,19 @@
  * null stream) and the call returns without waiting; the results are ready when the stream
  * reaches that point. Calls on different streams may run concurrently.
  * Scratch: the causal and global forms need temporary device memory for per-segment partial
- * states (size: la_workspace_bytes()). The library keeps it in blocks cached per (device,
- * stream handle) until the process ends: a call reuses a free block of its stream, which is
- * safe without any wait because later calls on one stream run after it in stream order.
- * A new block is allocated (hipMalloc) when a stream first needs one or needs a larger one;
- * only then may the call wait for that stream to drain. Under stream capture the memory comes
- * from the device's default stream-ordered pool instead (hipMallocAsync / hipFreeAsync:
- * allocation nodes in the graph). A stream handle must not be destroyed while library work on
- * it is pending and then reused by a new stream.
+ * states (size: la_workspace_bytes()).
+ *   - la_causal_fwd_ws and la_global_fwd_ws take it from the caller (`ws`, `ws_bytes`): they
+ *     allocate nothing, never wait on the host and keep no state between calls. The caller
+ *     must not reuse or free `ws` before the stream has passed the call; calls running at the
+ *     same time need workspaces of their own.
+ *   - Every other entry point (the convenience forms) takes it from blocks the library caches
+ *     per device until la_release_cache() or the end of the process. A call takes any free
+ *     block large enough and makes its stream wait, on the device, for that block's last use
+ *     (an event recorded after the kernels of the call that used it last); the host does not
+ *     wait. When no free block is large enough, a new one is allocated with hipMalloc (which
+ *     may wait for the device). Under stream capture the memory comes from the device's
+ *     default stream-ordered pool instead (hipMallocAsync / hipFreeAsync: allocation nodes in
+ *     the graph).
  *
  * Errors: every call validates all arguments before enqueuing anything and returns a status.
  *   LA_OK       enqueued
@@ -150,6 +155,8 @@ int la_causal_fwd_ex(const void *q, const void *k, const void *v, void *out, con
  *   gamma  device memory, H float32 values (one per head, shared by the batch), 4-byte
  *          aligned, read only; values in [0, 1] (0 keeps only the current token, 1 is
  *          la_causal_fwd_ex). Values are not inspected on the host; one above 1 can overflow.
+ *          A negative or NaN value makes every output and the state of its head NaN, in this
+ *          form and in la_decode_step_decay alike (nothing is clamped).
  *          NULL, misaligned, or overlapping out, S or z: LA_EINVAL.
  * Every other argument, the layout, ownership and errors as for la_causal_fwd_ex (S0, z0: the
  * state before token 0; S, z: the state after token N-1, both in the decayed recurrence).
@@ -264,6 +271,46 @@ int la_causal_fwd_rf(const void *q, const void *k, const void *v, void *out, con
                      const float *S0, const float *z0, float *S, float *z, int B, int H, int N,
                      int d, int d_v, int m, int chunk, int seg_len, int flags, la_dtype dtype,
                      hipStream_t stream);
+
+/*
+ * Causal prefill with a caller-supplied workspace: la_causal_fwd_ex (gamma = NULL) or
+ * la_causal_fwd_decay (gamma non-NULL: the per-head decay of the carried state, as there), with
+ * the segment states in `ws` instead of library memory. Same definition, citations, arguments,
+ * layout and results as those two calls.
+ *   ws        device memory of at least la_workspace_bytes(0, B, H, N, d, d_v, chunk, seg_len,
+ *             dtype) bytes, 16-byte aligned, owned by the caller; no part of it needs any
+ *             initial value (every byte the call reads it first writes). May be NULL when that
+ *             size is 0 (one segment per head).
+ *   ws_bytes  its size in bytes.
+ * The call allocates nothing, does not wait on the host and keeps no state: it is reentrant,
+ * and usable under stream capture (the graph then holds kernel nodes only). `ws` belongs to
+ * the call until the stream has passed it.
+ * Errors: as for la_causal_fwd_ex / la_causal_fwd_decay, plus LA_EINVAL when the workspace is
+ * needed and is NULL, misaligned, smaller than required, or overlaps q, k, v, out, S0, z0, S,
+ * z or gamma.
+ */
+int la_causal_fwd_ws(const void *q, const void *k, const void *v, void *out, const float *S0,
+                     const float *z0, float *S, float *z, const float *gamma, int B, int H, int N,
+                     int d, int d_v, int chunk, int seg_len, int flags, la_dtype dtype, void *ws,
+                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Global form with a caller-supplied workspace: la_global_fwd_ex with the per-segment partial
+ * sums in `ws` (la_workspace_bytes(1, B, H, N, d, d_v, chunk, 0, dtype) bytes; rules for `ws`,
+ * `ws_bytes` and the errors as for la_causal_fwd_ws). Same definition and citations as
+ * la_global_fwd ("Linear Attention Math", section "The associativity trick, written out").
+ */
+int la_global_fwd_ws(const void *q, const void *k, const void *v, void *out, float *S, float *z,
+                     int B, int H, int N, int d, int d_v, int chunk, int flags, la_dtype dtype,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Frees the scratch blocks the convenience entry points cached, each after the work that last
+ * used it has finished (this waits on the host). Blocks held by a call running on another
+ * thread at that moment are kept. Returns LA_OK, or LA_EHIP if the runtime reported an error
+ * (a block that could not be freed stays cached).
+ */
+int la_release_cache(void);
 
 /* Bytes of scratch device memory a causal (form = 0) or global (form = 1)
  * call with these arguments takes (0 when none). seg_len as in la_causal_fwd_seg (0 = auto).

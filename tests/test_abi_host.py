@@ -364,3 +364,38 @@ def test_binding_checks_random_feature_layout():
         la.la_rf_features(q, W, _host(B, H, N, m + 1))
     with pytest.raises(ValueError, match="one dtype"):
         la.la_rf_features(q, W, _host(B, H, N, m, dtype=f32))
+
+
+def test_workspace_argument_checks():
+    """The caller-supplied workspace forms reject a missing, misaligned, short or overlapping
+    workspace with LA_EINVAL (after the usual argument checks), before any HIP call."""
+    B, H, N, d = 1, 2, 4096, 64
+    need = la.la_workspace_bytes(0, B, H, N, d, d, 0, 512, la.LA_BF16)
+    gneed = la.la_workspace_bytes(1, B, H, N, d, d, 0, 0, la.LA_BF16)
+    assert need > 0 and gneed > 0
+    W = 64 * A
+
+    def causal(ws, ws_bytes, q=A, gamma=None, seg=512, flags=0, dtype=la.LA_BF16):
+        return la.lib.la_causal_fwd_ws(q, 2 * A, 3 * A, 4 * A, None, None, 5 * A, 6 * A, gamma, B,
+                                       H, N, d, d, 0, seg, flags, dtype, ws, ws_bytes, None)
+
+    def glob(ws, ws_bytes):
+        return la.lib.la_global_fwd_ws(A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, B, H, N, d, d, 0, 0,
+                                       la.LA_BF16, ws, ws_bytes, None)
+
+    assert causal(None, 0) == la.LA_EINVAL
+    assert causal(W, need - 16) == la.LA_EINVAL
+    assert causal(W + 8, need) == la.LA_EINVAL
+    assert causal(5 * A - 16, need) == la.LA_EINVAL          # overlaps S
+    assert causal(W, need, q=None) == la.LA_EINVAL
+    assert causal(W, need, flags=4) == la.LA_EINVAL
+    assert causal(W, need, seg=100) == la.LA_ENOTSUP
+    assert causal(W, need, gamma=A + 2) == la.LA_EINVAL       # misaligned decay vector
+    assert causal(W, need, gamma=W + 64) == la.LA_EINVAL      # decay vector inside the workspace
+    assert glob(None, 0) == la.LA_EINVAL
+    assert glob(W, gneed - 1) == la.LA_EINVAL
+    assert glob(3 * A, gneed) == la.LA_EINVAL                 # overlaps v
+
+
+def test_release_cache_without_blocks():
+    assert la.lib.la_release_cache() == la.LA_OK

@@ -6,6 +6,7 @@ from __future__ import annotations
 
 import math
 
+import numpy as np
 import pytest
 import torch
 
@@ -136,3 +137,180 @@ def test_scratch_host_threads():
     for i, (q, k, v) in enumerate(cases):
         for j, (out, S, z) in enumerate(results[i]):
             _check_oracle(f"thread {i} call {j}", q, k, v, out, S, z)
+
+
+# ---------------------------------------------------------------- caller-supplied workspace
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("dtype,d,seg,decay", [("bf16", 128, 0, False), ("bf16", 64, 128, False),
+                                               ("f32", 32, 64, False), ("bf16", 128, 256, True)])
+def test_workspace_causal(dtype, d, seg, decay):
+    """la_causal_fwd_ws with the segment states in a caller-owned buffer that starts as NaN
+    (no part of it needs an initial value): the oracle's results, and bit-identical to the
+    convenience form with the library's scratch."""
+    mod = la()
+    B, H, N = 2, 3, 1500
+    q, k, v = _inputs(B, H, N, d, 810 + d, dtype)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    gam = torch.tensor([0.9, 0.99, 0.5], dtype=torch.float32, device=DEV) if decay else None
+    need = mod.la_workspace_bytes(0, B, H, N, d, d, 0, seg, datagen_code(dtype))
+    assert need > 0
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    say(f"workspace causal dtype={dtype} d={d} seg={seg} decay={decay} ws={need} B")
+    res = []
+    for use_ws in (True, False):
+        out = torch.full((B, H, N, d), float("nan"), dtype=q.dtype, device=DEV)
+        S = torch.full((B, H, d, d), float("nan"), device=DEV)
+        z = torch.full((B, H, d), float("nan"), device=DEV)
+        if use_ws:
+            mod.la_causal_fwd_ws(qd, kd, vd, out, ws, None, None, S, z, gamma=gam, seg_len=seg)
+        elif decay:
+            mod.la_causal_fwd_decay(qd, kd, vd, out, gam, None, None, S, z, seg_len=seg)
+        else:
+            mod.la_causal_fwd_ex(qd, kd, vd, out, None, None, S, z, seg_len=seg)
+        torch.cuda.synchronize()
+        res.append((out, S, z))
+    for a, b in zip(*res):
+        assert torch.equal(_bits(a), _bits(b)), "workspace form differs from the cached form"
+    gnp = None if gam is None else gam.cpu().numpy().astype(np.float64)
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v), gamma=gnp)
+    out, S, z = res[0]
+    check("out", f64(out), oo, TOL[dtype])
+    check("S", f64(S), So, TOL[dtype])
+    check("z", f64(z)[..., None], zo[..., None], TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype,d,N", [("bf16", 128, 20000), ("f32", 64, 3000)])
+def test_workspace_global(dtype, d, N):
+    mod = la()
+    B, H = 1, 2
+    q, k, v = _inputs(B, H, N, d, 830 + d, dtype)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    need = mod.la_workspace_bytes(1, B, H, N, d, d, 0, 0, datagen_code(dtype))
+    assert need > 0
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    say(f"workspace global dtype={dtype} d={d} N={N} ws={need} B")
+    res = []
+    for use_ws in (True, False):
+        out = torch.full((B, H, N, d), float("nan"), dtype=q.dtype, device=DEV)
+        S = torch.full((B, H, d, d), float("nan"), device=DEV)
+        z = torch.full((B, H, d), float("nan"), device=DEV)
+        if use_ws:
+            mod.la_global_fwd_ws(qd, kd, vd, out, S, z, ws)
+        else:
+            mod.la_global_fwd(qd, kd, vd, out, S, z)
+        torch.cuda.synchronize()
+        res.append((out, S, z))
+    for a, b in zip(*res):
+        assert torch.equal(_bits(a), _bits(b)), "workspace form differs from the cached form"
+    oo, So, zo, _, _ = oracle.global_(f64(q), f64(k), f64(v))
+    out, S, z = res[0]
+    check("out", f64(out), oo, TOL[dtype])
+    check("S", f64(S), So, TOL[dtype])
+
+
+def test_workspace_graph_capture():
+    """A la_causal_fwd_ws call captured into a HIP graph (kernel nodes only) and replayed, with
+    eager calls between the replays: every replay equals the eager result bit for bit."""
+    mod = la()
+    q, k, v = _inputs(1, 4, 2048, 128, 850)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    need = mod.la_workspace_bytes(0, 1, 4, 2048, 128, 128, 0, 256, 1)
+    ws = torch.empty(need // 4, dtype=torch.float32, device=DEV)
+    out_e = torch.empty_like(qd)
+    S_e = torch.empty(1, 4, 128, 128, device=DEV)
+    z_e = torch.empty(1, 4, 128, device=DEV)
+    say("workspace graph capture")
+    mod.la_causal_fwd_ws(qd, kd, vd, out_e, ws, None, None, S_e, z_e, seg_len=256)
+    torch.cuda.synchronize()
+    out_g = torch.empty_like(qd)
+    S_g = torch.empty_like(S_e)
+    z_g = torch.empty_like(z_e)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            mod.la_causal_fwd_ws(qd, kd, vd, out_g, ws, None, None, S_g, z_g, seg_len=256)
+    torch.cuda.synchronize()
+    q2, k2, v2 = (to_dev(x) for x in _inputs(1, 4, 2048, 128, 851))
+    for rep in range(3):
+        out_g.fill_(float("nan"))
+        S_g.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out_g), _bits(out_e)), f"replay {rep}: outputs differ"
+        assert torch.equal(S_g, S_e) and torch.equal(z_g, z_e), f"replay {rep}: state differs"
+        # eager work through the same workspace between replays
+        o2 = torch.empty_like(q2)
+        mod.la_causal_fwd_ws(q2, k2, v2, o2, ws, seg_len=256)
+        torch.cuda.synchronize()
+
+
+def test_per_thread_streams():
+    """Two host threads, both on the per-thread default stream (one handle, a different stream
+    in each thread), each enqueue calls of changing sizes without synchronising: scratch is
+    reused only after its last use has finished, so every result equals the single-stream
+    result bit for bit."""
+    import ctypes
+    import threading
+    mod = la()
+    per_thread = ctypes.c_void_p(2)  # hipStreamPerThread
+    shapes = [(1, 2, 1024 + 256 * i, 64) for i in range(4)]
+    cases = [tuple(to_dev(x) for x in _inputs(*sh, 870 + i)) for i, sh in enumerate(shapes)]
+    want = []
+    for q, k, v in cases:
+        want.append(_run(mod, q, k, v, 128))
+    torch.cuda.synchronize()
+    results = {}
+    errors = []
+
+    def work(tid):
+        try:
+            for rep in range(6):
+                i = (rep + tid) % len(cases)
+                q, k, v = cases[i]
+                B, H, N, d = q.shape
+                out = torch.full((B, H, N, d), float("nan"), dtype=q.dtype, device=DEV)
+                S = torch.full((B, H, d, d), float("nan"), device=DEV)
+                z = torch.full((B, H, d), float("nan"), device=DEV)
+                st = mod.lib.la_causal_fwd_state(
+                    q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, None,
+                    S.data_ptr(), z.data_ptr(), B, H, N, d, d, 0, 128, mod.LA_BF16, per_thread)
+                assert st == mod.LA_OK, st
+                results[(tid, rep)] = (i, out, S, z)
+        except Exception as e:  # reported below, on the main thread
+            errors.append(e)
+
+    torch.cuda.synchronize()
+    say("per-thread streams: 2 threads x 6 calls, d=64, seg_len=128")
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (tid, rep), (i, out, S, z) in results.items():
+        wo, wS, wz = want[i]
+        assert torch.equal(_bits(out), _bits(wo)), (tid, rep)
+        assert torch.equal(S, wS) and torch.equal(z, wz), (tid, rep)
+
+
+def test_release_cache():
+    """la_release_cache frees the cached blocks; later calls allocate anew and stay correct."""
+    mod = la()
+    q, k, v = (to_dev(x) for x in _inputs(1, 4, 3000, 128, 880))
+    say("release cache")
+    a = _run(mod, q, k, v, 512)
+    mod.la_release_cache()
+    b = _run(mod, q, k, v, 512)
+    mod.la_release_cache()
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(_bits(x), _bits(y))
+
+
+def datagen_code(dtype):
+    return 1 if dtype == "bf16" else 0
