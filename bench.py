@@ -118,15 +118,13 @@ def bench_decode(args):
     z = torch.empty(w.B, w.H, w.d, device=dev)
     # starting state: sums of phi(k) v^T over a 4096-token seeded prior, built with the
     # library's global form (state only) in blocks of batch rows
-    blk = 16
-    for b0 in range(0, w.B, blk):
-        _, kp, vp = datagen.qkv_cuda(blk, w.H, w.prior, w.d, w.dv, w.seed * 1000 + b0, w.scale, "bf16")
-        la.la_global_fwd(None, kp, vp, None, S[b0:b0 + blk], z[b0:b0 + blk])
+    for b0 in range(0, w.B, datagen.DECODE_PRIOR_BLOCK):
+        kp, vp = datagen.decode_prior(w, b0)
+        la.la_global_fwd(None, kp, vp, None, S[b0:b0 + kp.shape[0]], z[b0:b0 + kp.shape[0]])
         del kp, vp
     steps = args.decode_steps
-    # fresh q, k, v for every step, drawn up front: [steps, B*H, 1, d] viewed as [steps, B, H, d]
-    toks = datagen.qkv_cuda(steps, w.B * w.H, 1, w.d, w.dv, w.seed + 1, w.scale, "bf16")
-    toks = [x.view(steps, w.B, w.H, -1) for x in toks]
+    # fresh q, k, v for every step, drawn up front as [steps, B, H, d]
+    toks = datagen.decode_tokens(w, steps)
     out = torch.empty(w.B, w.H, w.dv, dtype=torch.bfloat16, device=dev)
 
     def step(i):

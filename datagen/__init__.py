@@ -68,6 +68,31 @@ def qkv_cuda(B: int, H: int, N: int, d: int, dv: int, seed: int, scale: float = 
     return tuple(out)
 
 
+# The decode workload's draws (all on the device, torch's seeded Philox generator):
+#   * the prior: for each block of DECODE_PRIOR_BLOCK batch rows starting at row b0, one qkv_cuda
+#     call of [block, H, prior, d] with seed = seed * 1000 + b0 (its q is drawn and unused);
+#     the starting state of those heads is S0 = sum_t phi(k_t) v_t^T, z0 = sum_t phi(k_t)
+#     over the block's prior tokens;
+#   * the step tokens: one qkv_cuda call of [steps, B * H, 1, d] with seed = seed + 1, viewed
+#     as [steps, B, H, d] (token t of head (b, h) is row t of that view).
+DECODE_PRIOR_BLOCK = 16
+
+
+def decode_prior(w: "Workload", b0: int, device: str = "cuda"):
+    """k, v [blk, H, prior, d] of the prior tokens of batch rows b0 .. b0 + blk - 1 (blk =
+    DECODE_PRIOR_BLOCK, or fewer at the end) of decode workload ``w``."""
+    blk = min(DECODE_PRIOR_BLOCK, w.B - b0)
+    _, k, v = qkv_cuda(blk, w.H, w.prior, w.d, w.dv, w.seed * 1000 + b0, w.scale, w.dtype,
+                       device=device)
+    return k, v
+
+
+def decode_tokens(w: "Workload", steps: int, device: str = "cuda"):
+    """q, k, v [steps, B, H, d] of the per-step tokens of decode workload ``w``."""
+    toks = qkv_cuda(steps, w.B * w.H, 1, w.d, w.dv, w.seed + 1, w.scale, w.dtype, device=device)
+    return tuple(x.view(steps, w.B, w.H, -1) for x in toks)
+
+
 def projections(m: int, d: int, seed: int, dtype: str = "bf16") -> torch.Tensor:
     """Random-feature projections W [m, d]: IID standard normal rows, rounded to ``dtype``
     (the draw the unbiasedness of positive random features assumes)."""
@@ -89,8 +114,14 @@ def decay_rates(H: int) -> torch.Tensor:
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
-    """Exact float64 copy of a bf16/fp32 tensor (both embed exactly in float64)."""
-    return t.detach().to("cpu").to(torch.float64).numpy()
+    """Exact float64 host copy of a bf16/fp32 tensor (both embed exactly in float64). A device
+    tensor is widened where it lives and then copied (the host-side widening of the large
+    device-drawn tensors is the slow part otherwise); the value of every element is the same
+    either way."""
+    t = t.detach()
+    if t.is_cuda:
+        return t.to(torch.float64).cpu().numpy()
+    return t.to(torch.float64).numpy()
 
 
 @dataclass(frozen=True)

@@ -155,16 +155,15 @@ def test_workload3_causal_full():
     check("z", z[..., None], zo[..., None], TOL["bf16"])
 
 
-def test_workload4_global_sampled():
-    """Full state; outputs on 2048 sampled rows per head plus the ragged tail (N = 100000)."""
+def test_workload4_global_full():
+    """The global workload (B=1 H=8 N=100000 d=128) in the bench's launch configuration: every
+    one of the 800,000 output rows (including the ragged last 32 of each head), S and z."""
     w, q, k, v = _workload(4)
     say(f"workload 4 {w.name}")
     o, S, z = global_(q, k, v)
-    rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([rng.choice(w.N, 2048, replace=False), np.arange(w.N - 96, w.N)]))
-    qs = q[:, :, torch.from_numpy(rows)]
-    oo, So, zo, _, _ = oracle.global_(f64(qs), f64(k), f64(v))
-    check("out[sampled rows]", o[:, :, rows], oo, TOL["bf16"])
+    oo, So, zo, _, _ = oracle.global_(f64(q), f64(k), f64(v))
+    check("out (all rows)", o, oo, TOL["bf16"])
+    check("out (last 32 rows of each head)", o[:, :, -32:], oo[:, :, -32:], TOL["bf16"])
     check("S", S, So, TOL["bf16"])
     check("z", z[..., None], zo[..., None], TOL["bf16"])
 
@@ -192,14 +191,86 @@ def _decode_run(B, H, d, prior, steps, seed):
     check("z", f64(z)[..., None], zo[..., None], 1e-6)
 
 
-def test_workload5_decode_all_heads():
-    """All 256 x 32 heads of the decode workload (prior of 32 tokens to keep the oracle short)."""
+@pytest.mark.timeout(900)
+def test_workload5_decode_bench_configuration():
+    """The decode workload exactly as the bench runs it: 256 x 32 heads, a starting state built
+    by the library's global form from the seeded 4096-token prior of every head, then 1000
+    decode steps of fresh tokens, the state updated in place. Against the oracle (its own
+    starting state from the same prior, then the recurrence over the 1000 step tokens): the
+    starting state of every head; the outputs of every head at every step (so every head at the
+    last step, and the 256-head sample below at steps 1, 10 and 100); the state after 1, 10, 100
+    and 1000 steps on a 256-head sample; and the final state of every head."""
     w = datagen.WORKLOADS[5]
-    _decode_run(w.B, w.H, w.d, prior=32, steps=3, seed=w.seed)
+    B, H, d, steps = w.B, w.H, w.d, w.steps
+    m = la()
+    S = torch.empty(B, H, d, d, device=DEV)
+    z = torch.empty(B, H, d, device=DEV)
+    blocks = []
+    say(f"decode workload {w.name}: prior states ({B // datagen.DECODE_PRIOR_BLOCK} blocks)")
+    for b0 in range(0, B, datagen.DECODE_PRIOR_BLOCK):
+        kp, vp = datagen.decode_prior(w, b0)
+        n = kp.shape[0]
+        m.la_global_fwd(None, kp, vp, None, S[b0:b0 + n], z[b0:b0 + n])
+        _, So, zo, _, _ = oracle.global_(None, f64(kp), f64(vp))
+        del kp, vp
+        torch.cuda.synchronize()
+        check(f"prior S rows {b0}..{b0 + n - 1}", f64(S[b0:b0 + n]), So, TOL["bf16"])
+        check(f"prior z rows {b0}..{b0 + n - 1}", f64(z[b0:b0 + n])[..., None], zo[..., None],
+              TOL["bf16"])
+        blocks.append((b0, n, So, zo))
+    # 256-head sample (fixed seed): (batch row, head) pairs
+    rng = np.random.default_rng(5)
+    sample = np.sort(rng.choice(B * H, 256, replace=False))
+    sb, sh = sample // H, sample % H
+    sbd, shd = torch.from_numpy(sb).to(DEV), torch.from_numpy(sh).to(DEV)
+    snaps = {}
+    toks = datagen.decode_tokens(w, steps)
+    outs = torch.empty(steps, B, H, d, dtype=torch.bfloat16, device=DEV)
+    say(f"decode workload {w.name}: {steps} steps on the GPU")
+    for t in range(steps):
+        m.la_decode_step(toks[0][t], toks[1][t], toks[2][t], outs[t], S, z)
+        if t + 1 in (1, 10, 100):
+            snaps[t + 1] = (S[sbd, shd].clone(), z[sbd, shd].clone())
+    torch.cuda.synchronize()
+    snaps[steps] = (S[sbd, shd].clone(), z[sbd, shd].clone())
+    # the oracle, one block of batch rows at a time: the recurrence over the step tokens from the
+    # oracle's own starting state
+    Ssamp = {}
+    for b0, n, So, zo in blocks:
+        qs, ks, vs = (f64(x[:, b0:b0 + n].permute(1, 2, 0, 3).contiguous()) for x in toks)
+        oo, Sn, zn, _, _ = oracle.causal(qs, ks, vs, S0=So, z0=zo)
+        got = f64(outs[:, b0:b0 + n].permute(1, 2, 0, 3).contiguous())
+        say(f"  rows {b0}..{b0 + n - 1}")
+        check(f"outs rows {b0}..{b0 + n - 1} (all steps)", got, oo, TOL["bf16"])
+        check(f"out at step {steps}", got[:, :, -1], oo[:, :, -1], TOL["bf16"])
+        check(f"final S rows {b0}..{b0 + n - 1}", f64(S[b0:b0 + n]), Sn, TOL["bf16"])
+        check(f"final z rows {b0}..{b0 + n - 1}", f64(z[b0:b0 + n])[..., None], zn[..., None],
+              TOL["bf16"])
+        # the sampled heads of this block: state after 1, 10, 100 steps
+        sel = np.nonzero((sb >= b0) & (sb < b0 + n))[0]
+        if sel.size == 0:
+            continue
+        for t in (1, 10, 100):
+            _, St, zt, _, _ = oracle.causal(qs[sb[sel] - b0, sh[sel]][None, :, :t],
+                                            ks[sb[sel] - b0, sh[sel]][None, :, :t],
+                                            vs[sb[sel] - b0, sh[sel]][None, :, :t],
+                                            S0=So[sb[sel] - b0, sh[sel]][None],
+                                            z0=zo[sb[sel] - b0, sh[sel]][None])
+            Ssamp.setdefault(t, []).append((sel, St[0], zt[0]))
+        Ssamp.setdefault(steps, []).append((sel, Sn[sb[sel] - b0, sh[sel]], zn[sb[sel] - b0, sh[sel]]))
+    for t, parts in Ssamp.items():
+        Sw = np.empty((256, d, d))
+        zw = np.empty((256, d))
+        for sel, St, zt in parts:
+            Sw[sel] = St
+            zw[sel] = zt
+        check(f"sampled S after {t} steps", f64(snaps[t][0]), Sw, TOL["bf16"])
+        check(f"sampled z after {t} steps", f64(snaps[t][1])[..., None], zw[..., None], TOL["bf16"])
 
 
-def test_workload5_decode_full_prior():
-    """The decode workload's 4096-token prior state, on 64 of its heads."""
+def test_workload5_decode_full_prior_float32_state():
+    """The decode workload's 4096-token prior on 64 of its heads, starting from the oracle's
+    state rounded to float32 (so the state itself is checked at float32 precision)."""
     w = datagen.WORKLOADS[5]
     _decode_run(2, w.H, w.d, prior=w.prior, steps=2, seed=w.seed + 10)
 
