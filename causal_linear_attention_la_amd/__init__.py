@@ -20,6 +20,8 @@ The entry points keep the C names:
     la_causal_fwd_ws(q, k, v, out, ws, S0=None, z0=None, S=None, z=None, gamma=None, chunk=0,
                      seg_len=0, flags=0)               # caller-supplied workspace ws
     la_global_fwd_ws(q, k, v, out, S, z, ws, chunk=0, flags=0)
+    la_causal_fwd_noalloc(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk=0, seg_len=0,
+                          flags=0)                     # static scratch: allocates nothing
     la_release_cache()                                 # frees the library's cached scratch
 with q, k [B,H,N,d], v, out [B,H,N,d_v] (bf16 or float32, contiguous, on the GPU),
 S [B,H,d,d_v] and z [B,H,d] float32; flags is a bitwise or of LA_PHI_IDENTITY and
@@ -45,14 +47,15 @@ _PKG = Path(__file__).resolve().parent
 LIB_PATH = Path(os.environ.get("LINATTN_LIB", _PKG / "liblinattn.so"))
 
 LA_F32, LA_BF16 = 0, 1
-LA_OK, LA_EINVAL, LA_ENOTSUP, LA_EHIP = 0, 1, 2, 3
+LA_OK, LA_EINVAL, LA_ENOTSUP, LA_EHIP, LA_ENOSPACE = 0, 1, 2, 3, 4
 LA_PHI_IDENTITY, LA_UNNORMALIZED = 1, 2
 
 # Every symbol include/la.h declares.
 EXPORTS = ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
            "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
            "la_decode_step_ex", "la_causal_fwd_decay", "la_decode_step_decay", "la_rf_features",
-           "la_causal_fwd_rf", "la_causal_fwd_ws", "la_global_fwd_ws", "la_release_cache",
+           "la_causal_fwd_rf", "la_causal_fwd_ws", "la_global_fwd_ws", "la_causal_fwd_noalloc",
+           "la_release_cache",
            "la_workspace_bytes", "la_segments", "la_strerror", "la_version")
 
 
@@ -86,11 +89,13 @@ def _load(path: Path):
     sz = ctypes.c_size_t
     lib.la_causal_fwd_ws.argtypes = [vp, vp, vp, vp, fp, fp, fp, fp, fp] + [i] * 9 + [vp, sz, vp]
     lib.la_global_fwd_ws.argtypes = core + [i, i, vp, sz, vp]
+    lib.la_causal_fwd_noalloc.argtypes = state + [i, i, vp]
     lib.la_release_cache.argtypes = []
     for f in ("la_causal_fwd", "la_causal_fwd_seg", "la_causal_fwd_state", "la_causal_fwd_ex",
               "la_causal_fwd_profiled", "la_global_fwd", "la_global_fwd_ex", "la_decode_step",
               "la_decode_step_ex", "la_rf_features", "la_causal_fwd_decay", "la_decode_step_decay",
-              "la_causal_fwd_rf", "la_causal_fwd_ws", "la_global_fwd_ws", "la_release_cache"):
+              "la_causal_fwd_rf", "la_causal_fwd_ws", "la_global_fwd_ws", "la_causal_fwd_noalloc",
+              "la_release_cache"):
         getattr(lib, f).restype = ctypes.c_int
     lib.la_workspace_bytes.argtypes = [i] * 8 + [i]
     lib.la_workspace_bytes.restype = ctypes.c_size_t
@@ -359,6 +364,19 @@ def la_global_fwd_ws(q, k, v, out, S, z, ws, chunk: int = 0, flags: int = 0):
     st = lib.la_global_fwd_ws(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S), _ptr(z), B, H, N, d,
                               dv, chunk, flags, _dtype_code(k), _ptr(ws), nbytes, _stream(k))
     _check(st, "la_global_fwd_ws")
+    return out
+
+
+def la_causal_fwd_noalloc(q, k, v, out, S0=None, z0=None, S=None, z=None, chunk: int = 0,
+                          seg_len: int = 0, flags: int = 0):
+    """la_causal_fwd_ex with the segment states in the library's static per-device scratch
+    array (64 MiB): allocates nothing. Calls that overlap in time on one device race."""
+    B, H, N, d, dv = _layout(q, k, v, out, states=((S0, z0), (S, z)))
+    _check_tensors(q, k, v, out, S0, z0, S, z)
+    st = lib.la_causal_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(S0), _ptr(z0),
+                                   _ptr(S), _ptr(z), B, H, N, d, dv, chunk, seg_len, flags,
+                                   _dtype_code(k), _stream(k))
+    _check(st, "la_causal_fwd_noalloc")
     return out
 
 

@@ -324,6 +324,38 @@ struct Workspace {
     ~Workspace() { (void)finish(); }
 };
 
+// Scratch of la_causal_fwd_noalloc, for callers that cannot allocate device memory: one array
+// per GPU (each device holds its own copy for the life of the process), 64 MiB -- enough for
+// every sequence split the library chooses for the matrix-core kernels (at most 510 segment
+// states of 66,048 B at d = d_v = 128). In host code `scratch` is only a stand-in for the
+// symbol: its device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is ever passed to kernels.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void **out)
+{
+    static std::mutex mu;
+    static void *ptr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return hipSuccess;
+}
+
 // HIP events marking the phase boundaries of one causal call (profiling form only).
 struct Stamps {
     hipEvent_t ev[4] = {};
@@ -737,6 +769,27 @@ int la_global_fwd_ws(const void *q, const void *k, const void *v, void *out, flo
                       static_cast<float *>(ws), stream);
 }
 
+int la_causal_fwd_noalloc(const void *q, const void *k, const void *v, void *out,
+                          const float *S0, const float *z0, float *S, float *z, int B, int H,
+                          int N, int d, int d_v, int chunk, int seg_len, int flags, la_dtype dtype,
+                          hipStream_t stream)
+{
+    if (!flags_ok(flags))
+        return LA_EINVAL;
+    Plan pl;
+    const int s = validate(CAUSAL, q, k, v, out, S0, z0, S, z, B, H, N, d, d_v, chunk, seg_len,
+                           dtype, &pl);
+    if (s != LA_OK)
+        return s;
+    if (pl.ws_bytes > kStaticScratchBytes)
+        return LA_ENOSPACE;
+    void *ws = nullptr;
+    if (pl.ws_bytes && static_scratch(&ws) != hipSuccess)
+        return LA_EHIP;
+    return run_causal(q, k, v, out, S0, z0, S, z, N, d, d_v, dtype == LA_BF16, flags, nullptr, 1, pl,
+                      static_cast<float *>(ws), stream);
+}
+
 int la_release_cache(void)
 {
     return block_cache().release() == hipSuccess ? LA_OK : LA_EHIP;
@@ -856,6 +909,9 @@ const char *la_strerror(int status)
                "32 or 64 as the shape allows; random features: d <= 256, m <= 4096)";
     case LA_EHIP:
         return "HIP runtime error (allocation or kernel launch failed)";
+    case LA_ENOSPACE:
+        return "the call needs more scratch than the library's static scratch array holds "
+               "(64 MiB per device; la_causal_fwd_noalloc)";
     default:
         return "unknown status";
     }

@@ -57,6 +57,8 @@
  *               for this shape/dtype, or a size whose index arithmetic would overflow
  *   LA_EHIP     the HIP runtime reported an error (allocation or launch); work enqueued before
  *               the failure may have run
+ *   LA_ENOSPACE la_causal_fwd_noalloc only: the call needs more scratch than the library's
+ *               static array holds; nothing was enqueued
  * Nothing aborts, exits or throws across this interface.
  */
 #ifndef LINATTN_LA_H
@@ -71,7 +73,7 @@ extern "C" {
 
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 
-enum { LA_OK = 0, LA_EINVAL = 1, LA_ENOTSUP = 2, LA_EHIP = 3 };
+enum { LA_OK = 0, LA_EINVAL = 1, LA_ENOTSUP = 2, LA_EHIP = 3, LA_ENOSPACE = 4 };
 
 /*
  * Variant flags of the *_ex entry points (bitwise or; any other bit set: LA_EINVAL).
@@ -303,6 +305,28 @@ int la_causal_fwd_ws(const void *q, const void *k, const void *v, void *out, con
 int la_global_fwd_ws(const void *q, const void *k, const void *v, void *out, float *S, float *z,
                      int B, int H, int N, int d, int d_v, int chunk, int flags, la_dtype dtype,
                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * la_causal_fwd_ex for callers that cannot allocate device memory (code under stream capture
+ * that must not record allocation nodes, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, definition and results, with the segment states in a static device
+ * array of the library instead of allocated scratch. The call allocates nothing (no hipMalloc,
+ * hipMallocAsync or pool memory; no host wait).
+ *   Limit: 64 MiB of scratch per device, enough for every split the library chooses for the
+ *   matrix-core kernels (bf16, d = d_v in {64, 128}); a call needing more
+ *   (la_workspace_bytes(0, ...) > 64 MiB, e.g. a small explicit seg_len over many heads) returns
+ *   LA_ENOSPACE and enqueues nothing.
+ *   Sharing: every call on one device uses that device's one array, which keeps the last call's
+ *   contents (no part of it needs an initial value: every byte a call reads it first writes).
+ *   Calls that overlap in time on one device -- on different streams, or from several threads
+ *   -- race on it: callers serialise them (e.g. one stream). The array is held until the
+ *   process ends.
+ * Errors: as for la_causal_fwd_ex, plus LA_ENOSPACE.
+ */
+int la_causal_fwd_noalloc(const void *q, const void *k, const void *v, void *out,
+                          const float *S0, const float *z0, float *S, float *z, int B, int H,
+                          int N, int d, int d_v, int chunk, int seg_len, int flags, la_dtype dtype,
+                          hipStream_t stream);
 
 /*
  * Frees the scratch blocks the convenience entry points cached, each after the work that last

@@ -399,3 +399,24 @@ def test_workspace_argument_checks():
 
 def test_release_cache_without_blocks():
     assert la.lib.la_release_cache() == la.LA_OK
+
+
+def test_noalloc_argument_checks():
+    """la_causal_fwd_noalloc validates like la_causal_fwd_ex and refuses a split that needs
+    more than its 64 MiB static scratch with LA_ENOSPACE, before any HIP call."""
+    f = la.lib.la_causal_fwd_noalloc
+
+    def call(q=A, S=5 * A, z=6 * A, B=1, H=2, N=8, d=16, seg=0, flags=0, T=1):
+        return f(q * T if q else None, 2 * A * T, 3 * A * T, 4 * A * T, None, None,
+                 S * T if S else None, z * T if z else None, B, H, N, d, d, 0, seg, flags,
+                 la.LA_BF16, None)
+
+    assert call(q=None) == la.LA_EINVAL
+    assert call(S=None) == la.LA_EINVAL
+    assert call(flags=8) == la.LA_EINVAL
+    assert call(d=48) == la.LA_ENOTSUP
+    # 64 heads x 2048 segments of 64 tokens x 66,048 B: far above 64 MiB
+    big = dict(B=1, H=64, N=131072, d=128, seg=64, T=1 << 20)
+    assert la.la_workspace_bytes(0, 1, 64, 131072, 128, 128, 0, 64) > 64 << 20
+    assert call(**big) == la.LA_ENOSPACE
+    assert "static scratch" in la.strerror(la.LA_ENOSPACE)
