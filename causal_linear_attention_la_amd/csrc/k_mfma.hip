@@ -1083,14 +1083,17 @@ __global__ __launch_bounds__(NT, 3) void k_gread(const uint16_t *__restrict__ q,
             sts<u32x2>(tile + li * OS + 16 * ct + 4 * g,
                        u32x2{pack_bf2(c[0] * inv, c[1] * inv), pack_bf2(c[2] * inv, c[3] * inv)});
         }
-        // the tile back as whole rows (this wave's LDS only: its accesses stay in order)
+        // the tile back as whole rows (this wave's LDS only: its accesses stay in order), with
+        // non-temporal stores: the outputs (as many bytes as q) are not left dirty in the caches,
+        // where the next call's segment sums would find their write-back in the way of their
+        // reads (measured on MI355X for B=1 H=8 N=100000 d=128: 189 -> 174 us per call)
         const int r0 = tb + 16 * t;
 #pragma unroll
         for (int i = 0; i < 16 / RPI; ++i) {
             const int row = RPI * i + l / LPR, col = 8 * (l % LPR);
             const u32x4 x = lds<u32x4>(tile + row * OS + col);
             if (r0 + row < te)
-                *reinterpret_cast<u32x4 *>(out + hoff + (size_t)(r0 + row) * D + col) = x;
+                __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(out + hoff + (size_t)(r0 + row) * D + col));
         }
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
