@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the linear-attention hot path on one MI355X.
 
-One step = one causal prefill call of a fresh sequence (la_causal_fwd_state from the zero
-state: phi on the loads, chunked matrix-core intra-chunk product, carried float32 state,
-normaliser, bf16 store, final state S, z written) over the workload B=2 H=16 N=8192
+One step = one causal prefill call of a fresh sequence (la_causal_fwd_ws, the entry point with a
+caller-owned workspace, from the zero state: phi on the loads, chunked matrix-core intra-chunk
+product, carried float32 state, normaliser, bf16 store, final state S, z written) over the
+workload B=2 H=16 N=8192
 d=d_v=128 bf16, inputs IID N(0, 1/128). K steps are timed
 between device synchronisations; input sets rotate over three copies (806 MB > the 256 MB
 last-level cache) so a step does not find its inputs cached by the previous one.
@@ -84,12 +85,21 @@ def bench_prefill(args):
         z = torch.empty(w.B, w.H, w.d, device=dev)
         sets.append((q, k, v, out, S, z))
 
+    # the segment-state workspace, owned by the caller and shared by the steps (one stream)
+    need = la.la_workspace_bytes(0, w.B, w.H, w.N, w.d, w.dv, args.chunk, args.seg_len)
+    ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device=dev)
+
     def step(i):
         # a fresh sequence: zero initial state (no buffer), final state written to S, z
         q, k, v, out, S, z = sets[i % len(sets)]
-        la.la_causal_fwd_state(q, k, v, out, None, None, S, z, chunk=args.chunk,
-                               seg_len=args.seg_len)
+        la.la_causal_fwd_ws(q, k, v, out, ws if need else None, None, None, S, z,
+                            chunk=args.chunk, seg_len=args.seg_len)
 
+    # The same call in the chip's steady state first (200 untimed calls, then 200 timed), reported
+    # on its own: measured on MI355X, the first few hundred calls of a process run 3-15 % slower
+    # than the sustained rate (calls 5-25 at 95-97 us, 25-100 at 98-107 us, 300-400 at 92 us), so
+    # the headline's own W warm-up and K timed steps follow it.
+    ms_steady, _ = time_calls(step, 200, 200)
     ms, wall = time_calls(step, args.steps, args.warmup)
     # same buffers every step (inputs may stay in the last-level cache)
     ms_hot, _ = time_calls(lambda i: step(0), args.steps, 2)
@@ -104,7 +114,58 @@ def bench_prefill(args):
     byts, flops = algo_prefill(w.B, w.H, w.N, w.d, w.dv)
     # segments per head the library chose
     P = la.la_segments(0, w.B, w.H, w.N, w.d, w.dv, args.chunk, args.seg_len)
-    return w, ms, ms_hot, wall, byts, flops, P, kern_ms
+    return w, ms, ms_hot, wall, byts, flops, P, kern_ms, ms_steady
+
+
+def time_flushed(fn, reps, flush_bytes=512 << 20):
+    """Average device ms of fn() when each call starts with none of its data in the caches:
+    before every call a 512 MiB buffer (twice the 256 MB last-level cache) is read through, and
+    only the call itself is timed, between HIP events on the launch stream."""
+    import torch
+    buf = torch.ones(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    fn()
+    torch.cuda.synchronize()
+    for a, b in evs:
+        buf.max()
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def bench_causal_small(args, n):
+    """Causal workloads 1 (B=1 H=1 N=64 d=16 float32, the vector-ALU kernels) and 2 (B=4 H=8
+    N=2048 d=64 bf16, chunk 64: the d = 64 matrix-core kernels), through la_causal_fwd_ws from
+    the zero state with the final state written. Both are small enough to sit in the caches, so
+    they are timed hot (the same buffers back to back) and flushed (time_flushed); for workload
+    2 the per-kernel times come from the library's own HIP events (la_causal_fwd_profiled)."""
+    import torch
+    import causal_linear_attention_la_amd as la
+    import datagen
+
+    w = datagen.WORKLOADS[n]
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in datagen.qkv(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale, w.dtype))
+    out = torch.empty_like(v)
+    S = torch.empty(w.B, w.H, w.d, w.dv, device=dev)
+    z = torch.empty(w.B, w.H, w.d, device=dev)
+    code = la.LA_BF16 if w.dtype == "bf16" else la.LA_F32
+    need = la.la_workspace_bytes(0, w.B, w.H, w.N, w.d, w.dv, w.chunk, 0, code)
+    ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device=dev) if need else None
+
+    def call(i=0):
+        la.la_causal_fwd_ws(q, k, v, out, ws, None, None, S, z, chunk=w.chunk)
+
+    ms_hot, _ = time_calls(call, args.steps, args.warmup)
+    ms_flushed = time_flushed(call, max(10, args.steps // 4))
+    kern = la.la_causal_fwd_profiled(q, k, v, out, None, None, S, z, chunk=w.chunk,
+                                     reps=args.steps)
+    P = la.la_segments(0, w.B, w.H, w.N, w.d, w.dv, w.chunk, 0, code)
+    return w, ms_hot, ms_flushed, kern, P
 
 
 def bench_decode(args):
@@ -321,6 +382,75 @@ def cpu_model():
     return "unknown"
 
 
+def _median_runs(fn, seconds, at_least=3):
+    times = []
+    while len(times) < at_least or sum(times) < seconds:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return statistics.median(times), len(times)
+
+
+def cpu_baseline_causal(n, seconds=5.0):
+    """The float64 oracle, as it stands, on causal workload n (the whole workload), on all host
+    threads: median of repeated runs."""
+    import datagen
+    import oracle
+
+    w = datagen.WORKLOADS[n]
+    q, k, v = (datagen.to_f64(x) for x in datagen.qkv(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale,
+                                                       w.dtype))
+    t, runs = _median_runs(lambda: oracle.causal(q, k, v), seconds)
+    return {"value": w.B * w.H * w.N / t, "unit": "tokens/s (B*H*N/s)", "cores": oracle.threads(),
+            "kind": "oracle", "us_per_call": t * 1e6,
+            "sample": f"{w.name}, the whole workload, float64 token-serial recurrence, median of "
+                      f"{runs} runs of {t * 1e3:.2f} ms"}
+
+
+def cpu_baseline_global(seconds=10.0):
+    """The float64 oracle on the global workload (B=1 H=8 N=100000 d=128, the whole workload:
+    state from every key, then every query read); its 8 heads split over the host threads."""
+    import datagen
+    import oracle
+
+    w = datagen.WORKLOADS[4]
+    q, k, v = (datagen.to_f64(x) for x in datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed,
+                                                            w.scale, "bf16"))
+    t, runs = _median_runs(lambda: oracle.global_(q, k, v), seconds, at_least=2)
+    return {"value": w.B * w.H * w.N / t, "unit": "tokens/s (B*H*N/s)", "cores": oracle.threads(),
+            "kind": "oracle", "us_per_call": t * 1e6,
+            "sample": f"{w.name}, the whole workload (inputs drawn on the device as the GPU leg "
+                      f"does), float64, median of {runs} runs of {t:.2f} s; 8 heads, so at most 8 "
+                      "threads have work"}
+
+
+def cpu_baseline_decode(seconds=10.0):
+    """The float64 oracle's decode step on all 256 x 32 heads of the decode workload: steps per
+    second over a few consecutive steps. The state is a seeded synthetic one of the decode
+    state's shape and magnitude (building the 4096-token prior takes the oracle minutes; the
+    time of a step does not depend on the values), the step tokens are the workload's."""
+    import datagen
+    import oracle
+
+    w = datagen.WORKLOADS[5]
+    S = datagen.to_f64(datagen.normal_cuda((w.B, w.H, w.d, w.dv), w.seed + 7, 6.0))
+    z = 4096.0 + datagen.to_f64(datagen.normal_cuda((w.B, w.H, w.d), w.seed + 8, 64.0))
+    nsteps = 4
+    toks = [datagen.to_f64(x[:nsteps]) for x in datagen.decode_tokens(w, nsteps)]
+    state = {"S": S, "z": z}
+
+    def run():
+        Sc, zc = state["S"], state["z"]
+        for t in range(nsteps):
+            _, Sc, zc = oracle.decode_step(toks[0][t], toks[1][t], toks[2][t], Sc, zc)
+
+    t, runs = _median_runs(run, seconds, at_least=2)
+    return {"value": nsteps / t, "unit": "decode steps/s (all 8192 heads per step)",
+            "cores": oracle.threads(), "kind": "oracle", "us_per_step": t / nsteps * 1e6,
+            "sample": f"{nsteps} consecutive decode steps of {w.name} from a seeded synthetic "
+                      f"float64 state, median of {runs} runs of {t:.2f} s"}
+
+
 def cpu_baseline():
     """The float64 oracle, as it stands, on the prefill workload's 32 heads (full size) on all
     host threads, and on 4 of its heads single-threaded: each repeated for about 10 s and 5 s
@@ -364,6 +494,18 @@ def copy_bandwidth(nbytes=256 << 20, reps=20):
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
     dst = [torch.empty_like(src) for _ in range(2)]
     ms, _ = time_calls(lambda i: torch.mul(src, 1.0, out=dst[i % 2]), reps, 3)
+    return 2 * nbytes / (ms * 1e-3)
+
+
+def d2d_bandwidth(nbytes=205 << 20, reps=20):
+    """Read + write bandwidth of a device-to-device copy (hipMemcpyAsync through tensor.copy_) of
+    `nbytes` of varied bf16 data: the rate of a plain mixed read/write stream, which the causal
+    kernel (218 MB read, 69 MB written per launch) is."""
+    import torch
+    n = nbytes // 2
+    src = (torch.arange(n, device="cuda", dtype=torch.int32) * 40503).to(torch.int16).view(torch.bfloat16)
+    dst = torch.empty_like(src)
+    ms, _ = time_calls(lambda i: dst.copy_(src), reps, 3)
     return 2 * nbytes / (ms * 1e-3)
 
 
@@ -439,7 +581,7 @@ def main():
     ap.add_argument("--serve-steps", dest="serve_steps", type=int, default=256,
                     help="decode steps after the prefill in the serving leg")
     ap.add_argument("--only", choices=["prefill", "decode", "global", "favor", "variants",
-                                       "retention", "serving", "copycal"],
+                                       "retention", "serving", "copycal", "small"],
                     default=None,
                     help="run one form only (for profiling); no JSON line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -459,6 +601,14 @@ def main():
         n = copy_calibration()
         print(f"copycal: copied {n} bytes x 5", flush=True)
         return
+    if args.only == "small":
+        if args.copycal:
+            copy_calibration()
+        for n in (1, 2):
+            wn, hot, flushed, kern_n, _ = bench_causal_small(args, n)
+            print(f"workload {n} ({wn.name}): hot {hot * 1e3:.1f} us, flushed {flushed * 1e3:.1f} us",
+                  flush=True)
+        return
     if args.only:
         if args.copycal:
             copy_calibration()
@@ -476,16 +626,9 @@ def main():
         print(f"{args.only}: {ms:.4f} ms/step{extra}", flush=True)
         return
 
-    w, ms, ms_hot, wall, byts, flops, P, kern_ms = bench_prefill(args)
-    print(f"prefill: {ms * 1e3:.1f} us/step (hot {ms_hot * 1e3:.1f} us); kernels "
-          f"agg {kern_ms[0] * 1e3:.1f} scan {kern_ms[1] * 1e3:.1f} causal {kern_ms[2] * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
-    th = w.B * w.H * w.N
-    value = th / (ms * 1e-3)
-    achieved = byts / (kern_ms[2] * 1e-3)
-    copy_bw = copy_bandwidth()
-    traffic = recorded_traffic()
-    issued = mfma_issued_prefill(w.B, w.H, w.N, P)
+    # The other forms run first: by the time the headline's own warm-up and timed steps run, the
+    # chip has worked for several seconds and runs at its sustained clock (on a cold chip the
+    # first few hundred calls run several percent slower while it ramps up).
     wd, ms_d, byts_d = bench_decode(args)
     # reference for the decode step: an in-place read-modify-write over a buffer of its state's
     # size (S and z in float32, 541 MB for the decode workload)
@@ -503,6 +646,25 @@ def main():
     ws_, K_s, ms_s, ms_sp = bench_serving(args)
     print(f"serving: {ms_s * 1e3:.1f} us per prefill + {K_s} decode steps", file=sys.stderr,
           flush=True)
+    small = {}
+    for n in (1, 2):
+        wn, hot, flushed, kern_n, P_n = bench_causal_small(args, n)
+        small[n] = (wn, hot, flushed, kern_n, P_n)
+        print(f"workload {n} ({wn.name}): hot {hot * 1e3:.1f} us, flushed {flushed * 1e3:.1f} us; "
+              "kernels " + ", ".join(f"{t * 1e3:.1f}" for t in kern_n) + " us",
+              file=sys.stderr, flush=True)
+
+    w, ms, ms_hot, wall, byts, flops, P, kern_ms, ms_steady = bench_prefill(args)
+    print(f"prefill: {ms * 1e3:.1f} us/step (hot {ms_hot * 1e3:.1f} us); kernels "
+          f"agg {kern_ms[0] * 1e3:.1f} scan {kern_ms[1] * 1e3:.1f} causal {kern_ms[2] * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    th = w.B * w.H * w.N
+    value = th / (ms * 1e-3)
+    achieved = byts / (kern_ms[2] * 1e-3)
+    copy_bw = copy_bandwidth()
+    d2d_bw = d2d_bandwidth()
+    traffic = recorded_traffic()
+    issued = mfma_issued_prefill(w.B, w.H, w.N, P)
 
     rec = {
         "metric": METRIC,
@@ -529,6 +691,7 @@ def main():
                      "kernel_us": kern_ms[2] * 1e3,
                      "algorithmic_bytes_per_launch": byts,
                      "copy_GBps": copy_bw / 1e9, "frac_of_copy": achieved / copy_bw,
+                     "d2d_copy_GBps": d2d_bw / 1e9, "frac_of_d2d_copy": achieved / d2d_bw,
                      "call_us": ms * 1e3, "call_frac": byts / (ms * 1e-3) / HBM_PEAK,
                      "call_kernels_us": {"segment_sums": kern_ms[0] * 1e3,
                                          "segment_scan": kern_ms[1] * 1e3,
@@ -537,6 +700,9 @@ def main():
                  "issued_frac": issued / (ms * 1e-3) / BF16_PEAK,
                  "peak_tflops": BF16_PEAK / 1e12},
         "hot_cache_ms_per_step": ms_hot,
+        "steady_state": {"ms_per_step": ms_steady, "token_heads_per_s": th / (ms_steady * 1e-3),
+                         "warmup": 200, "steps": 200,
+                         "hbm_frac": byts / (ms_steady * 1e-3) / HBM_PEAK},
         "decode": {"workload": wd.name, "us_per_step": ms_d * 1e3,
                    "GB_per_s": byts_d / (ms_d * 1e-3) / 1e9,
                    "hbm_frac": byts_d / (ms_d * 1e-3) / HBM_PEAK,
@@ -565,8 +731,40 @@ def main():
                     "token_heads_per_s": ws_.B * ws_.H * (ws_.N + K_s) / (ms_s * 1e-3)},
         "wall_s_timed_region": wall,
     }
+    workloads = {}
+    for n, (wn, hot, flushed, kern_n, P_n) in small.items():
+        th_n = wn.B * wn.H * wn.N
+        es = 2 if wn.dtype == "bf16" else 4
+        byts_n = algo_prefill(wn.B, wn.H, wn.N, wn.d, wn.dv, es)[0]
+        entry = {"form": "causal", "dtype": wn.dtype, "chunk": wn.chunk or None,
+                 "segments_per_head": P_n, "entry_point": "la_causal_fwd_ws",
+                 "us_per_call_hot": hot * 1e3, "us_per_call_flushed": flushed * 1e3,
+                 "token_heads_per_s_flushed": th_n / (flushed * 1e-3),
+                 "kernels_us": {"segment_sums": kern_n[0] * 1e3, "segment_scan": kern_n[1] * 1e3,
+                                "causal": kern_n[2] * 1e3},
+                 "algorithmic_bytes_per_call": byts_n,
+                 "call_hbm_frac_flushed": byts_n / (flushed * 1e-3) / HBM_PEAK}
+        if wn.dtype == "bf16":
+            entry["roofline"] = {"bound": "hbm", "kernel": f"k_causal<{wn.d}, 0, false, false>",
+                                 "achieved": byts_n / (kern_n[2] * 1e-3) / 1e9,
+                                 "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                                 "frac": byts_n / (kern_n[2] * 1e-3) / HBM_PEAK,
+                                 "note": "kernel timed hot (inputs fit in the last-level cache)"}
+        else:
+            entry["bound"] = "launch latency (64 token-heads, three launches)"
+        workloads[wn.name] = entry
+    workloads[wd.name] = rec.pop("decode")
+    workloads[wg.name] = rec.pop("global")
+    rec["workloads"] = workloads
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline()
+        workloads[small[1][0].name]["cpu_baseline"] = cpu_baseline_causal(1, 2.0)
+        workloads[small[2][0].name]["cpu_baseline"] = cpu_baseline_causal(2, 5.0)
+        print("cpu baselines: workloads 1, 2 done", file=sys.stderr, flush=True)
+        workloads[wg.name]["cpu_baseline"] = cpu_baseline_global()
+        print("cpu baselines: global done", file=sys.stderr, flush=True)
+        workloads[wd.name]["cpu_baseline"] = cpu_baseline_decode()
+        print("cpu baselines: decode done", file=sys.stderr, flush=True)
     print(json.dumps(rec), flush=True)
 
 

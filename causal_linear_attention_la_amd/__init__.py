@@ -108,9 +108,6 @@ def _load(path: Path):
     return lib
 
 
-lib = _load(LIB_PATH)
-
-
 def hip_runtimes() -> list:
     """Paths of the HIP runtime libraries (libamdhip64) mapped into this process."""
     paths = set()
@@ -120,6 +117,14 @@ def hip_runtimes() -> list:
             if len(parts) >= 6 and "libamdhip64" in parts[-1]:
                 paths.add(os.path.realpath(parts[-1]))
     return sorted(paths)
+
+
+lib = _load(LIB_PATH)
+if len(hip_runtimes()) > 1:
+    # two runtimes in one process do not share devices, memory or streams: the library's calls
+    # on PyTorch's tensors would fault, so refuse here instead
+    raise ImportError("liblinattn bound to a second HIP runtime (import torch before this "
+                      f"package): {hip_runtimes()}")
 
 
 def strerror(status: int) -> str:

@@ -24,6 +24,7 @@ constexpr long kCUs = 256;
 bool dim_ok(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
 
 constexpr int kRfMaxFeatures = 4096; // projections per random-feature map
+constexpr size_t kLdsBytes = 160 * 1024; // LDS one workgroup can hold on gfx950
 
 struct Span {
     uintptr_t lo, hi; // [lo, hi); empty when lo == hi
@@ -75,12 +76,14 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
     if (chunk == 0) {
         pl.mfma = mfma_ok;
         pl.chunk = mfma_ok ? 64 : 32;
-    } else if (chunk == 64) {
-        if (!mfma_ok)
-            return LA_ENOTSUP;
+    } else if (chunk == 64 && mfma_ok) {
         pl.mfma = true;
         pl.chunk = 64;
-    } else if (chunk == 16 || chunk == 32) {
+    } else if (chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128) {
+        // the vector-ALU kernels take any chunk whose working set fits the 160 KiB of LDS a
+        // workgroup can hold (chunks 64 and 128 at small head sizes)
+        if (la::valu_lds_bytes(d, dv, chunk) > kLdsBytes)
+            return LA_ENOTSUP;
         pl.mfma = false;
         pl.chunk = chunk;
     } else {
@@ -908,7 +911,7 @@ const char *la_strerror(int status)
                "decode with N != 1, unknown dtype or unknown flag bits)";
     case LA_ENOTSUP:
         return "unsupported shape or chunk (d and d_v must be 16, 32, 64 or 128; chunk 0, 16, "
-               "32 or 64 as the shape allows; random features: d <= 256, m <= 4096)";
+               "32, 64 or 128 as the shape allows; random features: d <= 256, m <= 4096)";
     case LA_EHIP:
         return "HIP runtime error (allocation or kernel launch failed)";
     case LA_ENOSPACE:

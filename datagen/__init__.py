@@ -49,6 +49,18 @@ def qkv(B: int, H: int, N: int, d: int, dv: int, seed: int, scale: float = 1.0,
     return tuple(out)
 
 
+def normal_cuda(shape, seed: int, scale: float = 1.0, dtype: str = "f32",
+                device: str = "cuda") -> torch.Tensor:
+    """One tensor of IID N(0, scale^2) values drawn on the device (torch's seeded Philox
+    generator), rounded to ``dtype``."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32)
+    if scale != 1.0:
+        x.mul_(scale)
+    return x.to(DTYPES[dtype])
+
+
 def qkv_cuda(B: int, H: int, N: int, d: int, dv: int, seed: int, scale: float = 1.0,
              dtype: str = "bf16", device: str = "cuda"):
     """Large inputs drawn directly on the device with torch's seeded Philox generator.

@@ -54,7 +54,8 @@
  *   LA_EINVAL   a required pointer is NULL or misaligned, a size is <= 0, decode with N != 1,
  *               dtype unknown, or buffers overlap as forbidden above; nothing was enqueued
  *   LA_ENOTSUP  valid but unsupported: d or d_v not in {16, 32, 64, 128}, chunk not accepted
- *               for this shape/dtype, or a size whose index arithmetic would overflow
+ *               for this shape/dtype (see la_causal_fwd), or a size whose index arithmetic
+ *               would overflow
  *   LA_EHIP     the HIP runtime reported an error (allocation or launch); work enqueued before
  *               the failure may have run
  *   LA_ENOSPACE la_causal_fwd_noalloc only: the call needs more scratch than the library's
@@ -98,9 +99,12 @@ enum { LA_PHI_IDENTITY = 1, LA_UNNORMALIZED = 2 };
  *          sequence) and overwritten with the state after token N-1, so a long sequence can
  *          be processed in pieces and handed to la_decode_step. One NULL and one not: LA_EINVAL.
  *   chunk  tokens per intra-chunk tile: 0 lets the library choose; 64 selects the
- *          matrix-core kernel (bf16, d = d_v in {64, 128}); 16 or 32 select the vector-ALU
- *          kernel (any supported d, d_v, either dtype). Other values: LA_ENOTSUP. Results are
- *          the same within rounding for every accepted chunk.
+ *          matrix-core kernel for bf16 with d = d_v in {64, 128}; otherwise 16, 32, 64 or 128
+ *          select the vector-ALU kernel (any supported d, d_v, either dtype) when its working
+ *          set, 4 (d d_v + d + chunk (2 d + d_v) + chunk^2 + chunk) bytes, fits the 160 KiB of
+ *          LDS of a workgroup (chunk 128 at d, d_v <= 32 or so). Other values, or a working set
+ *          that does not fit: LA_ENOTSUP. Results are the same within rounding for every
+ *          accepted chunk.
  * Defined by the recurrence S_i = S_{i-1} + phi(k_i) v_i^T, z_i = z_{i-1} + phi(k_i) of
  * "Linear Attention Math", section "The recurrent form: a running KV state"; the chunked
  * evaluation (within-chunk part plus the state carried from earlier chunks) is the one that

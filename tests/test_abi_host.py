@@ -179,7 +179,8 @@ def test_causal_rf_argument_checks():
     assert crf(d=257) == la.LA_ENOTSUP
     assert crf(m=48) == la.LA_ENOTSUP                           # the attention runs over m
     assert crf(dv=256) == la.LA_ENOTSUP
-    assert crf(chunk=64, dtype=la.LA_F32) == la.LA_ENOTSUP
+    # a chunk whose vector-ALU working set exceeds the LDS of a workgroup
+    assert crf(chunk=128, dv=128, dtype=la.LA_F32) == la.LA_ENOTSUP
 
 
 def test_profiled_argument_checks():
@@ -205,12 +206,18 @@ def test_separate_state_checks():
 
 
 def test_chunk_and_segment_checks():
-    assert call("la_causal_fwd", chunk=128) == la.LA_ENOTSUP
     assert call("la_causal_fwd", chunk=-1) == la.LA_EINVAL
-    # the matrix-core chunk needs bf16 with d == d_v in {64, 128}
-    assert call("la_causal_fwd", chunk=64, d=16, dv=16) == la.LA_ENOTSUP
-    assert call("la_causal_fwd", chunk=64, d=64, dv=64, dtype=la.LA_F32) == la.LA_ENOTSUP
-    assert call("la_causal_fwd", chunk=64, d=64, dv=128) == la.LA_ENOTSUP
+    assert call("la_causal_fwd", chunk=96) == la.LA_ENOTSUP
+    # chunks 64 and 128 outside the matrix-core shapes go to the vector-ALU kernels when their
+    # working set fits 160 KiB of LDS: not at d = d_v = 64 or 128 with chunk 128
+    assert call("la_causal_fwd", chunk=128, d=128, dv=128) == la.LA_ENOTSUP
+    assert call("la_causal_fwd", chunk=128, d=64, dv=64, dtype=la.LA_F32) == la.LA_ENOTSUP
+    assert call("la_global_fwd", chunk=128, d=128, dv=64) == la.LA_ENOTSUP
+    for d, dv, chunk, dtype in [(16, 16, 128, la.LA_F32), (32, 32, 128, la.LA_BF16),
+                                (16, 64, 64, la.LA_F32), (64, 64, 64, la.LA_F32),
+                                (64, 128, 64, la.LA_BF16)]:
+        assert la.la_segments(0, 1, 2, 1000, d, dv, chunk, 0, dtype) > 0, (d, dv, chunk)
+        assert la.la_segments(0, 1, 2, 1000, d, dv, chunk, 2 * chunk, dtype) == -(-1000 // (2 * chunk))
     assert call("la_global_fwd", chunk=48) == la.LA_ENOTSUP
     assert call("la_causal_fwd_seg", chunk=32, seg=48) == la.LA_ENOTSUP
     assert call("la_causal_fwd_seg", chunk=32, seg=-32) == la.LA_EINVAL

@@ -123,7 +123,7 @@ def _workload(n):
     return w, q, k, v
 
 
-@pytest.mark.parametrize("chunk", [0, 16, 32])
+@pytest.mark.parametrize("chunk", [0, 16, 32, 64, 128])
 def test_workload1_causal_f32(chunk):
     w, q, k, v = _workload(1)
     say(f"workload 1 {w.name} chunk={chunk}")
@@ -280,7 +280,9 @@ def test_workload5_decode_full_prior_float32_state():
     ("bf16", 128, 128, 1, 0), ("bf16", 128, 128, 63, 0), ("bf16", 128, 128, 65, 0),
     ("bf16", 128, 128, 1000, 0), ("bf16", 64, 64, 1, 0), ("bf16", 64, 64, 129, 0),
     ("f32", 128, 128, 65, 16), ("f32", 64, 32, 77, 32), ("bf16", 32, 128, 50, 0),
-    ("bf16", 128, 16, 50, 0), ("f32", 16, 16, 1, 0), ("bf16", 16, 64, 300, 16)])
+    ("bf16", 128, 16, 50, 0), ("f32", 16, 16, 1, 0), ("bf16", 16, 64, 300, 16),
+    ("f32", 32, 32, 300, 128), ("bf16", 16, 16, 1000, 128), ("f32", 64, 64, 333, 64),
+    ("bf16", 64, 128, 200, 64)])
 def test_ragged_and_mixed_shapes(dtype, d, dv, N, chunk):
     q, k, v = datagen.qkv(2, 3, N, d, dv, 77 + N, 1 / math.sqrt(d), dtype)
     say(f"ragged dtype={dtype} d={d} dv={dv} N={N} chunk={chunk}")
