@@ -99,7 +99,7 @@ def bench_prefill(args):
     # on its own: measured on MI355X, the first few hundred calls of a process run 3-15 % slower
     # than the sustained rate (calls 5-25 at 95-97 us, 25-100 at 98-107 us, 300-400 at 92 us), so
     # the headline's own W warm-up and K timed steps follow it.
-    ms_steady, _ = time_calls(step, 200, 200)
+    ms_steady = time_calls(step, args.steady, args.steady)[0] if args.steady else None
     ms, wall = time_calls(step, args.steps, args.warmup)
     # same buffers every step (inputs may stay in the last-level cache)
     ms_hot, _ = time_calls(lambda i: step(0), args.steps, 2)
@@ -574,6 +574,9 @@ def main():
     # 200, 91 us after 500; the per-kernel times settle within the first ~50 calls)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steady", type=int, default=200,
+                    help="untimed and then timed calls of the prefill's steady-state leg, run "
+                         "before the headline's W/K steps (0: skip)")
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--seg-len", dest="seg_len", type=int, default=0)
     ap.add_argument("--rotate", type=int, default=3, help="input sets cycled over the steps")
@@ -700,9 +703,10 @@ def main():
                  "issued_frac": issued / (ms * 1e-3) / BF16_PEAK,
                  "peak_tflops": BF16_PEAK / 1e12},
         "hot_cache_ms_per_step": ms_hot,
-        "steady_state": {"ms_per_step": ms_steady, "token_heads_per_s": th / (ms_steady * 1e-3),
-                         "warmup": 200, "steps": 200,
-                         "hbm_frac": byts / (ms_steady * 1e-3) / HBM_PEAK},
+        "steady_state": None if ms_steady is None else {
+            "ms_per_step": ms_steady, "token_heads_per_s": th / (ms_steady * 1e-3),
+            "warmup": args.steady, "steps": args.steady,
+            "hbm_frac": byts / (ms_steady * 1e-3) / HBM_PEAK},
         "decode": {"workload": wd.name, "us_per_step": ms_d * 1e3,
                    "GB_per_s": byts_d / (ms_d * 1e-3) / 1e9,
                    "hbm_frac": byts_d / (ms_d * 1e-3) / HBM_PEAK,

@@ -20,6 +20,7 @@ enum Form { CAUSAL = 0, GLOBAL = 1, DECODE = 2 };
 // segments, one per CU, 195.5 us). The other kernels fit two per CU. More segments than that
 // only add segment-state traffic (66 KB read and written per extra segment at d = 128).
 constexpr long kCUs = 256;
+constexpr long kMinChunks = 4;
 
 bool dim_ok(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
 
@@ -98,8 +99,15 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
     } else {
         const long target = (pl.mfma && d == 128) ? kCUs : 2 * kCUs;
         long want = (target + (long)BH - 1) / (long)BH; // segments per head
-        if (want > nchunks)
-            want = nchunks;
+        // matrix-core kernels: at least kMinChunks chunks per segment; a segment's fixed costs
+        // (its sum written and scanned, its prefix read, the pipeline filled) outweigh its
+        // parallelism below that (measured on MI355X, B=4 H=8 N=2048 d=64: 16 segments of 2
+        // chunks 27.1 us per call, 8 segments of 4 chunks 24.8 us, both with cold caches). The
+        // vector-ALU kernels spend far longer per chunk, so they keep every segment (one chunk
+        // of B=1 H=1 N=64 d=16 float32 per segment: 23.4 us per call; one segment: 27.1 us).
+        const long most = !pl.mfma ? nchunks : nchunks / kMinChunks > 1 ? nchunks / kMinChunks : 1;
+        if (want > most)
+            want = most;
         pl.L = (int)((nchunks + want - 1) / want) * pl.chunk;
     }
     pl.P = (int)((N + (long)pl.L - 1) / pl.L);

@@ -235,11 +235,17 @@ def test_workspace_bytes():
     # global B=1 H=8 N=100000 d=128: one segment per CU as well, 256 / 8 = 32 per head
     assert la.la_segments(1, 1, 8, 100000, 128, 128) == 32
     assert la.la_segments(0, 1, 1, 64, 48, 16) == 0
-    # d = 64: two workgroups per CU, 512 / 32 = 16 segments of 128 tokens
+    # d = 64: two workgroups per CU would give 512 / 32 = 16 segments, but a segment keeps at
+    # least 4 chunks: 8 segments of 256 tokens (32 chunks per head)
     E64 = 64 * 64 + 64
-    assert la.la_workspace_bytes(0, 4, 8, 2048, 64, 64) == 32 * 16 * E64 * 4
-    # N=64 float32: chunk 32, split in two segments of one chunk; one segment needs no workspace
+    assert la.la_segments(0, 4, 8, 2048, 64, 64) == 8
+    assert la.la_workspace_bytes(0, 4, 8, 2048, 64, 64) == 32 * 8 * E64 * 4
+    assert la.la_segments(0, 4, 8, 8192, 64, 64) == 16
+    # N=64 float32 (the vector-ALU kernels keep one chunk per segment): chunk 32, two segments
+    # of one chunk; one segment needs no workspace
+    assert la.la_segments(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 2
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 2 * (16 * 16 + 16) * 4
+    assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 32, la.LA_F32) == 2 * (16 * 16 + 16) * 4
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 64, la.LA_F32) == 0
     assert la.la_workspace_bytes(1, 1, 8, 100000, 128, 128) > 0
     assert la.la_workspace_bytes(2, 1, 8, 10, 128, 128) == 0

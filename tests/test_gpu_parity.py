@@ -123,11 +123,12 @@ def _workload(n):
     return w, q, k, v
 
 
-@pytest.mark.parametrize("chunk", [0, 16, 32, 64, 128])
-def test_workload1_causal_f32(chunk):
+@pytest.mark.parametrize("chunk,seg", [(0, 0), (16, 0), (32, 0), (64, 0), (128, 0), (16, 16),
+                                       (16, 32), (32, 32)])
+def test_workload1_causal_f32(chunk, seg):
     w, q, k, v = _workload(1)
-    say(f"workload 1 {w.name} chunk={chunk}")
-    o, S, z = causal(q, k, v, chunk=chunk)
+    say(f"workload 1 {w.name} chunk={chunk} seg_len={seg}")
+    o, S, z = causal(q, k, v, chunk=chunk, seg_len=seg)
     oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v))
     check("out", o, oo, TOL["f32"])
     check("S", S, So, TOL["f32"])
