@@ -1017,28 +1017,7 @@ __global__ __launch_bounds__(NT, 3) void k_gread(const uint16_t *__restrict__ q,
     const int tb = p * L, te = min(N, tb + L);
     const size_t hoff = (size_t)bh * N * D;
 
-    // S^T -> LDS: fragment fr = ct * NKB + kb, lane ll = lli + 16 lg holds S[32 kb + 8 lg + j]
-    // [16 ct + lli], j < 8 (the A operand: row = value column, k-slots = 8 features)
-    {
-        const float *Sh = S + (size_t)bh * D * D;
-        for (int e = tid; e < D * D / 8; e += NT) {
-            const int ll = e & 63, fr = e >> 6;
-            const int ct = fr / NKB, kb = fr % NKB, lli = ll & 15, lg = ll >> 4;
-            float x[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                x[j] = Sh[(32 * kb + 8 * lg + j) * D + 16 * ct + lli];
-            sts<u32x4>(sS + 8 * e, u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]),
-                                        pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])});
-        }
-        if (tid < D)
-            sz[tid] = z[(size_t)bh * D + tid];
-    }
-    __syncthreads();
-
     const int ntile = (te - tb + 15) / 16;
-    if (w >= ntile)
-        return;
     // B operand of tile t: row tb + 16 t + li (clamped to the segment's last row: every load is
     // in bounds), features 32 kb + 8 g .. + 7
     auto ldq = [&](u32x4 (&r)[NKB], int t) {
@@ -1047,9 +1026,48 @@ __global__ __launch_bounds__(NT, 3) void k_gread(const uint16_t *__restrict__ q,
         for (int kb = 0; kb < NKB; ++kb)
             r[kb] = *reinterpret_cast<const u32x4 *>(q + hoff + (size_t)row * D + 32 * kb + 8 * g);
     };
-    uint16_t *tile = sT[w];
+    // the wave's first tile is requested before S, so both loads are in flight together
     u32x4 qa[NKB], qn[NKB];
     ldq(qa, w);
+
+    // S^T -> LDS: fragment fr = ct * NKB + kb, lane ll = lli + 16 lg holds S[32 kb + 8 lg + j]
+    // [16 ct + lli], j < 8 (the A operand: row = value column, k-slots = 8 features). Item u
+    // is the 8 x 4 block of S at rows 8 rg .. + 7 (rg = 4 kb + lg), columns 4 c4 .. + 3: eight
+    // 16-byte row loads, all of a thread's items issued before any is converted, then four
+    // whole fragment entries.
+    {
+        constexpr int NU = D * D / 32, NI = (NU + NT - 1) / NT;
+        const float *Sh = S + (size_t)bh * D * D;
+        f32x4 x[NI][8];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int u = tid + i * NT, rg = u / (D / 4), c4 = u % (D / 4);
+            if (u < NU)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    x[i][j] = *reinterpret_cast<const f32x4 *>(Sh + (size_t)(8 * rg + j) * D + 4 * c4);
+        }
+        if (tid < D)
+            sz[tid] = z[(size_t)bh * D + tid];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int u = tid + i * NT, rg = u / (D / 4), c4 = u % (D / 4);
+            if (u < NU)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int col = 4 * c4 + c, ct = col / 16, lli = col % 16;
+                    const int kb = rg / 4, lg = rg % 4;
+                    sts<u32x4>(sS + ((ct * NKB + kb) * 64 + lli + 16 * lg) * 8,
+                               u32x4{pack_bf2(x[i][0][c], x[i][1][c]), pack_bf2(x[i][2][c], x[i][3][c]),
+                                     pack_bf2(x[i][4][c], x[i][5][c]), pack_bf2(x[i][6][c], x[i][7][c])});
+                }
+        }
+    }
+    __syncthreads();
+
+    if (w >= ntile)
+        return;
+    uint16_t *tile = sT[w];
     for (int t = w; t < ntile; t += 4) {
         ldq(qn, min(t + 4, ntile - 1)); // next tile (a re-read of the last one at the end)
         bf16x8 qb[NKB];

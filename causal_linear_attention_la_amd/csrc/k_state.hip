@@ -5,9 +5,10 @@
 // Pairwise Reads to a Recurrent State", section "A recurrence need not force token-serial
 // training"), so the state before segment p is the initial state plus the sums of segments
 // 0..p-1; the global state is the sum of all segments ("Linear Attention Math", section "The
-// associativity trick, written out"). Each thread owns one float of the E = d*d_v + d
-// floats of a head's state and walks the P segment slots in order (fixed order: the result
-// does not depend on scheduling).
+// associativity trick, written out"). Each lane owns four consecutive floats of the
+// E = d*d_v + d floats of a head's state; the prefix walks the P segment slots in order, the
+// total adds them in an order fixed by P (either way the result does not depend on
+// scheduling).
 //
 // Decode step ("Linear Attention Math", section "The recurrent form"): for each head,
 // S' = S + phi(k) v^T and z' = z + phi(k) are written back in place, then
@@ -76,30 +77,48 @@ __global__ __launch_bounds__(NT) void k_seg_scan(float *__restrict__ ws, const f
     *reinterpret_cast<float4 *>(slot + (size_t)(P - 1) * E) = run;
 }
 
+// The global state of a head, the sum of its P segment states, in an order fixed by P alone:
+// wave w of a workgroup adds segments w, w + 4, w + 8, ... (lane l owns four consecutive floats,
+// and a lane's loads are independent of one another, TB of them issued together), and the four
+// waves' partial sums are then added in wave order. A single in-order walk per thread waited for
+// each pair of loads before the next (measured on MI355X, 8 heads of 32 segments at
+// d = d_v = 128: 7.6 us).
+constexpr int TB = 8;
+
 __global__ __launch_bounds__(NT) void k_seg_total(const float *__restrict__ ws, float *__restrict__ S,
                                                   float *__restrict__ z, int P, int d, int dv,
                                                   int blocks_per_head)
 {
-    const int E = d * dv + d;
-    const int bh = blockIdx.x / blocks_per_head;
-    const int e = (blockIdx.x % blocks_per_head) * NT + threadIdx.x;
-    if (e >= E)
-        return;
-    const float *slot = ws + (size_t)bh * P * E + e;
-    float run = 0.f;
-    for (int p0 = 0; p0 < P; p0 += SB) {
-        float t[SB];
+    constexpr int NW = NT / 64;
+    __shared__ f32x4 part[NW][64];
+    const int E4 = (d * dv + d) / 4;
+    const int bh = blockIdx.x / blocks_per_head, w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int e4 = (blockIdx.x % blocks_per_head) * 64 + l;
+    f32x4 run = {0.f, 0.f, 0.f, 0.f};
+    if (e4 < E4) {
+        const f32x4 *slot = reinterpret_cast<const f32x4 *>(ws + (size_t)bh * P * E4 * 4) + e4;
+        for (int p0 = w; p0 < P; p0 += NW * TB) {
+            f32x4 t[TB];
 #pragma unroll
-        for (int i = 0; i < SB; ++i)
-            t[i] = p0 + i < P ? slot[(size_t)(p0 + i) * E] : 0.f;
+            for (int i = 0; i < TB; ++i)
+                t[i] = p0 + NW * i < P ? slot[(size_t)(p0 + NW * i) * E4] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < SB; ++i)
-            run += t[i];
+            for (int i = 0; i < TB; ++i)
+                run += t[i];
+        }
     }
+    part[w][l] = run;
+    __syncthreads();
+    if (w != 0 || e4 >= E4)
+        return;
+#pragma unroll
+    for (int i = 1; i < NW; ++i)
+        run += part[i][l];
+    const int e = 4 * e4;
     if (e < d * dv)
-        S[(size_t)bh * d * dv + e] = run;
+        *reinterpret_cast<f32x4 *>(S + (size_t)bh * d * dv + e) = run;
     else
-        z[(size_t)bh * d + (e - d * dv)] = run;
+        *reinterpret_cast<f32x4 *>(z + (size_t)bh * d + (e - d * dv)) = run;
 }
 
 // One head per workgroup. Thread layout over the [D, DV] state: CG = DV/4 column groups of 4
@@ -225,7 +244,9 @@ hipError_t seg_exclusive_scan(float *ws, const float *S0, const float *z0, int B
 hipError_t seg_total(const float *ws, float *S, float *z, int BH, int P, int d, int dv,
                      hipStream_t st)
 {
-    const int E = d * dv + d, bph = (E + NT - 1) / NT;
+    if (d % 4 || dv % 4 || ((uintptr_t)ws & 15) || ((uintptr_t)S & 15) || ((uintptr_t)z & 15))
+        return hipErrorInvalidValue;
+    const int E4 = (d * dv + d) / 4, bph = (E4 + 63) / 64;
     hipLaunchKernelGGL(k_seg_total, dim3((unsigned)(BH * bph)), dim3(NT), 0, st, ws, S, z, P, d,
                        dv, bph);
     return hipGetLastError();
