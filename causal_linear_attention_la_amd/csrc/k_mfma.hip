@@ -999,7 +999,7 @@ template <int D> struct GreadCfg {
 };
 
 // (at most 168 VGPRs: three waves per SIMD, so three workgroups share a CU)
-template <int D, int F>
+template <int D, int F, int RT = 2>
 __global__ __launch_bounds__(NT, 3) void k_gread(const uint16_t *__restrict__ q,
                                               uint16_t *__restrict__ out,
                                               const float *__restrict__ S,
@@ -1017,18 +1017,24 @@ __global__ __launch_bounds__(NT, 3) void k_gread(const uint16_t *__restrict__ q,
     const int tb = p * L, te = min(N, tb + L);
     const size_t hoff = (size_t)bh * N * D;
 
-    const int ntile = (te - tb + 15) / 16;
+    const int ntile = (te - tb + 15) / 16, ngrp = (ntile + RT - 1) / RT;
     // B operand of tile t: row tb + 16 t + li (clamped to the segment's last row: every load is
-    // in bounds), features 32 kb + 8 g .. + 7
+    // in bounds), features 32 kb + 8 g .. + 7; a group is RT consecutive tiles (tiles past the
+    // segment's end load its last tile again and store nothing)
     auto ldq = [&](u32x4 (&r)[NKB], int t) {
         const int row = min(tb + 16 * t + li, te - 1);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
             r[kb] = *reinterpret_cast<const u32x4 *>(q + hoff + (size_t)row * D + 32 * kb + 8 * g);
     };
-    // the wave's first tile is requested before S, so both loads are in flight together
-    u32x4 qa[NKB], qn[NKB];
-    ldq(qa, w);
+    auto ldg = [&](u32x4 (&r)[RT][NKB], int gi) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            ldq(r[rt], min(gi * RT + rt, ntile - 1));
+    };
+    // the wave's first group is requested before S, so both loads are in flight together
+    u32x4 qa[RT][NKB], qn[RT][NKB];
+    ldg(qa, w);
 
     // S^T -> LDS: fragment fr = ct * NKB + kb, lane ll = lli + 16 lg holds S[32 kb + 8 lg + j]
     // [16 ct + lli], j < 8 (the A operand: row = value column, k-slots = 8 features). Item u
@@ -1065,46 +1071,14 @@ __global__ __launch_bounds__(NT, 3) void k_gread(const uint16_t *__restrict__ q,
     }
     __syncthreads();
 
-    if (w >= ntile)
+    if (w >= ngrp)
         return;
     uint16_t *tile = sT[w];
-    for (int t = w; t < ntile; t += 4) {
-        ldq(qn, min(t + 4, ntile - 1)); // next tile (a re-read of the last one at the end)
-        bf16x8 qb[NKB];
-        float den = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            const u32x4 y = PHI ? phi8(qa[kb]) : qa[kb];
-            qb[kb] = __builtin_bit_cast(bf16x8, y);
-            if (NORM) {
-                const float4 z0 = *reinterpret_cast<const float4 *>(sz + 32 * kb + 8 * g);
-                const float4 z1 = *reinterpret_cast<const float4 *>(sz + 32 * kb + 8 * g + 4);
-                const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h)
-                    den = fmaf(bf_lo(y[h]), zz[2 * h], fmaf(bf_hi(y[h]), zz[2 * h + 1], den));
-            }
-        }
-        float inv = 1.f;
-        if (NORM) {
-            den += __shfl_xor(den, 16, 64);
-            den += __shfl_xor(den, 32, 64);
-            inv = __builtin_amdgcn_rcpf(den);
-        }
-#pragma unroll 2
-        for (int ct = 0; ct < NCT; ++ct) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-                c = mfma(lds<bf16x8>(sS + ((ct * NKB + kb) * 64 + l) * 8), qb[kb], c);
-            // c[r] = num[query row li][value column 16 ct + 4 g + r]
-            sts<u32x2>(tile + li * OS + 16 * ct + 4 * g,
-                       u32x2{pack_bf2(c[0] * inv, c[1] * inv), pack_bf2(c[2] * inv, c[3] * inv)});
-        }
-        // the tile back as whole rows (this wave's LDS only: its accesses stay in order), with
-        // non-temporal stores: the outputs (as many bytes as q) are not left dirty in the caches,
-        // where the next call's segment sums would find their write-back in the way of their
-        // reads (measured on MI355X for B=1 H=8 N=100000 d=128: 189 -> 174 us per call)
+    // a 16-row tile of outputs back as whole rows (this wave's LDS only: its accesses stay in
+    // order), with non-temporal stores: the outputs (as many bytes as q) are not left dirty in
+    // the caches, where the next call's segment sums would find their write-back in the way of
+    // their reads (measured on MI355X for B=1 H=8 N=100000 d=128: 189 -> 174 us per call)
+    auto put_rows = [&](int t) {
         const int r0 = tb + 16 * t;
 #pragma unroll
         for (int i = 0; i < 16 / RPI; ++i) {
@@ -1113,9 +1087,75 @@ __global__ __launch_bounds__(NT, 3) void k_gread(const uint16_t *__restrict__ q,
             if (r0 + row < te)
                 __builtin_nontemporal_store(x, reinterpret_cast<u32x4 *>(out + hoff + (size_t)(r0 + row) * D + col));
         }
+    };
+    for (int gi = w; gi < ngrp; gi += 4) {
+        ldg(qn, min(gi + 4, ngrp - 1)); // next group (a re-read of the last one at the end)
+        bf16x8 qb[RT][NKB];
+        float inv[RT];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-            qa[kb] = qn[kb];
+        for (int rt = 0; rt < RT; ++rt) {
+            float den = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const u32x4 y = PHI ? phi8(qa[rt][kb]) : qa[rt][kb];
+                qb[rt][kb] = __builtin_bit_cast(bf16x8, y);
+                if (NORM) {
+                    const float4 z0 = *reinterpret_cast<const float4 *>(sz + 32 * kb + 8 * g);
+                    const float4 z1 = *reinterpret_cast<const float4 *>(sz + 32 * kb + 8 * g + 4);
+                    const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h)
+                        den = fmaf(bf_lo(y[h]), zz[2 * h], fmaf(bf_hi(y[h]), zz[2 * h + 1], den));
+                }
+            }
+            inv[rt] = 1.f;
+            if (NORM) {
+                den += __shfl_xor(den, 16, 64);
+                den += __shfl_xor(den, 32, 64);
+                inv[rt] = __builtin_amdgcn_rcpf(den);
+            }
+        }
+        // every S fragment read from LDS feeds the group's RT tiles; the first tile goes to the
+        // wave's LDS tile at once, the others wait in registers as packed bf16
+        u32x2 later[RT - 1][NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 c[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                c[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8 a = lds<bf16x8>(sS + ((ct * NKB + kb) * 64 + l) * 8);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    c[rt] = mfma(a, qb[rt][kb], c[rt]);
+            }
+            // c[rt][r] = num[query row li of tile rt][value column 16 ct + 4 g + r]
+            sts<u32x2>(tile + li * OS + 16 * ct + 4 * g,
+                       u32x2{pack_bf2(c[0][0] * inv[0], c[0][1] * inv[0]),
+                             pack_bf2(c[0][2] * inv[0], c[0][3] * inv[0])});
+#pragma unroll
+            for (int rt = 1; rt < RT; ++rt)
+                later[rt - 1][ct] = u32x2{pack_bf2(c[rt][0] * inv[rt], c[rt][1] * inv[rt]),
+                                          pack_bf2(c[rt][2] * inv[rt], c[rt][3] * inv[rt])};
+            // (the loop is unrolled for the register array above; without this fence the
+            // scheduler hoists every S fragment read of the group and spills)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        put_rows(gi * RT);
+#pragma unroll
+        for (int rt = 1; rt < RT; ++rt) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+                sts<u32x2>(tile + li * OS + 16 * ct + 4 * g, later[rt - 1][ct]);
+            put_rows(gi * RT + rt);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                qa[rt][kb] = qn[rt][kb];
     }
 }
 
