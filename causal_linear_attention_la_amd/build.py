@@ -20,7 +20,7 @@ INCLUDE = ROOT / "include"
 LIB = PKG / "liblinattn.so"
 OBJDIR = PKG / "_build"
 
-SOURCES = ["la_api.hip", "k_mfma.hip", "k_valu.hip", "k_state.hip", "k_rf.hip"]
+SOURCES = ["la_api.hip", "k_mfma.hip", "k_mfma32.hip", "k_valu.hip", "k_state.hip", "k_rf.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -42,7 +42,8 @@ bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Plan {
-    bool mfma;  // matrix-core family
+    bool mfma;  // bf16 matrix-core family
+    bool mfma32; // float32 matrix-core family
     int chunk;  // tokens per chunk
     int L;      // tokens per segment
     int P;      // segments per head
@@ -74,12 +75,17 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
         return LA_OK;
     }
     const bool mfma_ok = dtype == LA_BF16 && d == dv && (d == 64 || d == 128);
+    const bool mfma32_ok = dtype == LA_F32 && d == dv && (d == 64 || d == 128);
     if (chunk == 0) {
         pl.mfma = mfma_ok;
+        pl.mfma32 = mfma32_ok;
         pl.chunk = mfma_ok ? 64 : 32;
     } else if (chunk == 64 && mfma_ok) {
         pl.mfma = true;
         pl.chunk = 64;
+    } else if (chunk == 32 && mfma32_ok) {
+        pl.mfma32 = true;
+        pl.chunk = 32;
     } else if (chunk == 16 || chunk == 32 || chunk == 64 || chunk == 128) {
         // the vector-ALU kernels take any chunk whose working set fits the 160 KiB of LDS a
         // workgroup can hold (chunks 64 and 128 at small head sizes)
@@ -97,7 +103,9 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
             return LA_ENOTSUP;
         pl.L = seg_len;
     } else {
-        const long target = (pl.mfma && d == 128) ? kCUs : 2 * kCUs;
+        // one causal workgroup per CU for the bf16 kernels at d = 128 and the float32 ones
+        // (their LDS holds one), two elsewhere
+        const long target = ((pl.mfma && d == 128) || pl.mfma32) ? kCUs : 2 * kCUs;
         long want = (target + (long)BH - 1) / (long)BH; // segments per head
         // matrix-core kernels: at least kMinChunks chunks per segment; a segment's fixed costs
         // (its sum written and scanned, its prefix read, the pipeline filled) outweigh its
@@ -105,7 +113,8 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
         // chunks 27.1 us per call, 8 segments of 4 chunks 24.8 us, both with cold caches). The
         // vector-ALU kernels spend far longer per chunk, so they keep every segment (one chunk
         // of B=1 H=1 N=64 d=16 float32 per segment: 23.4 us per call; one segment: 27.1 us).
-        const long most = !pl.mfma ? nchunks : nchunks / kMinChunks > 1 ? nchunks / kMinChunks : 1;
+        const bool matrix = pl.mfma || pl.mfma32;
+        const long most = !matrix ? nchunks : nchunks / kMinChunks > 1 ? nchunks / kMinChunks : 1;
         if (want > most)
             want = most;
         pl.L = (int)((nchunks + want - 1) / want) * pl.chunk;
@@ -424,6 +433,9 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
 {
     const int BH = (int)pl.BH, P = pl.P, L = pl.L;
     const long E = (long)d * dv + d;
+    // the float32 matrix-core kernels take no decay: a decayed float32 call runs the vector-ALU
+    // kernels on the same plan (their chunk and segments are valid there too)
+    const bool m32 = pl.mfma32 && !gamma;
     hipError_t e = mark(ts, 0, st);
     const float *preS = S0, *prez = z0; // P == 1: the initial state (or none) is the prefix
     long ps = (long)d * dv, pzs = d;
@@ -431,6 +443,8 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
         // sums of segments 0..P-2, then the exclusive prefix over segments in place
         e = pl.mfma ? la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
                                    P - 1, P, gamma, H, st)
+            : m32   ? la::agg_mfma32(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
+                                     P - 1, P, st)
                     : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
                                    d, dv, pl.chunk, L, P - 1, P, gamma, H, st);
         if (e == hipSuccess)
@@ -448,6 +462,8 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
     if (e == hipSuccess)
         e = pl.mfma ? la::causal_mfma(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N, L,
                                       P, gamma, H, st)
+            : m32   ? la::causal_mfma32(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N,
+                                        L, P, st)
                     : la::out_valu(bf16, true, flags, q, k, v, out, preS, prez, ps, pzs,
                                    P > 1 ? P : 1, S, z, BH, N, d, dv, pl.chunk, L, P, gamma, H, st);
     if (e == hipSuccess)
@@ -462,21 +478,25 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
     const long E = (long)d * dv + d;
     hipError_t e;
     if (P > 1) {
-        e = pl.mfma ? la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
-                                   P, P, nullptr, 1, st)
-                    : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
-                                   d, dv, pl.chunk, L, P, P, nullptr, 1, st);
+        e = pl.mfma   ? la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
+                                     P, P, nullptr, 1, st)
+            : pl.mfma32 ? la::agg_mfma32(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
+                                         L, P, P, st)
+                      : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
+                                     d, dv, pl.chunk, L, P, P, nullptr, 1, st);
         if (e == hipSuccess)
             e = la::seg_total(wsp, S, z, BH, P, d, dv, st);
     } else {
-        e = pl.mfma ? la::agg_mfma(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1, nullptr,
-                                   1, st)
-                    : la::agg_valu(bf16, flags, k, v, S, z, (long)d * dv, d, BH, N, d, dv,
-                                   pl.chunk, L, 1, 1, nullptr, 1, st);
+        e = pl.mfma   ? la::agg_mfma(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1,
+                                     nullptr, 1, st)
+            : pl.mfma32 ? la::agg_mfma32(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1, st)
+                      : la::agg_valu(bf16, flags, k, v, S, z, (long)d * dv, d, BH, N, d, dv,
+                                     pl.chunk, L, 1, 1, nullptr, 1, st);
     }
     if (e == hipSuccess && q)
-        e = pl.mfma ? la::global_read_mfma(d, flags, q, out, S, z, BH, N, L, P, st)
-                    : la::out_valu(bf16, false, flags, q, nullptr, nullptr, out, S, z, (long)d * dv,
+        e = pl.mfma   ? la::global_read_mfma(d, flags, q, out, S, z, BH, N, L, P, st)
+            : pl.mfma32 ? la::global_read_mfma32(d, flags, q, out, S, z, BH, N, st)
+                      : la::out_valu(bf16, false, flags, q, nullptr, nullptr, out, S, z, (long)d * dv,
                                    d, 1, nullptr, nullptr, BH, N, d, dv, pl.chunk, L, P, nullptr, 1,
                                    st);
     return e == hipSuccess ? LA_OK : LA_EHIP;

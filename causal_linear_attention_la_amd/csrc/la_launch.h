@@ -43,6 +43,18 @@ hipError_t causal_rf_mfma(int D, int flags, const void *q, const void *k, const 
 hipError_t global_read_mfma(int D, int flags, const void *q, void *out, const float *S,
                             const float *z, int BH, int N, int L, int P, hipStream_t st);
 
+// ---- float32 matrix-core family: d = d_v in {64, 128}, float32 inputs, chunks of 32 -------
+// The same three roles as above (no decay, no in-kernel feature map); the global read takes its
+// own split of the rows.
+hipError_t agg_mfma32(int D, int flags, const void *k, const void *v, float *dstS, float *dstz,
+                      long sstride, long zstride, int BH, int N, int L, int nseg, int P,
+                      hipStream_t st);
+hipError_t causal_mfma32(int D, int flags, const void *q, const void *k, const void *v, void *out,
+                         const float *preS, const float *prez, long pstride, long pzstride,
+                         float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st);
+hipError_t global_read_mfma32(int D, int flags, const void *q, void *out, const float *S,
+                              const float *z, int BH, int N, hipStream_t st);
+
 // ---- vector-ALU family: any d, d_v in {16, 32, 64, 128}, float32 or bf16, chunk 16/32 ----
 hipError_t agg_valu(bool bf16, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int d, int dv, int chunk, int L,

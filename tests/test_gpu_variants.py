@@ -25,7 +25,8 @@ MODE = {0: ("elu1", True), IDENT: ("identity", True), UNNORM: ("elu1", False),
         IDENT | UNNORM: ("identity", False)}
 
 # (dtype, d, chunk): matrix-core (bf16, d in {64, 128}, chunk 64) and vector-ALU kernels
-PATHS = [("bf16", 128, 0), ("bf16", 64, 0), ("f32", 32, 16), ("bf16", 16, 32), ("f32", 128, 32)]
+PATHS = [("bf16", 128, 0), ("bf16", 64, 0), ("f32", 32, 16), ("bf16", 16, 32), ("f32", 128, 32),
+         ("f32", 64, 0), ("f32", 128, 16)]
 
 
 def causal_ex(q, k, v, flags, S0=None, z0=None, chunk=0, seg_len=0):
