@@ -45,9 +45,12 @@ __device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c)
 __device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
 __device__ __forceinline__ void st4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
 
+// The hardware exponential (exp2 of x log2 e): relative error about |x| 2^-24 against expf, far
+// below the float32 tolerance of the outputs, and 5 % of the causal kernel's time
+// (B=2 H=16 N=8192 d=128 on MI355X: 245 -> 234 us).
 __device__ __forceinline__ f32x4 phi4(f32x4 x)
 {
-    return f32x4{phi_exact(x[0]), phi_exact(x[1]), phi_exact(x[2]), phi_exact(x[3])};
+    return f32x4{phi_fast(x[0]), phi_fast(x[1]), phi_fast(x[2]), phi_fast(x[3])};
 }
 
 template <int D> struct C32 {
@@ -113,19 +116,25 @@ template <int D> struct Stage {
 
 // S += Kf^T V_c for this wave's value columns: step r of key tile kt gives lane group g the key
 // 16 kt + 4 g + r (A: Kf^T rows from the feature-major array; B: the V values vb).
+// The NFT accumulators take turns (feature tile innermost), so consecutive products never wait
+// for each other's results.
 template <int D>
 __device__ __forceinline__ void update_state(f32x4 (&sacc)[C32<D>::NFT], const float *kt,
                                              const float (&vb)[2][4], int li, int g)
 {
+    constexpr int NFT = C32<D>::NFT;
 #pragma unroll
-    for (int ft = 0; ft < C32<D>::NFT; ++ft)
+    for (int t = 0; t < 2; ++t) {
+        f32x4 a[NFT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const f32x4 a = ld4(kt + (16 * ft + li) * C32<D>::TS + 16 * t + 4 * g);
+        for (int ft = 0; ft < NFT; ++ft)
+            a[ft] = ld4(kt + (16 * ft + li) * C32<D>::TS + 16 * t + 4 * g);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sacc[ft] = mma(a[r], vb[t][r], sacc[ft]);
-        }
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+                sacc[ft] = mma(a[ft][r], vb[t][r], sacc[ft]);
+    }
 }
 
 // column sum of the chunk's features into z (feature f = thread index, keys in order)
@@ -359,12 +368,11 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_causal32(
             d1 += __shfl_xor(d1, 16, 64);
             d0 += __shfl_xor(d0, 32, 64);
             d1 += __shfl_xor(d1, 32, 64);
-            d0 += sdz[li];
-            d1 += sdz[16 + li];
+            const float i0 = 1.f / (d0 + sdz[li]), i1 = 1.f / (d1 + sdz[16 + li]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                inv[0][r] = 1.f / __shfl(d0, 4 * g + r, 64);
-                inv[1][r] = 1.f / __shfl(d1, 4 * g + r, 64);
+                inv[0][r] = __shfl(i0, 4 * g + r, 64);
+                inv[1][r] = __shfl(i1, 4 * g + r, 64);
             }
         }
         const int t0 = tb + c * CH, n = te - t0;

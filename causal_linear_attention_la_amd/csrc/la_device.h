@@ -38,8 +38,9 @@ __device__ __forceinline__ uint16_t to_bf(float x)
 
 // ---- feature map ------------------------------------------------------------------------
 // phi(x) = ELU(x) + 1 with alpha = 1: x + 1 for x > 0, exp(x) otherwise (strictly positive).
-// The fast form feeds bf16 matrix-core operands (its result is rounded to bf16 right after);
-// the accurate form is used where the arithmetic stays in float32.
+// The fast form (the hardware exp2 of x log2 e, relative error about |x| 2^-24) feeds the
+// matrix-core kernels, bf16 and float32; the accurate form serves the vector-ALU and decode
+// kernels.
 __device__ __forceinline__ float phi_fast(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 __device__ __forceinline__ float phi_exact(float x) { return x > 0.f ? x + 1.f : expf(x); }
 // The feature of one element: phi_exact(x), or x itself when q and k are already features.
