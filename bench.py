@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
 BF16_PEAK = 2.5e15         # flop/s, dense bf16 MFMA
+FP32_MFMA_PEAK = 157.3e12  # flop/s, dense float32 MFMA
 METRIC = "causal prefill tokens/s (B·H·N/s) at d=128 + %MFMA peak; decode step GB/s"
 
 
@@ -49,6 +50,15 @@ def mfma_issued_prefill(B, H, N, P, d=128):
     chunks = B * H * math.ceil(N / 64)
     per_chunk = 40 + 48 + 128 + 128 + 128 * (P - 1) / P
     return chunks * per_chunk * 16384
+
+
+def mfma32_issued_prefill(B, H, N, P, d=128):
+    """Matrix-core flops the float32 kernels issue (16x16x4 = 2048 flops each) for d = d_v,
+    chunk 32: per token 4 d^2 (state read and state update) plus the three 16x16 score tiles and
+    the twelve score-value products of a chunk per 16 value columns (48 (d + d_v) per token) in
+    the output kernel, and 2 d^2 per token in the segment sums for segments 0..P-2."""
+    th = B * H * N
+    return th * (4 * d * d + 96 * d + 2 * d * d * (P - 1) / P)
 
 
 def time_calls(fn, steps, warmup):
@@ -298,6 +308,35 @@ def bench_variants(args):
 
     ms, _ = time_calls(step, args.steps, args.warmup)
     return w, ms
+
+
+def bench_f32(args):
+    """The prefill workload's shape in float32 (its inputs drawn in float32), through the
+    workspace entry point: the float32 matrix-core kernels."""
+    import torch
+    import causal_linear_attention_la_amd as la
+    import datagen
+
+    w = datagen.WORKLOADS[3]
+    dev = torch.device("cuda:0")
+    sets = []
+    for r in range(2):
+        q, k, v = datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed + 100 * r, w.scale, "f32")
+        sets.append((q, k, v, torch.empty_like(q), torch.empty(w.B, w.H, w.d, w.dv, device=dev),
+                     torch.empty(w.B, w.H, w.d, device=dev)))
+    need = la.la_workspace_bytes(0, w.B, w.H, w.N, w.d, w.dv, 0, 0, la.LA_F32)
+    ws = torch.empty(max(need, 16) // 4, dtype=torch.float32, device=dev)
+
+    def step(i):
+        q, k, v, out, S, z = sets[i % len(sets)]
+        la.la_causal_fwd_ws(q, k, v, out, ws if need else None, None, None, S, z)
+
+    steps = max(20, args.steps // 4)
+    ms, _ = time_calls(step, steps, max(5, args.warmup // 4))
+    q, k, v, out, S, z = sets[0]
+    kern_ms = list(la.la_causal_fwd_profiled(q, k, v, out, None, None, S, z, reps=steps))
+    P = la.la_segments(0, w.B, w.H, w.N, w.d, w.dv, 0, 0, la.LA_F32)
+    return w, ms, kern_ms, P
 
 
 def bench_retention(args):
@@ -583,7 +622,7 @@ def main():
     ap.add_argument("--decode-steps", dest="decode_steps", type=int, default=1000)
     ap.add_argument("--serve-steps", dest="serve_steps", type=int, default=256,
                     help="decode steps after the prefill in the serving leg")
-    ap.add_argument("--only", choices=["prefill", "decode", "global", "favor", "variants",
+    ap.add_argument("--only", choices=["prefill", "decode", "global", "favor", "variants", "f32",
                                        "retention", "serving", "copycal", "small"],
                     default=None,
                     help="run one form only (for profiling); no JSON line")
@@ -617,11 +656,14 @@ def main():
             copy_calibration()
         fn = {"prefill": bench_prefill, "decode": bench_decode, "global": bench_global,
               "favor": bench_favor, "variants": bench_variants, "retention": bench_retention,
+              "f32": bench_f32,
               "serving": bench_serving}[args.only]
         r = fn(args)
         extra = ""
         if args.only == "prefill":
             extra = " (kernels: " + ", ".join(f"{t * 1e3:.1f}" for t in r[7]) + " us)"
+        if args.only == "f32":
+            extra = " (kernels: " + ", ".join(f"{t * 1e3:.1f}" for t in r[2]) + " us)"
         if args.only == "favor":
             extra = f" (two-pass {r[6] * 1e3:.1f} us: features {r[3] * 1e3:.1f} us per tensor; " + \
                 "attention kernels " + ", ".join(f"{t * 1e3:.1f}" for t in r[5]) + " us)"
@@ -646,6 +688,9 @@ def main():
     print(f"identity+unnormalised causal: {ms_v * 1e3:.1f} us/call", file=sys.stderr, flush=True)
     wr, ms_r = bench_retention(args)
     print(f"retention causal: {ms_r * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+    w32, ms_32, kern_32, P_32 = bench_f32(args)
+    print(f"float32 causal: {ms_32 * 1e3:.1f} us/call; kernels "
+          + ", ".join(f"{t * 1e3:.1f}" for t in kern_32) + " us", file=sys.stderr, flush=True)
     ws_, K_s, ms_s, ms_sp = bench_serving(args)
     print(f"serving: {ms_s * 1e3:.1f} us per prefill + {K_s} decode steps", file=sys.stderr,
           flush=True)
@@ -727,6 +772,16 @@ def main():
                                            "causal": kern_f[2] * 1e3}},
         "identity_unnormalized": {"workload": wv.name, "us_per_call": ms_v * 1e3,
                                   "token_heads_per_s": wv.B * wv.H * wv.N / (ms_v * 1e-3)},
+        "float32": {"workload": w32.name.replace("_bf16", "_f32"), "entry_point": "la_causal_fwd_ws",
+                    "chunk": 32, "segments_per_head": P_32, "us_per_call": ms_32 * 1e3,
+                    "token_heads_per_s": w32.B * w32.H * w32.N / (ms_32 * 1e-3),
+                    "kernels_us": {"segment_sums": kern_32[0] * 1e3, "segment_scan": kern_32[1] * 1e3,
+                                   "causal": kern_32[2] * 1e3},
+                    "mfma": {"bound": "mfma (float32)", "peak_tflops": FP32_MFMA_PEAK / 1e12,
+                             "issued_frac": mfma32_issued_prefill(w32.B, w32.H, w32.N, P_32, w32.d)
+                             / (ms_32 * 1e-3) / FP32_MFMA_PEAK,
+                             "algorithmic_frac": algo_prefill(w32.B, w32.H, w32.N, w32.d, w32.dv, 4)[1]
+                             / (ms_32 * 1e-3) / FP32_MFMA_PEAK}},
         "retention": {"workload": retention_name(), "us_per_call": ms_r * 1e3,
                       "token_heads_per_s": wr.B * wr.H * wr.N / (ms_r * 1e-3)},
         "serving": {"workload": f"prefill {ws_.name} then {K_s} decode steps (HIP graph)",
