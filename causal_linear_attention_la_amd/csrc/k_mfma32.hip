@@ -9,7 +9,8 @@
 //   num = Qf S + mask(Qf Kf^T) V_c,  den = Qf z + rowsum(mask(Qf Kf^T)),  out = num / den,
 //   then S += Kf^T V_c, z += colsum(Kf)
 // (mask: key <= query). The global read is out = Qf S / Qf z ("Linear Attention Math", section
-// "The associativity trick, written out").
+// "The associativity trick, written out"). The segment sums and the causal kernel also take a
+// per-head decay (below, at decayed_values).
 //
 // Operand layout. A 16x16x4 product takes A[l % 16][k = l / 16] and B[k = l / 16][l % 16] from
 // lane l and leaves D[4 (l / 16) + r][l % 16] (r < 4) in lane l (checked on gfx950). A product
@@ -149,15 +150,49 @@ template <int D> __device__ __forceinline__ float key_col_sum(const float *kt, i
     return s;
 }
 
+// With a decay gamma (the retention recurrence S_t = gamma S_{t-1} + Kf_t V_t^T of "Linear
+// Attention Math", section "The kernel cousins: SSMs and RetNet"), a chunk of n valid keys updates
+// S = gamma^n S + sum_j gamma^(n - 1 - j) Kf_j V_j^T (z alike): the V values of the product are
+// weighted per key. Keys past the end weigh 0 (their staged rows are zero, and gamma^(n - 1 - j)
+// would overflow there for gamma = 0).
+__device__ __forceinline__ void decayed_values(float (&vbs)[2][4], const float (&vb)[2][4], float lg,
+                                               int n, int g)
+{
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int key = 16 * t + 4 * g + r;
+            vbs[t][r] = key < n ? vb[t][r] * decay_pow(lg, n - 1 - key) : 0.f;
+        }
+}
+template <int D>
+__device__ __forceinline__ float key_col_sum_decayed(const float *kt, int f, float lg, int n)
+{
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < CH / 4; ++j) {
+        const f32x4 x = ld4(kt + f * C32<D>::TS + 4 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int key = 4 * j + i;
+            s = fmaf(x[i], key < n ? decay_pow(lg, n - 1 - key) : 0.f, s);
+        }
+    }
+    return s;
+}
+
 // ---------------------------------------------------------------------------------------------
-// Segment sums dS = Kf^T V, dz = colsum(Kf) over segments 0 .. nseg - 1 of each head.
-template <int D, bool PHI>
+// Segment sums dS = Kf^T V, dz = colsum(Kf) over segments 0 .. nseg - 1 of each head (with a
+// decay: decayed to the segment's last token).
+template <int D, bool PHI, bool DECAY>
 __global__ __launch_bounds__(C32<D>::THREADS) void k_agg32(const float *__restrict__ k,
                                                           const float *__restrict__ v,
                                                           float *__restrict__ dstS,
                                                           float *__restrict__ dstz, long sstride,
                                                           long zstride, int N, int L, int nseg,
-                                                          int P)
+                                                          int P, const float *__restrict__ gamma,
+                                                          int H)
 {
     using G = C32<D>;
     __shared__ __attribute__((aligned(16))) float sKT[2][D * G::TS];
@@ -168,6 +203,7 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_agg32(const float *__restri
     const float *kh = k + (size_t)bh * N * D, *vh = v + (size_t)bh * N * D;
     const int c0 = 16 * w;
     const Stage<D> stg(tid);
+    const float lg = DECAY ? decay_log2(gamma, bh, H) : 0.f;
 
     f32x4 sacc[G::NFT];
 #pragma unroll
@@ -198,9 +234,22 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_agg32(const float *__restri
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 vb[t][r] = sV[b][(16 * t + 4 * g + r) * G::RS + c0 + li];
-        update_state<D>(sacc, sKT[b], vb, li, g);
-        if (tid < D)
-            zr += key_col_sum<D>(sKT[b], tid);
+        if (DECAY) {
+            const int n = min(CH, te - (tb + c * CH));
+            const float gn = decay_pow(lg, n);
+            float vbs[2][4];
+            decayed_values(vbs, vb, lg, n, g);
+#pragma unroll
+            for (int ft = 0; ft < G::NFT; ++ft)
+                sacc[ft] *= gn;
+            update_state<D>(sacc, sKT[b], vbs, li, g);
+            if (tid < D)
+                zr = fmaf(gn, zr, key_col_sum_decayed<D>(sKT[b], tid, lg, n));
+        } else {
+            update_state<D>(sacc, sKT[b], vb, li, g);
+            if (tid < D)
+                zr += key_col_sum<D>(sKT[b], tid);
+        }
         if (c + 1 < nch)
             put(b ^ 1, c + 1);
         load(c + 2);
@@ -219,12 +268,12 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_agg32(const float *__restri
 // ---------------------------------------------------------------------------------------------
 // Causal outputs of one segment of one head from its prefix state (or zero), and the final
 // state from the last segment. F: F_IDENTITY (q, k are the features), F_UNNORM (no division).
-template <int D, int F>
+template <int D, int F, bool DECAY>
 __global__ __launch_bounds__(C32<D>::THREADS) void k_causal32(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     float *__restrict__ out, const float *__restrict__ preS, const float *__restrict__ prez,
     long pstride, long pzstride, float *__restrict__ Sout, float *__restrict__ zout, int N, int L,
-    int P)
+    int P, const float *__restrict__ gamma, int H)
 {
     using G = C32<D>;
     constexpr bool PHI = !(F & F_IDENTITY), NORM = !(F & F_UNNORM);
@@ -245,6 +294,7 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_causal32(
     float *oh = out + hoff;
     const int c0 = 16 * w;
     const Stage<D> stg(tid);
+    const float lg = DECAY ? decay_log2(gamma, bh, H) : 0.f;
 
     // state before the segment: lane (g, li) of tile ft holds S[16 ft + 4 g + r][c0 + li]
     f32x4 sacc[NFT];
@@ -338,12 +388,30 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_causal32(
             for (int ww = 1; ww < 4; ++ww)
                 at[t] += ld4(&sPart[ww][t][4 * l]);
         }
+        if (DECAY) {
+            // key 16 kt + 4 g + r reaches query 16 qt + li with weight gamma^(query - key), keys
+            // after the query none; the carried state reaches row i scaled by gamma^(i + 1)
+            constexpr int KTI[3] = {0, 0, 1}, QTI[3] = {0, 1, 1};
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (4 * g + r > li) {
-                at[0][r] = 0.f;
-                at[2][r] = 0.f;
-            }
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int dq = 16 * QTI[t] + li - (16 * KTI[t] + 4 * g + r);
+                    at[t][r] = dq >= 0 ? at[t][r] * decay_pow(lg, dq) : 0.f;
+                }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    num[t][r] *= decay_pow(lg, 16 * t + 4 * g + r + 1);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r > li) {
+                    at[0][r] = 0.f;
+                    at[2][r] = 0.f;
+                }
+        }
         float vb[2][4];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -368,7 +436,9 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_causal32(
             d1 += __shfl_xor(d1, 16, 64);
             d0 += __shfl_xor(d0, 32, 64);
             d1 += __shfl_xor(d1, 32, 64);
-            const float i0 = 1.f / (d0 + sdz[li]), i1 = 1.f / (d1 + sdz[16 + li]);
+            const float z0 = DECAY ? sdz[li] * decay_pow(lg, li + 1) : sdz[li];
+            const float z1 = DECAY ? sdz[16 + li] * decay_pow(lg, 17 + li) : sdz[16 + li];
+            const float i0 = 1.f / (d0 + z0), i1 = 1.f / (d1 + z1);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 inv[0][r] = __shfl(i0, 4 * g + r, 64);
@@ -384,9 +454,22 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_causal32(
                 if (row < n)
                     oh[(size_t)(t0 + row) * D + c0 + li] = NORM ? num[t][r] * inv[t][r] : num[t][r];
             }
-        update_state<D>(sacc, sKT[b], vb, li, g);
-        if (tid < D)
-            sz[tid] += key_col_sum<D>(sKT[b], tid);
+        if (DECAY) {
+            const int nk = min(CH, n);
+            const float gn = decay_pow(lg, nk);
+            float vbs[2][4];
+            decayed_values(vbs, vb, lg, nk, g);
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+                sacc[ft] *= gn;
+            update_state<D>(sacc, sKT[b], vbs, li, g);
+            if (tid < D)
+                sz[tid] = fmaf(gn, sz[tid], key_col_sum_decayed<D>(sKT[b], tid, lg, nk));
+        } else {
+            update_state<D>(sacc, sKT[b], vb, li, g);
+            if (tid < D)
+                sz[tid] += key_col_sum<D>(sKT[b], tid);
+        }
         if (c + 1 < nch)
             put(b ^ 1, c + 1);
         load(c + 2);
@@ -494,18 +577,42 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_gread32(const float *__rest
     }
 }
 
+template <int D, int F>
+void launch_causal32_f(dim3 grid, hipStream_t st, const float *q, const float *k, const float *v,
+                       float *o, const float *preS, const float *prez, long ps, long pzs,
+                       float *Sout, float *zout, int N, int L, int P, const float *gamma, int H)
+{
+    const dim3 block(C32<D>::THREADS);
+    if (gamma)
+        hipLaunchKernelGGL((k_causal32<D, F, true>), grid, block, 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
+    else
+        hipLaunchKernelGGL((k_causal32<D, F, false>), grid, block, 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
+}
+
 template <int D>
 void launch_causal32(int flags, dim3 grid, hipStream_t st, const float *q, const float *k,
                      const float *v, float *o, const float *preS, const float *prez, long ps,
-                     long pzs, float *Sout, float *zout, int N, int L, int P)
+                     long pzs, float *Sout, float *zout, int N, int L, int P, const float *gamma,
+                     int H)
+{
+    switch (flags & (F_IDENTITY | F_UNNORM)) {
+    case 0: launch_causal32_f<D, 0>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
+    case F_IDENTITY: launch_causal32_f<D, F_IDENTITY>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
+    case F_UNNORM: launch_causal32_f<D, F_UNNORM>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
+    default: launch_causal32_f<D, F_IDENTITY | F_UNNORM>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
+    }
+}
+
+template <int D, bool PHI>
+void launch_agg32_f(dim3 grid, hipStream_t st, const float *k, const float *v, float *dstS,
+                    float *dstz, long sstride, long zstride, int N, int L, int nseg, int P,
+                    const float *gamma, int H)
 {
     const dim3 block(C32<D>::THREADS);
-    switch (flags & (F_IDENTITY | F_UNNORM)) {
-    case 0: hipLaunchKernelGGL((k_causal32<D, 0>), grid, block, 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
-    case F_IDENTITY: hipLaunchKernelGGL((k_causal32<D, F_IDENTITY>), grid, block, 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
-    case F_UNNORM: hipLaunchKernelGGL((k_causal32<D, F_UNNORM>), grid, block, 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
-    default: hipLaunchKernelGGL((k_causal32<D, F_IDENTITY | F_UNNORM>), grid, block, 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P); break;
-    }
+    if (gamma)
+        hipLaunchKernelGGL((k_agg32<D, PHI, true>), grid, block, 0, st, k, v, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
+    else
+        hipLaunchKernelGGL((k_agg32<D, PHI, false>), grid, block, 0, st, k, v, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
 }
 
 template <int D>
@@ -525,7 +632,7 @@ void launch_gread32(int flags, dim3 grid, hipStream_t st, const float *q, float 
 
 hipError_t agg_mfma32(int D, int flags, const void *k, const void *v, float *dstS, float *dstz,
                       long sstride, long zstride, int BH, int N, int L, int nseg, int P,
-                      hipStream_t st)
+                      const float *gamma, int H, hipStream_t st)
 {
     const dim3 grid((unsigned)(BH * nseg));
     const auto *kk = static_cast<const float *>(k);
@@ -533,21 +640,22 @@ hipError_t agg_mfma32(int D, int flags, const void *k, const void *v, float *dst
     const bool phi = !(flags & F_IDENTITY);
     if (D == 128) {
         if (phi)
-            hipLaunchKernelGGL((k_agg32<128, true>), grid, dim3(C32<128>::THREADS), 0, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
+            launch_agg32_f<128, true>(grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
         else
-            hipLaunchKernelGGL((k_agg32<128, false>), grid, dim3(C32<128>::THREADS), 0, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
+            launch_agg32_f<128, false>(grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
     } else {
         if (phi)
-            hipLaunchKernelGGL((k_agg32<64, true>), grid, dim3(C32<64>::THREADS), 0, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
+            launch_agg32_f<64, true>(grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
         else
-            hipLaunchKernelGGL((k_agg32<64, false>), grid, dim3(C32<64>::THREADS), 0, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P);
+            launch_agg32_f<64, false>(grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
     }
     return hipGetLastError();
 }
 
 hipError_t causal_mfma32(int D, int flags, const void *q, const void *k, const void *v, void *out,
                          const float *preS, const float *prez, long pstride, long pzstride,
-                         float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st)
+                         float *Sout, float *zout, int BH, int N, int L, int P, const float *gamma,
+                         int H, hipStream_t st)
 {
     const dim3 grid((unsigned)(BH * P));
     const auto *qq = static_cast<const float *>(q);
@@ -555,9 +663,9 @@ hipError_t causal_mfma32(int D, int flags, const void *q, const void *k, const v
     const auto *vv = static_cast<const float *>(v);
     auto *oo = static_cast<float *>(out);
     if (D == 128)
-        launch_causal32<128>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout, zout, N, L, P);
+        launch_causal32<128>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout, zout, N, L, P, gamma, H);
     else
-        launch_causal32<64>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout, zout, N, L, P);
+        launch_causal32<64>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout, zout, N, L, P, gamma, H);
     return hipGetLastError();
 }
 

@@ -433,9 +433,6 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
 {
     const int BH = (int)pl.BH, P = pl.P, L = pl.L;
     const long E = (long)d * dv + d;
-    // the float32 matrix-core kernels take no decay: a decayed float32 call runs the vector-ALU
-    // kernels on the same plan (their chunk and segments are valid there too)
-    const bool m32 = pl.mfma32 && !gamma;
     hipError_t e = mark(ts, 0, st);
     const float *preS = S0, *prez = z0; // P == 1: the initial state (or none) is the prefix
     long ps = (long)d * dv, pzs = d;
@@ -443,8 +440,8 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
         // sums of segments 0..P-2, then the exclusive prefix over segments in place
         e = pl.mfma ? la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
                                    P - 1, P, gamma, H, st)
-            : m32   ? la::agg_mfma32(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
-                                     P - 1, P, st)
+            : pl.mfma32 ? la::agg_mfma32(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
+                                     P - 1, P, gamma, H, st)
                     : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
                                    d, dv, pl.chunk, L, P - 1, P, gamma, H, st);
         if (e == hipSuccess)
@@ -462,8 +459,8 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
     if (e == hipSuccess)
         e = pl.mfma ? la::causal_mfma(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N, L,
                                       P, gamma, H, st)
-            : m32   ? la::causal_mfma32(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N,
-                                        L, P, st)
+            : pl.mfma32 ? la::causal_mfma32(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N,
+                                        L, P, gamma, H, st)
                     : la::out_valu(bf16, true, flags, q, k, v, out, preS, prez, ps, pzs,
                                    P > 1 ? P : 1, S, z, BH, N, d, dv, pl.chunk, L, P, gamma, H, st);
     if (e == hipSuccess)
@@ -481,7 +478,7 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
         e = pl.mfma   ? la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
                                      P, P, nullptr, 1, st)
             : pl.mfma32 ? la::agg_mfma32(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
-                                         L, P, P, st)
+                                         L, P, P, nullptr, 1, st)
                       : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
                                      d, dv, pl.chunk, L, P, P, nullptr, 1, st);
         if (e == hipSuccess)
@@ -489,7 +486,8 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
     } else {
         e = pl.mfma   ? la::agg_mfma(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1,
                                      nullptr, 1, st)
-            : pl.mfma32 ? la::agg_mfma32(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1, st)
+            : pl.mfma32 ? la::agg_mfma32(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1,
+                                         nullptr, 1, st)
                       : la::agg_valu(bf16, flags, k, v, S, z, (long)d * dv, d, BH, N, d, dv,
                                      pl.chunk, L, 1, 1, nullptr, 1, st);
     }

@@ -44,14 +44,15 @@ hipError_t global_read_mfma(int D, int flags, const void *q, void *out, const fl
                             const float *z, int BH, int N, int L, int P, hipStream_t st);
 
 // ---- float32 matrix-core family: d = d_v in {64, 128}, float32 inputs, chunks of 32 -------
-// The same three roles as above (no decay, no in-kernel feature map); the global read takes its
-// own split of the rows.
+// The same three roles as above, with the optional decay (no in-kernel feature map); the global
+// read takes its own split of the rows.
 hipError_t agg_mfma32(int D, int flags, const void *k, const void *v, float *dstS, float *dstz,
                       long sstride, long zstride, int BH, int N, int L, int nseg, int P,
-                      hipStream_t st);
+                      const float *gamma, int H, hipStream_t st);
 hipError_t causal_mfma32(int D, int flags, const void *q, const void *k, const void *v, void *out,
                          const float *preS, const float *prez, long pstride, long pzstride,
-                         float *Sout, float *zout, int BH, int N, int L, int P, hipStream_t st);
+                         float *Sout, float *zout, int BH, int N, int L, int P, const float *gamma,
+                         int H, hipStream_t st);
 hipError_t global_read_mfma32(int D, int flags, const void *q, void *out, const float *S,
                               const float *z, int BH, int N, hipStream_t st);
 

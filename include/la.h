@@ -100,8 +100,7 @@ enum { LA_PHI_IDENTITY = 1, LA_UNNORMALIZED = 2 };
  *          be processed in pieces and handed to la_decode_step. One NULL and one not: LA_EINVAL.
  *   chunk  tokens per intra-chunk tile: 0 lets the library choose; 64 selects the
  *          matrix-core kernel for bf16 with d = d_v in {64, 128}, 32 the float32 matrix-core
- *          kernel for float32 with d = d_v in {64, 128} (with a decay, the vector-ALU kernel at
- *          chunk 32); otherwise 16, 32, 64 or 128
+ *          kernel for float32 with d = d_v in {64, 128}; otherwise 16, 32, 64 or 128
  *          select the vector-ALU kernel (any supported d, d_v, either dtype) when its working
  *          set, 4 (d d_v + d + chunk (2 d + d_v) + chunk^2 + chunk) bytes, fits the 160 KiB of
  *          LDS of a workgroup (chunk 128 at d, d_v <= 32 or so). Other values, or a working set

@@ -50,7 +50,7 @@ def _feat(rows, d, dtype):
 
 
 @pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 0), ("bf16", 64, 0), ("f32", 16, 16),
-                                           ("bf16", 32, 32)])
+                                           ("bf16", 32, 32), ("f32", 128, 0)])
 def test_decay_worked_example(golden, dtype, d, chunk):
     """The hand-derived gamma = 0.5 example: causal outputs, S3, z3, and the three reads of
     S3 as decode steps, in the retention form (identity map, no division)."""
@@ -91,7 +91,8 @@ GAMMAS = [0.9, 0.5, 1.0, 0.0, 0.99]
 @pytest.mark.parametrize("flags", [0, UNNORM, IDENT | UNNORM])
 @pytest.mark.parametrize("dtype,d,chunk,seg", [("bf16", 128, 0, 0), ("bf16", 128, 0, 128),
                                                ("bf16", 64, 0, 192), ("f32", 32, 16, 0),
-                                               ("bf16", 16, 32, 96), ("f32", 64, 32, 64)])
+                                               ("bf16", 16, 32, 96), ("f32", 64, 32, 64),
+                                               ("f32", 128, 0, 0), ("f32", 128, 0, 96)])
 def test_decay_causal(flags, dtype, d, chunk, seg):
     """Per-head gamma including 0 and 1, a carried initial state, several segments (the
     decayed scan) and a ragged tail."""
@@ -121,7 +122,7 @@ def test_decay_causal(flags, dtype, d, chunk, seg):
 
 
 @pytest.mark.parametrize("flags", [0, IDENT | UNNORM])
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 32), ("bf16", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 32), ("bf16", 64), ("f32", 128)])
 def test_decay_decode_chain(flags, dtype, d):
     """Prefill of N tokens, then decode steps, equals the causal form over all tokens."""
     B, H, N, steps = 2, len(GAMMAS), 300, 3
@@ -181,7 +182,8 @@ def test_retention_workload_full():
     check("S", S, So, TOL["bf16"])
 
 
-@pytest.mark.parametrize("dtype,d,chunk,seg", [("bf16", 128, 0, 64), ("f32", 32, 16, 0)])
+@pytest.mark.parametrize("dtype,d,chunk,seg", [("bf16", 128, 0, 64), ("f32", 32, 16, 0),
+                                               ("f32", 128, 0, 64)])
 def test_decay_out_of_range_is_nan(dtype, d, chunk, seg):
     """A negative or NaN gamma (outside the [0, 1] contract) makes every output and the state
     of its head NaN, in the prefill and in the decode step alike; the other heads are
