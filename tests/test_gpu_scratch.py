@@ -145,7 +145,8 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("dtype,d,seg,decay", [("bf16", 128, 0, False), ("bf16", 64, 128, False),
-                                               ("f32", 32, 64, False), ("bf16", 128, 256, True)])
+                                               ("f32", 32, 64, False), ("bf16", 128, 256, True),
+                                               ("f32", 128, 0, False), ("f32", 64, 96, True)])
 def test_workspace_causal(dtype, d, seg, decay):
     """la_causal_fwd_ws with the segment states in a caller-owned buffer that starts as NaN
     (no part of it needs an initial value): the oracle's results, and bit-identical to the
