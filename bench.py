@@ -810,7 +810,7 @@ def main():
                                  "frac": byts_n / (kern_n[2] * 1e-3) / HBM_PEAK,
                                  "note": "kernel timed hot (inputs fit in the last-level cache)"}
         else:
-            entry["bound"] = "launch latency (64 token-heads, three launches)"
+            entry["bound"] = "launch latency (64 token-heads, one launch)"
         workloads[wn.name] = entry
     workloads[wd.name] = rec.pop("decode")
     workloads[wg.name] = rec.pop("global")

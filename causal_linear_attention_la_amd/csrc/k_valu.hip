@@ -23,6 +23,29 @@ namespace {
 
 constexpr int NT = 256;
 
+// The sum s + term(0) + ... + term(n - 1) in increasing order, n a multiple of 16 (every head
+// size and chunk is): blocks of 16 terms are unrolled so that their LDS reads leave together
+// instead of one dependent read per step (measured on MI355X: B=1 H=1 N=64 d=16 float32 as two
+// segments 22.8 -> 18.8 us per call, B=1 H=8 N=4096 d=32 float32 92 -> 68 us, B=1 H=4 N=1024
+// d=128 bf16 at chunk 16 206 -> 126 us). Sums over a chunk's keys run over the whole chunk: its rows past the end
+// and the scores above the diagonal are stored as zeros, so the extra terms add exact zeros.
+template <typename Term> __device__ __forceinline__ float sum16(int n, Term term, float s = 0.f)
+{
+    for (int j0 = 0; j0 < n; j0 += 16) {
+#pragma unroll
+        for (int j = j0; j < j0 + 16; ++j)
+            s += term(j);
+    }
+    return s;
+}
+
+// decay weight of key j in a chunk of n valid keys: gamma^(n - 1 - j), and 0 past the end
+// (where the power would overflow for gamma = 0)
+__device__ __forceinline__ float key_weight(float lg, int n, int j)
+{
+    return j < n ? decay_pow(lg, n - 1 - j) : 0.f;
+}
+
 // dynamic LDS carve-up (float32): S [d*dv] | z [d] | Qf [CH*d] | Kf [CH*d] | V [CH*dv] |
 // A [CH*CH] | den [CH]
 struct Lay {
@@ -79,30 +102,20 @@ __global__ __launch_bounds__(NT) void k_agg_valu(const T *__restrict__ k, const 
             const float fc = decay_pow(lg, nvalid);
             for (int e = tid; e < d * dv; e += NT) {
                 const int f = e / dv, c = e % dv;
-                float s = 0.f;
-                for (int j = 0; j < nvalid; ++j)
-                    s += decay_pow(lg, nvalid - 1 - j) * sK[j * d + f] * sV[j * dv + c];
+                const float s = sum16(ch, [&](int j) { return key_weight(lg, nvalid, j) * sK[j * d + f] * sV[j * dv + c]; });
                 sS[e] = fc * sS[e] + s;
             }
             for (int f = tid; f < d; f += NT) {
-                float s = 0.f;
-                for (int j = 0; j < nvalid; ++j)
-                    s += decay_pow(lg, nvalid - 1 - j) * sK[j * d + f];
+                const float s = sum16(ch, [&](int j) { return key_weight(lg, nvalid, j) * sK[j * d + f]; });
                 sz[f] = fc * sz[f] + s;
             }
         } else {
             for (int e = tid; e < d * dv; e += NT) {
                 const int f = e / dv, c = e % dv;
-                float s = 0.f;
-                for (int j = 0; j < ch; ++j)
-                    s += sK[j * d + f] * sV[j * dv + c];
-                sS[e] += s;
+                sS[e] += sum16(ch, [&](int j) { return sK[j * d + f] * sV[j * dv + c]; });
             }
             for (int f = tid; f < d; f += NT) {
-                float s = 0.f;
-                for (int j = 0; j < ch; ++j)
-                    s += sK[j * d + f];
-                sz[f] += s;
+                sz[f] += sum16(ch, [&](int j) { return sK[j * d + f]; });
             }
         }
     }
@@ -166,22 +179,16 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
         if (CAUSAL)
             for (int e = tid; e < ch * ch; e += NT) {
                 const int i = e / ch, j = e % ch;
-                float s = 0.f;
-                if (j <= i)
-                    for (int f = 0; f < d; ++f)
-                        s += sQ[i * d + f] * sK[j * d + f];
+                const float s = j <= i ? sum16(d, [&](int f) { return sQ[i * d + f] * sK[j * d + f]; }) : 0.f;
                 sA[e] = gamma && j <= i ? s * decay_pow(lg, i - j) : s;
             }
         __syncthreads();
         for (int i = tid; i < ch; i += NT) {
-            float s = 0.f;
-            for (int f = 0; f < d; ++f)
-                s += sQ[i * d + f] * sz[f];
+            float s = sum16(d, [&](int f) { return sQ[i * d + f] * sz[f]; });
             if (gamma)
                 s *= decay_pow(lg, i + 1);
             if (CAUSAL)
-                for (int j = 0; j <= i; ++j)
-                    s += sA[i * ch + j];
+                s = sum16(ch, [&](int j) { return sA[i * ch + j]; }, s);
             sden[i] = s;
         }
         __syncthreads();
@@ -189,14 +196,11 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
             const int i = e / dv, c = e % dv;
             if (i >= nvalid)
                 continue;
-            float s = 0.f;
-            for (int f = 0; f < d; ++f)
-                s += sQ[i * d + f] * sS[f * dv + c];
+            float s = sum16(d, [&](int f) { return sQ[i * d + f] * sS[f * dv + c]; });
             if (gamma)
                 s *= decay_pow(lg, i + 1);
             if (CAUSAL)
-                for (int j = 0; j <= i; ++j)
-                    s += sA[i * ch + j] * sV[j * dv + c];
+                s = sum16(ch, [&](int j) { return sA[i * ch + j] * sV[j * dv + c]; }, s);
             Elem<T>::st(ob, (size_t)(t0 + i) * dv + c, norm ? s / sden[i] : s);
         }
         if (CAUSAL && gamma) {
@@ -204,31 +208,21 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
             const float fc = decay_pow(lg, nvalid);
             for (int e = tid; e < d * dv; e += NT) {
                 const int f = e / dv, c = e % dv;
-                float s = 0.f;
-                for (int j = 0; j < nvalid; ++j)
-                    s += decay_pow(lg, nvalid - 1 - j) * sK[j * d + f] * sV[j * dv + c];
+                const float s = sum16(ch, [&](int j) { return key_weight(lg, nvalid, j) * sK[j * d + f] * sV[j * dv + c]; });
                 sS[e] = fc * sS[e] + s;
             }
             for (int f = tid; f < d; f += NT) {
-                float s = 0.f;
-                for (int j = 0; j < nvalid; ++j)
-                    s += decay_pow(lg, nvalid - 1 - j) * sK[j * d + f];
+                const float s = sum16(ch, [&](int j) { return key_weight(lg, nvalid, j) * sK[j * d + f]; });
                 sz[f] = fc * sz[f] + s;
             }
         } else if (CAUSAL) {
             __syncthreads();
             for (int e = tid; e < d * dv; e += NT) {
                 const int f = e / dv, c = e % dv;
-                float s = 0.f;
-                for (int j = 0; j < ch; ++j)
-                    s += sK[j * d + f] * sV[j * dv + c];
-                sS[e] += s;
+                sS[e] += sum16(ch, [&](int j) { return sK[j * d + f] * sV[j * dv + c]; });
             }
             for (int f = tid; f < d; f += NT) {
-                float s = 0.f;
-                for (int j = 0; j < ch; ++j)
-                    s += sK[j * d + f];
-                sz[f] += s;
+                sz[f] += sum16(ch, [&](int j) { return sK[j * d + f]; });
             }
         }
     }

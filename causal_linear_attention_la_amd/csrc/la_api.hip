@@ -110,11 +110,14 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
         // matrix-core kernels: at least kMinChunks chunks per segment; a segment's fixed costs
         // (its sum written and scanned, its prefix read, the pipeline filled) outweigh its
         // parallelism below that (measured on MI355X, B=4 H=8 N=2048 d=64: 16 segments of 2
-        // chunks 27.1 us per call, 8 segments of 4 chunks 24.8 us, both with cold caches). The
-        // vector-ALU kernels spend far longer per chunk, so they keep every segment (one chunk
-        // of B=1 H=1 N=64 d=16 float32 per segment: 23.4 us per call; one segment: 27.1 us).
+        // chunks 27.1 us per call, 8 segments of 4 chunks 24.8 us, both with cold caches).
+        // The vector-ALU kernels otherwise keep every segment, except that a sequence of at most
+        // two chunks runs as one segment: one launch instead of three (B=1 H=1 N=64 d=16
+        // float32: 16.5 us per call, against 18.9 us as two segments; with eight chunks, eight
+        // segments take 19.6 us and one 60.0 us).
         const bool matrix = pl.mfma || pl.mfma32;
-        const long most = !matrix ? nchunks : nchunks / kMinChunks > 1 ? nchunks / kMinChunks : 1;
+        const long most = !matrix ? (nchunks <= 2 ? 1 : nchunks)
+                                  : nchunks / kMinChunks > 1 ? nchunks / kMinChunks : 1;
         if (want > most)
             want = most;
         pl.L = (int)((nchunks + want - 1) / want) * pl.chunk;

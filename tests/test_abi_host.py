@@ -241,10 +241,12 @@ def test_workspace_bytes():
     assert la.la_segments(0, 4, 8, 2048, 64, 64) == 8
     assert la.la_workspace_bytes(0, 4, 8, 2048, 64, 64) == 32 * 8 * E64 * 4
     assert la.la_segments(0, 4, 8, 8192, 64, 64) == 16
-    # N=64 float32 (the vector-ALU kernels keep one chunk per segment): chunk 32, two segments
-    # of one chunk; one segment needs no workspace
-    assert la.la_segments(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 2
-    assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 2 * (16 * 16 + 16) * 4
+    # N=64 float32 on the vector-ALU kernels: chunk 32, and a sequence of two chunks runs as one
+    # segment (no workspace); an explicit seg_len of one chunk gives two segments. N=96 (three
+    # chunks): one chunk per segment, as the vector-ALU kernels keep every segment otherwise
+    assert la.la_segments(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 1
+    assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 0
+    assert la.la_segments(0, 1, 1, 96, 16, 16, 0, 0, la.LA_F32) == 3
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 32, la.LA_F32) == 2 * (16 * 16 + 16) * 4
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 64, la.LA_F32) == 0
     assert la.la_workspace_bytes(1, 1, 8, 100000, 128, 128) > 0
