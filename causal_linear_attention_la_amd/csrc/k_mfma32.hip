@@ -22,8 +22,9 @@
 // the same reason, so that they are A operands of the product with V without any exchange.
 // All other operands are 16-byte LDS reads of four consecutive features or keys.
 //
-// Workgroup: D/16 waves, wave w owning the value columns 16 w .. 16 w + 15 of S, num and out.
-// Per chunk, phase 1: waves 0-3 form partial scores over a quarter of the features each (one
+// Causal and global workgroups: D/16 waves, wave w owning the value columns 16 w .. 16 w + 15
+// of S, num and out (the segment sums, which only update S, use twice the waves; see A32).
+// Causal, per chunk, phase 1: waves 0-3 form partial scores over a quarter of the features each (one
 // wave per SIMD), every wave computes Qf S for its columns, the last wave forms Qf z; barrier;
 // phase 2: every wave adds the four partial score tiles (in a fixed order), divides, forms
 // num += A V and updates its columns of S; the next chunk is staged into the other half of the
