@@ -249,6 +249,12 @@ def test_workspace_bytes():
     assert la.la_segments(0, 1, 1, 96, 16, 16, 0, 0, la.LA_F32) == 3
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 32, la.LA_F32) == 2 * (16 * 16 + 16) * 4
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 64, la.LA_F32) == 0
+    # float32, d = d_v in {64, 128}: the float32 matrix-core kernels (chunk 32, one causal
+    # workgroup per CU, at least 4 chunks per segment): 256 / 32 = 8 segments at both sizes
+    assert la.la_segments(0, 2, 16, 8192, 128, 128, 0, 0, la.LA_F32) == 8
+    assert la.la_workspace_bytes(0, 2, 16, 8192, 128, 128, 0, 0, la.LA_F32) == 32 * 8 * E * 4
+    assert la.la_segments(0, 4, 8, 2048, 64, 64, 0, 0, la.LA_F32) == 8
+    assert la.la_segments(0, 2, 16, 8192, 128, 128, 32, 0, la.LA_F32) == 8
     assert la.la_workspace_bytes(1, 1, 8, 100000, 128, 128) > 0
     assert la.la_workspace_bytes(2, 1, 8, 10, 128, 128) == 0
     assert la.la_workspace_bytes(0, 1, 1, 64, 48, 16) == 0
