@@ -299,28 +299,32 @@ def causal_rf(q, k, v, W, flags=0, S0=None, z0=None, chunk=0, seg_len=0):
     return f64(out), f64(S), f64(z)
 
 
-@pytest.mark.parametrize("d,m,dv,N,seg,flags", [
-    (128, 128, 128, 3000, 0, 0), (128, 128, 128, 1000, 192, UNNORM), (64, 64, 64, 1111, 0, 0),
-    (64, 64, 64, 65, 0, UNNORM), (128, 128, 128, 1, 0, 0), (128, 64, 128, 700, 0, 0),
-    (128, 64, 64, 500, 0, 0), (64, 128, 64, 300, 0, 0)])
-def test_causal_rf(d, m, dv, N, seg, flags):
+@pytest.mark.parametrize("dtype,d,m,dv,N,seg,flags", [
+    ("bf16", 128, 128, 128, 3000, 0, 0), ("bf16", 128, 128, 128, 1000, 192, UNNORM),
+    ("bf16", 64, 64, 64, 1111, 0, 0), ("bf16", 64, 64, 64, 65, 0, UNNORM),
+    ("bf16", 128, 128, 128, 1, 0, 0), ("bf16", 128, 64, 128, 700, 0, 0),
+    ("bf16", 128, 64, 64, 500, 0, 0), ("bf16", 64, 128, 64, 300, 0, 0),
+    ("f32", 128, 128, 128, 1000, 0, 0), ("f32", 64, 64, 64, 300, 96, UNNORM),
+    ("f32", 32, 16, 32, 200, 0, 0)])
+def test_causal_rf(dtype, d, m, dv, N, seg, flags):
     """la_causal_fwd_rf against the oracle's features and recurrence, with a carried initial
-    state: m == d == d_v maps inside the attention kernels, other shapes go through memory."""
-    q, k, v = datagen.qkv(2, 2, N, d, dv, 1500 + d + m + N, 1 / math.sqrt(d), "bf16")
-    W = datagen.projections(m, d, 1600 + m, "bf16")
+    state: bf16 with m == d == d_v maps inside the attention kernels, other shapes and float32
+    go through memory (float32 with m == d_v in {64, 128}: then the float32 matrix-core kernels)."""
+    q, k, v = datagen.qkv(2, 2, N, d, dv, 1500 + d + m + N, 1 / math.sqrt(d), dtype)
+    W = datagen.projections(m, d, 1600 + m, dtype)
     fq, fk = oracle.rf_map(f64(q), f64(W)), oracle.rf_map(f64(k), f64(W))
     mode, norm = MODE[IDENT | flags]
     # a carried state from 64 earlier tokens
-    qp, kp, vp = datagen.qkv(2, 2, 64, d, dv, 1700 + d, 1 / math.sqrt(d), "bf16")
+    qp, kp, vp = datagen.qkv(2, 2, 64, d, dv, 1700 + d, 1 / math.sqrt(d), dtype)
     _, S0, z0, _, _ = oracle.causal(oracle.rf_map(f64(qp), f64(W)), oracle.rf_map(f64(kp), f64(W)),
                                     f64(vp), mode="identity")
     S0, z0 = S0.astype(np.float32), z0.astype(np.float32)
-    say(f"causal rf d={d} m={m} dv={dv} N={N} seg={seg} flags={flags}")
+    say(f"causal rf dtype={dtype} d={d} m={m} dv={dv} N={N} seg={seg} flags={flags}")
     o, S, z = causal_rf(q, k, v, W, flags=flags, S0=S0, z0=z0, seg_len=seg)
     oo, So, zo, _, _ = oracle.causal(fq, fk, f64(v), S0=S0, z0=z0, mode=mode, normalize=norm)
-    check("out", o, oo, TOL["bf16"])
-    check("S", S, So, TOL["bf16"])
-    check("z", z, zo, TOL["bf16"])
+    check("out", o, oo, TOL[dtype])
+    check("S", S, So, TOL[dtype])
+    check("z", z, zo, TOL[dtype])
 
 
 def test_causal_rf_fused_equals_two_pass():
