@@ -150,6 +150,31 @@ template <int D> __device__ __forceinline__ float key_col_sum(const float *kt, i
     return s;
 }
 
+// Qf z for the CH queries of a chunk (Qb: row-major features, row stride C32<D>::RS), spread
+// over the NW waves of a workgroup: wave w takes queries QPW w .. + QPW - 1, LPQ lanes per query
+// each add up their groups of four features, then a fixed shuffle tree. (One wave doing all
+// queries sat on the path to the barrier that follows: the float32 causal kernel with 2 D/16
+// waves took 232 us at B=2 H=16 N=8192 d=128 that way, 211 us this way.)
+template <int D, int NW>
+__device__ __forceinline__ void chunk_qz(float *sdz, const float *Qb, const float *sz, int w, int l)
+{
+    constexpr int QPW = CH / NW, LPQ = 64 / QPW, G = D / (4 * LPQ);
+    static_assert(QPW * NW == CH && G * 4 * LPQ == D, "queries and features must divide evenly");
+    const int qq = QPW * w + l / LPQ, fg = l % LPQ;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        const int f = 4 * (fg + LPQ * i);
+        const f32x4 x = ld4(Qb + qq * C32<D>::RS + f), zz = ld4(sz + f);
+        s = fmaf(x[0], zz[0], fmaf(x[1], zz[1], fmaf(x[2], zz[2], fmaf(x[3], zz[3], s))));
+    }
+#pragma unroll
+    for (int off = LPQ / 2; off > 0; off >>= 1)
+        s += __shfl_xor(s, off, 64);
+    if (fg == 0)
+        sdz[qq] = s;
+}
+
 // With a decay gamma (the retention recurrence S_t = gamma S_{t-1} + Kf_t V_t^T of "Linear
 // Attention Math", section "The kernel cousins: SSMs and RetNet"), a chunk of n valid keys updates
 // S = gamma^n S + sum_j gamma^(n - 1 - j) Kf_j V_j^T (z alike): the V values of the product are
@@ -375,20 +400,9 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_causal32(
                 num[1] = mma(a1[j], sacc[ft][j], num[1]);
             }
         }
-        // Qf z for the chunk's queries (two lanes per query, half the features each)
-        if (NORM && w == NW - 1) {
-            const int qq = l & 31, hf = l >> 5;
-            float s = 0.f;
-#pragma unroll
-            for (int f = 0; f < D / 2; f += 4) {
-                const f32x4 x = ld4(Qb + qq * RS + hf * (D / 2) + f);
-                const f32x4 zz = ld4(sz + hf * (D / 2) + f);
-                s = fmaf(x[0], zz[0], fmaf(x[1], zz[1], fmaf(x[2], zz[2], fmaf(x[3], zz[3], s))));
-            }
-            s += __shfl_xor(s, 32, 64);
-            if (hf == 0)
-                sdz[qq] = s;
-        }
+        // Qf z for the chunk's queries
+        if (NORM)
+            chunk_qz<D, NW>(sdz, Qb, sz, w, l);
         __syncthreads();
 
         // phase 2. Scores: the four partial tiles in order, then the causal mask on the
@@ -500,6 +514,232 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_causal32(
     }
 }
 
+// The causal kernel with twice the waves (four per SIMD): wave w owns the value columns
+// 16 (w mod D/16) .. + 15 and the feature half fh = w div (D/16) of S, and writes the outputs of
+// query tile fh. In phase 1 it forms Qf S over its features for both query tiles and leaves
+// the other tile's partial in LDS for the wave with the same columns and the other half; in
+// phase 2 it adds that partial (features 0 .. D/2 - 1 first), the scores and the division for
+// its query tile, and updates its half of S. The scores read K from the feature-major array
+// (the row-major copy is left out, so the LDS still holds one workgroup).
+template <int D> struct C32H {
+    static constexpr int NCT = D / 16;
+    static constexpr int NW = 2 * NCT;
+    static constexpr int THREADS = NW * 64;
+    static constexpr int NFH = D / 32;       // feature tiles per wave
+};
+
+template <int D, int F, bool DECAY>
+__global__ __launch_bounds__(C32H<D>::THREADS) void k_causal32h(
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
+    float *__restrict__ out, const float *__restrict__ preS, const float *__restrict__ prez,
+    long pstride, long pzstride, float *__restrict__ Sout, float *__restrict__ zout, int N, int L,
+    int P, const float *__restrict__ gamma, int H)
+{
+    using G = C32<D>;
+    using W2 = C32H<D>;
+    using ST = Stage<D, W2::THREADS>;
+    constexpr bool PHI = !(F & F_IDENTITY), NORM = !(F & F_UNNORM);
+    constexpr int NW = W2::NW, RS = G::RS, TS = G::TS, NFH = W2::NFH, FQ = D / 4;
+    __shared__ __attribute__((aligned(16))) float sQ[2][CH * RS];
+    __shared__ __attribute__((aligned(16))) float sKT[2][D * TS];
+    __shared__ __attribute__((aligned(16))) float sV[2][CH * RS];
+    __shared__ __attribute__((aligned(16))) float sPart[4][3][64 * 4]; // partial score tiles
+    __shared__ __attribute__((aligned(16))) float sNum[NW][64 * 4];    // partial Qf S handed over
+    __shared__ float sz[D];
+    __shared__ float sdz[CH];
+
+    const int tid = threadIdx.x, w = wave_index(), l = tid & 63, li = l & 15, g = l >> 4;
+    const int fh = w / W2::NCT, c0 = 16 * (w % W2::NCT), f0 = fh * (D / 2);
+    const int partner = (w + W2::NCT) % NW;
+    const int p = blockIdx.x % P, bh = blockIdx.x / P;
+    const int tb = p * L, te = min(N, tb + L), nch = (te - tb + CH - 1) / CH;
+    const size_t hoff = (size_t)bh * N * D;
+    const float *qh = q + hoff, *kh = k + hoff, *vh = v + hoff;
+    float *oh = out + hoff;
+    const ST stg(tid);
+    const float lg = DECAY ? decay_log2(gamma, bh, H) : 0.f;
+
+    // this wave's part of the state: lane (g, li) of tile ft holds S[f0 + 16 ft + 4 g + r][c0 + li]
+    f32x4 sacc[NFH];
+    {
+        const float *S0 = preS ? preS + ((long)bh * P + p) * pstride : nullptr;
+        const float *z0 = preS ? prez + ((long)bh * P + p) * pzstride : nullptr;
+#pragma unroll
+        for (int ft = 0; ft < NFH; ++ft)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sacc[ft][r] = S0 ? S0[(size_t)(f0 + 16 * ft + 4 * g + r) * D + c0 + li] : 0.f;
+        if (tid < D)
+            sz[tid] = z0 ? z0[tid] : 0.f;
+    }
+
+    f32x4 rq[ST::PER], rk[ST::PER], rv[ST::PER];
+    auto load = [&](int cc) {
+        const int t0 = tb + min(cc, nch - 1) * CH;
+        stg.rows(rq, qh, t0, te - t0);
+        stg.keys(rk, kh, t0, te - t0);
+        stg.rows(rv, vh, t0, te - t0);
+    };
+    auto put = [&](int b, int cc) {
+        const int n = te - (tb + cc * CH);
+        stg.template put_rows<PHI>(sQ[b], rq, n);
+        stg.template put_keys<PHI>(sKT[b], nullptr, rk, n);
+        stg.template put_rows<false>(sV[b], rv, n);
+    };
+    load(0);
+    put(0, 0);
+    load(1);
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+        const int b = c & 1;
+        const float *Qb = sQ[b], *KTb = sKT[b];
+
+        // phase 1. Partial scores A^T over features [w D/4, (w + 1) D/4) (waves 0-3, one per
+        // SIMD); the key operand comes from the feature-major array, four single reads per block
+        if (w < 4) {
+            f32x4 pa[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int fb = w * FQ; fb < (w + 1) * FQ; fb += 16) {
+                f32x4 k0, k1;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    k0[j] = KTb[(fb + 4 * g + j) * TS + li];
+                    k1[j] = KTb[(fb + 4 * g + j) * TS + 16 + li];
+                }
+                const f32x4 q0 = ld4(Qb + li * RS + fb + 4 * g), q1 = ld4(Qb + (16 + li) * RS + fb + 4 * g);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    pa[0] = mma(k0[j], q0[j], pa[0]);
+                    pa[1] = mma(k0[j], q1[j], pa[1]);
+                    pa[2] = mma(k1[j], q1[j], pa[2]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+                st4(&sPart[w][t][4 * l], pa[t]);
+        }
+        // Qf S over this wave's features, both query tiles; the other tile's part is handed over
+        f32x4 num[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ft = 0; ft < NFH; ++ft) {
+            const f32x4 a0 = ld4(Qb + li * RS + f0 + 16 * ft + 4 * g);
+            const f32x4 a1 = ld4(Qb + (16 + li) * RS + f0 + 16 * ft + 4 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                num[0] = mma(a0[j], sacc[ft][j], num[0]);
+                num[1] = mma(a1[j], sacc[ft][j], num[1]);
+            }
+        }
+        st4(&sNum[w][4 * l], fh ? num[0] : num[1]);
+        const f32x4 mine = fh ? num[1] : num[0]; // (only this tile's part lives across the barrier)
+        if (NORM)
+            chunk_qz<D, NW>(sdz, Qb, sz, w, l);
+        __syncthreads();
+
+        // phase 2, query tile fh: Qf S with both feature halves (half 0 first)
+        const f32x4 other = ld4(&sNum[partner][4 * l]);
+        f32x4 acc = fh ? other + mine : mine + other;
+        f32x4 at[3];
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            at[t] = ld4(&sPart[0][t][4 * l]);
+#pragma unroll
+            for (int ww = 1; ww < 4; ++ww)
+                at[t] += ld4(&sPart[ww][t][4 * l]);
+        }
+        if (DECAY) {
+            constexpr int KTI[3] = {0, 0, 1}, QTI[3] = {0, 1, 1};
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int dq = 16 * QTI[t] + li - (16 * KTI[t] + 4 * g + r);
+                    at[t][r] = dq >= 0 ? at[t][r] * decay_pow(lg, dq) : 0.f;
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[r] *= decay_pow(lg, 16 * fh + 4 * g + r + 1);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * g + r > li) {
+                    at[0][r] = 0.f;
+                    at[2][r] = 0.f;
+                }
+        }
+        float vb[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vb[t][r] = sV[b][(16 * t + 4 * g + r) * RS + c0 + li];
+        // num += A V for query tile fh (wave-uniform branch)
+        if (fh == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc = mma(at[0][r], vb[0][r], acc);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc = mma(at[1][r], vb[0][r], acc);
+                acc = mma(at[2][r], vb[1][r], acc);
+            }
+        }
+        float inv[4];
+        if (NORM) {
+            float dn = fh ? ((at[1][0] + at[1][1]) + (at[1][2] + at[1][3])) +
+                                ((at[2][0] + at[2][1]) + (at[2][2] + at[2][3]))
+                          : (at[0][0] + at[0][1]) + (at[0][2] + at[0][3]);
+            dn += __shfl_xor(dn, 16, 64);
+            dn += __shfl_xor(dn, 32, 64);
+            const int qi = 16 * fh + li;
+            const float zq = DECAY ? sdz[qi] * decay_pow(lg, qi + 1) : sdz[qi];
+            const float iv = 1.f / (dn + zq);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                inv[r] = __shfl(iv, 4 * g + r, 64);
+        }
+        const int t0 = tb + c * CH, n = te - t0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * fh + 4 * g + r;
+            if (row < n)
+                oh[(size_t)(t0 + row) * D + c0 + li] = NORM ? acc[r] * inv[r] : acc[r];
+        }
+        const float *kt = KTb + f0 * TS;
+        if (DECAY) {
+            const int nk = min(CH, n);
+            const float gn = decay_pow(lg, nk);
+            float vbs[2][4];
+            decayed_values(vbs, vb, lg, nk, g);
+#pragma unroll
+            for (int ft = 0; ft < NFH; ++ft)
+                sacc[ft] *= gn;
+            update_state<D, NFH>(sacc, kt, vbs, li, g);
+            if (tid < D)
+                sz[tid] = fmaf(gn, sz[tid], key_col_sum_decayed<D>(KTb, tid, lg, nk));
+        } else {
+            update_state<D, NFH>(sacc, kt, vb, li, g);
+            if (tid < D)
+                sz[tid] += key_col_sum<D>(KTb, tid);
+        }
+        if (c + 1 < nch)
+            put(b ^ 1, c + 1);
+        load(c + 2);
+        __syncthreads();
+    }
+    if (Sout && p == P - 1) {
+        float *So = Sout + (size_t)bh * D * D;
+#pragma unroll
+        for (int ft = 0; ft < NFH; ++ft)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                So[(size_t)(f0 + 16 * ft + 4 * g + r) * D + c0 + li] = sacc[ft][r];
+        if (tid < D)
+            zout[(size_t)bh * D + tid] = sz[tid];
+    }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Global read out = Qf S / Qf z over one segment of rows of one head. The outputs of chunk c
 // are stored after the barrier that ends it (Qf z from the last wave is visible there; the
@@ -561,19 +801,8 @@ __global__ __launch_bounds__(C32<D>::THREADS) void k_gread32(const float *__rest
                 num[1] = mma(a1[j], sacc[ft][j], num[1]);
             }
         }
-        if (NORM && w == NW - 1) {
-            const int qq = l & 31, hf = l >> 5;
-            float s = 0.f;
-#pragma unroll
-            for (int f = 0; f < D / 2; f += 4) {
-                const f32x4 x = ld4(Qb + qq * RS + hf * (D / 2) + f);
-                const f32x4 zz = ld4(sz + hf * (D / 2) + f);
-                s = fmaf(x[0], zz[0], fmaf(x[1], zz[1], fmaf(x[2], zz[2], fmaf(x[3], zz[3], s))));
-            }
-            s += __shfl_xor(s, 32, 64);
-            if (hf == 0)
-                sdz[b][qq] = s;
-        }
+        if (NORM)
+            chunk_qz<D, NW>(sdz[b], Qb, sz, w, l);
         if (c + 1 < nch)
             stg.template put_rows<PHI>(sQ[b ^ 1], rq, te - (tb + (c + 1) * CH));
         load(c + 2);
@@ -595,11 +824,12 @@ void launch_causal32_f(dim3 grid, hipStream_t st, const float *q, const float *k
                        float *o, const float *preS, const float *prez, long ps, long pzs,
                        float *Sout, float *zout, int N, int L, int P, const float *gamma, int H)
 {
-    const dim3 block(C32<D>::THREADS);
+    // the decayed form keeps D/16 waves: its extra registers do not fit the 128 of four waves
+    // per SIMD (152 bytes per lane spilled at D = 128)
     if (gamma)
-        hipLaunchKernelGGL((k_causal32<D, F, true>), grid, block, 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
+        hipLaunchKernelGGL((k_causal32<D, F, true>), grid, dim3(C32<D>::THREADS), 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
     else
-        hipLaunchKernelGGL((k_causal32<D, F, false>), grid, block, 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
+        hipLaunchKernelGGL((k_causal32h<D, F, false>), grid, dim3(C32H<D>::THREADS), 0, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H);
 }
 
 template <int D>
