@@ -157,6 +157,25 @@ def test_decay_decode_chain(flags, dtype, d):
         check("z", f64(zd), zo, TOL[dtype])
 
 
+@pytest.mark.parametrize("d,seg", [(128, 0), (64, 96), (32, 0)])
+def test_retention_float32_rowwise(d, seg):
+    """The float32 retention form (identity map, no division, per-head decay) with positive q,
+    k and v: no row can cancel, so the plain row-wise bar of 1e-5 applies (the signed cases
+    above are bounded by their absolute-value sums instead). d = 128, 64 run the float32
+    matrix-core kernels, d = 32 the vector-ALU ones."""
+    B, H, N = 2, len(GAMMAS), 900 + d
+    q = datagen.positive((B, H, N, d), 980 + d, 1 / math.sqrt(d), "f32")
+    k = datagen.positive((B, H, N, d), 981 + d, 1 / math.sqrt(d), "f32")
+    v = datagen.positive((B, H, N, d), 982 + d, 1.0, "f32")
+    say(f"float32 retention, positive inputs, d={d} seg={seg}")
+    o, S, z = causal_decay(q, k, v, GAMMAS, IDENT | UNNORM, seg_len=seg)
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v), mode="identity", normalize=False,
+                                     gamma=GAMMAS)
+    check("out", o, oo, TOL["f32"])
+    check("S", S, So, TOL["f32"])
+    check("z", z, zo, TOL["f32"])
+
+
 def test_decay_one_equals_base():
     """gamma = 1 for every head gives the undecayed form (within rounding of the decay path)."""
     q, k, v = datagen.qkv(1, 4, 1500, 128, 128, 971, 1 / math.sqrt(128), "bf16")
