@@ -115,7 +115,8 @@ def bench_prefill(args):
     ms_hot, _ = time_calls(lambda i: step(0), args.steps, 2)
 
     # per-kernel device times: HIP events recorded by the library on the launch stream around
-    # each kernel of `steps` back-to-back calls (segment sums, segment scan, causal outputs)
+    # each kernel of `steps` back-to-back calls (segment sums, the scan where one is launched,
+    # causal outputs)
     q, k, v, out, S, z = sets[0]
     la.la_causal_fwd_profiled(q, k, v, out, None, None, S, z, chunk=args.chunk,
                               seg_len=args.seg_len, reps=2)
@@ -125,6 +126,20 @@ def bench_prefill(args):
     # segments per head the library chose
     P = la.la_segments(0, w.B, w.H, w.N, w.d, w.dv, args.chunk, args.seg_len)
     return w, ms, ms_hot, wall, byts, flops, P, kern_ms, ms_steady
+
+
+def kernels_us(kern, P, scan):
+    """Per-kernel device times (us) of one causal call from la_causal_fwd_profiled: the segment
+    sums, the scan over segment states (launched on the float32 and vector-ALU paths only: on
+    the bf16 matrix-core path each causal segment adds up the sums before it itself) and the
+    causal kernel; with one segment the causal kernel alone."""
+    if P <= 1:
+        return {"causal": kern[2] * 1e3}
+    out = {"segment_sums": kern[0] * 1e3}
+    if scan:
+        out["segment_scan"] = kern[1] * 1e3
+    out["causal"] = kern[2] * 1e3
+    return out
 
 
 def time_flushed(fn, reps, flush_bytes=512 << 20):
@@ -699,12 +714,13 @@ def main():
         wn, hot, flushed, kern_n, P_n = bench_causal_small(args, n)
         small[n] = (wn, hot, flushed, kern_n, P_n)
         print(f"workload {n} ({wn.name}): hot {hot * 1e3:.1f} us, flushed {flushed * 1e3:.1f} us; "
-              "kernels " + ", ".join(f"{t * 1e3:.1f}" for t in (kern_n if P_n > 1 else kern_n[2:]))
+              "kernels " + ", ".join(f"{name} {t:.1f}" for name, t in
+                                     kernels_us(kern_n, P_n, wn.dtype != "bf16").items())
               + " us", file=sys.stderr, flush=True)
 
     w, ms, ms_hot, wall, byts, flops, P, kern_ms, ms_steady = bench_prefill(args)
     print(f"prefill: {ms * 1e3:.1f} us/step (hot {ms_hot * 1e3:.1f} us); kernels "
-          f"agg {kern_ms[0] * 1e3:.1f} scan {kern_ms[1] * 1e3:.1f} causal {kern_ms[2] * 1e3:.1f} us",
+          f"agg {kern_ms[0] * 1e3:.1f} causal {kern_ms[2] * 1e3:.1f} us",
           file=sys.stderr, flush=True)
     th = w.B * w.H * w.N
     value = th / (ms * 1e-3)
@@ -735,15 +751,13 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK,
                      "traffic": traffic["bytes_per_launch"] if traffic else None,
                      "kernel": "k_causal<128, 0, false, false> (causal outputs + final state; reads q, k, v and "
-                               "the segment prefix states, writes out and S, z)",
+                               "the segment sums before each segment, writes out and S, z)",
                      "kernel_us": kern_ms[2] * 1e3,
                      "algorithmic_bytes_per_launch": byts,
                      "copy_GBps": copy_bw / 1e9, "frac_of_copy": achieved / copy_bw,
                      "d2d_copy_GBps": d2d_bw / 1e9, "frac_of_d2d_copy": achieved / d2d_bw,
                      "call_us": ms * 1e3, "call_frac": byts / (ms * 1e-3) / HBM_PEAK,
-                     "call_kernels_us": {"segment_sums": kern_ms[0] * 1e3,
-                                         "segment_scan": kern_ms[1] * 1e3,
-                                         "causal": kern_ms[2] * 1e3}},
+                     "call_kernels_us": kernels_us(kern_ms, P, False)},
         "mfma": {"algorithmic_frac": flops / (ms * 1e-3) / BF16_PEAK,
                  "issued_frac": issued / (ms * 1e-3) / BF16_PEAK,
                  "peak_tflops": BF16_PEAK / 1e12},
@@ -767,16 +781,13 @@ def main():
                   "two_pass_us_per_step": ms_f2 * 1e3,
                   "features_us_per_tensor": ms_rf * 1e3,
                   "features_hbm_frac": rf_bytes / (ms_rf * 1e-3) / HBM_PEAK,
-                  "two_pass_attention_kernels_us": {"segment_sums": kern_f[0] * 1e3,
-                                           "segment_scan": kern_f[1] * 1e3,
-                                           "causal": kern_f[2] * 1e3}},
+                  "two_pass_attention_kernels_us": kernels_us(kern_f, P, False)},
         "identity_unnormalized": {"workload": wv.name, "us_per_call": ms_v * 1e3,
                                   "token_heads_per_s": wv.B * wv.H * wv.N / (ms_v * 1e-3)},
         "float32": {"workload": w32.name.replace("_bf16", "_f32"), "entry_point": "la_causal_fwd_ws",
                     "chunk": 32, "segments_per_head": P_32, "us_per_call": ms_32 * 1e3,
                     "token_heads_per_s": w32.B * w32.H * w32.N / (ms_32 * 1e-3),
-                    "kernels_us": {"segment_sums": kern_32[0] * 1e3, "segment_scan": kern_32[1] * 1e3,
-                                   "causal": kern_32[2] * 1e3},
+                    "kernels_us": kernels_us(kern_32, P_32, True),
                     # the float32 call is bound by the float32 matrix rate (its algorithmic
                     # bytes take 67 us at 8 TB/s, its issued products 177 us at 157.3 TFLOP/s)
                     "roofline": {"bound": "mfma", "unit": "TFLOP/s",
@@ -806,9 +817,7 @@ def main():
                  "segments_per_head": P_n, "entry_point": "la_causal_fwd_ws",
                  "us_per_call_hot": hot * 1e3, "us_per_call_flushed": flushed * 1e3,
                  "token_heads_per_s_flushed": th_n / (flushed * 1e-3),
-                 # one segment launches the causal kernel alone (the other stamps then time nothing)
-                 "kernels_us": ({"segment_sums": kern_n[0] * 1e3, "segment_scan": kern_n[1] * 1e3,
-                                 "causal": kern_n[2] * 1e3} if P_n > 1 else {"causal": kern_n[2] * 1e3}),
+                 "kernels_us": kernels_us(kern_n, P_n, wn.dtype != "bf16"),
                  "algorithmic_bytes_per_call": byts_n,
                  "call_hbm_frac_flushed": byts_n / (flushed * 1e-3) / HBM_PEAK}
         if wn.dtype == "bf16":

@@ -515,7 +515,9 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
                                                            float *__restrict__ dstz, long sstride,
                                                            long zstride, int N, int L, int nseg,
                                                            int P, const float *__restrict__ gamma,
-                                                           int H, const uint16_t *__restrict__ W)
+                                                           int H, const uint16_t *__restrict__ W,
+                                                           const float *__restrict__ S0,
+                                                           const float *__restrict__ z0)
 {
     using K = Cfg<D>;
     using TL = Tile<D, AggCfg<D>::THREADS>;
@@ -543,6 +545,17 @@ __global__ __launch_bounds__(AggCfg<D>::THREADS) void k_agg(const uint16_t *__re
     f32x4 sacc[K::NFT][1];
     f32x4 zacc[1];
     zero_acc<D, 1, 1>(sacc, zacc);
+    if (S0 && p == 0) {
+        // the head's initial state into slot nseg, where the causal kernel reads it (so the
+        // final state may overwrite S0 there)
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(S0 + (size_t)bh * D * D);
+        f32x4 *dst = reinterpret_cast<f32x4 *>(dstS + ((long)bh * P + nseg) * sstride);
+        for (int i = tid; i < D * D / 4; i += AggCfg<D>::THREADS)
+            dst[i] = src[i];
+        if (tid < D / 4)
+            reinterpret_cast<f32x4 *>(dstz + ((long)bh * P + nseg) * zstride)[tid] =
+                reinterpret_cast<const f32x4 *>(z0 + (size_t)bh * D)[tid];
+    }
 
     // K staging: phi (or as given) through the tile map, or random features (RF) with each
     // wave taking its row tile and feature half of every chunk
@@ -676,11 +689,71 @@ template <int D> struct CausalLds {
 struct CausalArgs {
     const uint16_t *qh, *kh, *vh; // the head's [N, D] rows
     uint16_t *oh;
-    const float *S0, *z0;         // state before the segment (null: zero)
+    const float *S0, *z0;         // state before the segment (null: zero, or formed from pre)
     float *Sout, *zout;           // final state of the head (null: not written)
     int tb, te, nch;              // token range of the segment, chunks in it
     float lg;                     // log2 of the head's decay (0: none)
+    // the state before the segment formed from the head's segment sums (pre non-null): slots
+    // of pe floats (S, then z), the sums of segments 0..np-1 and the initial state in slot ini
+    // (-1: zero state)
+    const float *pre;
+    long pe;
+    int np, ini, L;
 };
+
+// The state before a segment from the head's segment sums: the sums of segments 0..np-1, each
+// decayed over the whole segments after it (gamma^(L (np - 1 - t)) for segment t; no weight
+// without a decay), plus the initial state decayed over all np of them -- the recurrence of the
+// state over segments ("Linear Attention: From Pairwise Reads to a Recurrent State", section "A
+// recurrence need not force token-serial training"; with the decay, "Linear Attention Math",
+// section "The kernel cousins: SSMs and RetNet") unrolled. The walk runs from the newest slot
+// down, so that at each step the workgroups of a head read different slots: each slot comes
+// from memory once, for the workgroup right after it, and from the L2 for the later ones (the
+// head's workgroups share an XCD). Each lane reads the 4 NFT floats of S it holds in the
+// accumulators (rows 16 ft + 4 g + r of column 16 w + li) and 4 of z.
+template <int D, bool DECAY>
+__device__ __forceinline__ void prefix_state(f32x4 (&sacc)[Cfg<D>::NFT][1], f32x4 (&zacc)[1],
+                                             const CausalArgs &a, int w, int li, int g, int L)
+{
+    constexpr int NFT = Cfg<D>::NFT, NX = 4 * NFT + 4;
+    const int cw0 = 16 * w;
+    auto ld = [&](float (&x)[NX], int t) {
+        const float *s = a.pre + (size_t)t * a.pe;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                x[4 * ft + r] = s[(16 * ft + 4 * g + r) * D + cw0 + li];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            x[4 * NFT + r] = s[D * D + cw0 + 4 * g + r];
+    };
+    // run += weight * x (the first term is taken as it is)
+    auto add = [&](const float (&x)[NX], bool first, float wt) {
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sacc[ft][0][r] = first ? (DECAY ? x[4 * ft + r] * wt : x[4 * ft + r])
+                                       : (DECAY ? fmaf(x[4 * ft + r], wt, sacc[ft][0][r])
+                                                : sacc[ft][0][r] + x[4 * ft + r]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            zacc[0][r] = first ? (DECAY ? x[4 * NFT + r] * wt : x[4 * NFT + r])
+                               : (DECAY ? fmaf(x[4 * NFT + r], wt, zacc[0][r])
+                                        : zacc[0][r] + x[4 * NFT + r]);
+    };
+    // step j: slot np - 1 - j, decayed over the j segments after it; then the initial state.
+    // One slot is in flight per lane: a second one gains nothing measurable (the last segment's
+    // workgroup reads P - 1 slots, 448 KiB at d = 128 and P = 8, and it is these bytes through
+    // the one CU that take the time, measured on MI355X) and spills with the decay.
+    const int ns = a.np + (a.ini >= 0 ? 1 : 0);
+    for (int j = 0; j < ns; ++j) {
+        float x[NX];
+        ld(x, j < a.np ? a.np - 1 - j : a.ini);
+        add(x, j == 0, DECAY ? decay_pow(a.lg, j * L) : 1.f);
+    }
+}
 
 // Writes the wave's 16 features of z (rows 4g..4g+3 of its tile; lane li == 0 of each group)
 // into the key-sum operand rows: bf16(z) and bf16(z - bf16(z)).
@@ -714,7 +787,9 @@ __device__ __forceinline__ void causal_compute(CausalLds<D> &sm, const CausalArg
     f32x4 sacc[K::NFT][1];
     f32x4 zacc[1];
     zero_acc<D, 1, 1>(sacc, zacc);
-    if (a.S0) {
+    if (a.pre) {
+        prefix_state<D, DECAY>(sacc, zacc, a, w, li, g, a.L);
+    } else if (a.S0) {
 #pragma unroll
         for (int ft = 0; ft < K::NFT; ++ft)
 #pragma unroll
@@ -953,21 +1028,43 @@ __global__ __launch_bounds__(CausalCfg<D>::THREADS) void k_causal(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     uint16_t *__restrict__ out, const float *__restrict__ preS, const float *__restrict__ prez,
     long pstride, long pzstride, float *__restrict__ Sout, float *__restrict__ zout, int N, int L,
-    int P, const float *__restrict__ gamma, int H, const uint16_t *__restrict__ W)
+    int P, const float *__restrict__ gamma, int H, const uint16_t *__restrict__ W, int pm)
 {
     constexpr int NCW = CausalCfg<D>::NCW;
     __shared__ __attribute__((aligned(16))) CausalLds<D> sm;
     __shared__ __attribute__((aligned(16))) uint16_t sW[RF ? D * D : 8];
     const int tid = threadIdx.x, wave = wave_id(), l = tid & 63;
-    const int p = blockIdx.x % P, bh = blockIdx.x / P;
+    // block order: segment-minor, or (PM_XCD, the head count a multiple of 8) every segment of
+    // a head on the same XCD -- consecutive workgroups go to the eight XCDs in turn -- so that
+    // the head's segment sums, read by all of its workgroups, are fetched into one L2
+    int p, bh;
+    if (pm & PM_XCD) {
+        const int x = blockIdx.x & 7, y = blockIdx.x >> 3;
+        p = y % P;
+        bh = x + 8 * (y / P);
+    } else {
+        p = blockIdx.x % P;
+        bh = blockIdx.x / P;
+    }
     const size_t hoff = (size_t)bh * N * D;
     CausalArgs a;
     a.qh = q + hoff;
     a.kh = k + hoff;
     a.vh = v + hoff;
     a.oh = out + hoff;
-    a.S0 = preS ? preS + ((long)bh * P + p) * pstride : nullptr;
-    a.z0 = preS ? prez + ((long)bh * P + p) * pzstride : nullptr;
+    a.pre = nullptr;
+    a.S0 = a.z0 = nullptr;
+    if (pm & PM_SUMS) {
+        // preS: the workspace of segment sums (pstride floats per slot, P slots per head)
+        a.pre = preS + (long)bh * P * pstride;
+        a.pe = pstride;
+        a.np = p;
+        a.ini = (pm & PM_INIT) ? P - 1 : -1;
+        a.L = L;
+    } else if (preS) {
+        a.S0 = preS + ((long)bh * P + p) * pstride;
+        a.z0 = prez + ((long)bh * P + p) * pzstride;
+    }
     const bool last = p == P - 1;
     a.Sout = Sout && last ? Sout + (size_t)bh * D * D : nullptr;
     a.zout = Sout && last ? zout + (size_t)bh * D : nullptr;
@@ -1169,29 +1266,29 @@ __global__ __launch_bounds__(NT, 2) void k_gread(const uint16_t *__restrict__ q,
 template <int D, int F> void launch_causal(dim3 grid, hipStream_t st, const uint16_t *q,
                                            const uint16_t *k, const uint16_t *v, uint16_t *o,
                                            const float *preS, const float *prez, long ps, long pzs,
-                                           float *Sout, float *zout, int N, int L, int P,
+                                           int pm, float *Sout, float *zout, int N, int L, int P,
                                            const float *gamma, int H)
 {
     const uint16_t *W = nullptr;
     if (gamma)
         hipLaunchKernelGGL((k_causal<D, F, true, false>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q,
-                           k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H, W);
+                           k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H, W, pm);
     else
         hipLaunchKernelGGL((k_causal<D, F, false, false>), grid, dim3(CausalCfg<D>::THREADS), 0, st, q,
-                           k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H, W);
+                           k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H, W, pm);
 }
 
 template <int D> void launch_causal_f(int flags, dim3 grid, hipStream_t st, const uint16_t *q,
                                       const uint16_t *k, const uint16_t *v, uint16_t *o,
                                       const float *preS, const float *prez, long ps, long pzs,
-                                      float *Sout, float *zout, int N, int L, int P,
+                                      int pm, float *Sout, float *zout, int N, int L, int P,
                                       const float *gamma, int H)
 {
     switch (flags & (F_IDENTITY | F_UNNORM)) {
-    case 0: launch_causal<D, 0>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
-    case 1: launch_causal<D, 1>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
-    case 2: launch_causal<D, 2>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
-    default: launch_causal<D, 3>(grid, st, q, k, v, o, preS, prez, ps, pzs, Sout, zout, N, L, P, gamma, H); break;
+    case 0: launch_causal<D, 0>(grid, st, q, k, v, o, preS, prez, ps, pzs, pm, Sout, zout, N, L, P, gamma, H); break;
+    case 1: launch_causal<D, 1>(grid, st, q, k, v, o, preS, prez, ps, pzs, pm, Sout, zout, N, L, P, gamma, H); break;
+    case 2: launch_causal<D, 2>(grid, st, q, k, v, o, preS, prez, ps, pzs, pm, Sout, zout, N, L, P, gamma, H); break;
+    default: launch_causal<D, 3>(grid, st, q, k, v, o, preS, prez, ps, pzs, pm, Sout, zout, N, L, P, gamma, H); break;
     }
 }
 
@@ -1209,66 +1306,85 @@ template <int D> void launch_gread_f(int flags, dim3 grid, hipStream_t st, const
 template <int D, bool PHI> void launch_agg(dim3 grid, hipStream_t st, const uint16_t *k,
                                            const uint16_t *v, float *dstS, float *dstz, long ss,
                                            long zs, int N, int L, int nseg, int P,
-                                           const float *gamma, int H)
+                                           const float *gamma, int H, const float *S0,
+                                           const float *z0)
 {
     const uint16_t *W = nullptr;
     if (gamma)
         hipLaunchKernelGGL((k_agg<D, PHI, true, false>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v,
-                           dstS, dstz, ss, zs, N, L, nseg, P, gamma, H, W);
+                           dstS, dstz, ss, zs, N, L, nseg, P, gamma, H, W, S0, z0);
     else
         hipLaunchKernelGGL((k_agg<D, PHI, false, false>), grid, dim3(AggCfg<D>::THREADS), 0, st, k, v,
-                           dstS, dstz, ss, zs, N, L, nseg, P, gamma, H, W);
+                           dstS, dstz, ss, zs, N, L, nseg, P, gamma, H, W, S0, z0);
 }
 
 template <int D> void launch_agg_f(int flags, dim3 grid, hipStream_t st, const uint16_t *k,
                                    const uint16_t *v, float *dstS, float *dstz, long ss, long zs,
-                                   int N, int L, int nseg, int P, const float *gamma, int H)
+                                   int N, int L, int nseg, int P, const float *gamma, int H,
+                                   const float *S0, const float *z0)
 {
     if (flags & F_IDENTITY)
-        launch_agg<D, false>(grid, st, k, v, dstS, dstz, ss, zs, N, L, nseg, P, gamma, H);
+        launch_agg<D, false>(grid, st, k, v, dstS, dstz, ss, zs, N, L, nseg, P, gamma, H, S0, z0);
     else
-        launch_agg<D, true>(grid, st, k, v, dstS, dstz, ss, zs, N, L, nseg, P, gamma, H);
+        launch_agg<D, true>(grid, st, k, v, dstS, dstz, ss, zs, N, L, nseg, P, gamma, H, S0, z0);
 }
 
 } // namespace
 
 hipError_t agg_mfma(int D, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int L, int nseg, int P,
-                    const float *gamma, int H, hipStream_t st)
+                    const float *gamma, int H, const float *S0, const float *z0, hipStream_t st)
 {
+    if (S0 && (!z0 || nseg >= P))
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)(BH * nseg));
     const auto *kk = static_cast<const uint16_t *>(k);
     const auto *vv = static_cast<const uint16_t *>(v);
     if (D == 128)
-        launch_agg_f<128>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
+        launch_agg_f<128>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma,
+                          H, S0, z0);
     else
-        launch_agg_f<64>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, H);
+        launch_agg_f<64>(flags, grid, st, kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma,
+                         H, S0, z0);
     return hipGetLastError();
 }
 
+// The prefix modes' preconditions (see la_launch.h).
+static bool pm_ok(int pm, int D, const float *preS, const float *prez, long ps, long pzs, int BH)
+{
+    if (!(pm & PM_SUMS))
+        return pm == 0;
+    return preS && prez == preS + (long)D * D && ps == pzs && ps >= (long)D * D + D &&
+           (!(pm & PM_XCD) || BH % 8 == 0);
+}
+
 hipError_t causal_mfma(int D, int flags, const void *q, const void *k, const void *v, void *out,
-                       const float *preS, const float *prez, long pstride, long pzstride,
+                       const float *preS, const float *prez, long pstride, long pzstride, int pm,
                        float *Sout, float *zout, int BH, int N, int L, int P, const float *gamma,
                        int H, hipStream_t st)
 {
+    if (!pm_ok(pm, D, preS, prez, pstride, pzstride, BH))
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)(BH * P));
     const auto *qq = static_cast<const uint16_t *>(q);
     const auto *kk = static_cast<const uint16_t *>(k);
     const auto *vv = static_cast<const uint16_t *>(v);
     auto *oo = static_cast<uint16_t *>(out);
     if (D == 128)
-        launch_causal_f<128>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout,
+        launch_causal_f<128>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, pm, Sout,
                              zout, N, L, P, gamma, H);
     else
-        launch_causal_f<64>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout,
+        launch_causal_f<64>(flags, grid, st, qq, kk, vv, oo, preS, prez, pstride, pzstride, pm, Sout,
                             zout, N, L, P, gamma, H);
     return hipGetLastError();
 }
 
 hipError_t agg_rf_mfma(int D, const void *k, const void *v, const void *W, float *dstS, float *dstz,
                        long sstride, long zstride, int BH, int N, int L, int nseg, int P,
-                       hipStream_t st)
+                       const float *S0, const float *z0, hipStream_t st)
 {
+    if (S0 && (!z0 || nseg >= P))
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)(BH * nseg));
     const auto *kk = static_cast<const uint16_t *>(k);
     const auto *vv = static_cast<const uint16_t *>(v);
@@ -1276,18 +1392,20 @@ hipError_t agg_rf_mfma(int D, const void *k, const void *v, const void *W, float
     const float *gamma = nullptr;
     if (D == 128)
         hipLaunchKernelGGL((k_agg<128, false, false, true>), grid, dim3(AggCfg<128>::THREADS), 0, st,
-                           kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, 1, ww);
+                           kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, 1, ww, S0, z0);
     else
         hipLaunchKernelGGL((k_agg<64, false, false, true>), grid, dim3(AggCfg<64>::THREADS), 0, st,
-                           kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, 1, ww);
+                           kk, vv, dstS, dstz, sstride, zstride, N, L, nseg, P, gamma, 1, ww, S0, z0);
     return hipGetLastError();
 }
 
 hipError_t causal_rf_mfma(int D, int flags, const void *q, const void *k, const void *v,
                           const void *W, void *out, const float *preS, const float *prez,
-                          long pstride, long pzstride, float *Sout, float *zout, int BH, int N,
-                          int L, int P, hipStream_t st)
+                          long pstride, long pzstride, int pm, float *Sout, float *zout, int BH,
+                          int N, int L, int P, hipStream_t st)
 {
+    if (!pm_ok(pm, D, preS, prez, pstride, pzstride, BH))
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)(BH * P));
     const auto *qq = static_cast<const uint16_t *>(q);
     const auto *kk = static_cast<const uint16_t *>(k);
@@ -1298,7 +1416,7 @@ hipError_t causal_rf_mfma(int D, int flags, const void *q, const void *k, const 
 #define LA_RFC(DD, FF)                                                                          \
     hipLaunchKernelGGL((k_causal<DD, FF, false, true>), grid, dim3(CausalCfg<DD>::THREADS), 0, st, \
                        qq, kk, vv, oo, preS, prez, pstride, pzstride, Sout, zout, N, L, P, gamma, 1, \
-                       ww)
+                       ww, pm)
     const bool unnorm = flags & F_UNNORM;
     if (D == 128) {
         if (unnorm)

@@ -439,14 +439,24 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
     hipError_t e = mark(ts, 0, st);
     const float *preS = S0, *prez = z0; // P == 1: the initial state (or none) is the prefix
     long ps = (long)d * dv, pzs = d;
-    if (P > 1 && e == hipSuccess) {
+    int pm = 0;
+    if (P > 1 && e == hipSuccess && pl.mfma) {
+        // sums of segments 0..P-2, with the initial state copied into slot P-1; each causal
+        // segment then adds up the sums before it (no scan launch)
+        e = la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L, P - 1, P, gamma,
+                         H, S0, z0, st);
+        if (e == hipSuccess)
+            e = mark(ts, 1, st);
+        pm = la::PM_SUMS | (S0 ? la::PM_INIT : 0) | (BH % 8 == 0 ? la::PM_XCD : 0);
+        preS = wsp;
+        prez = wsp + (long)d * dv;
+        ps = pzs = E;
+    } else if (P > 1 && e == hipSuccess) {
         // sums of segments 0..P-2, then the exclusive prefix over segments in place
-        e = pl.mfma ? la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
-                                   P - 1, P, gamma, H, st)
-            : pl.mfma32 ? la::agg_mfma32(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
-                                     P - 1, P, gamma, H, st)
-                    : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
-                                   d, dv, pl.chunk, L, P - 1, P, gamma, H, st);
+        e = pl.mfma32 ? la::agg_mfma32(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
+                                       P - 1, P, gamma, H, st)
+                      : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
+                                     d, dv, pl.chunk, L, P - 1, P, gamma, H, st);
         if (e == hipSuccess)
             e = mark(ts, 1, st);
         if (e == hipSuccess)
@@ -460,8 +470,8 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
     if (e == hipSuccess)
         e = mark(ts, 2, st);
     if (e == hipSuccess)
-        e = pl.mfma ? la::causal_mfma(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N, L,
-                                      P, gamma, H, st)
+        e = pl.mfma ? la::causal_mfma(d, flags, q, k, v, out, preS, prez, ps, pzs, pm, S, z, BH, N,
+                                      L, P, gamma, H, st)
             : pl.mfma32 ? la::causal_mfma32(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N,
                                         L, P, gamma, H, st)
                     : la::out_valu(bf16, true, flags, q, k, v, out, preS, prez, ps, pzs,
@@ -479,7 +489,7 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
     hipError_t e;
     if (P > 1) {
         e = pl.mfma   ? la::agg_mfma(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N, L,
-                                     P, P, nullptr, 1, st)
+                                     P, P, nullptr, 1, nullptr, nullptr, st)
             : pl.mfma32 ? la::agg_mfma32(d, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
                                          L, P, P, nullptr, 1, st)
                       : la::agg_valu(bf16, flags, k, v, wsp, wsp + (long)d * dv, E, E, BH, N,
@@ -488,7 +498,7 @@ int run_global(const void *q, const void *k, const void *v, void *out, float *S,
             e = la::seg_total(wsp, S, z, BH, P, d, dv, st);
     } else {
         e = pl.mfma   ? la::agg_mfma(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1,
-                                     nullptr, 1, st)
+                                     nullptr, 1, nullptr, nullptr, st)
             : pl.mfma32 ? la::agg_mfma32(d, flags, k, v, S, z, (long)d * dv, d, BH, N, L, 1, 1,
                                          nullptr, 1, st)
                       : la::agg_valu(bf16, flags, k, v, S, z, (long)d * dv, d, BH, N, d, dv,
@@ -625,17 +635,20 @@ int run_causal_rf(const void *q, const void *k, const void *v, void *out, const 
         hipError_t e = hipSuccess;
         const float *preS = S0, *prez = z0;
         long ps = (long)d * dv, pzs = d;
+        int pm = 0;
         if (P > 1) {
-            e = la::agg_rf_mfma(d, k, v, W, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L, P - 1, P, st);
-            if (e == hipSuccess)
-                e = la::seg_exclusive_scan(ws.ptr, S0, z0, BH, P, d, dv, nullptr, 1, L, st);
+            // as in the plain form: the sums and the initial state in the workspace, each
+            // causal segment adds up the sums before it
+            e = la::agg_rf_mfma(d, k, v, W, ws.ptr, ws.ptr + (long)d * dv, E, E, BH, N, L, P - 1, P,
+                                S0, z0, st);
+            pm = la::PM_SUMS | (S0 ? la::PM_INIT : 0) | (BH % 8 == 0 ? la::PM_XCD : 0);
             preS = ws.ptr;
             prez = ws.ptr + (long)d * dv;
             ps = pzs = E;
         }
         if (e == hipSuccess)
-            e = la::causal_rf_mfma(d, flags, q, k, v, W, out, preS, prez, ps, pzs, S, z, BH, N, L, P,
-                                   st);
+            e = la::causal_rf_mfma(d, flags, q, k, v, W, out, preS, prez, ps, pzs, pm, S, z, BH, N, L,
+                                   P, st);
         const hipError_t ef = ws.finish();
         return e == hipSuccess && ef == hipSuccess ? LA_OK : LA_EHIP;
     }

@@ -19,26 +19,34 @@ constexpr int F_UNNORM = 2;   // out = phi(q)^T S, no division by phi(q)^T z
 // Segment sums dS = phi(K_seg)^T V_seg, dz = phi(K_seg)^T 1 of segments p < nseg of every
 // head, written to dstS + (bh * P + p) * sstride and dstz + (bh * P + p) * zstride.
 // gamma (optional, device [H] float32): per-head decay of the carried state; the sums are then
-// decayed to each segment's last token.
+// decayed to each segment's last token. S0/z0 (optional, with nseg < P): the initial state of
+// every head ([BH, D, D], [BH, D]), copied into slot nseg of the head on the way.
 hipError_t agg_mfma(int D, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int L, int nseg, int P,
-                    const float *gamma, int H, hipStream_t st);
-// Causal outputs of all P segments. Segment p starts from the state at preS/prez +
-// (bh * P + p) * stride (zero state if preS is null). The last segment writes the final
-// state to Sout/zout when they are non-null.
+                    const float *gamma, int H, const float *S0, const float *z0, hipStream_t st);
+// Where the causal kernels find the state before each segment (pm):
+//   0        preS/prez + (bh * P + p) * stride holds it (zero state if preS is null);
+//   PM_SUMS  preS/prez is the workspace written by agg_mfma with nseg = P - 1 (slot stride
+//            pstride == pzstride): segment p adds the sums of segments 0..p-1 itself, in
+//            order, to the initial state in slot P - 1 (PM_INIT) or to zero;
+//   PM_XCD   (with PM_SUMS, BH % 8 == 0) every segment of a head runs on the same XCD, so the
+//            head's sums are fetched into one L2.
+constexpr int PM_SUMS = 1, PM_INIT = 2, PM_XCD = 4;
+// Causal outputs of all P segments. The last segment writes the final state to Sout/zout when
+// they are non-null.
 hipError_t causal_mfma(int D, int flags, const void *q, const void *k, const void *v, void *out,
-                       const float *preS, const float *prez, long pstride, long pzstride,
+                       const float *preS, const float *prez, long pstride, long pzstride, int pm,
                        float *Sout, float *zout, int BH, int N, int L, int P, const float *gamma,
                        int H, hipStream_t st);
 // Random-feature forms of the two: q, k are mapped to exp(W x - |x|^2 / 2) / sqrt(D) while
 // staged (W bf16 [D][D]; m = d = d_v = D); the attention is the identity-map form over them.
 hipError_t agg_rf_mfma(int D, const void *k, const void *v, const void *W, float *dstS, float *dstz,
                        long sstride, long zstride, int BH, int N, int L, int nseg, int P,
-                       hipStream_t st);
+                       const float *S0, const float *z0, hipStream_t st);
 hipError_t causal_rf_mfma(int D, int flags, const void *q, const void *k, const void *v,
                           const void *W, void *out, const float *preS, const float *prez,
-                          long pstride, long pzstride, float *Sout, float *zout, int BH, int N,
-                          int L, int P, hipStream_t st);
+                          long pstride, long pzstride, int pm, float *Sout, float *zout, int BH,
+                          int N, int L, int P, hipStream_t st);
 // Global read: out = phi(Q) S / phi(Q) z for every token, S/z per head ([BH, D, D], [BH, D]).
 hipError_t global_read_mfma(int D, int flags, const void *q, void *out, const float *S,
                             const float *z, int BH, int N, int L, int P, hipStream_t st);

@@ -224,7 +224,9 @@ int la_decode_step_decay(const void *q, const void *k, const void *v, void *out,
  * every call's kernels. The function then waits for the last event and writes the average
  * device time in milliseconds of each phase to ms[0..2]:
  *   ms[0] segment sums (segments 0..P-2), ms[1] exclusive scan over segment states,
- *   ms[2] causal outputs and final state; a phase the call did not launch (P = 1) gets 0.
+ *   ms[2] causal outputs and final state; a phase the call did not launch gets 0 (about 0):
+ *   with P = 1 the first two, on the bf16 matrix-core path (d = d_v in {64, 128}, chunk 64)
+ *   the scan, since each causal segment adds up the sums before it itself.
  *   reps   1..4096; ms host array of 3 floats. reps out of range or ms NULL -> LA_EINVAL.
  * Blocks the calling thread until the work is done; for measurement, not for pipelines.
  * Errors as for la_causal_fwd_ex; a failure while creating or reading events -> LA_EHIP.

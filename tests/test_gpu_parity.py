@@ -331,6 +331,37 @@ def test_state_carry_split(dtype, d, chunk):
     check("prefill+decode", f64(out), oo[:, :, N:], TOL[dtype])
 
 
+@pytest.mark.parametrize("decay", [False, True])
+@pytest.mark.parametrize("B,H,N,seg", [(4, 16, 4096, 256), (3, 3, 2000, 128), (1, 8, 1000, 64)])
+def test_initial_state_in_place_segments(B, H, N, seg, decay):
+    """The initial state passed in S, z, which also receive the final state, with many
+    segments: 1,024 workgroups in the first case, more than the chip runs at once, so a head's
+    last segment may finish (and write the final state) before a later-dispatched segment of
+    the same head starts; every segment must still start from the initial state. B*H = 9
+    takes the plain block order, 64 and 8 the order that keeps a head's segments on one XCD."""
+    d, n0 = 128, 50
+    q, k, v = datagen.qkv(B, H, N + n0, d, d, 2100 + B * H + N, 1 / math.sqrt(d), "bf16")
+    gamma = np.linspace(0.9, 1.0, H) if decay else None
+    _, S0, z0, _, _ = oracle.causal(f64(q[:, :, :n0]), f64(k[:, :, :n0]), f64(v[:, :, :n0]),
+                                    gamma=gamma)
+    S0, z0 = S0.astype(np.float32), z0.astype(np.float32)
+    qb, kb, vb = (x[:, :, n0:].contiguous() for x in (q, k, v))
+    say(f"initial state in place B={B} H={H} N={N} seg_len={seg} decay={decay}")
+    out = torch.empty((B, H, N, d), dtype=qb.dtype, device=DEV)
+    S, z = torch.from_numpy(S0).to(DEV), torch.from_numpy(z0).to(DEV)
+    if decay:
+        g = torch.from_numpy(gamma.astype(np.float32)).to(DEV)
+        la().la_causal_fwd_decay(to_dev(qb), to_dev(kb), to_dev(vb), out, g, S, z, S, z,
+                                 seg_len=seg)
+    else:
+        la().la_causal_fwd(to_dev(qb), to_dev(kb), to_dev(vb), out, S, z, seg_len=seg)
+    torch.cuda.synchronize()
+    oo, So, zo, _, _ = oracle.causal(f64(qb), f64(kb), f64(vb), S0=S0, z0=z0, gamma=gamma)
+    check("out", f64(out), oo, TOL["bf16"])
+    check("S", f64(S), So, TOL["bf16"])
+    check("z", f64(z), zo, TOL["bf16"])
+
+
 def test_bit_reproducible():
     """Fixed reduction order: two runs give identical bytes (causal, global, decode)."""
     q, k, v = datagen.qkv(2, 8, 3000, 128, 128, 21, 1 / math.sqrt(128), "bf16")
