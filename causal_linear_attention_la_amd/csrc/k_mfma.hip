@@ -1004,7 +1004,9 @@ __device__ __forceinline__ void causal_stage(CausalLds<D> &sm, const uint16_t *s
 }
 
 // ------------------------------------------------------------------------------------------
-// Causal outputs of one segment, starting from the state before the segment.
+// Causal outputs of one segment, starting from the state before the segment: one slot of preS,
+// prez per segment, or (PM_SUMS) the head's segment sums, which the compute waves add up
+// (prefix_state) while the stage waves load and stage the segment's first chunks.
 //
 // Two roles share every SIMD. D/16 "compute" waves hold the float32 state S and key sum z in
 // accumulators (16 value columns of S and 16 features of z each) and run the matrix-core
