@@ -79,7 +79,12 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
     if (chunk == 0) {
         pl.mfma = mfma_ok;
         pl.mfma32 = mfma32_ok;
-        pl.chunk = mfma_ok ? 64 : 32;
+        // the vector-ALU kernels' work within a chunk grows with its square (sums over the
+        // chunk's keys per query), which dominates at their head sizes: chunk 16 for the causal
+        // form, 32 for the global read, which has no such sums (measured on MI355X, causal
+        // B=1 H=8 N=4096 d=32 float32 68.4 against 87.1 us, B=4 H=8 N=2048 d=16 47.3 against
+        // 59.2; global B=1 H=8 N=100000 d=32 bf16 578 us at chunk 32 against 638 at 16)
+        pl.chunk = mfma_ok ? 64 : mfma32_ok ? 32 : form == CAUSAL ? 16 : 32;
     } else if (chunk == 64 && mfma_ok) {
         pl.mfma = true;
         pl.chunk = 64;
@@ -112,11 +117,12 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
         // parallelism below that (measured on MI355X, B=4 H=8 N=2048 d=64: 16 segments of 2
         // chunks 27.1 us per call, 8 segments of 4 chunks 24.8 us, both with cold caches).
         // The vector-ALU kernels otherwise keep every segment, except that a sequence of at most
-        // two chunks runs as one segment: one launch instead of three (B=1 H=1 N=64 d=16
-        // float32: 16.5 us per call, against 18.9 us as two segments; with eight chunks, eight
-        // segments take 19.6 us and one 60.0 us).
+        // 64 tokens (or two chunks) runs as one segment: one launch instead of three (B=1 H=1
+        // N=64 d=16 float32: 14.0 us per call at chunk 16 as one segment, 19.7 us as four,
+        // 16.7 us at chunk 32; at N=128, eight segments of one chunk take 20.0 us, one 25.9 us).
         const bool matrix = pl.mfma || pl.mfma32;
-        const long most = !matrix ? (nchunks <= 2 ? 1 : nchunks)
+        const bool short_seq = N <= (64 > 2 * pl.chunk ? 64 : 2 * pl.chunk);
+        const long most = !matrix ? (short_seq ? 1 : nchunks)
                                   : nchunks / kMinChunks > 1 ? nchunks / kMinChunks : 1;
         if (want > most)
             want = most;

@@ -98,9 +98,12 @@ enum { LA_PHI_IDENTITY = 1, LA_UNNORMALIZED = 2 };
  *          both non-NULL: read as the state before token 0 (zero-fill them for a fresh
  *          sequence) and overwritten with the state after token N-1, so a long sequence can
  *          be processed in pieces and handed to la_decode_step. One NULL and one not: LA_EINVAL.
- *   chunk  tokens per intra-chunk tile: 0 lets the library choose; 64 selects the
- *          matrix-core kernel for bf16 with d = d_v in {64, 128}, 32 the float32 matrix-core
- *          kernel for float32 with d = d_v in {64, 128}; otherwise 16, 32, 64 or 128
+ *   chunk  tokens per intra-chunk tile: 0 lets the library choose (64 and the matrix-core
+ *          kernel for bf16 with d = d_v in {64, 128}, 32 and the float32 matrix-core kernel for
+ *          float32 with d = d_v in {64, 128}, else the vector-ALU kernel with chunk 16 for the
+ *          causal forms and 32 for the global form); 64 selects the matrix-core kernel for bf16
+ *          with d = d_v in {64, 128}, 32 the float32 matrix-core kernel for float32 with
+ *          d = d_v in {64, 128}; otherwise 16, 32, 64 or 128
  *          select the vector-ALU kernel (any supported d, d_v, either dtype) when its working
  *          set, 4 (d d_v + d + chunk (2 d + d_v) + chunk^2 + chunk) bytes, fits the 160 KiB of
  *          LDS of a workgroup (chunk 128 at d, d_v <= 32 or so). Other values, or a working set

@@ -241,12 +241,16 @@ def test_workspace_bytes():
     assert la.la_segments(0, 4, 8, 2048, 64, 64) == 8
     assert la.la_workspace_bytes(0, 4, 8, 2048, 64, 64) == 32 * 8 * E64 * 4
     assert la.la_segments(0, 4, 8, 8192, 64, 64) == 16
-    # N=64 float32 on the vector-ALU kernels: chunk 32, and a sequence of two chunks runs as one
-    # segment (no workspace); an explicit seg_len of one chunk gives two segments. N=96 (three
-    # chunks): one chunk per segment, as the vector-ALU kernels keep every segment otherwise
+    # N=64 float32 on the vector-ALU kernels: chunk 16 for the causal form, and a sequence of at
+    # most 64 tokens runs as one segment (no workspace); an explicit seg_len of 32 tokens gives
+    # two segments. N=96 (six chunks): one chunk per segment, as the vector-ALU kernels keep
+    # every segment otherwise; with chunk 32 given, N=64 (two chunks) is still one segment and
+    # the global form keeps chunk 32 (three chunks at N=96)
     assert la.la_segments(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 1
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 0, la.LA_F32) == 0
-    assert la.la_segments(0, 1, 1, 96, 16, 16, 0, 0, la.LA_F32) == 3
+    assert la.la_segments(0, 1, 1, 96, 16, 16, 0, 0, la.LA_F32) == 6
+    assert la.la_segments(0, 1, 1, 64, 16, 16, 32, 0, la.LA_F32) == 1
+    assert la.la_segments(1, 1, 1, 96, 16, 16, 0, 0, la.LA_F32) == 3
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 32, la.LA_F32) == 2 * (16 * 16 + 16) * 4
     assert la.la_workspace_bytes(0, 1, 1, 64, 16, 16, 0, 64, la.LA_F32) == 0
     # float32, d = d_v in {64, 128}: the float32 matrix-core kernels (chunk 32, one causal
