@@ -105,6 +105,59 @@ def test_scratch_under_graph_capture():
 
 
 
+@pytest.mark.parametrize("decay", [False, True])
+def test_graph_capture_initial_state_in_place(decay):
+    """A causal call with the initial state passed in S, z (read, then overwritten with the
+    final state; several segments, so the segment-sum kernel first copies the initial state
+    into the scratch for the causal kernel) captured into a graph. S, z are restored before
+    each replay, with eager calls between the replays: every replay equals the eager call bit
+    for bit, and the eager call matches the oracle."""
+    mod = la()
+    B, H, N, d, n0 = 2, 4, 3000, 128, 64
+    q, k, v = _inputs(B, H, N + n0, d, 520 + decay)
+    gamma = np.linspace(0.95, 1.0, H) if decay else None
+    _, S0, z0, _, _ = oracle.causal(f64(q[:, :, :n0]), f64(k[:, :, :n0]), f64(v[:, :, :n0]),
+                                    gamma=gamma)
+    S0d = torch.from_numpy(S0.astype(np.float32)).to(DEV)
+    z0d = torch.from_numpy(z0.astype(np.float32)).to(DEV)
+    q, k, v = (x[:, :, n0:].contiguous() for x in (q, k, v))
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    g_dev = None if gamma is None else torch.from_numpy(gamma.astype(np.float32)).to(DEV)
+
+    def call(out, S, z):
+        if decay:
+            mod.la_causal_fwd_decay(qd, kd, vd, out, g_dev, S, z, S, z, seg_len=512)
+        else:
+            mod.la_causal_fwd(qd, kd, vd, out, S, z, seg_len=512)
+
+    say(f"graph capture, initial state in place: B={B} H={H} N={N} d={d} seg_len=512 decay={decay}")
+    out_e = torch.empty_like(qd)
+    S_e, z_e = S0d.clone(), z0d.clone()
+    call(out_e, S_e, z_e)
+    torch.cuda.synchronize()
+    oo, So, zo, _, _ = oracle.causal(f64(q), f64(k), f64(v), S0=S0.astype(np.float32),
+                                     z0=z0.astype(np.float32), gamma=gamma)
+    check("eager out", f64(out_e), oo, TOL["bf16"])
+    check("eager S", f64(S_e), So, TOL["bf16"])
+    out_g = torch.empty_like(qd)
+    S_g, z_g = S0d.clone(), z0d.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out_g, S_g, z_g)
+    q2, k2, v2 = (to_dev(x) for x in _inputs(B, H, N, d, 530))
+    for rep in range(3):
+        S_g.copy_(S0d)
+        z_g.copy_(z0d)
+        out_g.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}")
+        assert torch.equal(out_g, out_e), f"replay {rep}: out differs from the eager call"
+        assert torch.equal(S_g, S_e) and torch.equal(z_g, z_e), f"replay {rep}: state differs"
+        _run(mod, q2, k2, v2, 512, S0d, z0d)
+        torch.cuda.synchronize()
+
+
 def test_scratch_host_threads():
     """Four host threads, each with its own stream, enqueue causal calls at the same time (the
     binding releases the interpreter lock during the C call); every result matches the oracle."""
