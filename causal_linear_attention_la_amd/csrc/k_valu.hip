@@ -235,6 +235,101 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
     }
 }
 
+// ---- short sequences ---------------------------------------------------------------------
+// The causal form of a sequence of at most SHORT_N tokens evaluated as one chunk, directly:
+//   out_i = (phi(q_i)^T S0 + sum_{j <= i} (phi(q_i) . phi(k_j)) v_j)
+//           / (phi(q_i) . z0 + sum_{j <= i} phi(q_i) . phi(k_j))
+// -- the chunked evaluation with the whole sequence as its one chunk ("Linear Attention: From
+// Pairwise Reads to a Recurrent State", section "A recurrence need not force token-serial
+// training": the state from before the chunk plus the pairwise reads inside it) -- followed by
+// the final state S0 + phi(K)^T V, z0 + phi(K)^T 1. One workgroup of 256 threads per head:
+// thread (i, part) keeps phi(q_i) in registers and accumulates the value columns
+// [part DV/4, (part + 1) DV/4) of row i, reading each key row from LDS together with the other
+// lanes of its wave (one address: a broadcast). No decay (the decayed form keeps the chunked
+// kernel). Against the chunked kernel there are no per-chunk phases and barriers: B=1 H=1 N=64
+// d=16 float32 takes 9.8 us per call against 13.5 us with four 16-token chunks (MI355X).
+constexpr int SHORT_N = 64;
+
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(NT) void k_short(const T *__restrict__ q, const T *__restrict__ k,
+                                              const T *__restrict__ v, T *__restrict__ out,
+                                              const float *__restrict__ S0,
+                                              const float *__restrict__ z0,
+                                              float *__restrict__ Sout, float *__restrict__ zout,
+                                              int N, int flags)
+{
+    static_assert(NT == 4 * SHORT_N, "one thread per (row, quarter of the value columns)");
+    constexpr int CW = DV / 4;
+    __shared__ float sK[SHORT_N][D], sV[SHORT_N][DV], sS[D * DV], sz[D];
+    const bool ident = flags & F_IDENTITY, norm = !(flags & F_UNNORM);
+    const int tid = threadIdx.x, i = tid >> 2, c0 = (tid & 3) * CW;
+    const size_t bh = blockIdx.x;
+    const T *qb = q + bh * N * D, *kb = k + bh * N * D, *vb = v + bh * N * DV;
+
+    for (int e = tid; e < N * D; e += NT)
+        sK[e / D][e % D] = feature(Elem<T>::ld(kb, e), ident);
+    for (int e = tid; e < N * DV; e += NT)
+        sV[e / DV][e % DV] = Elem<T>::ld(vb, e);
+    for (int e = tid; e < D * DV; e += NT)
+        sS[e] = S0 ? S0[bh * D * DV + e] : 0.f;
+    for (int f = tid; f < D; f += NT)
+        sz[f] = S0 ? z0[bh * D + f] : 0.f;
+    float qf[D];
+    const int ir = min(i, N - 1); // rows past the end compute on the last row and store nothing
+#pragma unroll
+    for (int f = 0; f < D; ++f)
+        qf[f] = feature(Elem<T>::ld(qb, (size_t)ir * D + f), ident);
+    __syncthreads();
+
+    // the state before the sequence
+    float num[CW], den = 0.f;
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+        num[c] = 0.f;
+#pragma unroll
+    for (int f = 0; f < D; ++f) {
+        den = fmaf(qf[f], sz[f], den);
+#pragma unroll
+        for (int c = 0; c < CW; ++c)
+            num[c] = fmaf(qf[f], sS[f * DV + c0 + c], num[c]);
+    }
+    // the pairs j <= i (keys past the wave's last row add nothing to any of its rows)
+    const int jend = min(N, (tid / 64) * 16 + 16);
+#pragma unroll 4
+    for (int j = 0; j < jend; ++j) {
+        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+        for (int f = 0; f < D; f += 2) {
+            a0 = fmaf(qf[f], sK[j][f], a0);
+            a1 = fmaf(qf[f + 1], sK[j][f + 1], a1);
+        }
+        const float a = j <= i ? a0 + a1 : 0.f;
+        den += a;
+#pragma unroll
+        for (int c = 0; c < CW; ++c)
+            num[c] = fmaf(a, sV[j][c0 + c], num[c]);
+    }
+    if (i < N)
+#pragma unroll
+        for (int c = 0; c < CW; ++c)
+            Elem<T>::st(out, (bh * N + i) * DV + c0 + c, norm ? num[c] / den : num[c]);
+    if (Sout) {
+        for (int e = tid; e < D * DV; e += NT) {
+            const int f = e / DV, c = e % DV;
+            float s = sS[e];
+            for (int j = 0; j < N; ++j)
+                s = fmaf(sK[j][f], sV[j][c], s);
+            Sout[bh * D * DV + e] = s;
+        }
+        for (int f = tid; f < D; f += NT) {
+            float s = sz[f];
+            for (int j = 0; j < N; ++j)
+                s += sK[j][f];
+            zout[bh * D + f] = s;
+        }
+    }
+}
+
 } // namespace
 
 hipError_t agg_valu(bool bf16, int flags, const void *k, const void *v, float *dstS, float *dstz,
@@ -288,6 +383,34 @@ hipError_t out_valu(bool bf16, bool causal, int flags, const void *q, const void
                   : (causal ? out_valu_t<float, true> : out_valu_t<float, false>);
     return f(flags, q, k, v, out, preS, prez, pstride, pzstride, pslots, Sout, zout, BH, N, d, dv, chunk,
              L, P, gamma, H, st);
+}
+
+bool short_ok(int N, int d, int dv)
+{
+    return N >= 1 && N <= SHORT_N && (d == 16 || d == 32) && (dv == 16 || dv == 32);
+}
+
+hipError_t short_causal(bool bf16, int flags, const void *q, const void *k, const void *v, void *out,
+                        const float *S0, const float *z0, float *S, float *z, int BH, int N, int d,
+                        int dv, hipStream_t st)
+{
+    if (!short_ok(N, d, dv))
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)BH), block(NT);
+#define LA_SH(TT, DD, VV)                                                                          \
+    if (d == DD && dv == VV) {                                                                     \
+        hipLaunchKernelGGL((k_short<TT, DD, VV>), grid, block, 0, st, static_cast<const TT *>(q),    \
+                           static_cast<const TT *>(k), static_cast<const TT *>(v),                 \
+                           static_cast<TT *>(out), S0, z0, S, z, N, flags);                        \
+        return hipGetLastError();                                                                  \
+    }
+    if (bf16) {
+        LA_SH(bf16_t, 16, 16) LA_SH(bf16_t, 16, 32) LA_SH(bf16_t, 32, 16) LA_SH(bf16_t, 32, 32)
+    } else {
+        LA_SH(float, 16, 16) LA_SH(float, 16, 32) LA_SH(float, 32, 16) LA_SH(float, 32, 32)
+    }
+#undef LA_SH
+    return hipErrorInvalidValue;
 }
 
 // Largest dynamic LDS the vector-ALU kernels take (d = d_v = 128, chunk 32): 118,912 bytes.

@@ -44,6 +44,7 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 struct Plan {
     bool mfma;  // bf16 matrix-core family
     bool mfma32; // float32 matrix-core family
+    bool shortseq; // causal, one segment of at most 64 tokens: the one-chunk kernel (no decay)
     int chunk;  // tokens per chunk
     int L;      // tokens per segment
     int P;      // segments per head
@@ -129,6 +130,10 @@ int make_plan(Form form, int B, int H, int N, int d, int dv, int chunk, int seg_
         pl.L = (int)((nchunks + want - 1) / want) * pl.chunk;
     }
     pl.P = (int)((N + (long)pl.L - 1) / pl.L);
+    // a short sequence in one segment, chunk left to the library: the whole sequence as one
+    // chunk, evaluated directly (see k_short)
+    pl.shortseq = form == CAUSAL && chunk == 0 && !pl.mfma && !pl.mfma32 && pl.P == 1 &&
+                  la::short_ok(N, d, dv);
     if ((size_t)pl.P * BH > (size_t)INT32_MAX / 8)
         return LA_ENOTSUP;
     const size_t E = (size_t)d * dv + d;
@@ -480,8 +485,10 @@ int run_causal(const void *q, const void *k, const void *v, void *out, const flo
                                       L, P, gamma, H, st)
             : pl.mfma32 ? la::causal_mfma32(d, flags, q, k, v, out, preS, prez, ps, pzs, S, z, BH, N,
                                         L, P, gamma, H, st)
-                    : la::out_valu(bf16, true, flags, q, k, v, out, preS, prez, ps, pzs,
-                                   P > 1 ? P : 1, S, z, BH, N, d, dv, pl.chunk, L, P, gamma, H, st);
+            : pl.shortseq && !gamma
+                ? la::short_causal(bf16, flags, q, k, v, out, S0, z0, S, z, BH, N, d, dv, st)
+                : la::out_valu(bf16, true, flags, q, k, v, out, preS, prez, ps, pzs, P > 1 ? P : 1, S,
+                               z, BH, N, d, dv, pl.chunk, L, P, gamma, H, st);
     if (e == hipSuccess)
         e = mark(ts, 3, st);
     return e == hipSuccess ? LA_OK : LA_EHIP;

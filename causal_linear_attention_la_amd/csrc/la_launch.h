@@ -78,6 +78,13 @@ hipError_t out_valu(bool bf16, bool causal, int flags, const void *q, const void
 
 // Dynamic LDS bytes of the vector-ALU kernels for this shape.
 size_t valu_lds_bytes(int d, int dv, int chunk);
+// The causal form of a short sequence (short_ok: N <= 64, d and d_v in {16, 32}) as one chunk, one
+// workgroup per head, no decay: out, and the final state into S, z when S is non-null; S0, z0
+// (optional, may be S, z) the state before token 0.
+bool short_ok(int N, int d, int dv);
+hipError_t short_causal(bool bf16, int flags, const void *q, const void *k, const void *v, void *out,
+                        const float *S0, const float *z0, float *S, float *z, int BH, int N, int d,
+                        int dv, hipStream_t st);
 
 // ---- segment joins -----------------------------------------------------------------------
 // In place: slots 0..P-2 hold segment sums on entry; on return slot p (0..P-1) holds the

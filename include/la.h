@@ -101,7 +101,8 @@ enum { LA_PHI_IDENTITY = 1, LA_UNNORMALIZED = 2 };
  *   chunk  tokens per intra-chunk tile: 0 lets the library choose (64 and the matrix-core
  *          kernel for bf16 with d = d_v in {64, 128}, 32 and the float32 matrix-core kernel for
  *          float32 with d = d_v in {64, 128}, else the vector-ALU kernel with chunk 16 for the
- *          causal forms and 32 for the global form); 64 selects the matrix-core kernel for bf16
+ *          causal forms -- a sequence of at most 64 tokens with d, d_v in {16, 32} and no decay
+ *          as one chunk -- and 32 for the global form); 64 selects the matrix-core kernel for bf16
  *          with d = d_v in {64, 128}, 32 the float32 matrix-core kernel for float32 with
  *          d = d_v in {64, 128}; otherwise 16, 32, 64 or 128
  *          select the vector-ALU kernel (any supported d, d_v, either dtype) when its working
