@@ -162,6 +162,9 @@ def time_flushed(fn, reps, flush_bytes=512 << 20):
     return sum(a.elapsed_time(b) for a, b in evs) / reps
 
 
+GRAPH_CALLS = 20
+
+
 def bench_causal_small(args, n):
     """Causal workloads 1 (B=1 H=1 N=64 d=16 float32, the vector-ALU kernels) and 2 (B=4 H=8
     N=2048 d=64 bf16, chunk 64: the d = 64 matrix-core kernels), through la_causal_fwd_ws from
@@ -187,10 +190,22 @@ def bench_causal_small(args, n):
 
     ms_hot, _ = time_calls(call, args.steps, args.warmup)
     ms_flushed = time_flushed(call, max(10, args.steps // 4))
+    # the same call replayed from a HIP graph (GRAPH_CALLS calls per graph, kernel nodes only):
+    # the device time per call without the host's per-call cost (argument checks, launch),
+    # which a call this small is otherwise bound by
+    graph = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(graph, stream=gs):
+            for _ in range(GRAPH_CALLS):
+                call()
+    torch.cuda.synchronize()
+    ms_graph = time_calls(lambda i: graph.replay(), max(10, args.steps // 2), 2)[0] / GRAPH_CALLS
     kern = la.la_causal_fwd_profiled(q, k, v, out, None, None, S, z, chunk=w.chunk,
                                      reps=args.steps)
     P = la.la_segments(0, w.B, w.H, w.N, w.d, w.dv, w.chunk, 0, code)
-    return w, ms_hot, ms_flushed, kern, P
+    return w, ms_hot, ms_flushed, ms_graph, kern, P
 
 
 def bench_decode(args):
@@ -662,9 +677,9 @@ def main():
         if args.copycal:
             copy_calibration()
         for n in (1, 2):
-            wn, hot, flushed, kern_n, _ = bench_causal_small(args, n)
-            print(f"workload {n} ({wn.name}): hot {hot * 1e3:.1f} us, flushed {flushed * 1e3:.1f} us",
-                  flush=True)
+            wn, hot, flushed, graph_ms, kern_n, _ = bench_causal_small(args, n)
+            print(f"workload {n} ({wn.name}): hot {hot * 1e3:.1f} us, flushed {flushed * 1e3:.1f} us, "
+                  f"graph-replayed {graph_ms * 1e3:.1f} us", flush=True)
         return
     if args.only:
         if args.copycal:
@@ -711,9 +726,10 @@ def main():
           flush=True)
     small = {}
     for n in (1, 2):
-        wn, hot, flushed, kern_n, P_n = bench_causal_small(args, n)
-        small[n] = (wn, hot, flushed, kern_n, P_n)
-        print(f"workload {n} ({wn.name}): hot {hot * 1e3:.1f} us, flushed {flushed * 1e3:.1f} us; "
+        wn, hot, flushed, graph_ms, kern_n, P_n = bench_causal_small(args, n)
+        small[n] = (wn, hot, flushed, graph_ms, kern_n, P_n)
+        print(f"workload {n} ({wn.name}): hot {hot * 1e3:.1f} us, flushed {flushed * 1e3:.1f} us, "
+              f"graph-replayed {graph_ms * 1e3:.1f} us; "
               "kernels " + ", ".join(f"{name} {t:.1f}" for name, t in
                                      kernels_us(kern_n, P_n, wn.dtype != "bf16").items())
               + " us", file=sys.stderr, flush=True)
@@ -809,13 +825,16 @@ def main():
         "wall_s_timed_region": wall,
     }
     workloads = {}
-    for n, (wn, hot, flushed, kern_n, P_n) in small.items():
+    for n, (wn, hot, flushed, graph_ms, kern_n, P_n) in small.items():
         th_n = wn.B * wn.H * wn.N
         es = 2 if wn.dtype == "bf16" else 4
         byts_n = algo_prefill(wn.B, wn.H, wn.N, wn.d, wn.dv, es)[0]
         entry = {"form": "causal", "dtype": wn.dtype, "chunk": wn.chunk or None,
                  "segments_per_head": P_n, "entry_point": "la_causal_fwd_ws",
                  "us_per_call_hot": hot * 1e3, "us_per_call_flushed": flushed * 1e3,
+                 # device time per call with the host's per-call cost taken out (replayed from a
+                 # HIP graph of GRAPH_CALLS calls)
+                 "us_per_call_graph": graph_ms * 1e3,
                  "token_heads_per_s_flushed": th_n / (flushed * 1e-3),
                  "kernels_us": kernels_us(kern_n, P_n, wn.dtype != "bf16"),
                  "algorithmic_bytes_per_call": byts_n,
