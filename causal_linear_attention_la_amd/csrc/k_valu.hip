@@ -1,7 +1,9 @@
 // k_valu.hip -- vector-ALU kernels of liblinattn for the shapes the matrix-core kernels do not
 // take: float32 inputs (all arithmetic stays in float32) and any d, d_v in {16, 32, 64, 128}
 // with either input dtype. One workgroup of 256 threads per (segment, head); the float32
-// state of the head lives in LDS; chunks of CH in {16, 32} tokens.
+// state of the head lives in LDS; chunks of CH in {16, 32} tokens (64 and 128 when asked for).
+// A short causal sequence (at most 64 tokens, d and d_v in {16, 32}, no decay) takes k_short
+// instead, the whole sequence as one chunk (at the end of this file).
 //
 // Per chunk, with Qf = phi(Q_c), Kf = phi(K_c) and the state S, z before the chunk:
 //   A[i][j] = Qf_i . Kf_j for j <= i (inclusive causal mask), 0 otherwise
