@@ -121,20 +121,33 @@ __global__ __launch_bounds__(NT) void k_seg_total(const float *__restrict__ ws, 
         *reinterpret_cast<f32x4 *>(z + (size_t)bh * d + (e - d * dv)) = run;
 }
 
-// One head per workgroup. Thread layout over the [D, DV] state: CG = DV/4 column groups of 4
-// floats, RP = 256/CG row phases; thread (rp, cg) owns rows rp, rp+RP, ... of columns
-// 4cg..4cg+3.
+// One workgroup per head. Thread layout over the [D, DV] state: CG = DV/4 column groups of 4
+// floats, RP row phases; thread (rp, cg) owns rows rp, rp+RP, ... of columns 4cg..4cg+3. RP is
+// D/4 (four rows per thread), at least one wave and at most 1024 threads in all: at
+// d = d_v = 128 that is sixteen waves per head, which keep more of the state's loads in flight per
+// CU than four (measured on MI355X, 256 x 32 heads: 186.0 -> 176.9 us per step; 512 threads:
+// 183.8 us), while at d = d_v = 64 one row per thread over 1024 threads was slower than four rows
+// over 256 (512 x 64 heads: 4.17 against 3.83 us).
+template <int D, int DV> struct DecCfg {
+    static constexpr int CG = DV / 4;
+    static constexpr int RPW = D / 4 > 64 / CG ? D / 4 : 64 / CG;
+    static constexpr int RP = 1024 / CG < RPW ? 1024 / CG : RPW;
+    static constexpr int THREADS = CG * RP;
+    static constexpr int RPT = (D + RP - 1) / RP;
+    static_assert(THREADS % 64 == 0 && THREADS >= D && THREADS >= DV, "decode block");
+};
+
 template <typename T, int D, int DV>
-__global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T *__restrict__ k,
-                                               const T *__restrict__ v, T *__restrict__ out,
-                                               float *__restrict__ S, float *__restrict__ z,
-                                               int flags, const float *__restrict__ gamma, int H)
+__global__ __launch_bounds__((DecCfg<D, DV>::THREADS)) void k_decode(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v, T *__restrict__ out,
+    float *__restrict__ S, float *__restrict__ z, int flags, const float *__restrict__ gamma, int H)
 {
     const bool ident = flags & F_IDENTITY;
-    constexpr int CG = DV / 4, RP = NT / CG, RPT = (D + RP - 1) / RP;
+    using G = DecCfg<D, DV>;
+    constexpr int CG = G::CG, RP = G::RP, RPT = G::RPT, NTH = G::THREADS;
     __shared__ float skf[D], sqf[D];
     __shared__ float red[RP][DV + 4];
-    __shared__ float sden[NT / 64];
+    __shared__ float sden[NTH / 64];
 
     const int tid = threadIdx.x, cg = tid % CG, rp = tid / CG;
     const size_t bh = blockIdx.x;
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(NT) void k_decode(const T *__restrict__ q, const T 
             num += red[i][tid];
         float den = 0.f;
 #pragma unroll
-        for (int w = 0; w < NT / 64; ++w)
+        for (int w = 0; w < NTH / 64; ++w)
             den += sden[w];
         Elem<T>::st(out, bh * DV + tid, (flags & F_UNNORM) ? num : num / den);
     }
@@ -206,14 +219,14 @@ template <typename T>
 hipError_t decode_t(int flags, const void *q, const void *k, const void *v, void *out, float *S,
                     float *z, int BH, int d, int dv, const float *gamma, int H, hipStream_t st)
 {
-    const dim3 grid((unsigned)BH), block(NT);
+    const dim3 grid((unsigned)BH);
     const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
             *vv = static_cast<const T *>(v);
     T *oo = static_cast<T *>(out);
 #define LA_DEC(DD, VV)                                                                          \
     if (d == DD && dv == VV) {                                                                  \
-        hipLaunchKernelGGL((k_decode<T, DD, VV>), grid, block, 0, st, qq, kk, vv, oo, S, z, flags, \
-                           gamma, H);                                                           \
+        hipLaunchKernelGGL((k_decode<T, DD, VV>), grid, dim3(DecCfg<DD, VV>::THREADS), 0, st, qq, kk, \
+                           vv, oo, S, z, flags, gamma, H);                                      \
         return hipGetLastError();                                                               \
     }
 #define LA_DEC_ROW(DD) LA_DEC(DD, 16) LA_DEC(DD, 32) LA_DEC(DD, 64) LA_DEC(DD, 128)
