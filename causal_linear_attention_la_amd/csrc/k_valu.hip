@@ -1,6 +1,6 @@
 // k_valu.hip -- vector-ALU kernels of liblinattn for the shapes the matrix-core kernels do not
 // take: float32 inputs (all arithmetic stays in float32) and any d, d_v in {16, 32, 64, 128}
-// with either input dtype. One workgroup of 256 threads per (segment, head); the float32
+// with either input dtype. One workgroup of 512 or 1024 threads per (segment, head); the float32
 // state of the head lives in LDS; chunks of CH in {16, 32} tokens (64 and 128 when asked for).
 // A short causal sequence (at most 64 tokens, d and d_v in {16, 32}, no decay) takes k_short
 // instead, the whole sequence as one chunk (at the end of this file).
@@ -23,7 +23,13 @@
 namespace la {
 namespace {
 
-constexpr int NT = 256;
+// Threads of the chunked kernels' workgroups: 1024 for heads with d d_v >= 4096, 512 below
+// (measured on MI355X against 256: causal B=1 H=4 N=1024 d=128 float32 at chunk 16 128.0 ->
+// 74.8 us; B=1 H=8 N=4096 d=32 68.2 -> 60.0 us at 512 and 68.6 at 1024; B=2 H=4 N=1024 d=16
+// d_v=64 32.8 -> 30.3 at 512 and 33.3 at 1024).
+__host__ __device__ constexpr int valu_threads(int d, int dv) { return d * dv >= 4096 ? 1024 : 512; }
+// threads of the short-sequence kernel: one per (row, quarter of the value columns)
+constexpr int SNT = 256;
 
 // The sum s + term(0) + ... + term(n - 1) in increasing order, n a multiple of 16 (every head
 // size and chunk is): blocks of 16 terms are unrolled so that their LDS reads leave together
@@ -65,7 +71,7 @@ struct Lay {
     }
 };
 
-template <typename T>
+template <typename T, int NT>
 __global__ __launch_bounds__(NT) void k_agg_valu(const T *__restrict__ k, const T *__restrict__ v,
                                                  float *__restrict__ dstS,
                                                  float *__restrict__ dstz, long sstride,
@@ -129,7 +135,7 @@ __global__ __launch_bounds__(NT) void k_agg_valu(const T *__restrict__ k, const 
         dstz[((long)bh * P + p) * zstride + f] = sz[f];
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, int NT>
 __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const T *__restrict__ k,
                                                  const T *__restrict__ v, T *__restrict__ out,
                                                  const float *__restrict__ preS,
@@ -253,14 +259,14 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
 constexpr int SHORT_N = 64;
 
 template <typename T, int D, int DV>
-__global__ __launch_bounds__(NT) void k_short(const T *__restrict__ q, const T *__restrict__ k,
+__global__ __launch_bounds__(SNT) void k_short(const T *__restrict__ q, const T *__restrict__ k,
                                               const T *__restrict__ v, T *__restrict__ out,
                                               const float *__restrict__ S0,
                                               const float *__restrict__ z0,
                                               float *__restrict__ Sout, float *__restrict__ zout,
                                               int N, int flags)
 {
-    static_assert(NT == 4 * SHORT_N, "one thread per (row, quarter of the value columns)");
+    static_assert(SNT == 4 * SHORT_N, "one thread per (row, quarter of the value columns)");
     constexpr int CW = DV / 4;
     __shared__ float sK[SHORT_N][D], sV[SHORT_N][DV], sS[D * DV], sz[D];
     const bool ident = flags & F_IDENTITY, norm = !(flags & F_UNNORM);
@@ -268,13 +274,13 @@ __global__ __launch_bounds__(NT) void k_short(const T *__restrict__ q, const T *
     const size_t bh = blockIdx.x;
     const T *qb = q + bh * N * D, *kb = k + bh * N * D, *vb = v + bh * N * DV;
 
-    for (int e = tid; e < N * D; e += NT)
+    for (int e = tid; e < N * D; e += SNT)
         sK[e / D][e % D] = feature(Elem<T>::ld(kb, e), ident);
-    for (int e = tid; e < N * DV; e += NT)
+    for (int e = tid; e < N * DV; e += SNT)
         sV[e / DV][e % DV] = Elem<T>::ld(vb, e);
-    for (int e = tid; e < D * DV; e += NT)
+    for (int e = tid; e < D * DV; e += SNT)
         sS[e] = S0 ? S0[bh * D * DV + e] : 0.f;
-    for (int f = tid; f < D; f += NT)
+    for (int f = tid; f < D; f += SNT)
         sz[f] = S0 ? z0[bh * D + f] : 0.f;
     float qf[D];
     const int ir = min(i, N - 1); // rows past the end compute on the last row and store nothing
@@ -316,14 +322,14 @@ __global__ __launch_bounds__(NT) void k_short(const T *__restrict__ q, const T *
         for (int c = 0; c < CW; ++c)
             Elem<T>::st(out, (bh * N + i) * DV + c0 + c, norm ? num[c] / den : num[c]);
     if (Sout) {
-        for (int e = tid; e < D * DV; e += NT) {
+        for (int e = tid; e < D * DV; e += SNT) {
             const int f = e / DV, c = e % DV;
             float s = sS[e];
             for (int j = 0; j < N; ++j)
                 s = fmaf(sK[j][f], sV[j][c], s);
             Sout[bh * D * DV + e] = s;
         }
-        for (int f = tid; f < D; f += NT) {
+        for (int f = tid; f < D; f += SNT) {
             float s = sz[f];
             for (int j = 0; j < N; ++j)
                 s += sK[j][f];
@@ -334,42 +340,44 @@ __global__ __launch_bounds__(NT) void k_short(const T *__restrict__ q, const T *
 
 } // namespace
 
+template <typename T, int NT>
+hipError_t agg_valu_t(int flags, const void *k, const void *v, float *dstS, float *dstz,
+                      long sstride, long zstride, int BH, int N, int d, int dv, int chunk, int L,
+                      int nseg, int P, const float *gamma, int H, hipStream_t st)
+{
+    const size_t lds = sizeof(float) * Lay(d, dv, chunk).total;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_agg_valu<T, NT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((k_agg_valu<T, NT>), dim3((unsigned)(BH * nseg)), dim3(NT), lds, st,
+                       static_cast<const T *>(k), static_cast<const T *>(v), dstS, dstz, sstride,
+                       zstride, N, d, dv, chunk, L, nseg, P, flags, gamma, H);
+    return hipGetLastError();
+}
+
 hipError_t agg_valu(bool bf16, int flags, const void *k, const void *v, float *dstS, float *dstz,
                     long sstride, long zstride, int BH, int N, int d, int dv, int chunk, int L,
                     int nseg, int P, const float *gamma, int H, hipStream_t st)
 {
-    const Lay lay(d, dv, chunk);
-    const size_t lds = sizeof(float) * lay.total;
-    const dim3 grid((unsigned)(BH * nseg)), block(NT);
-    hipError_t e = bf16 ? hipFuncSetAttribute(reinterpret_cast<const void *>(k_agg_valu<bf16_t>),
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
-                        : hipFuncSetAttribute(reinterpret_cast<const void *>(k_agg_valu<float>),
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess)
-        return e;
-    if (bf16)
-        hipLaunchKernelGGL(k_agg_valu<bf16_t>, grid, block, lds, st, static_cast<const bf16_t *>(k),
-                           static_cast<const bf16_t *>(v), dstS, dstz, sstride, zstride, N, d, dv,
-                           chunk, L, nseg, P, flags, gamma, H);
-    else
-        hipLaunchKernelGGL(k_agg_valu<float>, grid, block, lds, st, static_cast<const float *>(k),
-                           static_cast<const float *>(v), dstS, dstz, sstride, zstride, N, d, dv,
-                           chunk, L, nseg, P, flags, gamma, H);
-    return hipGetLastError();
+    const bool big = valu_threads(d, dv) == 1024;
+    auto f = bf16 ? (big ? agg_valu_t<bf16_t, 1024> : agg_valu_t<bf16_t, 512>)
+                  : (big ? agg_valu_t<float, 1024> : agg_valu_t<float, 512>);
+    return f(flags, k, v, dstS, dstz, sstride, zstride, BH, N, d, dv, chunk, L, nseg, P, gamma, H, st);
 }
 
-template <typename T, bool CAUSAL>
+template <typename T, bool CAUSAL, int NT>
 hipError_t out_valu_t(int flags, const void *q, const void *k, const void *v, void *out, const float *preS,
                       const float *prez, long pstride, long pzstride, int pslots, float *Sout,
                       float *zout, int BH, int N, int d, int dv, int chunk, int L, int P,
                       const float *gamma, int H, hipStream_t st)
 {
     const size_t lds = sizeof(float) * Lay(d, dv, chunk).total;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_out_valu<T, CAUSAL>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k_out_valu<T, CAUSAL, NT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((k_out_valu<T, CAUSAL>), dim3((unsigned)(BH * P)), dim3(NT), lds, st,
+    hipLaunchKernelGGL((k_out_valu<T, CAUSAL, NT>), dim3((unsigned)(BH * P)), dim3(NT), lds, st,
                        static_cast<const T *>(q), static_cast<const T *>(k),
                        static_cast<const T *>(v), static_cast<T *>(out), preS, prez, pstride,
                        pzstride, pslots, Sout, zout, N, d, dv, chunk, L, P, flags, gamma, H);
@@ -381,8 +389,11 @@ hipError_t out_valu(bool bf16, bool causal, int flags, const void *q, const void
                     long pzstride, int pslots, float *Sout, float *zout, int BH, int N, int d,
                     int dv, int chunk, int L, int P, const float *gamma, int H, hipStream_t st)
 {
-    auto f = bf16 ? (causal ? out_valu_t<bf16_t, true> : out_valu_t<bf16_t, false>)
-                  : (causal ? out_valu_t<float, true> : out_valu_t<float, false>);
+    const bool big = valu_threads(d, dv) == 1024;
+    auto f = bf16 ? (causal ? (big ? out_valu_t<bf16_t, true, 1024> : out_valu_t<bf16_t, true, 512>)
+                            : (big ? out_valu_t<bf16_t, false, 1024> : out_valu_t<bf16_t, false, 512>))
+                  : (causal ? (big ? out_valu_t<float, true, 1024> : out_valu_t<float, true, 512>)
+                            : (big ? out_valu_t<float, false, 1024> : out_valu_t<float, false, 512>));
     return f(flags, q, k, v, out, preS, prez, pstride, pzstride, pslots, Sout, zout, BH, N, d, dv, chunk,
              L, P, gamma, H, st);
 }
@@ -398,7 +409,7 @@ hipError_t short_causal(bool bf16, int flags, const void *q, const void *k, cons
 {
     if (!short_ok(N, d, dv))
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)BH), block(NT);
+    const dim3 grid((unsigned)BH), block(SNT);
 #define LA_SH(TT, DD, VV)                                                                          \
     if (d == DD && dv == VV) {                                                                     \
         hipLaunchKernelGGL((k_short<TT, DD, VV>), grid, block, 0, st, static_cast<const TT *>(q),    \
