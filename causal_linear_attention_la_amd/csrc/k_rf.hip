@@ -36,8 +36,8 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int M>
-__global__ __launch_bounds__(256) void k_rf_mfma(const uint16_t *__restrict__ x,
+template <int D, int M, int NTH>
+__global__ __launch_bounds__(NTH) void k_rf_mfma(const uint16_t *__restrict__ x,
                                                  const uint16_t *__restrict__ W,
                                                  uint16_t *__restrict__ f, long rows,
                                                  float neg_half_log2m)
@@ -47,14 +47,15 @@ __global__ __launch_bounds__(256) void k_rf_mfma(const uint16_t *__restrict__ x,
     constexpr float LOG2E = 1.44269504088896341f;
     constexpr int FS = M + 8;       // row stride (elements) of a wave's feature tile
     constexpr int LPR = M / 8;      // lanes per row when a tile is stored (16 bytes each)
+    constexpr int NW = NTH / 64;    // waves per workgroup
     __shared__ __attribute__((aligned(16))) uint16_t sW[M * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sF[4][16 * FS];
+    __shared__ __attribute__((aligned(16))) uint16_t sF[NW][16 * FS];
     const int tid = threadIdx.x, l = tid & 63, li = l & 15, g = l >> 4;
     uint16_t *tileF = sF[tid >> 6];
 
     const long ntile = (rows + 15) / 16;
-    const long nwave = (long)gridDim.x * 4;
-    const long w0 = (long)blockIdx.x * 4 + (tid >> 6);
+    const long nwave = (long)gridDim.x * NW;
+    const long w0 = (long)blockIdx.x * NW + (tid >> 6);
     // B operand of a 16-row tile: row 16 t + li (clamped to the last row: every load is in
     // bounds), k-slots 8g..8g+7 of block kk
     auto load = [&](u32x4 (&dst)[NKB], long t) {
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(256) void k_rf_mfma(const uint16_t *__restrict__ x,
     load(xb, min(w0, ntile - 1));
     // W (row-major [M][D]) -> LDS in fragment order: granule (row r, columns 8c..8c+7) is lane
     // (c % 4) * 16 + (row of r in its tile) of fragment (tile of r, kk = c / 4)
-    for (int e = tid; e < M * D / 8; e += 256) {
+    for (int e = tid; e < M * D / 8; e += NTH) {
         const int r = e / (D / 8), c = e % (D / 8);
         // projection r = (M/4) g + 4 mt + j sits in row 4g + j of tile mt, so that lane group g
         // of the product holds the M/4 consecutive features (M/4) g .. of its row
@@ -168,17 +169,27 @@ __global__ __launch_bounds__(256) void k_rf_generic(const T *__restrict__ x, con
     }
 }
 
+// Waves per workgroup: 4, or 8 where W takes more than 32 KiB of LDS. With the larger W only
+// one workgroup fits a CU (W plus one 16-row feature tile per wave), and 8 waves keep as many
+// row loads in flight as two 4-wave workgroups do on the other shapes: measured on MI355X at
+// d = 128, m = 256 over 2 x 16 x 8192 rows, 44 us with 8 waves against 57 with 4 (at m = 128 a
+// second 8-wave workgroup per CU gained nothing: 26.5 against 25.7 us).
+template <int D, int M> constexpr int rf_threads() { return M * D * 2 > 32768 ? 512 : 256; }
+
 template <int D, int M>
 void launch_rf(const void *x, const void *W, void *f, long rows, hipStream_t st)
 {
-    // workgroups: two per CU (one when W takes more than 32 KiB of LDS). Every workgroup copies
+    // workgroups: as many as fit the CUs at once, at most two per CU. Every workgroup copies
     // W from L2 first, all at the same time; measured on MI355X (d = m = 128), more workgroups
     // than this make the copies cost more than the extra waves bring.
+    constexpr int NTH = rf_threads<D, M>();
+    constexpr long LDS = (long)M * D * 2 + (NTH / 64) * 16L * (M + 8) * 2;
+    static_assert(LDS <= 160 * 1024, "feature kernel LDS");
     const long ntile = (rows + 15) / 16;
-    const long cap = 256L * (M * D * 2 > 32768 ? 1 : 2);
-    const long want = (ntile + 3) / 4;
+    const long cap = 256L * (2 * LDS <= 160 * 1024 ? 2 : 1);
+    const long want = (ntile + NTH / 64 - 1) / (NTH / 64);
     const unsigned grid = (unsigned)(want < cap ? want : cap);
-    hipLaunchKernelGGL((k_rf_mfma<D, M>), dim3(grid), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_rf_mfma<D, M, NTH>), dim3(grid), dim3(NTH), 0, st,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(W),
                        static_cast<uint16_t *>(f), rows, -0.5f * log2f((float)M));
 }
