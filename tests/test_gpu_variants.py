@@ -229,7 +229,9 @@ def check_rf(got, want, dtype):
     ("f32", 32, 48, 100), ("f32", 128, 128, 77), ("f32", 7, 5, 33),
     # enough rows for the full grid (two 4-wave workgroups per CU at m = 128, one 8-wave
     # workgroup per CU at m = 256) with several 16-row tiles per wave and a ragged last tile
-    ("bf16", 128, 128, 40003), ("bf16", 128, 256, 40003)])
+    ("bf16", 128, 128, 40003), ("bf16", 128, 256, 40003),
+    # one partial tile for the 8-wave workgroup: seven of its waves find no tile to sweep
+    ("bf16", 128, 256, 1), ("bf16", 128, 256, 15)])
 def test_rf_features(dtype, d, m, rows):
     x = datagen.normal((rows, d), 700 + d + m, 1 / math.sqrt(d) * 1.5, dtype)
     W = datagen.projections(m, d, 800 + m, dtype)
