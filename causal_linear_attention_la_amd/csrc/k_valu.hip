@@ -250,13 +250,29 @@ __global__ __launch_bounds__(NT) void k_out_valu(const T *__restrict__ q, const 
 // -- the chunked evaluation with the whole sequence as its one chunk ("Linear Attention: From
 // Pairwise Reads to a Recurrent State", section "A recurrence need not force token-serial
 // training": the state from before the chunk plus the pairwise reads inside it) -- followed by
-// the final state S0 + phi(K)^T V, z0 + phi(K)^T 1. One workgroup of 256 threads per head:
-// thread (i, part) keeps phi(q_i) in registers and accumulates the value columns
-// [part DV/4, (part + 1) DV/4) of row i, reading each key row from LDS together with the other
-// lanes of its wave (one address: a broadcast). No decay (the decayed form keeps the chunked
-// kernel). Against the chunked kernel there are no per-chunk phases and barriers: B=1 H=1 N=64
-// d=16 float32 takes 9.8 us per call against 13.5 us with four 16-token chunks (MI355X).
+// the final state S0 + phi(K)^T V, z0 + phi(K)^T 1. One workgroup of 256 threads per head,
+// four per row: thread (i, part) keeps phi(q_i) in registers, forms the scores of the keys
+// part, part + 4, ... and accumulates them and their value rows over all value columns, reading
+// each key row from LDS together with the other lanes of its wave; the row's four threads then
+// add their parts by lane exchange and each stores a quarter of the row. No decay (the decayed
+// form keeps the chunked kernel). Against the chunked kernel there are no per-chunk phases and
+// barriers. B=1 H=1 N=64 d=16 float32 on MI355X, per call replayed from a graph: 8.1 us (9.7 us
+// with one thread per (row, quarter of the value columns) forming every score four times and
+// the global loads issued one element per loop step; 13.5 us with four 16-token chunks).
 constexpr int SHORT_N = 64;
+
+// elements e .. e + 3 as float32 (e a multiple of 4 and the row 16-byte aligned: one 16-byte
+// load for float32, one 8-byte load for bf16)
+template <typename T> __device__ __forceinline__ f32x4 ld4(const T *p, size_t e);
+template <> __device__ __forceinline__ f32x4 ld4<float>(const float *p, size_t e)
+{
+    return *reinterpret_cast<const f32x4 *>(p + e);
+}
+template <> __device__ __forceinline__ f32x4 ld4<bf16_t>(const bf16_t *p, size_t e)
+{
+    const u32x2 w = *reinterpret_cast<const u32x2 *>(p + e);
+    return f32x4{bf_lo(w[0]), bf_hi(w[0]), bf_lo(w[1]), bf_hi(w[1])};
+}
 
 template <typename T, int D, int DV>
 __global__ __launch_bounds__(SNT) void k_short(const T *__restrict__ q, const T *__restrict__ k,
@@ -268,25 +284,72 @@ __global__ __launch_bounds__(SNT) void k_short(const T *__restrict__ q, const T 
 {
     static_assert(SNT == 4 * SHORT_N, "one thread per (row, quarter of the value columns)");
     constexpr int CW = DV / 4;
-    __shared__ float sK[SHORT_N][D], sV[SHORT_N][DV], sS[D * DV], sz[D];
+    __shared__ __attribute__((aligned(16))) float sK[SHORT_N][D], sV[SHORT_N][DV], sS[D * DV], sz[D];
     const bool ident = flags & F_IDENTITY, norm = !(flags & F_UNNORM);
     const int tid = threadIdx.x, i = tid >> 2, c0 = (tid & 3) * CW;
     const size_t bh = blockIdx.x;
     const T *qb = q + bh * N * D, *kb = k + bh * N * D, *vb = v + bh * N * DV;
 
-    for (int e = tid; e < N * D; e += SNT)
-        sK[e / D][e % D] = feature(Elem<T>::ld(kb, e), ident);
-    for (int e = tid; e < N * DV; e += SNT)
-        sV[e / DV][e % DV] = Elem<T>::ld(vb, e);
-    for (int e = tid; e < D * DV; e += SNT)
-        sS[e] = S0 ? S0[bh * D * DV + e] : 0.f;
-    for (int f = tid; f < D; f += SNT)
-        sz[f] = S0 ? z0[bh * D + f] : 0.f;
+    // every global load is issued before any of them is used: four consecutive elements per
+    // load, at most two per thread and tensor (the sequence fits one workgroup's pass), then
+    // the thread's query row. Issued one element per loop step, each load waited for its data
+    // before the next left: 9.5 us of kernel time at N = 64, d = 16 float32 (MI355X trace).
+    constexpr int KP = (SHORT_N * D / 4 + SNT - 1) / SNT, VP = (SHORT_N * DV / 4 + SNT - 1) / SNT;
+    constexpr int SP = (D * DV / 4 + SNT - 1) / SNT;
+    f32x4 kr[KP], vr[VP], sr[SP];
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+        const int e = 4 * (tid + u * SNT);
+        if (e < N * D)
+            kr[u] = ld4(kb, e);
+    }
+#pragma unroll
+    for (int u = 0; u < VP; ++u) {
+        const int e = 4 * (tid + u * SNT);
+        if (e < N * DV)
+            vr[u] = ld4(vb, e);
+    }
+#pragma unroll
+    for (int u = 0; u < SP; ++u) {
+        const int e = 4 * (tid + u * SNT);
+        if (e < D * DV)
+            sr[u] = S0 ? *reinterpret_cast<const f32x4 *>(S0 + bh * D * DV + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float zr = tid < D && S0 ? z0[bh * D + tid] : 0.f;
     float qf[D];
     const int ir = min(i, N - 1); // rows past the end compute on the last row and store nothing
 #pragma unroll
-    for (int f = 0; f < D; ++f)
-        qf[f] = feature(Elem<T>::ld(qb, (size_t)ir * D + f), ident);
+    for (int f = 0; f < D; f += 4) {
+        const f32x4 x = ld4(qb, (size_t)ir * D + f);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            qf[f + c] = feature(x[c], ident);
+    }
+    // rows N .. SHORT_N - 1 of both arrays hold zeros, so that the key loops below run over
+    // whole blocks of 16 keys: the extra terms are exact zeros
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+        const int e = 4 * (tid + u * SNT);
+        if (e < SHORT_N * D)
+            *reinterpret_cast<f32x4 *>(&sK[e / D][e % D]) =
+                e < N * D ? f32x4{feature(kr[u][0], ident), feature(kr[u][1], ident),
+                                  feature(kr[u][2], ident), feature(kr[u][3], ident)}
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < VP; ++u) {
+        const int e = 4 * (tid + u * SNT);
+        if (e < SHORT_N * DV)
+            *reinterpret_cast<f32x4 *>(&sV[e / DV][e % DV]) = e < N * DV ? vr[u] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < SP; ++u) {
+        const int e = 4 * (tid + u * SNT);
+        if (e < D * DV)
+            *reinterpret_cast<f32x4 *>(&sS[e]) = sr[u];
+    }
+    if (tid < D)
+        sz[tid] = zr;
     __syncthreads();
 
     // the state before the sequence
@@ -301,10 +364,18 @@ __global__ __launch_bounds__(SNT) void k_short(const T *__restrict__ q, const T 
         for (int c = 0; c < CW; ++c)
             num[c] = fmaf(qf[f], sS[f * DV + c0 + c], num[c]);
     }
-    // the pairs j <= i (keys past the wave's last row add nothing to any of its rows)
+    // the pairs j <= i (keys past the wave's last row add nothing to any of its rows): the
+    // row's four threads (adjacent lanes) take every fourth key each, p, p + 4, ..., over all
+    // value columns, so that each score phi(q_i) . phi(k_j) is formed once; their parts are then
+    // added in a fixed order (lane pairs, then pairs of pairs: every lane holds the same sums)
+    const int part = tid & 3;
     const int jend = min(N, (tid / 64) * 16 + 16);
-#pragma unroll 4
-    for (int j = 0; j < jend; ++j) {
+    float pn[DV], pd = 0.f;
+#pragma unroll
+    for (int c = 0; c < DV; ++c)
+        pn[c] = 0.f;
+#pragma unroll 2
+    for (int j = part; j < jend; j += 4) {
         float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int f = 0; f < D; f += 2) {
@@ -312,27 +383,44 @@ __global__ __launch_bounds__(SNT) void k_short(const T *__restrict__ q, const T 
             a1 = fmaf(qf[f + 1], sK[j][f + 1], a1);
         }
         const float a = j <= i ? a0 + a1 : 0.f;
-        den += a;
+        pd += a;
 #pragma unroll
-        for (int c = 0; c < CW; ++c)
-            num[c] = fmaf(a, sV[j][c0 + c], num[c]);
+        for (int c = 0; c < DV; ++c)
+            pn[c] = fmaf(a, sV[j][c], pn[c]);
     }
+    pd += __shfl_xor(pd, 1, 64);
+    pd += __shfl_xor(pd, 2, 64);
+    den += pd;
+#pragma unroll
+    for (int c = 0; c < DV; ++c) {
+        pn[c] += __shfl_xor(pn[c], 1, 64);
+        pn[c] += __shfl_xor(pn[c], 2, 64);
+    }
+    // this thread's value columns c0 .. c0 + CW - 1 (selected without indexing registers)
+#pragma unroll
+    for (int c = 0; c < CW; ++c)
+        num[c] += part == 0 ? pn[c] : part == 1 ? pn[CW + c] : part == 2 ? pn[2 * CW + c] : pn[3 * CW + c];
     if (i < N)
 #pragma unroll
         for (int c = 0; c < CW; ++c)
             Elem<T>::st(out, (bh * N + i) * DV + c0 + c, norm ? num[c] / den : num[c]);
     if (Sout) {
+        const int n16 = (N + 15) & ~15;
         for (int e = tid; e < D * DV; e += SNT) {
             const int f = e / DV, c = e % DV;
             float s = sS[e];
-            for (int j = 0; j < N; ++j)
-                s = fmaf(sK[j][f], sV[j][c], s);
+            for (int j0 = 0; j0 < n16; j0 += 16)
+#pragma unroll
+                for (int j = j0; j < j0 + 16; ++j)
+                    s = fmaf(sK[j][f], sV[j][c], s);
             Sout[bh * D * DV + e] = s;
         }
         for (int f = tid; f < D; f += SNT) {
             float s = sz[f];
-            for (int j = 0; j < N; ++j)
-                s += sK[j][f];
+            for (int j0 = 0; j0 < n16; j0 += 16)
+#pragma unroll
+                for (int j = j0; j < j0 + 16; ++j)
+                    s += sK[j][f];
             zout[bh * D + f] = s;
         }
     }
