@@ -282,7 +282,7 @@ __global__ __launch_bounds__(SNT) void k_short(const T *__restrict__ q, const T 
                                               float *__restrict__ Sout, float *__restrict__ zout,
                                               int N, int flags)
 {
-    static_assert(SNT == 4 * SHORT_N, "one thread per (row, quarter of the value columns)");
+    static_assert(SNT == 4 * SHORT_N, "four threads per row");
     constexpr int CW = DV / 4;
     __shared__ __attribute__((aligned(16))) float sK[SHORT_N][D], sV[SHORT_N][DV], sS[D * DV], sz[D];
     const bool ident = flags & F_IDENTITY, norm = !(flags & F_UNNORM);
@@ -325,8 +325,8 @@ __global__ __launch_bounds__(SNT) void k_short(const T *__restrict__ q, const T 
         for (int c = 0; c < 4; ++c)
             qf[f + c] = feature(x[c], ident);
     }
-    // rows N .. SHORT_N - 1 of both arrays hold zeros, so that the key loops below run over
-    // whole blocks of 16 keys: the extra terms are exact zeros
+    // rows N .. SHORT_N - 1 of both arrays hold zeros, so that the final-state sums below run
+    // over whole blocks of 16 keys: the extra terms are exact zeros
 #pragma unroll
     for (int u = 0; u < KP; ++u) {
         const int e = 4 * (tid + u * SNT);
