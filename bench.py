@@ -460,9 +460,20 @@ def _median_runs(fn, seconds, at_least=3):
     return statistics.median(times), len(times)
 
 
+def _single_thread(fn, seconds, at_least=2):
+    """_median_runs of fn with the oracle on one host thread."""
+    import oracle
+
+    prev = oracle.set_threads(1)
+    try:
+        return _median_runs(fn, seconds, at_least)
+    finally:
+        oracle.set_threads(prev)
+
+
 def cpu_baseline_causal(n, seconds=5.0):
     """The float64 oracle, as it stands, on causal workload n (the whole workload), on all host
-    threads: median of repeated runs."""
+    threads: median of repeated runs; and on at most 4 of its heads on one thread."""
     import datagen
     import oracle
 
@@ -470,10 +481,15 @@ def cpu_baseline_causal(n, seconds=5.0):
     q, k, v = (datagen.to_f64(x) for x in datagen.qkv(w.B, w.H, w.N, w.d, w.dv, w.seed, w.scale,
                                                        w.dtype))
     t, runs = _median_runs(lambda: oracle.causal(q, k, v), seconds)
+    h1 = min(4, w.H)
+    t1, runs1 = _single_thread(lambda: oracle.causal(q[:1, :h1], k[:1, :h1], v[:1, :h1]), seconds / 2)
     return {"value": w.B * w.H * w.N / t, "unit": "tokens/s (B*H*N/s)", "cores": oracle.threads(),
             "kind": "oracle", "us_per_call": t * 1e6,
             "sample": f"{w.name}, the whole workload, float64 token-serial recurrence, median of "
-                      f"{runs} runs of {t * 1e3:.2f} ms"}
+                      f"{runs} runs of {t * 1e3:.2f} ms",
+            "single_thread": {"value": h1 * w.N / t1, "unit": "tokens/s (B*H*N/s)", "cores": 1,
+                              "sample": f"{h1} of the {w.B * w.H} heads, median of {runs1} runs of "
+                                        f"{t1 * 1e3:.2f} ms"}}
 
 
 def cpu_baseline_global(seconds=10.0):
@@ -486,11 +502,15 @@ def cpu_baseline_global(seconds=10.0):
     q, k, v = (datagen.to_f64(x) for x in datagen.qkv_cuda(w.B, w.H, w.N, w.d, w.dv, w.seed,
                                                             w.scale, "bf16"))
     t, runs = _median_runs(lambda: oracle.global_(q, k, v), seconds, at_least=2)
+    t1, runs1 = _single_thread(lambda: oracle.global_(q[:1, :1], k[:1, :1], v[:1, :1]), seconds / 2)
     return {"value": w.B * w.H * w.N / t, "unit": "tokens/s (B*H*N/s)", "cores": oracle.threads(),
             "kind": "oracle", "us_per_call": t * 1e6,
             "sample": f"{w.name}, the whole workload (inputs drawn on the device as the GPU leg "
                       f"does), float64, median of {runs} runs of {t:.2f} s; 8 heads, so at most 8 "
-                      "threads have work"}
+                      "threads have work",
+            "single_thread": {"value": w.N / t1, "unit": "tokens/s (B*H*N/s)", "cores": 1,
+                              "sample": f"1 of the {w.B * w.H} heads, median of {runs1} runs of "
+                                        f"{t1:.2f} s"}}
 
 
 def cpu_baseline_decode(seconds=10.0):
@@ -514,10 +534,26 @@ def cpu_baseline_decode(seconds=10.0):
             _, Sc, zc = oracle.decode_step(toks[0][t], toks[1][t], toks[2][t], Sc, zc)
 
     t, runs = _median_runs(run, seconds, at_least=2)
+    # one thread: the same steps over the first 16 of the 256 batch entries (512 heads), scaled
+    # to all heads
+    b1 = 16
+    sub = {"S": state["S"][:b1], "z": state["z"][:b1]}
+
+    def run1():
+        Sc, zc = sub["S"], sub["z"]
+        for t_ in range(nsteps):
+            _, Sc, zc = oracle.decode_step(toks[0][t_][:b1], toks[1][t_][:b1], toks[2][t_][:b1], Sc, zc)
+
+    t1, runs1 = _single_thread(run1, seconds / 3)
+    scale = w.B / b1
     return {"value": nsteps / t, "unit": "decode steps/s (all 8192 heads per step)",
             "cores": oracle.threads(), "kind": "oracle", "us_per_step": t / nsteps * 1e6,
             "sample": f"{nsteps} consecutive decode steps of {w.name} from a seeded synthetic "
-                      f"float64 state, median of {runs} runs of {t:.2f} s"}
+                      f"float64 state, median of {runs} runs of {t:.2f} s",
+            "single_thread": {"value": nsteps / (t1 * scale),
+                              "unit": "decode steps/s (all 8192 heads per step)", "cores": 1,
+                              "sample": f"{nsteps} steps over {b1 * w.H} of the {w.B * w.H} heads, "
+                                        f"median of {runs1} runs of {t1:.2f} s, scaled by {scale:g}"}}
 
 
 def cpu_baseline():
@@ -789,7 +825,12 @@ def main():
                    "steps": args.decode_steps},
         "global": {"workload": wg.name, "us_per_call": ms_g * 1e3,
                    "token_heads_per_s": wg.B * wg.H * wg.N / (ms_g * 1e-3),
-                   "hbm_frac": byts_g / (ms_g * 1e-3) / HBM_PEAK},
+                   "hbm_frac": byts_g / (ms_g * 1e-3) / HBM_PEAK,
+                   "copy_GBps": copy_bw / 1e9, "frac_of_copy": byts_g / (ms_g * 1e-3) / copy_bw,
+                   # the algorithmic flops of the two passes: 4 d d_v + 3 d + d_v per token-head
+                   "mfma": {"algorithmic_frac": wg.B * wg.H * wg.N * (4 * wg.d * wg.dv + 3 * wg.d + wg.dv)
+                            / (ms_g * 1e-3) / BF16_PEAK,
+                            "busy_profile": "profiles/global_b1h8n100000_d128_mfma_busy.txt"}},
         "favor": {"workload": favor_name(), "m": m_f,
                   "us_per_step": ms_f * 1e3,
                   "token_heads_per_s": wf.B * wf.H * wf.N / (ms_f * 1e-3),
