@@ -169,6 +169,18 @@ def test_workload4_global_full():
     check("z", z[..., None], zo[..., None], TOL["bf16"])
 
 
+def test_global_d64_many_segments():
+    """The d = 64 global form with several segments per head (segment sums, their total) and the
+    read's own split of the sequence, with a ragged tail: every output row against the oracle."""
+    q, k, v = datagen.qkv(2, 4, 20011, 64, 64, 4242, 1 / 8, "bf16")
+    say("global d=64 B=2 H=4 N=20011")
+    o, S, z = global_(q, k, v)
+    oo, So, zo, _, _ = oracle.global_(f64(q), f64(k), f64(v))
+    check("out", o, oo, TOL["bf16"])
+    check("S", S, So, TOL["bf16"])
+    check("z", z[..., None], zo[..., None], TOL["bf16"])
+
+
 def _decode_run(B, H, d, prior, steps, seed):
     """Seeded prior tokens -> oracle state (float64, rounded to float32) -> `steps` decode
     steps on the GPU and in the oracle."""
