@@ -38,6 +38,7 @@ or streams). ``hip_runtimes()`` lists the HIP runtime copies mapped into the pro
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from pathlib import Path
 
@@ -145,11 +146,19 @@ def _dtype_code(t):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # (ctypes takes a plain int for a void * argument)
+    return None if t is None else t.data_ptr()
+
+
+# the raw handle of a device's current stream: torch's own accessor where it has one (no Stream
+# object per call: a few microseconds of host time on small calls), else the public one
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(t):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _check_tensors(*ts):
@@ -183,7 +192,7 @@ def _expect(name, t, shape, dtype):
     end."""
     if t is None:
         return
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
@@ -429,6 +438,8 @@ def la_segments(form: int, B: int, H: int, N: int, d: int, d_v: int, chunk: int 
     return int(lib.la_segments(form, B, H, N, d, d_v, chunk, seg_len, dtype))
 
 
+@functools.lru_cache(maxsize=1024)
 def la_workspace_bytes(form: int, B: int, H: int, N: int, d: int, d_v: int, chunk: int = 0,
                        seg_len: int = 0, dtype: int = LA_BF16) -> int:
+    # a function of its arguments alone, so it is asked of the library once per shape
     return int(lib.la_workspace_bytes(form, B, H, N, d, d_v, chunk, seg_len, dtype))
